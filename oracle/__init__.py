@@ -1,0 +1,251 @@
+"""CPU oracle of the Bi-Level Routing Attention forward pass (fp64, plain C).
+
+TEST INFRASTRUCTURE ONLY.  The tests, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this package; the product
+package never does, and shares no code with it.
+
+This module is the ctypes front of ``liboracle.so`` (built from
+``bra_oracle.c`` by ``oracle.build.build_oracle``).  Every array argument is
+converted to a C-contiguous float64 (or int32) numpy copy; the functions
+return new numpy arrays.  Layouts are those of ``bra_oracle.h``:
+q/k/v/out ``[B, H, W, C]``, means ``[B, heads, R, head_dim]``, affinity
+``[B, heads, R, R]``, routing ``[B, heads, R, k]`` (int32), LePE weight
+``[C, 5, 5]`` and bias ``[C]``.
+
+``OracleLib(path)`` wraps one build of the library (the tests also load
+deliberately broken builds through it, to show that the pins catch them); the
+module-level functions use the default build.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import numpy as np
+
+from .build import LIB_PATH, build_oracle
+
+__all__ = [
+    "OracleConfig", "OracleLib", "topk_effective", "region_means", "route", "attend", "lepe",
+    "attend_with_routing", "bra_forward", "num_threads", "default",
+]
+
+
+class _Cfg(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("height", ctypes.c_int32), ("width", ctypes.c_int32),
+        ("channels", ctypes.c_int32), ("num_heads", ctypes.c_int32),
+        ("n_win", ctypes.c_int32), ("topk", ctypes.c_int32), ("scale", ctypes.c_double),
+    ]
+
+
+@dataclass(frozen=True)
+class OracleConfig:
+    batch: int
+    height: int
+    width: int
+    channels: int
+    num_heads: int
+    n_win: int
+    topk: int
+    scale: float = 0.0  # <= 0: head_dim ** -0.5
+
+    @property
+    def head_dim(self) -> int:
+        return self.channels // self.num_heads
+
+    @property
+    def regions(self) -> int:
+        return self.n_win * self.n_win
+
+    def _c(self) -> _Cfg:
+        return _Cfg(self.batch, self.height, self.width, self.channels, self.num_heads,
+                    self.n_win, self.topk, float(self.scale))
+
+
+_DP = ctypes.POINTER(ctypes.c_double)
+_IP = ctypes.POINTER(ctypes.c_int32)
+
+
+def _f64(a):
+    if a is None:
+        return None, None
+    arr = np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+    return arr, arr.ctypes.data_as(_DP)
+
+
+def _i32(a):
+    arr = np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+    return arr, arr.ctypes.data_as(_IP)
+
+
+def _ptr(a):
+    return a.ctypes.data_as(_DP) if a is not None else None
+
+
+def _check(rc, what):
+    if rc != 0:
+        raise ValueError(f"oracle: {what} rejected the configuration")
+
+
+def _map_shape(cfg: OracleConfig):
+    return (cfg.batch, cfg.height, cfg.width, cfg.channels)
+
+
+def _bar_shape(cfg: OracleConfig):
+    return (cfg.batch, cfg.num_heads, cfg.regions, cfg.head_dim)
+
+
+class OracleLib:
+    """One loaded build of liboracle.so."""
+
+    def __init__(self, path: str):
+        lib = ctypes.CDLL(path)
+        cp = ctypes.POINTER(_Cfg)
+        lib.oracle_topk_effective.argtypes = [cp]
+        lib.oracle_topk_effective.restype = ctypes.c_int32
+        lib.oracle_region_means.argtypes = [cp, _DP, _DP]
+        lib.oracle_route.argtypes = [cp, _DP, _DP, _DP, _IP]
+        lib.oracle_attend.argtypes = [cp, _DP, _DP, _DP, _IP, _DP]
+        lib.oracle_lepe.argtypes = [cp, _DP, _DP, _DP, _DP]
+        lib.oracle_attend_with_routing.argtypes = [cp, _DP, _DP, _DP, _DP, _DP, _IP, _DP]
+        lib.oracle_bra_forward.argtypes = [cp, _DP, _DP, _DP, _DP, _DP, _DP, _IP, _DP, _DP,
+                                           _DP]
+        lib.oracle_num_threads.argtypes = []
+        for name in ("oracle_region_means", "oracle_route", "oracle_attend", "oracle_lepe",
+                     "oracle_attend_with_routing", "oracle_bra_forward",
+                     "oracle_num_threads"):
+            getattr(lib, name).restype = ctypes.c_int
+        self.lib = lib
+        self.path = path
+
+    def topk_effective(self, cfg: OracleConfig) -> int:
+        c = cfg._c()
+        return int(self.lib.oracle_topk_effective(ctypes.byref(c)))
+
+    def num_threads(self) -> int:
+        return int(self.lib.oracle_num_threads())
+
+    def region_means(self, cfg: OracleConfig, x) -> np.ndarray:
+        c = cfg._c()
+        xa, xp = _f64(x)
+        out = np.empty(_bar_shape(cfg), np.float64)
+        _check(self.lib.oracle_region_means(ctypes.byref(c), xp, _ptr(out)), "region_means")
+        return out
+
+    def route(self, cfg: OracleConfig, qbar, kbar, want_aff: bool = False):
+        """Return idx [B,h,R,k] (and the affinity [B,h,R,R] if want_aff)."""
+        c = cfg._c()
+        qa, qp = _f64(qbar)
+        ka, kp = _f64(kbar)
+        k = self.topk_effective(cfg)
+        idx = np.empty((cfg.batch, cfg.num_heads, cfg.regions, k), np.int32)
+        aff = np.empty((cfg.batch, cfg.num_heads, cfg.regions, cfg.regions), np.float64) \
+            if want_aff else None
+        _check(self.lib.oracle_route(ctypes.byref(c), qp, kp, _ptr(aff),
+                                     idx.ctypes.data_as(_IP)), "route")
+        return (idx, aff) if want_aff else idx
+
+    def attend(self, cfg: OracleConfig, q, k, v, idx) -> np.ndarray:
+        c = cfg._c()
+        qa, qp = _f64(q)
+        ka, kp = _f64(k)
+        va, vp = _f64(v)
+        ia, ip = _i32(idx)
+        out = np.empty(_map_shape(cfg), np.float64)
+        _check(self.lib.oracle_attend(ctypes.byref(c), qp, kp, vp, ip, _ptr(out)), "attend")
+        return out
+
+    def lepe(self, cfg: OracleConfig, v, w, b=None) -> np.ndarray:
+        c = cfg._c()
+        va, vp = _f64(v)
+        wa, wp = _f64(w)
+        ba, bp = _f64(b)
+        out = np.empty(_map_shape(cfg), np.float64)
+        _check(self.lib.oracle_lepe(ctypes.byref(c), vp, wp, bp, _ptr(out)), "lepe")
+        return out
+
+    def attend_with_routing(self, cfg: OracleConfig, q, k, v, w, b, idx) -> np.ndarray:
+        c = cfg._c()
+        qa, qp = _f64(q)
+        ka, kp = _f64(k)
+        va, vp = _f64(v)
+        wa, wp = _f64(w)
+        ba, bp = _f64(b)
+        ia, ip = _i32(idx)
+        out = np.empty(_map_shape(cfg), np.float64)
+        _check(self.lib.oracle_attend_with_routing(ctypes.byref(c), qp, kp, vp, wp, bp, ip,
+                                                   _ptr(out)), "attend_with_routing")
+        return out
+
+    def bra_forward(self, cfg: OracleConfig, q, k, v, w=None, b=None, *, want_aff=False,
+                    want_means=False):
+        """Whole forward; returns a dict with 'out', 'idx' (+ 'aff', 'qbar', 'kbar')."""
+        c = cfg._c()
+        qa, qp = _f64(q)
+        ka, kp = _f64(k)
+        va, vp = _f64(v)
+        wa, wp = _f64(w)
+        ba, bp = _f64(b)
+        kk = self.topk_effective(cfg)
+        out = np.empty(_map_shape(cfg), np.float64)
+        idx = np.empty((cfg.batch, cfg.num_heads, cfg.regions, kk), np.int32)
+        aff = np.empty((cfg.batch, cfg.num_heads, cfg.regions, cfg.regions), np.float64) \
+            if want_aff else None
+        qbar = np.empty(_bar_shape(cfg), np.float64) if want_means else None
+        kbar = np.empty(_bar_shape(cfg), np.float64) if want_means else None
+        _check(self.lib.oracle_bra_forward(ctypes.byref(c), qp, kp, vp, wp, bp, _ptr(out),
+                                           idx.ctypes.data_as(_IP), _ptr(aff), _ptr(qbar),
+                                           _ptr(kbar)), "bra_forward")
+        res = {"out": out, "idx": idx}
+        if want_aff:
+            res["aff"] = aff
+        if want_means:
+            res["qbar"], res["kbar"] = qbar, kbar
+        return res
+
+
+_default = None
+
+
+def default() -> OracleLib:
+    """The default build, compiled first only if it is not there yet."""
+    global _default
+    if _default is None:
+        if not os.path.exists(LIB_PATH):
+            build_oracle()
+        _default = OracleLib(LIB_PATH)
+    return _default
+
+
+def topk_effective(cfg):
+    return default().topk_effective(cfg)
+
+
+def num_threads():
+    return default().num_threads()
+
+
+def region_means(cfg, x):
+    return default().region_means(cfg, x)
+
+
+def route(cfg, qbar, kbar, want_aff=False):
+    return default().route(cfg, qbar, kbar, want_aff)
+
+
+def attend(cfg, q, k, v, idx):
+    return default().attend(cfg, q, k, v, idx)
+
+
+def lepe(cfg, v, w, b=None):
+    return default().lepe(cfg, v, w, b)
+
+
+def attend_with_routing(cfg, q, k, v, w, b, idx):
+    return default().attend_with_routing(cfg, q, k, v, w, b, idx)
+
+
+def bra_forward(cfg, q, k, v, w=None, b=None, *, want_aff=False, want_means=False):
+    return default().bra_forward(cfg, q, k, v, w, b, want_aff=want_aff, want_means=want_means)

@@ -1,0 +1,255 @@
+/*
+ * bra_oracle.c -- plain, slow, fp64 CPU oracle of the BRA forward pass.
+ * TEST INFRASTRUCTURE ONLY (tests, smoke check, CPU-baseline timing).
+ * Page keys [P1]..[P5] are listed in bra_oracle.h.
+ *
+ * The method is its own definition here (a sparse attention whose result is
+ * this algorithm, not an approximation of something simpler), so the code
+ * takes the steps in the order the pages give them:
+ *   1. split the map into n_win x n_win square windows      [P3 §1; P4 §1.1]
+ *   2. mean of Q and of K over each window, per head         [P4 §1.2; P5 §五 ③]
+ *   3. region affinity Qbar . Kbar                           [P4 §1.2; P5 §五 ③]
+ *   4. keep the k largest per row (torch.topk semantics,
+ *      exact ties to the lower region id)                    [P1 §2.1; P5 §五 ④]
+ *   5. softmax attention of each token over the tokens of
+ *      its k routed windows, scale head_dim^-0.5             [P3 §2.2; P5 §五 ⑤-⑦]
+ *   6. + depthwise 5x5 convolution of V (LePE), zero pad 2   [P5 §五 lepe, ⑧; P2 §2.2]
+ * Built with -O2 -fopenmp -ffp-contract=off and no fast-math.
+ */
+#include "bra_oracle.h"
+
+#include <math.h>
+#include <stddef.h>
+#include <stdlib.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* ---- shape helpers ------------------------------------------------------ */
+
+static int cfg_ok(const oracle_cfg_t* c) {
+    if (!c) return 0;
+    if (c->batch <= 0 || c->height <= 0 || c->width <= 0 || c->channels <= 0 ||
+        c->num_heads <= 0 || c->n_win <= 0)
+        return 0;
+    if (c->height % c->n_win != 0 || c->width % c->n_win != 0) return 0;
+    if (c->channels % c->num_heads != 0) return 0;
+    return 1;
+}
+
+int32_t oracle_topk_effective(const oracle_cfg_t* c) {
+    int32_t R = c->n_win * c->n_win;
+    if (c->topk <= 0 || c->topk > R) return R;
+    return c->topk;
+}
+
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* Index of element (b, y, x, ch) of a [B, H, W, C] map. */
+static size_t at(const oracle_cfg_t* c, int b, int y, int x, int ch) {
+    return (((size_t)b * c->height + y) * c->width + x) * c->channels + ch;
+}
+
+/* Map coordinates of slot `slot` of region `r` (window row-major inside). */
+static void region_slot_yx(const oracle_cfg_t* c, int r, int slot, int* y, int* x) {
+    int hs = c->height / c->n_win, ws = c->width / c->n_win;
+    int ri = r / c->n_win, rj = r % c->n_win;
+    *y = ri * hs + slot / ws;
+    *x = rj * ws + slot % ws;
+}
+
+/* ---- step 2: region means ----------------------------------------------- */
+
+int oracle_region_means(const oracle_cfg_t* c, const double* x, double* xbar) {
+    if (!cfg_ok(c) || !x || !xbar) return -1;
+    const int hd = c->channels / c->num_heads;
+    const int R = c->n_win * c->n_win;
+    const int t = (c->height / c->n_win) * (c->width / c->n_win);
+    const int nitems = c->batch * c->num_heads * R;
+#pragma omp parallel for schedule(static)
+    for (int item = 0; item < nitems; ++item) {
+        int r = item % R;
+        int h = (item / R) % c->num_heads;
+        int b = item / (R * c->num_heads);
+        for (int d = 0; d < hd; ++d) {
+            double s = 0.0;
+            for (int slot = 0; slot < t; ++slot) {
+                int y, xx;
+                region_slot_yx(c, r, slot, &y, &xx);
+                s += x[at(c, b, y, xx, h * hd + d)];
+            }
+            xbar[(size_t)item * hd + d] = s / (double)t;
+        }
+    }
+    return 0;
+}
+
+/* ---- steps 3-4: affinity and top-k -------------------------------------- */
+
+int oracle_route(const oracle_cfg_t* c, const double* qbar, const double* kbar,
+                 double* aff, int32_t* idx) {
+    if (!cfg_ok(c) || !qbar || !kbar || !idx) return -1;
+    const int hd = c->channels / c->num_heads;
+    const int R = c->n_win * c->n_win;
+    const int k = oracle_topk_effective(c);
+    const int nrows = c->batch * c->num_heads * R;
+#pragma omp parallel
+    {
+        double* row = (double*)malloc(sizeof(double) * (size_t)R);
+        unsigned char* taken = (unsigned char*)malloc((size_t)R);
+#pragma omp for schedule(static)
+        for (int rowid = 0; rowid < nrows; ++rowid) {
+            int bh = rowid / R; /* (b, h) pair */
+            const double* qr = qbar + (size_t)rowid * hd;
+            for (int s = 0; s < R; ++s) {
+                const double* ks = kbar + ((size_t)bh * R + s) * hd;
+                double a = 0.0;
+                for (int d = 0; d < hd; ++d) a += qr[d] * ks[d];
+                row[s] = a;
+                taken[s] = 0;
+                if (aff) aff[(size_t)rowid * R + s] = a;
+            }
+            /* k passes; each keeps the largest untaken entry.  Strict '>'
+             * while scanning upward leaves an exact tie with the lower id. */
+            for (int j = 0; j < k; ++j) {
+                int best = -1;
+                for (int s = 0; s < R; ++s) {
+                    if (taken[s]) continue;
+                    if (best < 0 || row[s] > row[best]) best = s;
+                }
+                taken[best] = 1;
+                idx[(size_t)rowid * k + j] = best;
+            }
+        }
+        free(row);
+        free(taken);
+    }
+    return 0;
+}
+
+/* ---- step 5: token attention over the routed windows -------------------- */
+
+int oracle_attend(const oracle_cfg_t* c, const double* q, const double* kk,
+                  const double* v, const int32_t* idx, double* o) {
+    if (!cfg_ok(c) || !q || !kk || !v || !idx || !o) return -1;
+    const int hd = c->channels / c->num_heads;
+    const int R = c->n_win * c->n_win;
+    const int t = (c->height / c->n_win) * (c->width / c->n_win);
+    const int k = oracle_topk_effective(c);
+    const int nkeys = k * t;
+    const double scale = c->scale > 0.0 ? c->scale : 1.0 / sqrt((double)hd);
+    const int nitems = c->batch * c->num_heads * R;
+#pragma omp parallel
+    {
+        double* logit = (double*)malloc(sizeof(double) * (size_t)nkeys);
+        size_t* key_at = (size_t*)malloc(sizeof(size_t) * (size_t)nkeys);
+        double* acc = (double*)malloc(sizeof(double) * (size_t)hd);
+#pragma omp for schedule(static)
+        for (int item = 0; item < nitems; ++item) {
+            int r = item % R;
+            int h = (item / R) % c->num_heads;
+            int b = item / (R * c->num_heads);
+            const int32_t* routed = idx + (size_t)item * k;
+            /* The gathered key list: routed window j, then its slots in order. */
+            for (int j = 0; j < k; ++j)
+                for (int slot = 0; slot < t; ++slot) {
+                    int y, x;
+                    region_slot_yx(c, routed[j], slot, &y, &x);
+                    key_at[j * t + slot] = at(c, b, y, x, h * hd);
+                }
+            for (int qslot = 0; qslot < t; ++qslot) {
+                int qy, qx;
+                region_slot_yx(c, r, qslot, &qy, &qx);
+                const double* qv = q + at(c, b, qy, qx, h * hd);
+                double mx = -INFINITY;
+                for (int m = 0; m < nkeys; ++m) {
+                    const double* kv = kk + key_at[m];
+                    double dot = 0.0;
+                    for (int d = 0; d < hd; ++d) dot += qv[d] * kv[d];
+                    logit[m] = scale * dot;
+                    if (logit[m] > mx) mx = logit[m];
+                }
+                double denom = 0.0;
+                for (int d = 0; d < hd; ++d) acc[d] = 0.0;
+                for (int m = 0; m < nkeys; ++m) {
+                    double w = exp(logit[m] - mx);
+                    denom += w;
+                    const double* vv = v + key_at[m];
+                    for (int d = 0; d < hd; ++d) acc[d] += w * vv[d];
+                }
+                double* ov = o + at(c, b, qy, qx, h * hd);
+                for (int d = 0; d < hd; ++d) ov[d] = acc[d] / denom;
+            }
+        }
+        free(logit);
+        free(key_at);
+        free(acc);
+    }
+    return 0;
+}
+
+/* ---- step 6: LePE -------------------------------------------------------- */
+
+int oracle_lepe(const oracle_cfg_t* c, const double* v, const double* w,
+                const double* bias, double* L) {
+    if (!cfg_ok(c) || !v || !w || !L) return -1;
+    const int H = c->height, W = c->width, C = c->channels;
+    const int nrows = c->batch * H;
+#pragma omp parallel for schedule(static)
+    for (int row = 0; row < nrows; ++row) {
+        int b = row / H, y = row % H;
+        for (int x = 0; x < W; ++x)
+            for (int ch = 0; ch < C; ++ch) {
+                double s = bias ? bias[ch] : 0.0;
+                for (int i = 0; i < 5; ++i)
+                    for (int j = 0; j < 5; ++j) {
+                        int yy = y + i - 2, xx = x + j - 2;
+                        if (yy < 0 || yy >= H || xx < 0 || xx >= W) continue; /* zero pad */
+                        s += w[(size_t)ch * 25 + i * 5 + j] * v[at(c, b, yy, xx, ch)];
+                    }
+                L[at(c, b, y, x, ch)] = s;
+            }
+    }
+    return 0;
+}
+
+/* ---- composition ---------------------------------------------------------- */
+
+int oracle_attend_with_routing(const oracle_cfg_t* c, const double* q, const double* k,
+                               const double* v, const double* w, const double* bias,
+                               const int32_t* idx, double* out) {
+    if (!cfg_ok(c) || !out) return -1;
+    if (oracle_attend(c, q, k, v, idx, out) != 0) return -1;
+    if (!w) return 0;
+    size_t n = (size_t)c->batch * c->height * c->width * c->channels;
+    double* L = (double*)malloc(sizeof(double) * n);
+    if (!L) return -1;
+    int rc = oracle_lepe(c, v, w, bias, L);
+    if (rc == 0)
+        for (size_t i = 0; i < n; ++i) out[i] = out[i] + L[i];
+    free(L);
+    return rc;
+}
+
+int oracle_bra_forward(const oracle_cfg_t* c, const double* q, const double* k,
+                       const double* v, const double* w, const double* bias, double* out,
+                       int32_t* idx, double* aff, double* qbar, double* kbar) {
+    if (!cfg_ok(c) || !q || !k || !v || !out || !idx) return -1;
+    const int hd = c->channels / c->num_heads;
+    const size_t nbar = (size_t)c->batch * c->num_heads * c->n_win * c->n_win * hd;
+    double* qb = qbar ? qbar : (double*)malloc(sizeof(double) * nbar);
+    double* kb = kbar ? kbar : (double*)malloc(sizeof(double) * nbar);
+    int rc = -1;
+    if (qb && kb && oracle_region_means(c, q, qb) == 0 && oracle_region_means(c, k, kb) == 0 &&
+        oracle_route(c, qb, kb, aff, idx) == 0)
+        rc = oracle_attend_with_routing(c, q, k, v, w, bias, idx, out);
+    if (!qbar) free(qb);
+    if (!kbar) free(kb);
+    return rc;
+}

@@ -1,0 +1,98 @@
+/*
+ * bra_oracle.h -- plain CPU oracle for the Bi-Level Routing Attention (BRA)
+ * forward pass.  TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the
+ * CPU-baseline leg of the benchmark call it; the product path never does.
+ * It shares no code, header, table or helper with the HIP library.
+ *
+ * Sources (web pages; cited below by key and section):
+ *   [P1] "从静态到动态：Bi-Level Routing Attention如何重塑视觉Transformer的注意力机制",
+ *        www.mhpn.cn/news/199372
+ *   [P2] "BiFormer用双层路由注意力重塑视觉Transformer效率极限", www.mooersco.com/news/894234
+ *   [P3] "从零构建BiFormer：PyTorch实战双层路由注意力机制与调试全攻略",
+ *        www.mhpn.cn/news/564882
+ *   [P4] "手把手解析BiFormer：双水平路由注意力机制与PyTorch实战指南", www.jsqmd.com/news/719213
+ *   [P5] "【医学图像分割模块】BiFormer / 双层路由注意力（CVPR 2023）", www.mhpn.cn/news/2512273
+ *
+ * Every floating-point value is an IEEE double; every sum is a plain
+ * left-to-right loop (the library is compiled with -ffp-contract=off, so a
+ * product is rounded before it is added).
+ *
+ * Tensor layouts (all row-major, host memory, owned by the caller):
+ *   q, k, v, out, o, lepe_out : [B, H, W, C]      C = heads * head_dim,
+ *                                                 channel of (head h, dim d) = h*head_dim + d
+ *   qbar, kbar                : [B, heads, R, head_dim]   R = n_win^2
+ *   aff                       : [B, heads, R, R]
+ *   idx                       : [B, heads, R, k_eff]      int32 region ids
+ *   lepe_w                    : [C, 5, 5]  (a depthwise Conv2d weight [C,1,5,5])
+ *   lepe_b                    : [C]
+ * Region r = i*n_win + j covers rows i*hs .. i*hs+hs-1 and columns
+ * j*ws .. j*ws+ws-1 (hs = H/n_win, ws = W/n_win); its t = hs*ws tokens are
+ * numbered in row-major order inside the window ("slot" u*ws + w).
+ *
+ * Every function returns 0 on success and -1 on an invalid configuration
+ * (non-positive sizes, H or W not divisible by n_win, C not divisible by
+ * heads).  Nothing is allocated that outlives a call.
+ *
+ * parity: every function is pinned by the CPU tests (dense-attention special
+ * case, constant inputs, brute-force argsort routing, forced ties, LePE versus
+ * a library convolution and its impulse response, an independent PyTorch
+ * formulation); see the tests for the list.
+ */
+#ifndef BRA_ORACLE_H
+#define BRA_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct {
+    int32_t batch, height, width, channels, num_heads;
+    int32_t n_win; /* regions per side */
+    int32_t topk;  /* <= 0 or > n_win^2 means all regions */
+    double scale;  /* <= 0 means head_dim^-0.5 */
+} oracle_cfg_t;
+
+/* k actually used: min(topk, R), with topk <= 0 meaning R.
+ * [P5 §五 step ④ clamps with min(topk, n*n); P2 §3.1 uses -1 for "all"] */
+int32_t oracle_topk_effective(const oracle_cfg_t* cfg);
+
+/* Region mean of one projected tensor, per head.  [P4 §1.2 step 1; P2 §2.1] */
+int oracle_region_means(const oracle_cfg_t* cfg, const double* x, double* xbar);
+
+/* Region affinity A = Qbar Kbar^T per (batch, head) and the top-k selection,
+ * descending affinity, exact ties to the lower region id.  aff may be NULL.
+ * [P4 §1.2 steps 2-3; P1 §2.1 TopkRouting; P5 §五 steps ③-④] */
+int oracle_route(const oracle_cfg_t* cfg, const double* qbar, const double* kbar,
+                 double* aff, int32_t* idx);
+
+/* Token-to-token attention of every token over the tokens of its k routed
+ * regions (idx as produced by oracle_route, any order).  o excludes LePE.
+ * [P3 §2.2 TokenAttention; P5 §五 steps ⑤-⑦] */
+int oracle_attend(const oracle_cfg_t* cfg, const double* q, const double* k,
+                  const double* v, const int32_t* idx, double* o);
+
+/* LePE: 5x5 depthwise convolution of V, zero padding 2, plus bias.
+ * lepe_b may be NULL (zero bias).  [P5 §五 self.lepe and step ⑧; P2 §2.2] */
+int oracle_lepe(const oracle_cfg_t* cfg, const double* v, const double* lepe_w,
+                const double* lepe_b, double* lepe_out);
+
+/* attend + LePE with a given routing (lepe_w NULL: no LePE term at all). */
+int oracle_attend_with_routing(const oracle_cfg_t* cfg, const double* q, const double* k,
+                               const double* v, const double* lepe_w, const double* lepe_b,
+                               const int32_t* idx, double* out);
+
+/* Whole forward: means -> route -> attend -> + LePE.  aff, qbar, kbar may be
+ * NULL; idx and out are required. */
+int oracle_bra_forward(const oracle_cfg_t* cfg, const double* q, const double* k,
+                       const double* v, const double* lepe_w, const double* lepe_b,
+                       double* out, int32_t* idx, double* aff, double* qbar, double* kbar);
+
+/* Number of OpenMP threads a parallel region of the oracle uses. */
+int oracle_num_threads(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

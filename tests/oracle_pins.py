@@ -1,0 +1,370 @@
+"""Pins of the CPU oracle to facts that do not come from the oracle itself.
+
+Each ``pin_*`` takes an ``oracle.OracleLib`` and raises ``AssertionError`` when
+the oracle disagrees with what the pages and the mathematics fix:
+
+* closed forms and special cases that reduce to a library routine (dense
+  softmax attention when every region is routed, one region per map, constant
+  V, all-zero K, a depthwise convolution),
+* brute force on tiny inputs (argsort of an affinity computed with numpy
+  window reshapes),
+* invariants (positive scaling of q, permutation of the routed set),
+* forced exact ties, a hand-worked example, and an independent PyTorch
+  formulation built from library gather/topk/softmax/conv2d calls.
+
+``tests/test_oracle_pins.py`` runs them against the real oracle and
+``tests/test_oracle_mutants.py`` against deliberately broken builds, each of
+which at least one pin must reject.
+
+Page keys: [P1] www.mhpn.cn/news/199372, [P2] www.mooersco.com/news/894234,
+[P3] www.mhpn.cn/news/564882, [P4] www.jsqmd.com/news/719213,
+[P5] www.mhpn.cn/news/2512273.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+
+from oracle import OracleConfig
+
+RTOL = 1e-10
+ATOL = 1e-12
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _rand_map(rng, cfg, scale=1.0):
+    return rng.standard_normal((cfg.batch, cfg.height, cfg.width, cfg.channels)) * scale
+
+
+def _rand_lepe(rng, cfg, bias=True):
+    w = rng.standard_normal((cfg.channels, 5, 5)) * 0.02
+    b = rng.standard_normal((cfg.channels,)) * 0.02 if bias else None
+    return w, b
+
+
+# ---- independent library formulations ------------------------------------
+
+def np_windows(x, n):
+    """[B,H,W,C] -> [B, R, t, C] with square windows, row-major inside.  [P3 §1]"""
+    B, H, W, C = x.shape
+    hs, ws = H // n, W // n
+    return x.reshape(B, n, hs, n, ws, C).transpose(0, 1, 3, 2, 4, 5).reshape(B, n * n, hs * ws, C)
+
+
+def np_unwindows(xw, n, H, W):
+    B, R, t, C = xw.shape
+    hs, ws = H // n, W // n
+    return xw.reshape(B, n, n, hs, ws, C).transpose(0, 1, 3, 2, 4, 5).reshape(B, H, W, C)
+
+
+def np_head_means(x, n, heads):
+    """Per-head region means [B, h, R, hd] via numpy mean over window tokens."""
+    xw = np_windows(x, n)
+    B, R, t, C = xw.shape
+    m = xw.mean(axis=2).reshape(B, R, heads, C // heads)
+    return m.transpose(0, 2, 1, 3)
+
+
+def torch_dense_attention(q, k, v, heads, scale=None):
+    """softmax(q k^T * scale) v over all tokens of each image, per head (library SDPA)."""
+    B, H, W, C = q.shape
+    hd = C // heads
+
+    def split(x):
+        return torch.from_numpy(np.ascontiguousarray(x)).reshape(B, H * W, heads, hd).permute(0, 2, 1, 3)
+
+    o = torch.nn.functional.scaled_dot_product_attention(split(q), split(k), split(v),
+                                                         scale=scale)
+    return o.permute(0, 2, 1, 3).reshape(B, H, W, C).numpy()
+
+
+def torch_lepe(v, w, b):
+    """Depthwise Conv2d(C, C, 5, padding=2, groups=C) in float64.  [P5 §五 self.lepe]"""
+    C = v.shape[-1]
+    x = torch.from_numpy(np.ascontiguousarray(v)).permute(0, 3, 1, 2)
+    wt = torch.from_numpy(np.ascontiguousarray(w)).reshape(C, 1, 5, 5)
+    bt = torch.from_numpy(np.ascontiguousarray(b)) if b is not None else None
+    y = torch.nn.functional.conv2d(x, wt, bt, padding=2, groups=C)
+    return y.permute(0, 2, 3, 1).numpy()
+
+
+def torch_bra_recipe(cfg: OracleConfig, q, k, v, w, b):
+    """The pages' PyTorch recipe in float64: window partition [P3 §1], per-head
+    means and affinity [P5 §五 ③], torch.topk [P5 §五 ④], torch.gather of the
+    routed windows [P5 §五 ⑤], softmax attention [P5 §五 ⑥], LePE of V added."""
+    B, H, W, C = q.shape
+    n, h = cfg.n_win, cfg.num_heads
+    hd = C // h
+    R = n * n
+    k_eff = R if cfg.topk <= 0 or cfg.topk > R else cfg.topk
+    scale = cfg.scale if cfg.scale > 0 else hd ** -0.5
+
+    def regions(x):  # [B, h, R, t, hd]
+        xw = torch.from_numpy(np_windows(x, n))
+        t = xw.shape[2]
+        return xw.reshape(B, R, t, h, hd).permute(0, 3, 1, 2, 4)
+
+    qr, kr, vr = regions(q), regions(k), regions(v)
+    t = qr.shape[3]
+    aff = qr.mean(dim=3) @ kr.mean(dim=3).transpose(-1, -2)
+    idx = aff.topk(k_eff, dim=-1).indices  # [B, h, R, k]
+
+    def gather(x):
+        xe = x.unsqueeze(2).expand(B, h, R, R, t, hd)
+        ie = idx[..., None, None].expand(B, h, R, k_eff, t, hd)
+        return torch.gather(xe, 3, ie).reshape(B, h, R, k_eff * t, hd)
+
+    kg, vg = gather(kr), gather(vr)
+    attn = torch.softmax((qr * scale) @ kg.transpose(-1, -2), dim=-1)
+    o = attn @ vg  # [B, h, R, t, hd]
+    o = o.permute(0, 2, 3, 1, 4).reshape(B, R, t, C).numpy()
+    out = np_unwindows(o, n, H, W)
+    if w is not None:
+        out = out + torch_lepe(v, w, b)
+    return out, idx.numpy().astype(np.int32)
+
+
+# ---- pins ----------------------------------------------------------------
+
+def pin_topk_all_is_dense_attention(orc):
+    """Routing every region to every region is dense attention over the map."""
+    for (B, H, W, heads, hd, n, topk, scale) in [
+        (2, 8, 12, 2, 8, 2, -1, 0.0),
+        (1, 6, 6, 3, 4, 3, 9, 0.0),
+        (1, 8, 8, 1, 32, 4, 1000, 0.3),
+    ]:
+        cfg = OracleConfig(B, H, W, heads * hd, heads, n, topk, scale)
+        rng = _rng(H * 100 + W)
+        q, k, v = (_rand_map(rng, cfg) for _ in range(3))
+        res = orc.bra_forward(cfg, q, k, v)
+        ref = torch_dense_attention(q, k, v, heads, scale if scale > 0 else None)
+        np.testing.assert_allclose(res["out"], ref, rtol=RTOL, atol=ATOL)
+        # every row of the routing is a permutation of all regions
+        R = n * n
+        assert res["idx"].shape[-1] == R
+        assert (np.sort(res["idx"], axis=-1) == np.arange(R)).all()
+
+
+def pin_one_region_is_dense_attention(orc):
+    """n_win = 1: one region, k = 1, again dense attention."""
+    cfg = OracleConfig(2, 6, 10, 16, 2, 1, 1)
+    rng = _rng(7)
+    q, k, v = (_rand_map(rng, cfg) for _ in range(3))
+    res = orc.bra_forward(cfg, q, k, v)
+    np.testing.assert_allclose(res["out"], torch_dense_attention(q, k, v, 2),
+                               rtol=RTOL, atol=ATOL)
+    assert (res["idx"] == 0).all()
+
+
+def pin_constant_v(orc):
+    """Softmax weights sum to one: V constant over the map returns that
+    constant; with LePE the border-aware sum of in-map taps is added."""
+    cfg = OracleConfig(2, 8, 8, 8, 2, 2, 2)
+    rng = _rng(11)
+    q, k = _rand_map(rng, cfg), _rand_map(rng, cfg)
+    c = rng.standard_normal(cfg.channels)
+    v = np.broadcast_to(c, (2, 8, 8, 8)).copy()
+    res = orc.bra_forward(cfg, q, k, v)
+    np.testing.assert_allclose(res["out"], v, rtol=0, atol=1e-12)
+    w, b = _rand_lepe(rng, cfg)
+    res = orc.bra_forward(cfg, q, k, v, w, b)
+    # in-map tap mask: tap (i, j) at (y, x) reads (y+i-2, x+j-2)
+    ys = np.arange(8)[:, None] + np.arange(5)[None, :] - 2
+    valid_y = (ys >= 0) & (ys < 8)  # [y, i]
+    tapmask = valid_y[:, None, :, None] & valid_y[None, :, None, :]  # [y, x, i, j]
+    wsum = np.einsum("yxij,cij->yxc", tapmask.astype(np.float64), w)
+    expect = c * (1.0 + wsum) + b
+    np.testing.assert_allclose(res["out"], np.broadcast_to(expect, v.shape), rtol=0, atol=1e-12)
+
+
+def pin_zero_k_uniform_over_lowest_regions(orc):
+    """K = 0 makes every affinity 0 (all tied, so regions 0..k-1 are routed)
+    and every logit 0 (uniform softmax): the output is the plain mean of V
+    over the tokens of regions 0..k-1."""
+    cfg = OracleConfig(2, 8, 12, 8, 2, 2, 3)
+    rng = _rng(13)
+    q, v = _rand_map(rng, cfg), _rand_map(rng, cfg)
+    k = np.zeros_like(q)
+    res = orc.bra_forward(cfg, q, k, v)
+    assert (res["idx"] == np.arange(3)).all()
+    vw = np_windows(v, 2)  # [B, R, t, C]
+    mean_lowest = vw[:, :3].reshape(2, -1, 8).mean(axis=1)  # [B, C]
+    np.testing.assert_allclose(res["out"], np.broadcast_to(mean_lowest[:, None, None, :],
+                                                           v.shape), rtol=RTOL, atol=ATOL)
+
+
+def pin_means_match_numpy(orc):
+    """Per-head window means equal numpy's mean over the reshaped windows."""
+    cfg = OracleConfig(2, 12, 8, 12, 3, 4, 2)
+    rng = _rng(17)
+    x = _rand_map(rng, cfg)
+    np.testing.assert_allclose(orc.region_means(cfg, x), np_head_means(x, 4, 3),
+                               rtol=1e-13, atol=1e-15)
+
+
+def pin_routing_bruteforce_argsort(orc):
+    """Routing equals a stable argsort of an independently computed affinity."""
+    for (B, H, W, heads, hd, n, topk, seed) in [
+        (2, 12, 8, 2, 8, 4, 5, 19), (1, 14, 14, 1, 32, 7, 4, 23), (3, 6, 9, 3, 4, 3, 9, 29)]:
+        cfg = OracleConfig(B, H, W, heads * hd, heads, n, topk)
+        rng = _rng(seed)
+        q, k = _rand_map(rng, cfg), _rand_map(rng, cfg)
+        res = orc.bra_forward(cfg, q, k, _rand_map(rng, cfg), want_aff=True, want_means=True)
+        qb, kb = np_head_means(q, n, heads), np_head_means(k, n, heads)
+        aff = np.einsum("bhrd,bhsd->bhrs", qb, kb)
+        np.testing.assert_allclose(res["aff"], aff, rtol=1e-12, atol=1e-14)
+        k_eff = min(topk, n * n) if topk > 0 else n * n
+        expect = np.argsort(-aff, axis=-1, kind="stable")[..., :k_eff]
+        assert (res["idx"] == expect).all()
+
+
+def pin_ties_go_to_lower_region(orc):
+    """Exact ties are broken toward the lower region id."""
+    cfg = OracleConfig(1, 8, 8, 8, 2, 4, 5)
+    rng = _rng(31)
+    q = _rand_map(rng, cfg)
+    # (a) every region of K identical -> every affinity in a row equal
+    tile = rng.standard_normal((2, 2, 8))
+    k = np.tile(tile, (4, 4, 1))[None]
+    res = orc.bra_forward(cfg, q, k, _rand_map(rng, cfg))
+    assert (res["idx"] == np.arange(5)).all()
+    # (b) region 2 and region 9 of K identical -> exact tie between 2 and 9
+    k = _rand_map(rng, cfg)
+    kw = np_windows(k, 4)
+    kw[:, 9] = kw[:, 2]
+    k = np_unwindows(kw, 4, 8, 8)
+    cfg16 = OracleConfig(1, 8, 8, 8, 2, 4, 16)
+    res = orc.bra_forward(cfg16, q, k, k)
+    for row in res["idx"].reshape(-1, 16):
+        pos = {int(s): j for j, s in enumerate(row)}
+        assert pos[9] == pos[2] + 1, row
+
+
+def pin_positive_scaling_keeps_routing(orc):
+    """Scaling q by a positive constant scales every affinity: routing unchanged."""
+    cfg = OracleConfig(2, 12, 12, 16, 2, 3, 4)
+    rng = _rng(37)
+    q, k, v = (_rand_map(rng, cfg) for _ in range(3))
+    base = orc.bra_forward(cfg, q, k, v)["idx"]
+    for a in (3.0, 0.37, 1e3):
+        assert (orc.bra_forward(cfg, q * a, k, v)["idx"] == base).all()
+
+
+def pin_routed_set_order_free(orc):
+    """Attention over the routed set does not depend on the order of its ids."""
+    cfg = OracleConfig(2, 8, 8, 8, 2, 4, 4)
+    rng = _rng(41)
+    q, k, v = (_rand_map(rng, cfg) for _ in range(3))
+    idx = orc.bra_forward(cfg, q, k, v)["idx"]
+    perm = np.ascontiguousarray(idx[..., ::-1])
+    np.testing.assert_allclose(orc.attend(cfg, q, k, v, perm), orc.attend(cfg, q, k, v, idx),
+                               rtol=RTOL, atol=ATOL)
+
+
+def pin_lepe_matches_conv2d(orc):
+    """LePE equals the library depthwise convolution (zero padding 2, bias)."""
+    cfg = OracleConfig(2, 7, 9, 6, 2, 1, 1)
+    rng = _rng(43)
+    v = _rand_map(rng, cfg)
+    w, b = _rand_lepe(rng, cfg)
+    np.testing.assert_allclose(orc.lepe(cfg, v, w, b), torch_lepe(v, w, b), rtol=1e-12,
+                               atol=1e-14)
+    np.testing.assert_allclose(orc.lepe(cfg, v, w, None), torch_lepe(v, w, None), rtol=1e-12,
+                               atol=1e-14)
+
+
+def pin_lepe_impulse_orientation(orc):
+    """A unit impulse at (y0, x0) puts tap (i, j) at (y0+2-i, x0+2-j) (the
+    cross-correlation orientation of Conv2d), e.g. w[3, 2] at (y0-1, x0)."""
+    cfg = OracleConfig(1, 9, 9, 2, 1, 1, 1)
+    rng = _rng(47)
+    w, _ = _rand_lepe(rng, cfg, bias=False)
+    v = np.zeros((1, 9, 9, 2))
+    v[0, 4, 4, 1] = 1.0
+    L = orc.lepe(cfg, v, w, None)
+    assert L[0, 3, 4, 1] == w[1, 3, 2]
+    for i in range(5):
+        for j in range(5):
+            assert L[0, 4 + 2 - i, 4 + 2 - j, 1] == w[1, i, j]
+    assert (L[..., 0] == 0).all()
+
+
+def pin_hand_worked_single_token_regions(orc):
+    """A 2x2 map with n_win = 2 has one token per region, so the region means
+    are the tokens and the affinity is q_p . k_s.  Worked by hand:
+      q = (1,0), (0,1), (-1,0), (0,-1);  k = (1,0), (0,1), (0,0), (2,2)
+      rows of A: [1,0,0,2], [0,1,0,2], [-1,0,0,-2], [0,-1,0,-2]
+      top-1: 3, 3, 1 (tie 1|2 -> 1), 0 (tie 0|2 -> 0); one key each, so out = v[idx].
+      top-2 of row 0 is (3, 0); the logits are 2s and 1s with s = 2^-0.5, so
+      out_0 = (e^{2s} v_3 + e^{s} v_0) / (e^{2s} + e^{s})."""
+    q = np.array([[1, 0], [0, 1], [-1, 0], [0, -1]], np.float64).reshape(1, 2, 2, 2)
+    k = np.array([[1, 0], [0, 1], [0, 0], [2, 2]], np.float64).reshape(1, 2, 2, 2)
+    v = np.array([[1, 2], [3, 4], [5, 6], [7, 8]], np.float64).reshape(1, 2, 2, 2)
+    cfg = OracleConfig(1, 2, 2, 2, 1, 2, 1)
+    res = orc.bra_forward(cfg, q, k, v)
+    assert res["idx"].reshape(-1).tolist() == [3, 3, 1, 0]
+    np.testing.assert_array_equal(res["out"].reshape(4, 2), v.reshape(4, 2)[[3, 3, 1, 0]])
+    cfg2 = OracleConfig(1, 2, 2, 2, 1, 2, 2)
+    res = orc.bra_forward(cfg2, q, k, v)
+    assert res["idx"][0, 0, 0].tolist() == [3, 0]
+    s = 2 ** -0.5
+    e2, e1 = math.exp(2 * s), math.exp(s)
+    expect0 = (e2 * np.array([7.0, 8.0]) + e1 * np.array([1.0, 2.0])) / (e2 + e1)
+    np.testing.assert_allclose(res["out"][0, 0, 0], expect0, rtol=1e-14)
+
+
+def pin_matches_torch_recipe(orc):
+    """The whole forward equals the pages' PyTorch recipe in float64."""
+    for (B, H, W, heads, hd, n, topk, seed) in [
+        (2, 8, 8, 2, 8, 2, 2, 53), (1, 12, 16, 2, 32, 4, 3, 59), (2, 9, 6, 3, 4, 3, 4, 61)]:
+        cfg = OracleConfig(B, H, W, heads * hd, heads, n, topk)
+        rng = _rng(seed)
+        q, k, v = (_rand_map(rng, cfg) for _ in range(3))
+        w, b = _rand_lepe(rng, cfg)
+        res = orc.bra_forward(cfg, q, k, v, w, b)
+        ref_out, ref_idx = torch_bra_recipe(cfg, q, k, v, w, b)
+        assert (res["idx"] == ref_idx).all()
+        np.testing.assert_allclose(res["out"], ref_out, rtol=RTOL, atol=ATOL)
+
+
+def pin_lepe_reads_v(orc):
+    """The LePE term is a convolution of V (not of q, k or the attention
+    output): with q = k = 0 the forward is mean(V) plus conv(V)."""
+    cfg = OracleConfig(1, 8, 8, 4, 1, 2, 4)
+    rng = _rng(67)
+    v = _rand_map(rng, cfg)
+    w, b = _rand_lepe(rng, cfg)
+    z = np.zeros_like(v)
+    res = orc.bra_forward(cfg, z, z, v, w, b)
+    mean = v.reshape(-1, 4).mean(axis=0)
+    np.testing.assert_allclose(res["out"], mean + torch_lepe(v, w, b), rtol=RTOL, atol=ATOL)
+
+
+def pin_topk_clamp(orc):
+    """k actually used: min(topk, R), topk <= 0 meaning all regions."""
+    for topk, expect in [(-1, 16), (0, 16), (16, 16), (40, 16), (1, 1), (7, 7)]:
+        assert orc.topk_effective(OracleConfig(1, 8, 8, 4, 1, 4, topk)) == expect
+
+
+ALL_PINS = [
+    pin_topk_all_is_dense_attention,
+    pin_one_region_is_dense_attention,
+    pin_constant_v,
+    pin_zero_k_uniform_over_lowest_regions,
+    pin_means_match_numpy,
+    pin_routing_bruteforce_argsort,
+    pin_ties_go_to_lower_region,
+    pin_positive_scaling_keeps_routing,
+    pin_routed_set_order_free,
+    pin_lepe_matches_conv2d,
+    pin_lepe_impulse_orientation,
+    pin_hand_worked_single_token_regions,
+    pin_matches_torch_recipe,
+    pin_lepe_reads_v,
+    pin_topk_clamp,
+]
