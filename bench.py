@@ -1,0 +1,215 @@
+"""Benchmark of the BRA forward (libbra.so) on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload stage1]
+
+A step is one bra_forward (region-pool kernel + routing/attention/LePE
+kernel) over one batch of the workload, inputs already in HBM.  By default
+the steps rotate over enough input/output buffer sets that consecutive steps
+never find their inputs in the 256 MB last-level cache (MALL), so the
+figures are HBM figures.  Prints one JSON line with the throughput, the
+roofline of the dominant kernel (timed per launch with HIP events inside the
+timed region) and the CPU oracle timed on a bounded sample on the host.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "BRA fwd tokens/s (bf16) + % HBM roofline / % MFMA peak vs CPU oracle"
+HBM_PEAK_GBS = 8000.0
+MALL_BYTES = 256 << 20
+KERNEL_SRC = os.path.join(ROOT, "vision_transformer_sparse_region_amd", "csrc", "bra_kernels.hip")
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def algorithmic_bytes(wl) -> dict:
+    """Bytes each kernel must move once per launch (unique bytes; the k-fold
+    re-reads of routed K/V and of the LePE halo are cache traffic)."""
+    es = 2 if wl.dtype == "bf16" else 4
+    S = wl.tokens * wl.channels * es                     # one [B,H,W,C] tensor
+    kbar = wl.batch * wl.channels * wl.regions * 8       # fp64 K region means
+    idx = wl.batch * wl.num_heads * wl.regions * wl.topk_effective * 4
+    lepe = wl.channels * 26 * 4
+    return {
+        "pool": S + kbar,                                # read k, write means
+        "attend": 4 * S + kbar + idx + lepe,             # read q, k, v, means, w; write out, idx
+        "S": S,
+    }
+
+
+def attention_flops(wl) -> float:
+    return 4.0 * wl.tokens * wl.num_heads * wl.topk_effective * wl.tokens_per_region * \
+        wl.head_dim
+
+
+def stored_traffic(workload: str):
+    """HBM bytes per launch of the attention kernel from the committed counter
+    summary, or None when absent or taken on a different kernel source."""
+    path = os.path.join(PROFILES, f"route_attend_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(wl, inputs, gpu_out, target_s: float = 10.0) -> dict:
+    """Time the CPU oracle on the first images of the same batch (a bounded
+    sample) and check the GPU output for those images against it."""
+    import numpy as np
+
+    import oracle
+
+    def run(nimg):
+        cfg = oracle.OracleConfig(nimg, wl.height, wl.width, wl.channels, wl.num_heads,
+                                  wl.n_win, wl.topk)
+        f = {n: inputs[n][:nimg].double().numpy() for n in ("q", "k", "v")}
+        w, b = inputs["lepe_w"].double().numpy(), inputs["lepe_b"].double().numpy()
+        t0 = time.perf_counter()
+        res = oracle.bra_forward(cfg, f["q"], f["k"], f["v"], w, b)
+        return time.perf_counter() - t0, res
+
+    dt, res = run(1)
+    nimg = int(max(1, min(wl.batch, target_s / max(dt, 1e-6))))
+    if nimg > 1:
+        dt, res = run(nimg)
+    tokens = nimg * wl.height * wl.width
+    g = gpu_out[:nimg].double().numpy()
+    err = float(np.abs(g - res["out"]).max() / np.abs(res["out"]).max())
+    return {
+        "value": tokens / dt,
+        "unit": "tokens/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": f"{nimg} of {wl.batch} images of the same batch ({tokens} tokens), "
+                  f"{dt:.2f} s wall, fp64 C + OpenMP",
+        "sample_max_rel_err_vs_gpu": err,
+    }
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", default="stage1")
+    ap.add_argument("--buffer-sets", type=int, default=0,
+                    help="input/output sets to rotate over (0: enough to exceed the MALL)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on one GPU; the forward needs no collective and "
+              "its multi-GPU sharding is described but not built.", file=sys.stderr)
+        return 2
+
+    import torch
+
+    from vision_transformer_sparse_region_amd import bra
+    from vision_transformer_sparse_region_amd.workloads import WORKLOADS, make_inputs
+
+    wl = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    host = make_inputs(wl)
+    S = wl.tokens * wl.channels * (2 if wl.dtype == "bf16" else 4)
+    nsets = args.buffer_sets or max(1, -(-2 * MALL_BYTES // (4 * S)))
+    sets = []
+    for i in range(nsets):
+        d = {n: host[n].to(dev) for n in ("q", "k", "v", "lepe_w", "lepe_b")}
+        d["out"] = torch.empty_like(d["q"])
+        d["idx"] = torch.empty((wl.batch, wl.num_heads, wl.regions, wl.topk_effective),
+                               dtype=torch.int32, device=dev)
+        sets.append(d)
+
+    h = bra.BRA(wl.batch, wl.height, wl.width, wl.channels, wl.num_heads, wl.n_win, wl.topk,
+                wl.dtype)
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        d = sets[i % nsets]
+        bra.bra_forward(h.handle, d["q"], d["k"], d["v"], d["lepe_w"], d["lepe_b"], d["out"],
+                        d["idx"], stream.cuda_stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    bra.bra_timing_enable(h.handle, args.steps)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    for i in range(args.steps):
+        step(i)
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = start.elapsed_time(end)
+    times = bra.bra_timing_read(h.handle, args.steps)
+    h.close()
+
+    ms_per_step = gpu_ms / args.steps
+    tokens_per_s = wl.tokens / (ms_per_step * 1e-3)
+    pool_ms = sum(t[0] for t in times) / len(times)
+    attn_ms = sum(t[1] for t in times) / len(times)
+    ab = algorithmic_bytes(wl)
+    achieved = ab["attend"] / (attn_ms * 1e-3) / 1e9
+    traffic = stored_traffic(wl.name)
+    line = {
+        "metric": METRIC,
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": wl.description,
+            "batch": wl.batch, "height": wl.height, "width": wl.width,
+            "channels": wl.channels, "num_heads": wl.num_heads, "n_win": wl.n_win,
+            "topk": wl.topk, "buffer_sets": nsets,
+            "kernel_ms": {"region_pool": pool_ms, "route_attend": attn_ms},
+            "wall_s": wall,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "route_attend",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": traffic,
+            "algorithmic_bytes": ab["attend"],
+            "attention_tflops": attention_flops(wl) / (attn_ms * 1e-3) / 1e12,
+            "pool_frac_hbm": ab["pool"] / (pool_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "step_frac_hbm": (ab["pool"] + ab["attend"]) / (ms_per_step * 1e-3) / 1e9 /
+            HBM_PEAK_GBS,
+        },
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(wl, host, sets[(args.steps - 1) % nsets]["out"].cpu())
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

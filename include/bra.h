@@ -1,0 +1,128 @@
+/*
+ * bra.h -- C ABI of libbra.so: the Bi-Level Routing Attention (BRA) forward
+ * pass on AMD Instinct MI355X (gfx950), as hand-written HIP kernels.
+ *
+ * What is computed (pages cited by key):
+ *   [P1] "从静态到动态：Bi-Level Routing Attention如何重塑视觉Transformer的注意力机制",
+ *        www.mhpn.cn/news/199372
+ *   [P2] "BiFormer用双层路由注意力重塑视觉Transformer效率极限", www.mooersco.com/news/894234
+ *   [P3] "从零构建BiFormer：PyTorch实战双层路由注意力机制与调试全攻略",
+ *        www.mhpn.cn/news/564882
+ *   [P4] "手把手解析BiFormer：双水平路由注意力机制与PyTorch实战指南", www.jsqmd.com/news/719213
+ *   [P5] "【医学图像分割模块】BiFormer / 双层路由注意力（CVPR 2023）", www.mhpn.cn/news/2512273
+ *
+ *   1. The H x W map is cut into n_win x n_win square windows ("regions"),
+ *      R = n_win^2 of them, each hs x ws = (H/n_win) x (W/n_win) tokens
+ *      [P3 §1 region_partition; P4 §1.1].  Region r = i*n_win + j holds rows
+ *      i*hs.. and columns j*ws..; its tokens are numbered row-major.
+ *   2. Per head, Q and K are averaged over each region [P4 §1.2; P5 §五 ③].
+ *   3. Per head, A[r][s] = Qbar_r . Kbar_s (the head_dim^-0.5 factor of
+ *      [P5 §五 ③] does not change the order and is not applied) and each row
+ *      keeps its k largest entries, in descending order, exact ties to the
+ *      lower region id [P1 §2.1 TopkRouting; P5 §五 ④].  k = min(topk, R),
+ *      topk <= 0 meaning every region [P5 §五 ④; P2 §3.1].
+ *   4. Every token of region r attends, per head, to the k*t tokens of its
+ *      routed regions: softmax(scale * q K^T) V [P3 §2.2; P5 §五 ⑤-⑦].
+ *   5. out = attention + LePE, LePE = depthwise 5x5 convolution of V with
+ *      zero padding 2 over the whole map, plus a per-channel bias
+ *      [P5 §五 self.lepe and ⑧; P2 §2.2].
+ *   Routing is computed in fp64 (region sums are exact for bf16 input), so
+ *   routing_idx equals a float64 evaluation of steps 2-3.  Attention runs on
+ *   bf16 MFMA with fp32 accumulation and an fp32 online softmax (bf16 I/O)
+ *   or in fp32 VALU arithmetic (fp32 I/O); LePE accumulates in fp32.
+ *
+ * Layouts (device memory, C-contiguous, owned by the caller):
+ *   q, k, v, out   [B, H, W, C] (NHWC), C = heads * head_dim, the channel of
+ *                  (head h, dim d) is h*head_dim + d; element type = dtype
+ *   lepe_w         [C, 5, 5] fp32 (a PyTorch depthwise weight [C, 1, 5, 5])
+ *   lepe_b         [C] fp32
+ *   routing_idx    [B, heads, R, k] int32
+ *
+ * Errors: every call returns a bra_status_t; nothing throws or aborts across
+ * the ABI.  bra_last_error() gives a thread-local message for the last
+ * failing call.  A kernel fault is asynchronous and surfaces at the caller's
+ * next synchronisation.
+ *
+ * Threads and streams: a handle may be used from any host thread but by one
+ * stream at a time (its workspace is shared by the calls made with it).
+ */
+#ifndef BRA_H
+#define BRA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct bra_handle_s* bra_handle_t; /* opaque */
+
+typedef enum {
+    BRA_OK = 0,
+    BRA_ERR_NULL = 1,        /* a required pointer is NULL */
+    BRA_ERR_SHAPE = 2,       /* sizes not positive, H or W not divisible by n_win,
+                                C not divisible by num_heads, or too large for int32 indexing */
+    BRA_ERR_UNSUPPORTED = 3, /* head_dim != 32, unknown dtype, or a region too large
+                                for the kernels' on-chip tiles */
+    BRA_ERR_HIP = 4,         /* a HIP runtime call failed (see bra_last_error) */
+    BRA_ERR_NOMEM = 5,       /* device memory for the workspace could not be allocated */
+    BRA_ERR_BAD_HANDLE = 6,  /* not a live handle (never created, or destroyed) */
+    BRA_ERR_ALIGN = 7,       /* q, k, v or out not 16-byte aligned, or lepe_w, lepe_b,
+                                routing_idx not 4-byte aligned */
+    BRA_ERR_ALIAS = 8,       /* out overlaps q, k or v */
+    BRA_ERR_DEVICE = 9       /* the current HIP device is not the handle's device */
+} bra_status_t;
+
+typedef enum { BRA_F32 = 0, BRA_BF16 = 1 } bra_dtype_t;
+
+typedef struct {
+    int32_t batch, height, width, channels, num_heads;
+    int32_t n_win;     /* regions per side: H % n_win == 0 and W % n_win == 0 */
+    int32_t topk;      /* routed regions per region; <= 0 or > n_win^2 means all */
+    bra_dtype_t dtype; /* element type of q, k, v and out */
+    float scale;       /* attention logit scale; <= 0 means head_dim^-0.5 */
+} bra_config_t;
+
+/* Validate cfg and allocate the handle and its device workspace (the fp64
+ * region means of K, B*C*R*8 bytes) on the current HIP device.  On success
+ * *out is a live handle; on failure *out is left NULL. */
+bra_status_t bra_create(const bra_config_t* cfg, bra_handle_t* out);
+
+/* Enqueue the forward pass on `stream` (a hipStream_t; NULL = the null
+ * stream) and return without synchronising.  No allocation happens here.
+ *   q, k, v       device, [B,H,W,C], dtype, 16-byte aligned
+ *   lepe_w        device [C,5,5] fp32, or NULL for no LePE term (lepe_b is then ignored)
+ *   lepe_b        device [C] fp32, or NULL for a zero bias
+ *   out           device, [B,H,W,C], dtype, 16-byte aligned, must not overlap q/k/v
+ *   routing_idx   device [B,heads,R,k] int32 to receive the routing, or NULL
+ * The current device must be the handle's device. */
+bra_status_t bra_forward(bra_handle_t h, const void* q, const void* k, const void* v,
+                         const float* lepe_w, const float* lepe_b, void* out,
+                         int32_t* routing_idx, void* stream);
+
+/* Release the workspace and the handle.  NULL is a no-op (BRA_OK); a handle
+ * that is not live gives BRA_ERR_BAD_HANDLE. */
+bra_status_t bra_destroy(bra_handle_t h);
+
+/* k actually used by the handle (min(topk, R), or R); -1 for a bad handle. */
+int32_t bra_topk_effective(bra_handle_t h);
+
+/* Static description of a status code. */
+const char* bra_status_string(bra_status_t s);
+
+/* Thread-local detail of the last failing call on this thread ("" if none). */
+const char* bra_last_error(void);
+
+/* Per-kernel timing for profiling.  bra_timing_enable(h, n) makes the next n
+ * calls of bra_forward record HIP events around each of its kernels on the
+ * call's stream (n = 0 turns recording off).  bra_timing_read waits for the
+ * recorded events and writes, for each recorded call i < *count,
+ * ms[2*i] = region-pool kernel time and ms[2*i+1] = routing/attention kernel
+ * time (milliseconds), then clears the record.  `ms` holds at least 2*n floats. */
+bra_status_t bra_timing_enable(bra_handle_t h, int32_t n);
+bra_status_t bra_timing_read(bra_handle_t h, float* ms, int32_t* count);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

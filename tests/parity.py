@@ -1,0 +1,111 @@
+"""Shared parity machinery: run one workload through libbra.so on the GPU and
+through the CPU oracle on the same (bf16-exact) inputs, then compare.
+
+Bar (stated once, used by every GPU parity test):
+  * routing_idx bit-exact, except that a slot may hold a different region
+    when the two affinities are within 1e-6 of the row's largest |affinity|
+    (a near-tie); every such slot is reported, and the output is then
+    compared against the oracle's attention with the GPU's routing;
+  * out: max|gpu - oracle| / max|oracle| <= 1e-4 for fp32 I/O and 2e-2 for
+    bf16 I/O (fp32 accumulation).
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+from vision_transformer_sparse_region_amd import bra
+from vision_transformer_sparse_region_amd.workloads import Workload, make_inputs
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+TIE_REL = 1e-6
+
+
+def say(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def oracle_cfg(wl: Workload, scale: float = 0.0) -> oracle.OracleConfig:
+    return oracle.OracleConfig(wl.batch, wl.height, wl.width, wl.channels, wl.num_heads,
+                               wl.n_win, wl.topk, scale)
+
+
+def run_gpu(wl: Workload, inp: dict, lepe: bool = True, want_idx: bool = True,
+            scale: float = 0.0, handle: bra.BRA | None = None):
+    dev = torch.device("cuda:0")
+    q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
+    w = inp["lepe_w"].to(dev) if lepe else None
+    b = inp["lepe_b"].to(dev) if lepe else None
+    own = handle is None
+    h = handle or bra.BRA(wl.batch, wl.height, wl.width, wl.channels, wl.num_heads, wl.n_win,
+                          wl.topk, wl.dtype, scale)
+    try:
+        out, idx = h.forward(q, k, v, w, b, routing_idx=want_idx)
+        torch.cuda.synchronize()
+    finally:
+        if own:
+            h.close()
+    return out.cpu(), (idx.cpu().numpy() if idx is not None else None)
+
+
+def run_oracle(wl: Workload, inp: dict, lepe: bool = True, scale: float = 0.0):
+    cfg = oracle_cfg(wl, scale)
+    f = {n: inp[n].double().numpy() for n in ("q", "k", "v", "lepe_w", "lepe_b")}
+    return oracle.bra_forward(cfg, f["q"], f["k"], f["v"], f["lepe_w"] if lepe else None,
+                              f["lepe_b"] if lepe else None, want_aff=True)
+
+
+def check_routing(gpu_idx: np.ndarray, res: dict):
+    """Exact match up to logged near-ties; returns the list of accepted ties."""
+    oi, aff = res["idx"], res["aff"]
+    assert gpu_idx.shape == oi.shape, (gpu_idx.shape, oi.shape)
+    diff = np.argwhere(gpu_idx != oi)
+    ties = []
+    for b, h, r, j in diff:
+        row = aff[b, h, r]
+        sg, so = int(gpu_idx[b, h, r, j]), int(oi[b, h, r, j])
+        gap = abs(row[sg] - row[so])
+        lim = TIE_REL * np.abs(row).max()
+        assert gap <= lim, (f"routing mismatch at b={b} h={h} r={r} slot={j}: gpu {sg} "
+                            f"(A={row[sg]!r}) vs oracle {so} (A={row[so]!r})")
+        ties.append((int(b), int(h), int(r), int(j), sg, so, float(row[sg]), float(row[so])))
+    # every GPU row is k distinct regions
+    srt = np.sort(gpu_idx, axis=-1)
+    assert (srt[..., 1:] != srt[..., :-1]).all() and (gpu_idx >= 0).all() and \
+        (gpu_idx < aff.shape[-1]).all()
+    for t in ties:
+        say(f"  near-tie accepted: b={t[0]} h={t[1]} r={t[2]} slot={t[3]} gpu={t[4]} "
+            f"oracle={t[5]} A_gpu={t[6]!r} A_oracle={t[7]!r}")
+    return ties
+
+
+def max_rel_err(gpu_out: torch.Tensor, ref: np.ndarray) -> float:
+    g = gpu_out.double().numpy()
+    return float(np.abs(g - ref).max() / np.abs(ref).max())
+
+
+def check_parity(wl: Workload, inp: dict | None = None, lepe: bool = True,
+                 scale: float = 0.0, tol: float | None = None):
+    """Full comparison of one workload; returns (max relative error, ties)."""
+    inp = inp if inp is not None else make_inputs(wl)
+    say(f"[gpu] {wl.name}: B={wl.batch} H={wl.height} W={wl.width} C={wl.channels} "
+        f"heads={wl.num_heads} n_win={wl.n_win} topk={wl.topk} {wl.dtype} seed={wl.seed}")
+    gout, gidx = run_gpu(wl, inp, lepe=lepe, scale=scale)
+    say(f"[gpu] {wl.name}: kernels done, running the oracle")
+    res = run_oracle(wl, inp, lepe=lepe, scale=scale)
+    ties = check_routing(gidx, res)
+    ref = res["out"]
+    if ties:
+        f = {n: inp[n].double().numpy() for n in ("q", "k", "v", "lepe_w", "lepe_b")}
+        ref = oracle.attend_with_routing(oracle_cfg(wl, scale), f["q"], f["k"], f["v"],
+                                         f["lepe_w"] if lepe else None,
+                                         f["lepe_b"] if lepe else None, gidx)
+    err = max_rel_err(gout, ref)
+    bound = tol if tol is not None else TOL[wl.dtype]
+    say(f"[gpu] {wl.name}: max rel err {err:.3e} (bound {bound:g}), near-ties {len(ties)}")
+    assert err <= bound, f"{wl.name}: max relative error {err:.3e} > {bound:g}"
+    return err, ties

@@ -1,0 +1,105 @@
+"""GPU parity: libbra.so (through the C ABI) against the CPU oracle.
+
+The five workloads run at their full sizes (the oracle finishes them in
+seconds); the small cases span several tiles, ragged tiles and key chunks,
+odd head counts, non-square maps and windows, the degenerate settings (every
+region routed, topk above R, a single region), LePE off and with a bias, an
+explicit scale, and the fp32 path.  The bar is in tests/parity.py."""
+import numpy as np
+import pytest
+import torch
+
+from parity import check_parity, run_gpu, say
+from vision_transformer_sparse_region_amd import bra
+from vision_transformer_sparse_region_amd.workloads import WORKLOADS, Workload, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("name", ["tiny_f32", "stage1", "stage2", "stage3", "highres"])
+def test_workload_full_size(name):
+    check_parity(WORKLOADS[name])
+
+
+SMALL = [
+    Workload("ragged_t15_bias", 2, 12, 20, 64, 2, 4, 3, "bf16", 101, lepe_bias=True),
+    Workload("t36_three_heads", 2, 24, 24, 96, 3, 4, 5, "bf16", 102),
+    Workload("t144_one_head_all", 1, 24, 24, 32, 1, 2, -1, "bf16", 103),
+    Workload("every_region", 2, 28, 28, 64, 2, 7, 49, "bf16", 104),
+    Workload("topk_above_R", 2, 28, 28, 64, 2, 7, 100, "bf16", 105),
+    Workload("single_region", 2, 8, 8, 64, 2, 1, 1, "bf16", 106),
+    Workload("sixteen_heads_t1", 2, 7, 7, 512, 16, 7, 49, "bf16", 107),
+    Workload("smooth_highres_b1", 1, 128, 128, 64, 2, 16, 16, "bf16", 108, smooth=True),
+    Workload("f32_stage2_shape", 4, 28, 28, 128, 4, 7, 4, "f32", 109),
+    Workload("f32_ragged_bias", 2, 12, 20, 64, 2, 4, 3, "f32", 110, lepe_bias=True),
+]
+
+
+@pytest.mark.parametrize("wl", SMALL, ids=[w.name for w in SMALL])
+def test_small_case(wl):
+    check_parity(wl)
+
+
+def test_without_lepe():
+    check_parity(Workload("no_lepe", 4, 56, 56, 64, 2, 7, 1, "bf16", 111), lepe=False)
+
+
+def test_explicit_scale():
+    check_parity(Workload("scale_0p05", 2, 28, 28, 128, 4, 7, 4, "bf16", 112), scale=0.05)
+
+
+def test_routing_export_optional_and_deterministic():
+    wl = Workload("determinism", 8, 56, 56, 64, 2, 7, 1, "bf16", 113)
+    inp = make_inputs(wl)
+    say("[gpu] determinism: three runs, one without routing export")
+    a, ia = run_gpu(wl, inp)
+    b, ib = run_gpu(wl, inp)
+    c, ic = run_gpu(wl, inp, want_idx=False)
+    assert ic is None
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    assert torch.equal(a.view(torch.int16), c.view(torch.int16))
+    assert (ia == ib).all()
+
+
+def test_exact_ties_pick_lower_regions():
+    """Every K window identical: all affinities of a row tie exactly, so the
+    routing is regions 0..k-1 in order."""
+    wl = Workload("all_tied", 2, 28, 28, 128, 4, 7, 6, "bf16", 114)
+    inp = make_inputs(wl)
+    tile = inp["k"][:, :4, :4, :].clone()
+    inp["k"] = tile.repeat(1, 7, 7, 1).contiguous()
+    say("[gpu] all_tied")
+    _, idx = run_gpu(wl, inp)
+    assert (idx == np.arange(6, dtype=np.int32)).all()
+    check_parity(wl, inp)
+
+
+def test_handle_reuse_and_argument_checks():
+    wl = WORKLOADS["stage2"].with_(batch=2, seed=115)
+    inp = make_inputs(wl)
+    h = bra.BRA(wl.batch, wl.height, wl.width, wl.channels, wl.num_heads, wl.n_win, wl.topk)
+    try:
+        dev = torch.device("cuda:0")
+        q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
+        w, b = inp["lepe_w"].to(dev), inp["lepe_b"].to(dev)
+        out = torch.empty_like(q)
+        say("[gpu] argument checks")
+        st = bra.bra_forward_status(h.handle, q, k, v, w, b, q, None, 0)
+        assert st == bra.BRA_ERR_ALIAS
+        st = bra.bra_forward_status(h.handle, q.data_ptr() + 2, k, v, w, b, out, None, 0)
+        assert st == bra.BRA_ERR_ALIGN
+        st = bra.bra_forward_status(h.handle, None, k, v, w, b, out, None, 0)
+        assert st == bra.BRA_ERR_NULL
+        # the handle still works after rejected calls, and twice in a row
+        o1, _ = h.forward(q, k, v, w, b)
+        o2, _ = h.forward(q, k, v, w, b)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2)
+        bra.bra_timing_enable(h.handle, 2)
+        h.forward(q, k, v, w, b)
+        times = bra.bra_timing_read(h.handle, 2)
+        assert len(times) == 1 and times[0][0] > 0 and times[0][1] > 0
+    finally:
+        h.close()
+    assert bra.load_library().bra_forward(h.handle, None, None, None, None, None, None, None,
+                                          None) == bra.BRA_ERR_BAD_HANDLE

@@ -1,0 +1,230 @@
+"""ctypes binding of libbra.so (include/bra.h): the BRA forward on MI355X.
+
+The functions carry the C names and only marshal arguments; every step of
+the forward runs in the library's HIP kernels.  Torch tensors are accepted
+for device memory (their data pointers are passed) and the current torch
+stream is used unless a raw ``hipStream_t`` is given.
+
+If libbra.so has not been built, loading raises ``BraLibraryMissing``: there
+is no fallback path.  Build it with
+``python -m vision_transformer_sparse_region_amd.build``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libbra.so")
+HEADER = os.path.join(os.path.dirname(PKG), "include", "bra.h")
+
+BRA_OK = 0
+BRA_ERR_NULL = 1
+BRA_ERR_SHAPE = 2
+BRA_ERR_UNSUPPORTED = 3
+BRA_ERR_HIP = 4
+BRA_ERR_NOMEM = 5
+BRA_ERR_BAD_HANDLE = 6
+BRA_ERR_ALIGN = 7
+BRA_ERR_ALIAS = 8
+BRA_ERR_DEVICE = 9
+
+BRA_F32 = 0
+BRA_BF16 = 1
+
+
+class BraLibraryMissing(ImportError):
+    pass
+
+
+class BraError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        super().__init__(f"{where}: status {status} ({detail})")
+        self.status = status
+
+
+class BraConfig(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("height", ctypes.c_int32), ("width", ctypes.c_int32),
+        ("channels", ctypes.c_int32), ("num_heads", ctypes.c_int32), ("n_win", ctypes.c_int32),
+        ("topk", ctypes.c_int32), ("dtype", ctypes.c_int), ("scale", ctypes.c_float),
+    ]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libbra.so once; raise BraLibraryMissing if it is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise BraLibraryMissing(
+            f"{path} is not built; run `python -m vision_transformer_sparse_region_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i32 = ctypes.c_void_p, ctypes.c_int32
+    lib.bra_create.argtypes = [ctypes.POINTER(BraConfig), ctypes.POINTER(vp)]
+    lib.bra_forward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.bra_destroy.argtypes = [vp]
+    lib.bra_topk_effective.argtypes = [vp]
+    lib.bra_topk_effective.restype = i32
+    lib.bra_status_string.argtypes = [ctypes.c_int]
+    lib.bra_status_string.restype = ctypes.c_char_p
+    lib.bra_last_error.argtypes = []
+    lib.bra_last_error.restype = ctypes.c_char_p
+    lib.bra_timing_enable.argtypes = [vp, i32]
+    lib.bra_timing_read.argtypes = [vp, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(i32)]
+    for name in ("bra_create", "bra_forward", "bra_destroy", "bra_timing_enable",
+                 "bra_timing_read"):
+        getattr(lib, name).restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def declared_functions(header: str = HEADER):
+    """Names of the functions include/bra.h declares."""
+    with open(header) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"^\s*[A-Za-z_][\w\s\*]*?\b(bra_\w+)\s*\(", text, re.M)))
+
+
+def _check(status: int, where: str):
+    if status != BRA_OK:
+        lib = load_library()
+        detail = lib.bra_last_error().decode() or lib.bra_status_string(status).decode()
+        raise BraError(status, where, detail)
+
+
+def _ptr(x):
+    """Device address of a torch tensor, an int, or None."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream):
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+# ---- the C functions -------------------------------------------------------
+
+def bra_status_string(status: int) -> str:
+    return load_library().bra_status_string(status).decode()
+
+
+def bra_last_error() -> str:
+    return load_library().bra_last_error().decode()
+
+
+def bra_create(cfg: BraConfig) -> int:
+    """Return a live handle (an int) or raise BraError."""
+    h = ctypes.c_void_p()
+    _check(load_library().bra_create(ctypes.byref(cfg), ctypes.byref(h)), "bra_create")
+    return h.value
+
+
+def bra_create_status(cfg) -> int:
+    """Call bra_create and return the raw status (handle destroyed on success)."""
+    lib = load_library()
+    h = ctypes.c_void_p()
+    st = lib.bra_create(ctypes.byref(cfg) if cfg is not None else None, ctypes.byref(h))
+    if st == BRA_OK:
+        lib.bra_destroy(h)
+    return st
+
+
+def bra_forward(h: int, q, k, v, lepe_w, lepe_b, out, routing_idx=None, stream=None):
+    """Enqueue the forward on the stream (torch's current stream by default)."""
+    st = load_library().bra_forward(h, _ptr(q), _ptr(k), _ptr(v), _ptr(lepe_w), _ptr(lepe_b),
+                                    _ptr(out), _ptr(routing_idx), _stream(stream))
+    _check(st, "bra_forward")
+
+
+def bra_forward_status(h, q, k, v, lepe_w, lepe_b, out, routing_idx=None, stream=0) -> int:
+    """Raw status of bra_forward (for tests of the argument checks)."""
+    return load_library().bra_forward(h, _ptr(q), _ptr(k), _ptr(v), _ptr(lepe_w), _ptr(lepe_b),
+                                      _ptr(out), _ptr(routing_idx), stream)
+
+
+def bra_destroy(h) -> None:
+    _check(load_library().bra_destroy(h), "bra_destroy")
+
+
+def bra_topk_effective(h) -> int:
+    return int(load_library().bra_topk_effective(h))
+
+
+def bra_timing_enable(h, n: int) -> None:
+    _check(load_library().bra_timing_enable(h, n), "bra_timing_enable")
+
+
+def bra_timing_read(h, capacity: int):
+    """Return a list of (pool_ms, attend_ms), one per recorded forward."""
+    buf = (ctypes.c_float * (2 * max(capacity, 1)))()
+    cnt = ctypes.c_int32()
+    _check(load_library().bra_timing_read(h, buf, ctypes.byref(cnt)), "bra_timing_read")
+    return [(buf[2 * i], buf[2 * i + 1]) for i in range(cnt.value)]
+
+
+# ---- convenience wrapper ---------------------------------------------------
+
+class BRA:
+    """One handle: ``BRA(batch, height, width, channels, num_heads, n_win, topk, dtype)``.
+
+    ``forward(q, k, v, lepe_w, lepe_b)`` takes CUDA (HIP) torch tensors in NHWC,
+    returns ``(out, routing_idx)``; torch only allocates the outputs.
+    """
+
+    def __init__(self, batch, height, width, channels, num_heads, n_win, topk, dtype="bf16",
+                 scale=0.0):
+        self.cfg = BraConfig(batch, height, width, channels, num_heads, n_win, topk,
+                             BRA_BF16 if dtype == "bf16" else BRA_F32, scale)
+        self.dtype = dtype
+        self.handle = bra_create(self.cfg)
+        self.k = bra_topk_effective(self.handle)
+
+    def forward(self, q, k, v, lepe_w=None, lepe_b=None, out=None, routing_idx=True,
+                stream=None):
+        import torch
+        c = self.cfg
+        want = torch.bfloat16 if self.dtype == "bf16" else torch.float32
+        shape = (c.batch, c.height, c.width, c.channels)
+        for name, t in (("q", q), ("k", k), ("v", v)):
+            if t.dtype != want or tuple(t.shape) != shape or not t.is_contiguous() or not t.is_cuda:
+                raise ValueError(f"{name}: expected a contiguous {want} CUDA tensor {shape}")
+        for name, t in (("lepe_w", lepe_w), ("lepe_b", lepe_b)):
+            if t is not None and (t.dtype != torch.float32 or not t.is_contiguous() or not t.is_cuda):
+                raise ValueError(f"{name}: expected a contiguous float32 CUDA tensor")
+        if out is None:
+            out = torch.empty_like(q)
+        if routing_idx is True:
+            routing_idx = torch.empty((c.batch, c.num_heads, c.n_win * c.n_win, self.k),
+                                      dtype=torch.int32, device=q.device)
+        elif routing_idx is False:
+            routing_idx = None
+        bra_forward(self.handle, q, k, v, lepe_w, lepe_b, out, routing_idx, stream)
+        return out, routing_idx
+
+    def close(self):
+        if self.handle:
+            bra_destroy(self.handle)
+            self.handle = None
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

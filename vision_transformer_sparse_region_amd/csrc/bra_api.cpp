@@ -1,0 +1,239 @@
+// bra_api.cpp -- the C ABI of libbra.so (declared in include/bra.h): argument
+// validation, handle registry, workspace, launches on the caller's stream and
+// optional per-kernel event timing.  No compute happens on the host.
+#include "bra.h"
+
+#include <hip/hip_runtime_api.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <new>
+#include <set>
+#include <string>
+#include <vector>
+
+#include "bra_launch.h"
+
+struct bra_handle_s {
+    bra_config_t cfg;
+    bra::Params params;
+    bool bf16;
+    int device;
+    double* kbar;        // [B, heads, R, 32] fp64 region means of K
+    size_t kbar_bytes;
+    // per-kernel timing (events recorded by bra_forward while slots remain)
+    std::vector<hipEvent_t> events;  // 3 per recorded call
+    int timing_capacity;
+    int timing_used;
+};
+
+namespace {
+
+std::mutex g_mutex;
+std::set<bra_handle_t> g_live;  // handles between create and destroy
+thread_local std::string g_last_error;
+
+bra_status_t fail(bra_status_t s, const std::string& msg) {
+    g_last_error = msg;
+    return s;
+}
+
+bra_status_t fail_hip(hipError_t e, const char* what) {
+    g_last_error = std::string(what) + ": " + hipGetErrorString(e);
+    return e == hipErrorOutOfMemory ? BRA_ERR_NOMEM : BRA_ERR_HIP;
+}
+
+bool is_live(bra_handle_t h) {
+    std::lock_guard<std::mutex> lock(g_mutex);
+    return h != nullptr && g_live.count(h) != 0;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool overlaps(const void* a, const void* b, size_t n) {
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + n && y < x + n;
+}
+
+void release_events(bra_handle_t h) {
+    for (hipEvent_t e : h->events) (void)hipEventDestroy(e);
+    h->events.clear();
+    h->timing_capacity = 0;
+    h->timing_used = 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* bra_status_string(bra_status_t s) {
+    switch (s) {
+        case BRA_OK: return "ok";
+        case BRA_ERR_NULL: return "a required pointer is NULL";
+        case BRA_ERR_SHAPE: return "invalid shape";
+        case BRA_ERR_UNSUPPORTED: return "unsupported configuration";
+        case BRA_ERR_HIP: return "HIP runtime error";
+        case BRA_ERR_NOMEM: return "out of device memory";
+        case BRA_ERR_BAD_HANDLE: return "not a live handle";
+        case BRA_ERR_ALIGN: return "misaligned pointer";
+        case BRA_ERR_ALIAS: return "output overlaps an input";
+        case BRA_ERR_DEVICE: return "current device is not the handle's device";
+    }
+    return "unknown status";
+}
+
+const char* bra_last_error(void) { return g_last_error.c_str(); }
+
+bra_status_t bra_create(const bra_config_t* cfg, bra_handle_t* out) {
+    if (!cfg || !out) return fail(BRA_ERR_NULL, "bra_create: cfg and out are required");
+    *out = nullptr;
+    const bra_config_t c = *cfg;
+    if (c.batch <= 0 || c.height <= 0 || c.width <= 0 || c.channels <= 0 || c.num_heads <= 0 ||
+        c.n_win <= 0)
+        return fail(BRA_ERR_SHAPE, "bra_create: sizes must be positive");
+    if (c.height % c.n_win || c.width % c.n_win)
+        return fail(BRA_ERR_SHAPE, "bra_create: height and width must be divisible by n_win");
+    if (c.channels % c.num_heads)
+        return fail(BRA_ERR_SHAPE, "bra_create: channels must be divisible by num_heads");
+    const double elems = static_cast<double>(c.height) * c.width * c.channels;
+    if (elems >= 2147483647.0 || static_cast<double>(c.batch) * c.n_win * c.n_win >= 2147483647.0)
+        return fail(BRA_ERR_SHAPE, "bra_create: one image or the region grid exceeds int32 indexing");
+    if (c.channels / c.num_heads != bra::kHeadDim)
+        return fail(BRA_ERR_UNSUPPORTED, "bra_create: head_dim must be 32");
+    if (c.dtype != BRA_F32 && c.dtype != BRA_BF16)
+        return fail(BRA_ERR_UNSUPPORTED, "bra_create: dtype must be BRA_F32 or BRA_BF16");
+    const int R = c.n_win * c.n_win;
+    const int k = (c.topk <= 0 || c.topk > R) ? R : c.topk;
+    const float scale = c.scale > 0.f ? c.scale : 1.0f / std::sqrt(static_cast<float>(bra::kHeadDim));
+    const bool bf16 = c.dtype == BRA_BF16;
+    bra::Params p;
+    if (!bra::plan(p, c.batch, c.height, c.width, c.channels, c.num_heads, c.n_win, k, scale,
+                   bf16))
+        return fail(BRA_ERR_UNSUPPORTED,
+                    "bra_create: a region (with its LePE halo) or the channel count is too large "
+                    "for the on-chip tiles (" + std::to_string(p.lds_bytes) + " bytes of LDS)");
+
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail_hip(e, "bra_create: hipGetDevice");
+    bra_handle_t h = new (std::nothrow) bra_handle_s();
+    if (!h) return fail(BRA_ERR_NOMEM, "bra_create: host allocation failed");
+    h->cfg = c;
+    h->params = p;
+    h->bf16 = bf16;
+    h->device = dev;
+    h->kbar_bytes = static_cast<size_t>(c.batch) * c.channels * R * sizeof(double);
+    h->kbar = nullptr;
+    h->timing_capacity = 0;
+    h->timing_used = 0;
+    e = hipMalloc(reinterpret_cast<void**>(&h->kbar), h->kbar_bytes);
+    if (e != hipSuccess) {
+        delete h;
+        return fail_hip(e, "bra_create: hipMalloc of the workspace");
+    }
+    {
+        std::lock_guard<std::mutex> lock(g_mutex);
+        g_live.insert(h);
+    }
+    *out = h;
+    return BRA_OK;
+}
+
+bra_status_t bra_destroy(bra_handle_t h) {
+    if (!h) return BRA_OK;
+    {
+        std::lock_guard<std::mutex> lock(g_mutex);
+        if (!g_live.erase(h)) return fail(BRA_ERR_BAD_HANDLE, "bra_destroy: not a live handle");
+    }
+    release_events(h);
+    hipError_t e = hipFree(h->kbar);
+    delete h;
+    if (e != hipSuccess) return fail_hip(e, "bra_destroy: hipFree");
+    return BRA_OK;
+}
+
+int32_t bra_topk_effective(bra_handle_t h) {
+    if (!is_live(h)) return -1;
+    return h->params.k;
+}
+
+bra_status_t bra_forward(bra_handle_t h, const void* q, const void* k, const void* v,
+                         const float* lepe_w, const float* lepe_b, void* out,
+                         int32_t* routing_idx, void* stream) {
+    if (!is_live(h)) return fail(BRA_ERR_BAD_HANDLE, "bra_forward: not a live handle");
+    if (!q || !k || !v || !out) return fail(BRA_ERR_NULL, "bra_forward: q, k, v and out are required");
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16))
+        return fail(BRA_ERR_ALIGN, "bra_forward: q, k, v and out must be 16-byte aligned");
+    if (!aligned(lepe_w, 4) || !aligned(lepe_b, 4) || !aligned(routing_idx, 4))
+        return fail(BRA_ERR_ALIGN, "bra_forward: lepe_w, lepe_b and routing_idx must be 4-byte aligned");
+    const bra_config_t& c = h->cfg;
+    const size_t bytes = static_cast<size_t>(c.batch) * c.height * c.width * c.channels *
+                         (h->bf16 ? 2 : 4);
+    if (overlaps(out, q, bytes) || overlaps(out, k, bytes) || overlaps(out, v, bytes))
+        return fail(BRA_ERR_ALIAS, "bra_forward: out must not overlap q, k or v");
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail_hip(e, "bra_forward: hipGetDevice");
+    if (dev != h->device) return fail(BRA_ERR_DEVICE, "bra_forward: wrong current device");
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const bool timed = h->timing_used < h->timing_capacity;
+    hipEvent_t* ev = timed ? &h->events[3 * h->timing_used] : nullptr;
+    if (timed && (e = hipEventRecord(ev[0], s)) != hipSuccess)
+        return fail_hip(e, "bra_forward: hipEventRecord");
+    e = bra::launch_pool_k(h->params, h->bf16, k, h->kbar, s);
+    if (e != hipSuccess) return fail_hip(e, "bra_forward: region-pool launch");
+    if (timed && (e = hipEventRecord(ev[1], s)) != hipSuccess)
+        return fail_hip(e, "bra_forward: hipEventRecord");
+    e = bra::launch_route_attend(h->params, h->bf16, q, k, v, h->kbar, lepe_w, lepe_b, out,
+                                 routing_idx, s);
+    if (e != hipSuccess) return fail_hip(e, "bra_forward: routing/attention launch");
+    if (timed) {
+        if ((e = hipEventRecord(ev[2], s)) != hipSuccess)
+            return fail_hip(e, "bra_forward: hipEventRecord");
+        ++h->timing_used;
+    }
+    return BRA_OK;
+}
+
+bra_status_t bra_timing_enable(bra_handle_t h, int32_t n) {
+    if (!is_live(h)) return fail(BRA_ERR_BAD_HANDLE, "bra_timing_enable: not a live handle");
+    if (n < 0) return fail(BRA_ERR_SHAPE, "bra_timing_enable: n must be >= 0");
+    release_events(h);
+    h->events.resize(static_cast<size_t>(3) * n);
+    for (size_t i = 0; i < h->events.size(); ++i) {
+        hipError_t e = hipEventCreate(&h->events[i]);
+        if (e != hipSuccess) {
+            h->events.resize(i);
+            release_events(h);
+            return fail_hip(e, "bra_timing_enable: hipEventCreate");
+        }
+    }
+    h->timing_capacity = n;
+    h->timing_used = 0;
+    return BRA_OK;
+}
+
+bra_status_t bra_timing_read(bra_handle_t h, float* ms, int32_t* count) {
+    if (!is_live(h)) return fail(BRA_ERR_BAD_HANDLE, "bra_timing_read: not a live handle");
+    if (!ms || !count) return fail(BRA_ERR_NULL, "bra_timing_read: ms and count are required");
+    *count = 0;
+    for (int i = 0; i < h->timing_used; ++i) {
+        hipEvent_t* ev = &h->events[3 * i];
+        hipError_t e = hipEventSynchronize(ev[2]);
+        if (e != hipSuccess) return fail_hip(e, "bra_timing_read: hipEventSynchronize");
+        float a = 0.f, b = 0.f;
+        if ((e = hipEventElapsedTime(&a, ev[0], ev[1])) != hipSuccess ||
+            (e = hipEventElapsedTime(&b, ev[1], ev[2])) != hipSuccess)
+            return fail_hip(e, "bra_timing_read: hipEventElapsedTime");
+        ms[2 * i] = a;
+        ms[2 * i + 1] = b;
+    }
+    *count = h->timing_used;
+    h->timing_used = 0;
+    return BRA_OK;
+}
+
+}  // extern "C"
