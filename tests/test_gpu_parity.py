@@ -30,6 +30,10 @@ SMALL = [
     Workload("single_region", 2, 8, 8, 64, 2, 1, 1, "bf16", 106),
     Workload("sixteen_heads_t1", 2, 7, 7, 512, 16, 7, 49, "bf16", 107),
     Workload("smooth_highres_b1", 1, 128, 128, 64, 2, 16, 16, "bf16", 108, smooth=True),
+    Workload("stage1_shape_bias", 2, 56, 56, 64, 2, 7, 1, "bf16", 116, lepe_bias=True),
+    Workload("stage2_shape_bias", 2, 28, 28, 128, 4, 7, 4, "bf16", 117, lepe_bias=True),
+    Workload("highres_shape_bias", 1, 128, 128, 64, 2, 16, 16, "bf16", 118, smooth=True,
+             lepe_bias=True),
     Workload("f32_stage2_shape", 4, 28, 28, 128, 4, 7, 4, "f32", 109),
     Workload("f32_ragged_bias", 2, 12, 20, 64, 2, 4, 3, "f32", 110, lepe_bias=True),
 ]

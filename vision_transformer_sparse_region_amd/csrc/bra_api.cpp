@@ -21,8 +21,10 @@ struct bra_handle_s {
     bra::Params params;
     bool bf16;
     int device;
-    double* kbar;        // [B, heads, R, 32] fp64 region means of K
-    size_t kbar_bytes;
+    double* means;       // [2][B, heads, R, 32] fp64 region means of Q, then of K,
+                         // followed by the MFMA LePE operand table
+    size_t means_bytes;
+    uint2* lepe_table;
     // per-kernel timing (events recorded by bra_forward while slots remain)
     std::vector<hipEvent_t> events;  // 3 per recorded call
     int timing_capacity;
@@ -124,15 +126,18 @@ bra_status_t bra_create(const bra_config_t* cfg, bra_handle_t* out) {
     h->params = p;
     h->bf16 = bf16;
     h->device = dev;
-    h->kbar_bytes = static_cast<size_t>(c.batch) * c.channels * R * sizeof(double);
-    h->kbar = nullptr;
+    const size_t mean_bytes = 2 * static_cast<size_t>(c.batch) * c.channels * R * sizeof(double);
+    h->means_bytes = mean_bytes + static_cast<size_t>(p.table_items) * sizeof(uint2);
+    h->means = nullptr;
+    h->lepe_table = nullptr;
     h->timing_capacity = 0;
     h->timing_used = 0;
-    e = hipMalloc(reinterpret_cast<void**>(&h->kbar), h->kbar_bytes);
+    e = hipMalloc(reinterpret_cast<void**>(&h->means), h->means_bytes);
     if (e != hipSuccess) {
         delete h;
         return fail_hip(e, "bra_create: hipMalloc of the workspace");
     }
+    h->lepe_table = reinterpret_cast<uint2*>(reinterpret_cast<char*>(h->means) + mean_bytes);
     {
         std::lock_guard<std::mutex> lock(g_mutex);
         g_live.insert(h);
@@ -148,7 +153,7 @@ bra_status_t bra_destroy(bra_handle_t h) {
         if (!g_live.erase(h)) return fail(BRA_ERR_BAD_HANDLE, "bra_destroy: not a live handle");
     }
     release_events(h);
-    hipError_t e = hipFree(h->kbar);
+    hipError_t e = hipFree(h->means);
     delete h;
     if (e != hipSuccess) return fail_hip(e, "bra_destroy: hipFree");
     return BRA_OK;
@@ -183,11 +188,12 @@ bra_status_t bra_forward(bra_handle_t h, const void* q, const void* k, const voi
     hipEvent_t* ev = timed ? &h->events[3 * h->timing_used] : nullptr;
     if (timed && (e = hipEventRecord(ev[0], s)) != hipSuccess)
         return fail_hip(e, "bra_forward: hipEventRecord");
-    e = bra::launch_pool_k(h->params, h->bf16, k, h->kbar, s);
+    e = bra::launch_pool_qk(h->params, h->bf16, q, k, lepe_w, h->means, h->lepe_table, s);
     if (e != hipSuccess) return fail_hip(e, "bra_forward: region-pool launch");
     if (timed && (e = hipEventRecord(ev[1], s)) != hipSuccess)
         return fail_hip(e, "bra_forward: hipEventRecord");
-    e = bra::launch_route_attend(h->params, h->bf16, q, k, v, h->kbar, lepe_w, lepe_b, out,
+    e = bra::launch_route_attend(h->params, h->bf16, q, k, v, h->means, lepe_w, lepe_b,
+                                 h->lepe_table, out,
                                  routing_idx, s);
     if (e != hipSuccess) return fail_hip(e, "bra_forward: routing/attention launch");
     if (timed) {

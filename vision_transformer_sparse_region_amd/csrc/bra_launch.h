@@ -7,13 +7,17 @@
 
 namespace bra {
 
-constexpr int kHeadDim = 32;   // the only head_dim the kernels implement
-constexpr int kThreads = 256;  // threads per workgroup (4 wave64s)
+constexpr int kHeadDim = 32;     // the only head_dim the kernels implement
+constexpr int kThreads = 256;    // threads per workgroup (4 wave64s)
 constexpr int kWaves = kThreads / 64;
 constexpr int kMaxLdsBytes = 64 * 1024;
 constexpr int kPoolChunkBytes = 16 * 1024;
-constexpr int kVtStride = 36;   // bf16 elements per staged V row (32 dims + pad)
-constexpr int kMaxQTiles = 4;   // 16-query tiles one wave carries at once
+constexpr int kVtStride = 36;    // bf16 elements per staged V row (32 dims + pad)
+constexpr int kMaxQTiles = 2;    // 16-query tiles one wave carries at once
+constexpr int kLepeCols = 8;     // output columns one LePE work item covers
+constexpr int kHaloRegs = 8;     // 16-byte halo pieces a thread keeps in flight
+constexpr int kWRegs = 2;        // 16-byte LePE weight pieces a thread keeps in flight
+constexpr int kMaxChannels = 1024;
 
 // Problem geometry plus the on-chip layout of the routing/attention kernel.
 struct Params {
@@ -24,10 +28,17 @@ struct Params {
     int nkeys;       // k * t keys per query
     float scale_log2e;
     int has_lepe;
-    // LDS byte offsets (routing/attention kernel)
-    int qstride;     // elements per staged Q row (C plus padding)
-    int off_q, off_vt, off_o, off_vh, off_aff, off_qbar, off_idx, lds_bytes;
-    int pool_chunk;  // tokens staged per step by the pool kernel
+    int lstride;     // floats per staged output row (C plus 16 bytes)
+    int lepe_items;  // (channel pair, window row, 8-column block) work items
+    int lepe_alias;  // 1: outputs overwrite the V halo after a single LePE round
+    int lepe_mfma;   // 1: LePE on the 4x4x4 MFMA with a channel-planar halo
+    int halo_pieces; // 16-byte pieces of the V window with its 2-token halo
+    // LDS byte offsets of the routing/attention kernel
+    int off_vt, off_aff, off_vh, off_l, off_w, off_idx, lds_bytes;
+    int table_items; // 8-byte entries of the MFMA LePE Toeplitz operand table (0: none)
+    // region-pool kernel
+    int pool_blocks; // workgroups computing means (the table follows them)
+    int pool_chunk;  // staged path: tokens staged per step
     int pool_lds_bytes;
 };
 
@@ -36,11 +47,15 @@ bool plan(Params& p, int B, int H, int W, int C, int heads, int n_win, int k, fl
           bool bf16);
 
 // Kernel launches on `stream`; return the launch status.
-hipError_t launch_pool_k(const Params& p, bool bf16, const void* k, double* kbar,
-                         hipStream_t stream);
+//   means: [2][B][heads][R][32] fp64 -- region means of Q, then of K.
+//   lepe_table: p.table_items 8-byte entries (written by the pool kernel when
+//   lepe_w is given and the shape runs LePE on MFMA).
+hipError_t launch_pool_qk(const Params& p, bool bf16, const void* q, const void* k,
+                          const float* lepe_w, double* means, uint2* lepe_table,
+                          hipStream_t stream);
 hipError_t launch_route_attend(const Params& p, bool bf16, const void* q, const void* k,
-                               const void* v, const double* kbar, const float* lepe_w,
-                               const float* lepe_b, void* out, int32_t* routing_idx,
-                               hipStream_t stream);
+                               const void* v, const double* means, const float* lepe_w,
+                               const float* lepe_b, const uint2* lepe_table, void* out,
+                               int32_t* routing_idx, hipStream_t stream);
 
 }  // namespace bra
