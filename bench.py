@@ -2,8 +2,8 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload stage1]
 
-A step is one bra_forward (region-pool kernel + routing/attention/LePE
-kernel) over one batch of the workload, inputs already in HBM.  By default
+A step is one bra_forward (region-means kernel, routing kernel,
+attention/LePE kernel) over one batch of the workload, inputs already in HBM.  By default
 the steps rotate over enough input/output buffer sets that consecutive steps
 never find their inputs in the 256 MB last-level cache (MALL), so the
 figures are HBM figures.  Prints one JSON line with the throughput, the
@@ -26,7 +26,7 @@ if ROOT not in sys.path:
 METRIC = "BRA fwd tokens/s (bf16) + % HBM roofline / % MFMA peak vs CPU oracle"
 HBM_PEAK_GBS = 8000.0
 MALL_BYTES = 256 << 20
-KERNEL_SRC = os.path.join(ROOT, "vision_transformer_sparse_region_amd", "csrc", "bra_kernels.hip")
+KERNEL_SRC = os.path.join(ROOT, "vision_transformer_sparse_region_amd", "csrc", "bra_attend.hip")
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -58,7 +58,7 @@ def attention_flops(wl) -> float:
 def stored_traffic(workload: str):
     """HBM bytes per launch of the attention kernel from the committed counter
     summary, or None when absent or taken on a different kernel source."""
-    path = os.path.join(PROFILES, f"route_attend_{workload}_traffic.json")
+    path = os.path.join(PROFILES, f"attend_{workload}_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -172,7 +172,8 @@ def main(argv=None) -> int:
     ms_per_step = gpu_ms / args.steps
     tokens_per_s = wl.tokens / (ms_per_step * 1e-3)
     pool_ms = sum(t[0] for t in times) / len(times)
-    attn_ms = sum(t[1] for t in times) / len(times)
+    route_ms = sum(t[1] for t in times) / len(times)
+    attn_ms = sum(t[2] for t in times) / len(times)
     ab = algorithmic_bytes(wl)
     achieved = ab["attend"] / (attn_ms * 1e-3) / 1e9
     traffic = stored_traffic(wl.name)
@@ -194,12 +195,12 @@ def main(argv=None) -> int:
             "batch": wl.batch, "height": wl.height, "width": wl.width,
             "channels": wl.channels, "num_heads": wl.num_heads, "n_win": wl.n_win,
             "topk": wl.topk, "buffer_sets": nsets,
-            "kernel_ms": {"region_pool": pool_ms, "route_attend": attn_ms},
+            "kernel_ms": {"region_pool": pool_ms, "route": route_ms, "attend": attn_ms},
             "wall_s": wall,
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "route_attend",
+            "kernel": "attend",
             "achieved": achieved,
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",

@@ -62,8 +62,8 @@ typedef enum {
     BRA_ERR_NULL = 1,        /* a required pointer is NULL */
     BRA_ERR_SHAPE = 2,       /* sizes not positive, H or W not divisible by n_win,
                                 C not divisible by num_heads, or too large for int32 indexing */
-    BRA_ERR_UNSUPPORTED = 3, /* head_dim != 32, unknown dtype, or a region too large
-                                for the kernels' on-chip tiles */
+    BRA_ERR_UNSUPPORTED = 3, /* head_dim != 32, unknown dtype, n_win > 16,
+                                or a region too large for the kernels' on-chip tiles */
     BRA_ERR_HIP = 4,         /* a HIP runtime call failed (see bra_last_error) */
     BRA_ERR_NOMEM = 5,       /* device memory for the workspace could not be allocated */
     BRA_ERR_BAD_HANDLE = 6,  /* not a live handle (never created, or destroyed) */
@@ -83,13 +83,16 @@ typedef struct {
     float scale;       /* attention logit scale; <= 0 means head_dim^-0.5 */
 } bra_config_t;
 
-/* Validate cfg and allocate the handle and its device workspace (the fp64
- * region means of K, B*C*R*8 bytes) on the current HIP device.  On success
- * *out is a live handle; on failure *out is left NULL. */
+/* Validate cfg and allocate the handle and its device workspace on the
+ * current HIP device: the fp64 region means of Q and K (2*B*C*R*8 bytes), a
+ * routing buffer (B*heads*R*k*4 bytes) and, for window shapes whose LePE
+ * runs on MFMA, a C*320-byte operand table.  On success *out is a live
+ * handle; on failure *out is left NULL. */
 bra_status_t bra_create(const bra_config_t* cfg, bra_handle_t* out);
 
 /* Enqueue the forward pass on `stream` (a hipStream_t; NULL = the null
- * stream) and return without synchronising.  No allocation happens here.
+ * stream) as three kernels -- region means, routing, attention + LePE -- and
+ * return without synchronising.  No allocation happens here.
  *   q, k, v       device, [B,H,W,C], dtype, 16-byte aligned
  *   lepe_w        device [C,5,5] fp32, or NULL for no LePE term (lepe_b is then ignored)
  *   lepe_b        device [C] fp32, or NULL for a zero bias
@@ -114,11 +117,12 @@ const char* bra_status_string(bra_status_t s);
 const char* bra_last_error(void);
 
 /* Per-kernel timing for profiling.  bra_timing_enable(h, n) makes the next n
- * calls of bra_forward record HIP events around each of its kernels on the
- * call's stream (n = 0 turns recording off).  bra_timing_read waits for the
- * recorded events and writes, for each recorded call i < *count,
- * ms[2*i] = region-pool kernel time and ms[2*i+1] = routing/attention kernel
- * time (milliseconds), then clears the record.  `ms` holds at least 2*n floats. */
+ * calls of bra_forward record HIP events around each of its three kernels on
+ * the call's stream (n = 0 turns recording off).  bra_timing_read waits for
+ * the recorded events and writes, for each recorded call i < *count,
+ * ms[3*i] = region-pool kernel, ms[3*i+1] = routing kernel and
+ * ms[3*i+2] = attention/LePE kernel time (milliseconds), then clears the
+ * record.  `ms` holds at least 3*n floats. */
 bra_status_t bra_timing_enable(bra_handle_t h, int32_t n);
 bra_status_t bra_timing_read(bra_handle_t h, float* ms, int32_t* count);
 

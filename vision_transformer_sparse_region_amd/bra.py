@@ -165,12 +165,16 @@ def bra_timing_enable(h, n: int) -> None:
     _check(load_library().bra_timing_enable(h, n), "bra_timing_enable")
 
 
+KERNELS = ("region_pool", "route", "attend")
+
+
 def bra_timing_read(h, capacity: int):
-    """Return a list of (pool_ms, attend_ms), one per recorded forward."""
-    buf = (ctypes.c_float * (2 * max(capacity, 1)))()
+    """Return a list of (pool_ms, route_ms, attend_ms), one per recorded forward."""
+    n = len(KERNELS)
+    buf = (ctypes.c_float * (n * max(capacity, 1)))()
     cnt = ctypes.c_int32()
     _check(load_library().bra_timing_read(h, buf, ctypes.byref(cnt)), "bra_timing_read")
-    return [(buf[2 * i], buf[2 * i + 1]) for i in range(cnt.value)]
+    return [tuple(buf[n * i + j] for j in range(n)) for i in range(cnt.value)]
 
 
 # ---- convenience wrapper ---------------------------------------------------

@@ -16,10 +16,12 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG, "libbra.so")
-SOURCES = [os.path.join(CSRC, "bra_kernels.hip"), os.path.join(CSRC, "bra_api.cpp")]
+SOURCES = [os.path.join(CSRC, n) for n in
+           ("bra_pool.hip", "bra_route.hip", "bra_attend.hip", "bra_api.cpp")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
+BUILD_TIMEOUT_S = 600  # a compile that runs longer is a code-size blow-up, not progress
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -37,13 +39,13 @@ def build_library(out: str = LIB_PATH, extra_flags=(), verbose: bool = False) ->
         cmd = [HIPCC, *FLAGS, *extra_flags, *lang, "-c", src, "-o", obj]
         if verbose:
             print(" ".join(cmd), file=sys.stderr)
-        subprocess.run(cmd, check=True)
+        subprocess.run(cmd, check=True, timeout=BUILD_TIMEOUT_S)
         objs.append(obj)
     tmp = out + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), file=sys.stderr)
-    subprocess.run(cmd, check=True)
+    subprocess.run(cmd, check=True, timeout=BUILD_TIMEOUT_S)
     os.replace(tmp, out)
     for obj in objs:
         os.remove(obj)

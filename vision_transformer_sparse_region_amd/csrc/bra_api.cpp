@@ -21,17 +21,21 @@ struct bra_handle_s {
     bra::Params params;
     bool bf16;
     int device;
-    double* means;       // [2][B, heads, R, 32] fp64 region means of Q, then of K,
-                         // followed by the MFMA LePE operand table
+    double* means;       // workspace: [2][B, heads, R, 32] fp64 region means of Q, then
+                         // of K; the routing [B, heads, R, k] int32; the MFMA LePE
+                         // operand table
     size_t means_bytes;
+    int32_t* routing;
     uint2* lepe_table;
     // per-kernel timing (events recorded by bra_forward while slots remain)
-    std::vector<hipEvent_t> events;  // 3 per recorded call
+    std::vector<hipEvent_t> events;  // kEventsPerCall per recorded call
     int timing_capacity;
     int timing_used;
 };
 
 namespace {
+
+constexpr int kEventsPerCall = 4;  // before pool, route, attend; after attend
 
 std::mutex g_mutex;
 std::set<bra_handle_t> g_live;  // handles between create and destroy
@@ -127,8 +131,11 @@ bra_status_t bra_create(const bra_config_t* cfg, bra_handle_t* out) {
     h->bf16 = bf16;
     h->device = dev;
     const size_t mean_bytes = 2 * static_cast<size_t>(c.batch) * c.channels * R * sizeof(double);
-    h->means_bytes = mean_bytes + static_cast<size_t>(p.table_items) * sizeof(uint2);
+    const size_t route_bytes =
+        ((static_cast<size_t>(c.batch) * c.num_heads * R * k * sizeof(int32_t)) + 15) & ~size_t{15};
+    h->means_bytes = mean_bytes + route_bytes + static_cast<size_t>(p.table_items) * sizeof(uint2);
     h->means = nullptr;
+    h->routing = nullptr;
     h->lepe_table = nullptr;
     h->timing_capacity = 0;
     h->timing_used = 0;
@@ -137,7 +144,9 @@ bra_status_t bra_create(const bra_config_t* cfg, bra_handle_t* out) {
         delete h;
         return fail_hip(e, "bra_create: hipMalloc of the workspace");
     }
-    h->lepe_table = reinterpret_cast<uint2*>(reinterpret_cast<char*>(h->means) + mean_bytes);
+    h->routing = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(h->means) + mean_bytes);
+    h->lepe_table =
+        reinterpret_cast<uint2*>(reinterpret_cast<char*>(h->means) + mean_bytes + route_bytes);
     {
         std::lock_guard<std::mutex> lock(g_mutex);
         g_live.insert(h);
@@ -185,19 +194,24 @@ bra_status_t bra_forward(bra_handle_t h, const void* q, const void* k, const voi
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     const bool timed = h->timing_used < h->timing_capacity;
-    hipEvent_t* ev = timed ? &h->events[3 * h->timing_used] : nullptr;
+    hipEvent_t* ev = timed ? &h->events[kEventsPerCall * h->timing_used] : nullptr;
     if (timed && (e = hipEventRecord(ev[0], s)) != hipSuccess)
         return fail_hip(e, "bra_forward: hipEventRecord");
     e = bra::launch_pool_qk(h->params, h->bf16, q, k, lepe_w, h->means, h->lepe_table, s);
     if (e != hipSuccess) return fail_hip(e, "bra_forward: region-pool launch");
     if (timed && (e = hipEventRecord(ev[1], s)) != hipSuccess)
         return fail_hip(e, "bra_forward: hipEventRecord");
-    e = bra::launch_route_attend(h->params, h->bf16, q, k, v, h->means, lepe_w, lepe_b,
-                                 h->lepe_table, out,
-                                 routing_idx, s);
-    if (e != hipSuccess) return fail_hip(e, "bra_forward: routing/attention launch");
+    // the routing goes to the caller's buffer when one is given
+    int32_t* routing = routing_idx ? routing_idx : h->routing;
+    e = bra::launch_route(h->params, h->bf16, h->means, routing, s);
+    if (e != hipSuccess) return fail_hip(e, "bra_forward: routing launch");
+    if (timed && (e = hipEventRecord(ev[2], s)) != hipSuccess)
+        return fail_hip(e, "bra_forward: hipEventRecord");
+    e = bra::launch_attend(h->params, h->bf16, q, k, v, routing, lepe_w, lepe_b, h->lepe_table,
+                           out, s);
+    if (e != hipSuccess) return fail_hip(e, "bra_forward: attention launch");
     if (timed) {
-        if ((e = hipEventRecord(ev[2], s)) != hipSuccess)
+        if ((e = hipEventRecord(ev[3], s)) != hipSuccess)
             return fail_hip(e, "bra_forward: hipEventRecord");
         ++h->timing_used;
     }
@@ -208,7 +222,7 @@ bra_status_t bra_timing_enable(bra_handle_t h, int32_t n) {
     if (!is_live(h)) return fail(BRA_ERR_BAD_HANDLE, "bra_timing_enable: not a live handle");
     if (n < 0) return fail(BRA_ERR_SHAPE, "bra_timing_enable: n must be >= 0");
     release_events(h);
-    h->events.resize(static_cast<size_t>(3) * n);
+    h->events.resize(static_cast<size_t>(kEventsPerCall) * n);
     for (size_t i = 0; i < h->events.size(); ++i) {
         hipError_t e = hipEventCreate(&h->events[i]);
         if (e != hipSuccess) {
@@ -227,15 +241,15 @@ bra_status_t bra_timing_read(bra_handle_t h, float* ms, int32_t* count) {
     if (!ms || !count) return fail(BRA_ERR_NULL, "bra_timing_read: ms and count are required");
     *count = 0;
     for (int i = 0; i < h->timing_used; ++i) {
-        hipEvent_t* ev = &h->events[3 * i];
-        hipError_t e = hipEventSynchronize(ev[2]);
+        hipEvent_t* ev = &h->events[kEventsPerCall * i];
+        hipError_t e = hipEventSynchronize(ev[kEventsPerCall - 1]);
         if (e != hipSuccess) return fail_hip(e, "bra_timing_read: hipEventSynchronize");
-        float a = 0.f, b = 0.f;
-        if ((e = hipEventElapsedTime(&a, ev[0], ev[1])) != hipSuccess ||
-            (e = hipEventElapsedTime(&b, ev[1], ev[2])) != hipSuccess)
-            return fail_hip(e, "bra_timing_read: hipEventElapsedTime");
-        ms[2 * i] = a;
-        ms[2 * i + 1] = b;
+        for (int j = 0; j < kEventsPerCall - 1; ++j) {
+            float x = 0.f;
+            if ((e = hipEventElapsedTime(&x, ev[j], ev[j + 1])) != hipSuccess)
+                return fail_hip(e, "bra_timing_read: hipEventElapsedTime");
+            ms[(kEventsPerCall - 1) * i + j] = x;
+        }
     }
     *count = h->timing_used;
     h->timing_used = 0;

@@ -1,0 +1,769 @@
+// bra_attend.hip -- token attention over the routed regions plus LePE, one
+// workgroup per (image, region), all heads (page keys in bra_device.h).
+//
+//   1  issue every load at once: the routed region ids of this region
+//      (written by the routing kernel), the LePE weights or the Toeplitz LePE
+//      operands, the V window with its 2-token halo, the first job's Q
+//      operands                                                [P5 §五 ⑤]
+//   2  each wave issues the gather of its first routed K/V chunk ...
+//   3  ... the halo goes to LDS and the 5x5 depthwise LePE of V runs while
+//      those loads are in flight                       [P5 §五 lepe, ⑧; P2 §2.2]
+//   4  token attention over the routed tokens: S^T = K Q^T and O^T += V^T P^T
+//      on bf16 MFMA (fp32 VALU for fp32 input), fp32 online softmax, the next
+//      chunk's gather in flight during each chunk         [P3 §2.2; P5 §五 ⑤-⑦]
+//   5  out = LePE + O, one rounding, 16-byte NHWC stores
+// The routed K/V tokens are never copied to HBM: [P3 §4.2] and [P1 §2.2]
+// build a dense k-fold gathered tensor with torch.gather; here the routing
+// index drives the loads straight into MFMA operands.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "bra_device.h"
+#include "bra_shapes.h"
+
+namespace bra {
+namespace {
+
+// ---------------------------------------------------------------------------
+// bf16 MFMA token attention.
+//
+// A wave owns "jobs": one head and up to kMaxQTiles tiles of 16 query tokens.
+// Keys stream in chunks of 32; the wave's (job, chunk) steps are flattened so
+// that the gather of step s+1 is in flight while step s computes.  For a
+// chunk, two v_mfma_f32_16x16x32_bf16 give S^T (keys x queries): operand A
+// row i (lane & 15) is the key 32c + 8*(i/4) + 4*blk + i%4, so that output
+// lane (query li, group g = lane/16) holds the scores of the 8 consecutive
+// keys 32c + 8g .. 32c + 8g + 7.  Those 8 probabilities are exactly that
+// lane's B operand of O^T += V^T P^T (k-slot 8g + e = key 32c + 8g + e), so P
+// never leaves registers; V^T is read transposed from a per-wave LDS buffer.
+// O^T lands with the query on lane & 15 like the scores, so the online-softmax
+// rescale is lane-local.
+struct WaveJobs {
+    int QT, G, tpg, njobs, nchunks, nsteps;
+    __device__ __forceinline__ WaveJobs(const Params& p, int w) {
+        QT = (p.t + 15) / 16;
+        const int wph = max(1, kWaves / p.heads);
+        const int g0 = max(min(wph, QT), (QT + kMaxQTiles - 1) / kMaxQTiles);
+        tpg = (QT + g0 - 1) / g0;
+        G = (QT + tpg - 1) / tpg;  // every group non-empty
+        njobs = p.heads * G;
+        nchunks = (p.nkeys + 31) / 32;
+        const int mine = w < njobs ? (njobs - 1 - w) / kWaves + 1 : 0;
+        nsteps = mine * nchunks;
+    }
+};
+
+// Registers of one (job, chunk) step: the two K^T operands (16 B per lane)
+// and this lane's two 16-byte pieces of the 32-key x 32-dim V chunk.
+struct StepRegs {
+    bf16x8_t ka[2];
+    uint4 vv[2];
+};
+
+// Q^T operands of a job: lane (query li, group g) holds dims 8g..8g+7 of
+// query (qt0 + jq) * 16 + li of head h (zero past the window).
+__device__ __forceinline__ void load_q_operands(const Params& p, const WaveJobs& J, int job,
+                                                const uint16_t* __restrict__ qimg, int r,
+                                                bf16x8_t (&qb)[kMaxQTiles]) {
+    const int lane = threadIdx.x & 63, li = lane & 15, g = lane >> 4;
+    const int h = job / J.G, grp = job - h * J.G;
+    const int qt0 = grp * J.tpg;
+    const int nq = min(J.tpg, J.QT - qt0);
+#pragma unroll
+    for (int jq = 0; jq < kMaxQTiles; ++jq) {
+        const int qi = (qt0 + jq) * 16 + li;
+        uint4 u = {0u, 0u, 0u, 0u};
+        if (jq < nq && qi < p.t)
+            u = *reinterpret_cast<const uint4*>(qimg + token_offset(p, r, qi) + h * kHeadDim +
+                                                8 * g);
+        qb[jq] = __builtin_bit_cast(bf16x8_t, u);
+    }
+}
+
+__device__ __forceinline__ void gather_step(const Params& p, const WaveJobs& J, int w, int step,
+                                            const uint16_t* __restrict__ kimg,
+                                            const uint16_t* __restrict__ vimg, const int* sIdx,
+                                            StepRegs& g8) {
+    const int lane = threadIdx.x & 63, li = lane & 15, g = lane >> 4;
+    const int jl = step / J.nchunks, c = step - jl * J.nchunks;
+    const int job = w + kWaves * jl;
+    const int h = job / J.G;
+    const int hoff = h * kHeadDim;
+    const int* idx = sIdx + h * p.k;
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+        const int key = 32 * c + 8 * (li >> 2) + 4 * blk + (li & 3);
+        uint4 u = {0u, 0u, 0u, 0u};
+        if (key < p.nkeys) {
+            const int j = key / p.t, slot = key - j * p.t;
+            u = *reinterpret_cast<const uint4*>(kimg + token_offset(p, idx[j], slot) + hoff +
+                                                8 * g);
+        }
+        g8.ka[blk] = __builtin_bit_cast(bf16x8_t, u);
+    }
+#pragma unroll
+    for (int pp = 0; pp < 2; ++pp) {
+        const int pc = lane + 64 * pp;
+        const int key = 32 * c + (pc >> 2);
+        uint4 u = {0u, 0u, 0u, 0u};
+        if (key < p.nkeys) {
+            const int j = key / p.t, slot = key - j * p.t;
+            u = *reinterpret_cast<const uint4*>(vimg + token_offset(p, idx[j], slot) + hoff +
+                                                8 * (pc & 3));
+        }
+        g8.vv[pp] = u;
+    }
+}
+
+__device__ __forceinline__ void attend_mfma(const Params& p, const WaveJobs& J, const uint16_t* __restrict__ qimg,
+                            const uint16_t* __restrict__ kimg, const uint16_t* __restrict__ vimg,
+                            int r, uint16_t* sVt_all, float* sL, const int* sIdx, StepRegs& cur,
+                            bf16x8_t (&qb)[kMaxQTiles]) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int li = lane & 15, g = lane >> 4;
+    uint16_t* sVt = sVt_all + w * 32 * kVtStride;
+
+    float m[kMaxQTiles], l[kMaxQTiles];
+    f32x4_t o0[kMaxQTiles], o1[kMaxQTiles];
+    for (int s = 0; s < J.nsteps; ++s) {
+        const int jl = s / J.nchunks, c = s - jl * J.nchunks;
+        const int job = w + kWaves * jl;
+        const int h = job / J.G, grp = job - h * J.G;
+        const int qt0 = grp * J.tpg;
+        const int nq = min(J.tpg, J.QT - qt0);
+        const int hoff = h * kHeadDim;
+        if (c == 0) {
+            // the first job's operands were loaded with its first gather
+            if (s > 0) load_q_operands(p, J, job, qimg, r, qb);
+#pragma unroll
+            for (int jq = 0; jq < kMaxQTiles; ++jq) {
+                m[jq] = -INFINITY;
+                l[jq] = 0.f;
+                o0[jq] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                o1[jq] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            }
+        }
+        StepRegs nxt;
+        if (s + 1 < J.nsteps) gather_step(p, J, w, s + 1, kimg, vimg, sIdx, nxt);
+
+        // This step's V chunk into the wave's LDS buffer, read back transposed.
+#pragma unroll
+        for (int pp = 0; pp < 2; ++pp) {
+            const int pc = lane + 64 * pp;
+            uint2* dst = reinterpret_cast<uint2*>(sVt + (pc >> 2) * kVtStride + 8 * (pc & 3));
+            dst[0] = uint2{cur.vv[pp].x, cur.vv[pp].y};
+            dst[1] = uint2{cur.vv[pp].z, cur.vv[pp].w};
+        }
+        // A wave's LDS operations complete in order; the fences keep the
+        // compiler from moving the transposed reads above the writes.
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        bf16x8_t va[2];
+#pragma unroll
+        for (int db = 0; db < 2; ++db) {
+            u16x8_t t8;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) t8[e] = sVt[(8 * g + e) * kVtStride + li + 16 * db];
+            va[db] = __builtin_bit_cast(bf16x8_t, t8);
+        }
+
+        const int kbase = 32 * c + 8 * g;
+#pragma unroll
+        for (int jq = 0; jq < kMaxQTiles; ++jq) {
+            if (jq >= nq) break;
+            const f32x4_t z4 = {0.f, 0.f, 0.f, 0.f};
+            const f32x4_t s0 =
+                __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur.ka[0], qb[jq], z4, 0, 0, 0);
+            const f32x4_t s1 =
+                __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur.ka[1], qb[jq], z4, 0, 0, 0);
+            // raw scores; the running max m is kept in raw units and the
+            // scale * log2(e) factor enters each exponent through one FMA
+            float x[8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                x[e] = s0[e];
+                x[4 + e] = s1[e];
+            }
+            if (kbase + 8 > p.nkeys) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    if (kbase + e >= p.nkeys) x[e] = -INFINITY;
+            }
+            const float mx = group4_max(fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
+                                              fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7]))));
+            const float mnew = fmaxf(m[jq], mx);
+            const float alpha = __builtin_amdgcn_exp2f((m[jq] - mnew) * p.scale_log2e);
+            const float mb = mnew * p.scale_log2e;
+            float psum = 0.f;
+            bf16x8_t pb;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float pe = __builtin_amdgcn_exp2f(fmaf(x[e], p.scale_log2e, -mb));
+                psum += pe;
+                pb[e] = static_cast<__bf16>(pe);
+            }
+            l[jq] = l[jq] * alpha + psum;
+            m[jq] = mnew;
+            o0[jq] *= alpha;
+            o1[jq] *= alpha;
+            o0[jq] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[0], pb, o0[jq], 0, 0, 0);
+            o1[jq] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[1], pb, o1[jq], 0, 0, 0);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+
+        if (c == J.nchunks - 1) {
+#pragma unroll
+            for (int jq = 0; jq < kMaxQTiles; ++jq) {
+                if (jq >= nq) break;
+                const float inv = __builtin_amdgcn_rcpf(group4_sum(l[jq]));
+                const int qi = (qt0 + jq) * 16 + li;
+                if (qi < p.t) {
+                    float* dst = sL + qi * p.lstride + hoff + 4 * g;
+                    const f32x4_t a = *reinterpret_cast<f32x4_t*>(dst);
+                    const f32x4_t bq = *reinterpret_cast<f32x4_t*>(dst + 16);
+                    *reinterpret_cast<f32x4_t*>(dst) = a + o0[jq] * inv;
+                    *reinterpret_cast<f32x4_t*>(dst + 16) = bq + o1[jq] * inv;
+                }
+            }
+        }
+        if (s + 1 < J.nsteps) cur = nxt;
+    }
+}
+
+// fp32 VALU token attention: 8 lanes per (query token, head), 4 dims each;
+// keys in routed order with an online softmax, the next key's loads in
+// flight while the current one is processed; fp32 throughout.
+__device__ __forceinline__ void attend_valu(const Params& p, const float* __restrict__ qimg,
+                            const float* __restrict__ kimg, const float* __restrict__ vimg, int r,
+                            float* sL, const int* sIdx) {
+    const int sub = threadIdx.x & 7;
+    for (int item = threadIdx.x >> 3; item < p.t * p.heads; item += kThreads / 8) {
+        const int h = item / p.t, slot = item - h * p.t;
+        const int hoff = h * kHeadDim + 4 * sub;
+        const float4 qv = *reinterpret_cast<const float4*>(qimg + token_offset(p, r, slot) + hoff);
+        const int* idx = sIdx + h * p.k;
+        float m = -INFINITY, l = 0.f;
+        float4 acc = {0.f, 0.f, 0.f, 0.f};
+        int off = token_offset(p, idx[0], 0) + hoff;
+        float4 kv = *reinterpret_cast<const float4*>(kimg + off);
+        float4 vv = *reinterpret_cast<const float4*>(vimg + off);
+        for (int key = 0; key < p.nkeys; ++key) {
+            float4 kn = kv, vn = vv;
+            if (key + 1 < p.nkeys) {
+                const int j = (key + 1) / p.t, ks = key + 1 - j * p.t;
+                const int o2 = token_offset(p, idx[j], ks) + hoff;
+                kn = *reinterpret_cast<const float4*>(kimg + o2);
+                vn = *reinterpret_cast<const float4*>(vimg + o2);
+            }
+            float d = qv.x * kv.x + qv.y * kv.y + qv.z * kv.z + qv.w * kv.w;
+            d += __shfl_xor(d, 1);
+            d += __shfl_xor(d, 2);
+            d += __shfl_xor(d, 4);
+            const float x = d * p.scale_log2e;
+            const float mnew = fmaxf(m, x);
+            const float alpha = __builtin_amdgcn_exp2f(m - mnew);
+            const float pe = __builtin_amdgcn_exp2f(x - mnew);
+            l = l * alpha + pe;
+            m = mnew;
+            acc.x = fmaf(pe, vv.x, acc.x * alpha);
+            acc.y = fmaf(pe, vv.y, acc.y * alpha);
+            acc.z = fmaf(pe, vv.z, acc.z * alpha);
+            acc.w = fmaf(pe, vv.w, acc.w * alpha);
+            kv = kn;
+            vv = vn;
+        }
+        const float inv = __builtin_amdgcn_rcpf(l);
+        float4* dst = reinterpret_cast<float4*>(sL + slot * p.lstride + hoff);
+        const float4 a = *dst;
+        *dst = float4{a.x + acc.x * inv, a.y + acc.y * inv, a.z + acc.z * inv, a.w + acc.w * inv};
+    }
+}
+
+// One LePE work item: channels c0, c0+1 of window row y, columns xs..xs+7
+// (fewer at the window's right edge), bias + 25 taps from the LDS halo.
+// Weights come from LDS (sW, [C][25] then the bias [C]) or from global memory.
+template <typename T>
+__device__ __forceinline__ void lepe_item(const Params& p, const T* sVh, const float* wsrc,
+                                          const float* bsrc, int c0, int y, int xs, int nx,
+                                          float (&acc)[2][kLepeCols]) {
+    float b0 = 0.f, b1 = 0.f;
+    if (p.has_lepe && bsrc) {
+        b0 = bsrc[c0];
+        b1 = bsrc[c0 + 1];
+    }
+#pragma unroll
+    for (int x = 0; x < kLepeCols; ++x) {
+        acc[0][x] = b0;
+        acc[1][x] = b1;
+    }
+    if (!p.has_lepe) return;
+    const int hw = p.ws + 4;
+#pragma unroll 1
+    for (int i = 0; i < 5; ++i) {
+        float w0[5], w1[5];
+#pragma unroll
+        for (int j = 0; j < 5; ++j) {
+            w0[j] = wsrc[c0 * 25 + i * 5 + j];
+            w1[j] = wsrc[(c0 + 1) * 25 + i * 5 + j];
+        }
+        const T* row = sVh + ((y + i) * hw + xs) * p.C + c0;
+        float in0[kLepeCols + 4], in1[kLepeCols + 4];
+#pragma unroll
+        for (int xx = 0; xx < kLepeCols + 4; ++xx) {
+            float2 v2 = {0.f, 0.f};
+            if (xx < nx + 4) v2 = Elem<T>::pair(row + xx * p.C);
+            in0[xx] = v2.x;
+            in1[xx] = v2.y;
+        }
+#pragma unroll
+        for (int x = 0; x < kLepeCols; ++x)
+#pragma unroll
+            for (int j = 0; j < 5; ++j) {
+                acc[0][x] = fmaf(w0[j], in0[x + j], acc[0][x]);
+                acc[1][x] = fmaf(w1[j], in1[x + j], acc[1][x]);
+            }
+    }
+}
+
+__device__ __forceinline__ void store_lepe(const Params& p, float* sL, int c0, int y, int xs,
+                                           int nx, const float (&acc)[2][kLepeCols]) {
+#pragma unroll
+    for (int x = 0; x < kLepeCols; ++x)
+        if (x < nx)
+            *reinterpret_cast<float2*>(sL + (y * p.ws + xs + x) * p.lstride + c0) =
+                float2{acc[0][x], acc[1][x]};
+}
+
+// The whole LePE step: every (channel pair, row, column block) item, written
+// to sL.  In alias mode sL overlays the halo, so the items (at most one per
+// thread) are computed first and stored after a barrier.  Ends with a barrier.
+template <typename T>
+__device__ __forceinline__ void lepe_phase(const Params& p, const T* sVh, float* sL, const float* wsrc,
+                           const float* bsrc) {
+    const int npairs = p.C / 2;
+    const int nxb = (p.ws + kLepeCols - 1) / kLepeCols;
+    float acc[2][kLepeCols];
+    int mine = -1;
+    for (int it = threadIdx.x; it < p.lepe_items; it += kThreads) {
+        const int cp = it % npairs, rest = it / npairs;
+        const int xb = rest % nxb, y = rest / nxb;
+        const int xs = xb * kLepeCols, nx = min(kLepeCols, p.ws - xs);
+        lepe_item<T>(p, sVh, wsrc, bsrc, 2 * cp, y, xs, nx, acc);
+        if (p.lepe_alias)
+            mine = it;
+        else
+            store_lepe(p, sL, 2 * cp, y, xs, nx, acc);
+    }
+    if (p.lepe_alias) {
+        __syncthreads();  // every halo read is done before sL overwrites it
+        if (mine >= 0) {
+            const int cp = mine % npairs, rest = mine / npairs;
+            const int xb = rest % nxb, y = rest / nxb;
+            const int xs = xb * kLepeCols;
+            store_lepe(p, sL, 2 * cp, y, xs, min(kLepeCols, p.ws - xs), acc);
+        }
+    }
+    __syncthreads();
+}
+
+// ---------------------------------------------------------------------------
+// LePE on the 4x4x4 MFMA with 16 independent blocks (bf16, fixed windows whose
+// sides are multiples of 4).  The depthwise 5x5 convolution has no channel
+// contraction, but v_mfma_f32_4x4x4_16b_bf16 runs 16 separate 4x4x4 products:
+// block b is one channel.  For a 4x4 output tile and tap row i,
+//   D[m][n] += sum_{k<4} A[m][k] B[k][n],  A[m][k] = V[y0+m+i][x0+4ks+k],
+//   B[k][n] = w[i][4ks+k-n] (zero outside 0..4),
+// over ks = 0, 1 covers the 8 halo columns a 4-wide tile reads, so ten
+// products give all 25 taps.  Lane l is block l/4; it holds A row l%4 (four
+// consecutive halo columns of one channel: the halo is staged channel-planar)
+// and B / D column l%4.  The Toeplitz B operands depend only on the channel
+// and the lane's column: the pool kernel writes them once per forward to a
+// small table (lepe_toeplitz_entry).  Weights enter the product as bf16 (the
+// accumulation is fp32).
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+
+// The Toeplitz B operands and the bias of this lane's channel in each of the
+// wave's channel groups, loaded from the table the pool kernel built.
+template <int HS, int WS, int HEADS>
+struct LepeOperands {
+    uint4 tb[LepeMfmaShape<HS, WS, HEADS>::GPW][5];  // 10 x 8 bytes per group
+    float bias[LepeMfmaShape<HS, WS, HEADS>::GPW];
+};
+
+template <int HS, int WS, int HEADS>
+__device__ __forceinline__ void lepe_mfma_load(const uint2* __restrict__ table,
+                                               const float* __restrict__ lepe_b,
+                                               LepeOperands<HS, WS, HEADS>& o) {
+    using S = LepeMfmaShape<HS, WS, HEADS>;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+    for (int g = 0; g < S::GPW; ++g) {
+        const int cg = w + kWaves * g;
+        o.bias[g] = 0.f;
+        if (cg < S::NG) {
+            const uint4* src = reinterpret_cast<const uint4*>(table + (cg * 64 + lane) * 10);
+#pragma unroll
+            for (int e = 0; e < 5; ++e) o.tb[g][e] = src[e];
+            if (lepe_b) o.bias[g] = lepe_b[16 * cg + (lane >> 2)];
+        }
+    }
+}
+
+template <int HS, int WS, int HEADS>
+__device__ __forceinline__ void lepe_mfma_compute(const Params& p, const uint16_t* sVp, float* sL,
+                                                  const LepeOperands<HS, WS, HEADS>& o) {
+    using S = LepeMfmaShape<HS, WS, HEADS>;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int blk = lane >> 2, n = lane & 3;
+    f32x4_t dacc[S::GPW][S::TY * S::TX];
+#pragma unroll
+    for (int g = 0; g < S::GPW; ++g) {
+        const int cg = w + kWaves * g;
+        if (cg < S::NG) {
+            const int c = 16 * cg + blk;
+            const uint16_t* plane = sVp + c * S::PS;
+#pragma unroll
+            for (int ty = 0; ty < S::TY; ++ty)
+#pragma unroll
+                for (int tx = 0; tx < S::TX; ++tx) {
+                    f32x4_t d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int i = 0; i < 5; ++i)
+#pragma unroll
+                        for (int ks = 0; ks < 2; ++ks) {
+                            const s16x4_t a = *reinterpret_cast<const s16x4_t*>(
+                                plane + (4 * ty + n + i) * S::HWP + 4 * tx + 4 * ks);
+                            const uint4 t4 = o.tb[g][i];
+                            const uint2 bw = ks == 0 ? uint2{t4.x, t4.y} : uint2{t4.z, t4.w};
+                            d = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(
+                                a, __builtin_bit_cast(s16x4_t, bw), d, 0, 0, 0);
+                        }
+                    dacc[g][ty * S::TX + tx] = d;
+                }
+        }
+    }
+    __syncthreads();  // every halo read is done; sL overlays the halo
+#pragma unroll
+    for (int g = 0; g < S::GPW; ++g) {
+        const int cg = w + kWaves * g;
+        if (cg < S::NG) {
+            const int c = 16 * cg + blk;
+#pragma unroll
+            for (int ty = 0; ty < S::TY; ++ty)
+#pragma unroll
+                for (int tx = 0; tx < S::TX; ++tx)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        sL[((4 * ty + e) * WS + 4 * tx + n) * p.lstride + c] =
+                            dacc[g][ty * S::TX + tx][e] + o.bias[g];
+        }
+    }
+    __syncthreads();
+}
+
+// ---------------------------------------------------------------------------
+// Fixed shapes whose LePE runs on MFMA need little LDS; all instances are
+// compiled for four waves per SIMD (more waves per SIMD did not pay: the
+// extra register pressure spills).
+template <typename T, int HS, int WS, int NW, int HEADS, int KTOP>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))) void
+attend_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+              const int32_t* __restrict__ routing, const float* __restrict__ lepe_w,
+              const float* __restrict__ lepe_b, const uint2* __restrict__ lepe_table,
+              T* __restrict__ out, Params p_in) {
+    const Params p = fold_geometry<HS, WS, NW, HEADS, KTOP, Elem<T>::kVec>(p_in);
+    extern __shared__ __align__(16) unsigned char smem[];
+    T* sVh = reinterpret_cast<T*>(smem + p.off_vh);
+    float* sL = reinterpret_cast<float*>(smem + p.off_l);
+    float* sW = reinterpret_cast<float*>(smem + p.off_w);
+    int* sIdx = reinterpret_cast<int*>(smem + p.off_idx);
+    const bool w_in_lds = p.off_w >= 0;
+
+    constexpr int VEC = Elem<T>::kVec;
+    constexpr bool kLepeMfma = VEC == 8 && LepeMfmaShape<HS, WS, HEADS>::ok;
+    const int tid = threadIdx.x, w = tid >> 6;
+    const int blk = xcd_logical_block(blockIdx.x, gridDim.x);
+    const int b = blk / p.R, r = blk - b * p.R;
+    const int y0 = (r / p.n) * p.hs, x0 = (r % p.n) * p.ws;
+    const size_t img = static_cast<size_t>(b) * p.H * p.W * p.C;
+    const int nvec = p.C / VEC;
+    const int hw = p.ws + 4;
+
+    // 1. Issue every load that does not depend on the routing first.
+    //    LePE weights and bias (nw + nb 16-byte pieces, VALU LePE with
+    //    weights in LDS): the first kWRegs pieces of each thread ride in
+    //    registers and are stored once all loads are issued.
+    const int nw = p.C * 25 / 4, nb = lepe_b ? p.C / 4 : 0;
+    const bool stage_w = !kLepeMfma && w_in_lds && p.has_lepe;
+    float4 wreg[kWRegs];
+#pragma unroll
+    for (int u = 0; u < kWRegs; ++u) {
+        const int i = tid + u * kThreads;
+        if (stage_w && i < nw + nb)
+            wreg[u] = i < nw ? reinterpret_cast<const float4*>(lepe_w)[i]
+                             : reinterpret_cast<const float4*>(lepe_b)[i - nw];
+    }
+    // the routed region ids of this region, one per (head, rank)
+    int ridx = 0;
+    if (tid < p.heads * p.k) {
+        const int h = tid / p.k, j = tid - h * p.k;
+        ridx = routing[((static_cast<size_t>(b) * p.heads + h) * p.R + r) * p.k + j];
+    }
+    LepeOperands<kLepeMfma ? HS : 4, kLepeMfma ? WS : 4, kLepeMfma ? HEADS : 1> lop;
+    if constexpr (kLepeMfma) {
+        if (p.has_lepe) lepe_mfma_load<HS, WS, HEADS>(lepe_table, lepe_b, lop);
+    }
+    // halo pieces kept in registers: all of them for a fixed shape (when they
+    // fit kHaloRegs per thread), kHaloRegs otherwise
+    constexpr int kHaloFixed =
+        (HS > 0 && WS > 0 && HEADS > 0)
+            ? ((HS + 4) * (WS + 4) * (HEADS * kHeadDim / VEC) + kThreads - 1) / kThreads
+            : kHaloRegs;
+    constexpr int kHR = kHaloFixed < kHaloRegs ? kHaloFixed : kHaloRegs;
+    uint4 hreg[kHR];
+#pragma unroll
+    for (int u = 0; u < kHR; ++u) {
+        const int i = tid + u * kThreads;
+        hreg[u] = uint4{0u, 0u, 0u, 0u};
+        if (p.has_lepe && i < p.halo_pieces) {
+            const int cell = i / nvec, pv = i - cell * nvec;
+            const int hy = cell / hw, hx = cell - hy * hw;
+            const int y = y0 + hy - 2, x = x0 + hx - 2;
+            if (y >= 0 && y < p.H && x >= 0 && x < p.W)
+                hreg[u] = *reinterpret_cast<const uint4*>(v + img + (y * p.W + x) * p.C + pv * VEC);
+        }
+    }
+    WaveJobs J(p, w);
+    bf16x8_t qb[kMaxQTiles];
+    if constexpr (VEC == 8) {
+        if (J.nsteps > 0) load_q_operands(p, J, w, reinterpret_cast<const uint16_t*>(q) + img, r, qb);
+    }
+    // Region ids are clamped into range, so a routing buffer holding
+    // garbage (non-finite inputs) cannot send the gather outside the image.
+    if (tid < p.heads * p.k) sIdx[tid] = min(max(ridx, 0), p.R - 1);
+    for (int i = tid + kThreads; i < p.heads * p.k; i += kThreads) {
+        const int h = i / p.k, j = i - h * p.k;
+        const int x = routing[((static_cast<size_t>(b) * p.heads + h) * p.R + r) * p.k + j];
+        sIdx[i] = min(max(x, 0), p.R - 1);
+    }
+    if (stage_w) {
+#pragma unroll
+        for (int u = 0; u < kWRegs; ++u) {
+            const int i = tid + u * kThreads;
+            if (i < nw + nb) reinterpret_cast<float4*>(sW)[i] = wreg[u];
+        }
+        for (int i = tid + kWRegs * kThreads; i < nw + nb; i += kThreads)
+            reinterpret_cast<float4*>(sW)[i] = i < nw
+                                                   ? reinterpret_cast<const float4*>(lepe_w)[i]
+                                                   : reinterpret_cast<const float4*>(lepe_b)[i - nw];
+    }
+    __syncthreads();
+
+    // 2. LePE with weights from global memory runs before the gather is
+    //    issued (a load queued behind the gather would wait for it); its halo
+    //    goes to LDS first.
+    const float* wsrc = w_in_lds ? sW : lepe_w;
+    const float* bsrc = w_in_lds ? (lepe_b ? sW + p.C * 25 : nullptr) : lepe_b;
+    auto halo_store = [&](int i, uint4 val) {
+        const int cell = i / nvec, pv = i - cell * nvec;
+        if constexpr (kLepeMfma) {
+            using S = LepeMfmaShape<HS, WS, HEADS>;
+            uint16_t* dst = reinterpret_cast<uint16_t*>(sVh) + pv * 8 * S::PS + cell;
+            const uint32_t wd[4] = {val.x, val.y, val.z, val.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                dst[(2 * e) * S::PS] = static_cast<uint16_t>(wd[e] & 0xffffu);
+                dst[(2 * e + 1) * S::PS] = static_cast<uint16_t>(wd[e] >> 16);
+            }
+        } else {
+            *reinterpret_cast<uint4*>(sVh + cell * p.C + pv * VEC) = val;
+        }
+    };
+    auto stage_halo = [&]() {
+        if (p.has_lepe) {
+#pragma unroll
+            for (int u = 0; u < kHR; ++u) {
+                const int i = tid + u * kThreads;
+                if (i < p.halo_pieces) halo_store(i, hreg[u]);
+            }
+            for (int i = tid + kHR * kThreads; i < p.halo_pieces; i += kThreads) {
+                const int cell = i / nvec, pv = i - cell * nvec;
+                const int hy = cell / hw, hx = cell - hy * hw;
+                const int y = y0 + hy - 2, x = x0 + hx - 2;
+                uint4 val = {0u, 0u, 0u, 0u};
+                if (y >= 0 && y < p.H && x >= 0 && x < p.W)
+                    val = *reinterpret_cast<const uint4*>(v + img + (y * p.W + x) * p.C + pv * VEC);
+                halo_store(i, val);
+            }
+        }
+        __syncthreads();
+    };
+    const bool early_lepe = !kLepeMfma && !w_in_lds;
+    if (early_lepe) {
+        stage_halo();
+        lepe_phase<T>(p, sVh, sL, wsrc, bsrc);
+    }
+
+    // 3. Each wave issues the gather of its first (job, chunk) step; the LePE
+    //    runs while it is in flight.
+    StepRegs cur;
+    if constexpr (VEC == 8) {
+        if (J.nsteps > 0)
+            gather_step(p, J, w, 0, reinterpret_cast<const uint16_t*>(k) + img,
+                        reinterpret_cast<const uint16_t*>(v) + img, sIdx, cur);
+    }
+    if (!early_lepe) {
+        stage_halo();
+        if constexpr (kLepeMfma) {
+            if (p.has_lepe) {
+                lepe_mfma_compute<HS, WS, HEADS>(p, reinterpret_cast<const uint16_t*>(sVh), sL,
+                                                 lop);
+            } else {
+                for (int i = tid; i < p.t * p.lstride; i += kThreads) sL[i] = 0.f;
+                __syncthreads();
+            }
+        } else {
+            lepe_phase<T>(p, sVh, sL, wsrc, bsrc);
+        }
+    }
+
+    // 4. Token attention over the routed tokens, added into sL.
+    if constexpr (VEC == 8) {
+        attend_mfma(p, J, reinterpret_cast<const uint16_t*>(q) + img,
+                    reinterpret_cast<const uint16_t*>(k) + img,
+                    reinterpret_cast<const uint16_t*>(v) + img, r,
+                    reinterpret_cast<uint16_t*>(smem + p.off_vt), sL, sIdx, cur, qb);
+    } else {
+        attend_valu(p, reinterpret_cast<const float*>(q) + img,
+                    reinterpret_cast<const float*>(k) + img,
+                    reinterpret_cast<const float*>(v) + img, r, sL, sIdx);
+    }
+    __syncthreads();
+
+    // 5. out = LePE + O, one rounding, 16-byte NHWC stores.
+    for (int i = tid; i < p.t * nvec; i += kThreads) {
+        const int slot = i / nvec, pv = i - slot * nvec;
+        const float* src = sL + slot * p.lstride + pv * VEC;
+        T* dst = out + img + token_offset(p, r, slot) + pv * VEC;
+        if constexpr (VEC == 8) {
+            const float4 a = *reinterpret_cast<const float4*>(src);
+            const float4 c = *reinterpret_cast<const float4*>(src + 4);
+            uint4 u;
+            u.x = f32_to_bf16(a.x) | (f32_to_bf16(a.y) << 16);
+            u.y = f32_to_bf16(a.z) | (f32_to_bf16(a.w) << 16);
+            u.z = f32_to_bf16(c.x) | (f32_to_bf16(c.y) << 16);
+            u.w = f32_to_bf16(c.z) | (f32_to_bf16(c.w) << 16);
+            *reinterpret_cast<uint4*>(dst) = u;
+        } else {
+            *reinterpret_cast<float4*>(dst) = *reinterpret_cast<const float4*>(src);
+        }
+    }
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+static long align16(long x) { return (x + 15) & ~15L; }
+
+bool plan(Params& p, int B, int H, int W, int C, int heads, int n_win, int k, float scale,
+          bool bf16) {
+    p.B = B;
+    p.H = H;
+    p.W = W;
+    p.C = C;
+    p.heads = heads;
+    p.n = n_win;
+    p.R = n_win * n_win;
+    p.hs = H / n_win;
+    p.ws = W / n_win;
+    p.t = p.hs * p.ws;
+    p.k = k;
+    p.nkeys = k * p.t;
+    p.scale_log2e = scale * 1.4426950408889634f;
+    p.has_lepe = 0;
+    const long es = bf16 ? 2 : 4;
+    const int vec = bf16 ? 8 : 4;
+    p.lstride = C + 4;
+    p.lepe_items = (C / 2) * p.hs * ((p.ws + kLepeCols - 1) / kLepeCols);
+    p.halo_pieces = (p.hs + 4) * (p.ws + 4) * (C / vec);
+    p.route_rows = kRouteMaxRows;
+
+    long off = 0;
+    auto take = [&](long bytes) {
+        const long o = off;
+        off = align16(off + bytes);
+        return static_cast<int>(o);
+    };
+    const long t = p.t;
+    p.off_vt = take(bf16 ? static_cast<long>(kWaves) * 32 * kVtStride * 2 : 0);
+    // The fixed bf16 shapes whose windows tile by 4x4 run LePE on MFMA with a
+    // channel-planar halo; the others on VALU with an NHWC halo.
+    p.lepe_mfma = bf16 && is_fixed_shape(p, bf16) && lepe_mfma_fits(p.hs, p.ws, heads);
+    const long vh_bytes =
+        p.lepe_mfma ? static_cast<long>(C) * ((p.hs + 4) * (p.ws + 4) + 4) * 2
+                    : static_cast<long>(p.hs + 4) * (p.ws + 4) * C * es;
+    const long l_bytes = t * p.lstride * 4;
+    p.lepe_alias = p.lepe_mfma || p.lepe_items <= kThreads;
+    if (p.lepe_alias) {
+        p.off_vh = take(std::max(vh_bytes, l_bytes));
+        p.off_l = p.off_vh;
+    } else {
+        p.off_vh = take(vh_bytes);
+        p.off_l = take(l_bytes);
+    }
+    p.off_idx = take(static_cast<long>(heads) * k * 4);
+    // VALU LePE: weights and bias go to LDS while four workgroups still fit a CU.
+    const long w_bytes = static_cast<long>(C) * 26 * 4;
+    if (!p.lepe_mfma && off + w_bytes <= 40 * 1024) {
+        p.off_w = take(w_bytes);
+    } else {
+        p.off_w = -1;
+    }
+    p.lds_bytes = static_cast<int>(off);
+    p.table_items = p.lepe_mfma ? C * 40 : 0;
+    {
+        const int nvec = C / vec;
+        const bool wave_path = bf16 && 64 % nvec == 0;
+        p.pool_blocks = wave_path ? (B * p.R + 1) / 2 : B * p.R;
+    }
+    p.pool_chunk = std::max(1, std::min(p.t, kPoolChunkBytes / (C * static_cast<int>(es))));
+    // LDS of the pool kernel's staged path (fp32, or C/8 not dividing 64)
+    p.pool_lds_bytes = p.pool_chunk * C * static_cast<int>(es);
+    return off <= kMaxLdsBytes && C <= kMaxChannels && C % 32 == 0 && p.R <= kMaxRegions;
+}
+
+hipError_t launch_attend(const Params& p, bool bf16, const void* q, const void* k, const void* v,
+                         const int32_t* routing, const float* lepe_w, const float* lepe_b,
+                         const uint2* lepe_table, void* out, hipStream_t stream) {
+    Params pp = p;
+    pp.has_lepe = lepe_w != nullptr;
+    if (!pp.has_lepe) lepe_b = nullptr;
+    const dim3 grid(p.B * p.R), block(kThreads);
+#define BRA_ATTEND(T, HS, WS, NW, HEADS, KTOP)                                                 \
+    if (matches(Inst<T, HS, WS, NW, HEADS, KTOP>::key, p, bf16, true)) {                       \
+        hipLaunchKernelGGL((attend_kernel<T, HS, WS, NW, HEADS, KTOP>), grid, block,           \
+                           p.lds_bytes, stream, static_cast<const T*>(q),                      \
+                           static_cast<const T*>(k), static_cast<const T*>(v), routing,        \
+                           lepe_w, lepe_b, lepe_table, static_cast<T*>(out), pp);              \
+        return hipGetLastError();                                                              \
+    }
+    BRA_FOR_EACH_SHAPE(BRA_ATTEND)
+#undef BRA_ATTEND
+    if (bf16)
+        hipLaunchKernelGGL((attend_kernel<uint16_t, 0, 0, 0, 0, 0>), grid, block, p.lds_bytes,
+                           stream, static_cast<const uint16_t*>(q),
+                           static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
+                           routing, lepe_w, lepe_b, lepe_table, static_cast<uint16_t*>(out), pp);
+    else
+        hipLaunchKernelGGL((attend_kernel<float, 0, 0, 0, 0, 0>), grid, block, p.lds_bytes,
+                           stream, static_cast<const float*>(q), static_cast<const float*>(k),
+                           static_cast<const float*>(v), routing, lepe_w, lepe_b, lepe_table,
+                           static_cast<float*>(out), pp);
+    return hipGetLastError();
+}
+
+}  // namespace bra

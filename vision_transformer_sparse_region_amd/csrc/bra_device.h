@@ -1,0 +1,224 @@
+// bra_device.h -- device helpers shared by the BRA kernels (gfx950).
+//
+// Pages cited by key in the kernels:
+//   [P1] "从静态到动态：Bi-Level Routing Attention如何重塑视觉Transformer的注意力机制",
+//        www.mhpn.cn/news/199372
+//   [P2] "BiFormer用双层路由注意力重塑视觉Transformer效率极限", www.mooersco.com/news/894234
+//   [P3] "从零构建BiFormer：PyTorch实战双层路由注意力机制与调试全攻略",
+//        www.mhpn.cn/news/564882
+//   [P4] "手把手解析BiFormer：双水平路由注意力机制与PyTorch实战指南", www.jsqmd.com/news/719213
+//   [P5] "【医学图像分割模块】BiFormer / 双层路由注意力（CVPR 2023）", www.mhpn.cn/news/2512273
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "bra_launch.h"
+
+namespace bra {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint16_t u16x8_t __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+    return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+__device__ __forceinline__ float bf16lo(uint32_t x) { return __uint_as_float(x << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
+
+// Round-to-nearest-even float -> bf16 bits.
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+}
+
+template <typename T>
+struct Elem;
+template <>
+struct Elem<float> {
+    static constexpr int kVec = 4;  // elements per 16-byte piece
+    __device__ static float f32(float x) { return x; }
+    // two consecutive channels
+    __device__ static float2 pair(const float* p) { return *reinterpret_cast<const float2*>(p); }
+};
+template <>
+struct Elem<uint16_t> {
+    static constexpr int kVec = 8;
+    __device__ static float f32(uint16_t x) { return bf16_to_f32(x); }
+    __device__ static float2 pair(const uint16_t* p) {
+        const uint32_t u = *reinterpret_cast<const uint32_t*>(p);
+        return float2{bf16lo(u), bf16hi(u)};
+    }
+};
+
+// Workgroups are dispatched round-robin over the 8 XCDs (each with its own
+// L2).  Remap so that consecutive logical ids -- the regions of one image --
+// run on one XCD and share its L2 for the routed K/V and halo reads.
+__device__ __forceinline__ int xcd_logical_block(int bid, int nblocks) {
+    const int full = nblocks & ~7;
+    if (bid >= full) return bid;
+    return (bid & 7) * (full >> 3) + (bid >> 3);
+}
+
+// Max and sum over the four lanes l, l^16, l^32, l^48 -- in the MFMA
+// attention these hold the four key groups of one query.  v_permlane16_swap
+// and v_permlane32_swap exchange rows of 16 and halves of 32 lanes in VALU
+// registers, without a trip through the LDS crossbar; every lane of the four
+// ends with the same value.
+__device__ __forceinline__ float group4_max(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x),
+                                                    false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                    false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float group4_sum(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x),
+                                                    false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                    false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// mean = sum / t, as a multiplication when t is a power of two (exact then).
+__device__ __forceinline__ double mean_of(double sum, int t) {
+    return (t & (t - 1)) == 0 ? sum * (1.0 / static_cast<double>(t)) : sum / static_cast<double>(t);
+}
+
+// Token offset (elements) of slot `slot` of region `reg` inside one image.
+__device__ __forceinline__ int token_offset(const Params& p, int reg, int slot) {
+    const int ri = reg / p.n, rj = reg - ri * p.n;
+    const int u = slot / p.ws, w = slot - u * p.ws;
+    return ((ri * p.hs + u) * p.W + rj * p.ws + w) * p.C;
+}
+
+// Window geometry as compile-time constants.  A kernel instantiated with
+// nonzero HS, WS, NW, HEADS, KTOP replaces the matching runtime fields (the
+// host launches such an instance only for exactly that shape), so divisions
+// and loop bounds fold; zeros keep the runtime values.
+template <int HS, int WS, int NW, int HEADS, int KTOP, int VEC>
+__device__ __forceinline__ Params fold_geometry(const Params& in) {
+    Params p = in;
+    if constexpr (HS > 0) p.hs = HS;
+    if constexpr (WS > 0) p.ws = WS;
+    if constexpr (NW > 0) {
+        p.n = NW;
+        p.R = NW * NW;
+    }
+    if constexpr (HEADS > 0) {
+        p.heads = HEADS;
+        p.C = HEADS * kHeadDim;
+        p.lstride = HEADS * kHeadDim + 4;
+    }
+    if constexpr (HS > 0 && WS > 0 && NW > 0 && HEADS > 0 && KTOP > 0) {
+        p.H = NW * HS;
+        p.W = NW * WS;
+        p.t = HS * WS;
+        p.k = KTOP;
+        p.nkeys = KTOP * HS * WS;
+        p.lepe_items = (HEADS * kHeadDim / 2) * HS * ((WS + kLepeCols - 1) / kLepeCols);
+        p.lepe_alias = p.lepe_items <= kThreads;
+        p.halo_pieces = (HS + 4) * (WS + 4) * (HEADS * kHeadDim / VEC);
+    }
+    return p;
+}
+
+// One entry of the Toeplitz operand table of the MFMA LePE (see
+// lepe_mfma_compute): entry it = ((cg * 64 + lane) * 5 + i) * 2 + ks holds the
+// B operand of lane `lane` for channel group cg, tap row i and column step ks:
+// four bf16 w[c][i][4ks + kk - n] (zero outside 0..4), c = 16cg + lane/4,
+// n = lane % 4.
+__device__ __forceinline__ uint2 lepe_toeplitz_entry(const float* __restrict__ lepe_w, int it) {
+    const int ks = it & 1, i = (it >> 1) % 5, lane_cg = it / 10;
+    const int lane = lane_cg & 63, cg = lane_cg >> 6;
+    const int c = 16 * cg + (lane >> 2), n = lane & 3;
+    uint32_t h[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+        const int j = 4 * ks + kk - n;
+        h[kk] = (j >= 0 && j <= 4) ? f32_to_bf16(lepe_w[c * 25 + i * 5 + j]) : 0u;
+    }
+    return uint2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+}
+
+// Q_r . K_s over the 32 dims of one head, left to right, each product rounded
+// before it is added -- the same IEEE operations as a plain fp64 loop.
+__device__ __forceinline__ double dot32_seq(const double* a, const double* b) {
+#pragma clang fp contract(off)
+    double s = 0.0;
+#pragma unroll
+    for (int d = 0; d < kHeadDim; ++d) s = s + a[d] * b[d];
+    return s;
+}
+
+// LePE on the 4x4x4 MFMA applies to windows whose sides are multiples of 4
+// when the per-wave accumulators (tiles x channel groups) stay small.
+__host__ __device__ constexpr bool lepe_mfma_fits(int hs, int ws, int heads) {
+    return hs > 0 && ws > 0 && heads > 0 && hs % 4 == 0 && ws % 4 == 0 &&
+           (hs / 4) * (ws / 4) * ((heads * kHeadDim / 16 + kWaves - 1) / kWaves) <= 8;
+}
+
+template <int HS, int WS, int HEADS>
+struct LepeMfmaShape {
+    static constexpr int C = HEADS * kHeadDim;
+    static constexpr int TY = HS / 4, TX = WS / 4;
+    static constexpr int HWP = WS + 4;                    // halo row pitch (elements)
+    static constexpr int PS = (HS + 4) * (WS + 4) + 4;    // channel plane stride (elements)
+    static constexpr int NG = C / 16;                     // groups of 16 channels
+    static constexpr int GPW = (NG + kWaves - 1) / kWaves;  // groups per wave
+    static constexpr bool ok = lepe_mfma_fits(HS, WS, HEADS);
+};
+
+// Wave-wide arg-max of (value, index) pairs: the larger value wins, an exact
+// tie goes to the lower index.  Partners: lane^1 and lane^2 by DPP quad
+// permutation, the other quad of 8 lanes by row_half_mirror, the other half of
+// 16 by row_mirror (every lane of a group holds the group's winner by then,
+// so any cross pairing works), then rows of 16 and halves of 32 by
+// v_permlane16_swap / v_permlane32_swap.  Every lane ends with the winner.
+__device__ __forceinline__ void argmax_take(double& best, int& bs, double ob, int os) {
+    if (ob > best || (ob == best && os < bs)) {
+        best = ob;
+        bs = os;
+    }
+}
+template <int CTRL>
+__device__ __forceinline__ void argmax_dpp(double& best, int& bs) {
+    const int2 u = __builtin_bit_cast(int2, best);
+    int2 o;
+    o.x = __builtin_amdgcn_mov_dpp(u.x, CTRL, 0xf, 0xf, false);
+    o.y = __builtin_amdgcn_mov_dpp(u.y, CTRL, 0xf, 0xf, false);
+    const int os = __builtin_amdgcn_mov_dpp(bs, CTRL, 0xf, 0xf, false);
+    argmax_take(best, bs, __builtin_bit_cast(double, o), os);
+}
+// The two elements a swap returns are this lane's and its partner's values
+// (in some order); both lanes keep the better of the two.
+template <bool ROWS16>
+__device__ __forceinline__ void argmax_swap(double& best, int& bs) {
+    const int2 u = __builtin_bit_cast(int2, best);
+    const auto lo = ROWS16 ? __builtin_amdgcn_permlane16_swap(u.x, u.x, false, false)
+                           : __builtin_amdgcn_permlane32_swap(u.x, u.x, false, false);
+    const auto hi = ROWS16 ? __builtin_amdgcn_permlane16_swap(u.y, u.y, false, false)
+                           : __builtin_amdgcn_permlane32_swap(u.y, u.y, false, false);
+    const auto ix = ROWS16 ? __builtin_amdgcn_permlane16_swap(bs, bs, false, false)
+                           : __builtin_amdgcn_permlane32_swap(bs, bs, false, false);
+    double a = __builtin_bit_cast(double, int2{static_cast<int>(lo[0]), static_cast<int>(hi[0])});
+    int ia = static_cast<int>(ix[0]);
+    argmax_take(a, ia,
+                __builtin_bit_cast(double, int2{static_cast<int>(lo[1]), static_cast<int>(hi[1])}),
+                static_cast<int>(ix[1]));
+    best = a;
+    bs = ia;
+}
+__device__ __forceinline__ void wave_argmax(double& best, int& bs) {
+    argmax_dpp<0xB1>(best, bs);   // quad_perm [1,0,3,2]: lane ^ 1
+    argmax_dpp<0x4E>(best, bs);   // quad_perm [2,3,0,1]: lane ^ 2
+    argmax_dpp<0x141>(best, bs);  // row_half_mirror: the other quad of 8
+    argmax_dpp<0x140>(best, bs);  // row_mirror: the other 8 of 16
+    argmax_swap<true>(best, bs);
+    argmax_swap<false>(best, bs);
+}
+
+
+}  // namespace bra

@@ -18,6 +18,8 @@ constexpr int kLepeCols = 8;     // output columns one LePE work item covers
 constexpr int kHaloRegs = 8;     // 16-byte halo pieces a thread keeps in flight
 constexpr int kWRegs = 2;        // 16-byte LePE weight pieces a thread keeps in flight
 constexpr int kMaxChannels = 1024;
+constexpr int kMaxRegions = 256;    // n_win <= 16
+constexpr int kRouteMaxRows = 16;   // query regions per routing workgroup
 
 // Problem geometry plus the on-chip layout of the routing/attention kernel.
 struct Params {
@@ -34,8 +36,9 @@ struct Params {
     int lepe_mfma;   // 1: LePE on the 4x4x4 MFMA with a channel-planar halo
     int halo_pieces; // 16-byte pieces of the V window with its 2-token halo
     // LDS byte offsets of the routing/attention kernel
-    int off_vt, off_aff, off_vh, off_l, off_w, off_idx, lds_bytes;
+    int off_vt, off_vh, off_l, off_w, off_idx, lds_bytes;
     int table_items; // 8-byte entries of the MFMA LePE Toeplitz operand table (0: none)
+    int route_rows;  // query regions per routing workgroup
     // region-pool kernel
     int pool_blocks; // workgroups computing means (the table follows them)
     int pool_chunk;  // staged path: tokens staged per step
@@ -50,12 +53,14 @@ bool plan(Params& p, int B, int H, int W, int C, int heads, int n_win, int k, fl
 //   means: [2][B][heads][R][32] fp64 -- region means of Q, then of K.
 //   lepe_table: p.table_items 8-byte entries (written by the pool kernel when
 //   lepe_w is given and the shape runs LePE on MFMA).
+//   routing: [B][heads][R][k] int32 region ids.
 hipError_t launch_pool_qk(const Params& p, bool bf16, const void* q, const void* k,
                           const float* lepe_w, double* means, uint2* lepe_table,
                           hipStream_t stream);
-hipError_t launch_route_attend(const Params& p, bool bf16, const void* q, const void* k,
-                               const void* v, const double* means, const float* lepe_w,
-                               const float* lepe_b, const uint2* lepe_table, void* out,
-                               int32_t* routing_idx, hipStream_t stream);
+hipError_t launch_route(const Params& p, bool bf16, const double* means, int32_t* routing,
+                        hipStream_t stream);
+hipError_t launch_attend(const Params& p, bool bf16, const void* q, const void* k, const void* v,
+                         const int32_t* routing, const float* lepe_w, const float* lepe_b,
+                         const uint2* lepe_table, void* out, hipStream_t stream);
 
 }  // namespace bra

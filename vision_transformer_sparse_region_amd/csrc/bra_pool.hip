@@ -1,0 +1,151 @@
+// bra_pool.hip -- region means of Q and K (fp64) for the routing, and the
+// Toeplitz operand table of the MFMA LePE.  [P4 §1.2; P2 §2.1; P5 §五 ③]
+// (page keys in bra_device.h)
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "bra_device.h"
+#include "bra_shapes.h"
+
+namespace bra {
+namespace {
+
+// ---------------------------------------------------------------------------
+// Region means of Q and K (fp64).
+//  bf16, C/8 dividing 64: one wave per (region, tensor).  Lane (pv, tg) holds
+//        fp64 sums of channels 8pv..8pv+7 over every (64/(C/8))-th token of the
+//        window; the lanes of one pv are then combined with shuffles.  A bf16
+//        value has an 8-bit significand, so every partial sum of a window is an
+//        exact fp64 number: the order of the additions cannot change the
+//        result, and the mean is the correctly rounded exact mean.
+//  otherwise (fp32, or other channel counts): one thread per channel sums
+//        the tokens in slot order -- the order of a plain loop -- staged
+//        through LDS in chunks.
+template <typename T, int HS, int WS, int NW, int HEADS>
+__global__ __launch_bounds__(kThreads) void pool_qk_kernel(const T* __restrict__ q,
+                                                           const T* __restrict__ k,
+                                                           double* __restrict__ means,
+                                                           const float* __restrict__ lepe_w,
+                                                           uint2* __restrict__ lepe_table,
+                                                           Params p_in) {
+    constexpr int VEC = Elem<T>::kVec;
+    const Params p = fold_geometry<HS, WS, NW, HEADS, 1, VEC>(p_in);
+    const int tid = threadIdx.x;
+    if (static_cast<int>(blockIdx.x) >= p.pool_blocks) {
+        // Trailing workgroups: the Toeplitz LePE operands of the MFMA LePE.
+        const int it = (blockIdx.x - p.pool_blocks) * kThreads + tid;
+        if (it < p.table_items) lepe_table[it] = lepe_toeplitz_entry(lepe_w, it);
+        return;
+    }
+    const size_t mstride = static_cast<size_t>(p.B) * p.heads * p.R * kHeadDim;
+    const int nvec = p.C / VEC;
+
+    if (VEC == 8 && 64 % nvec == 0) {
+        // two regions per workgroup: wave w -> region 2*blk + (w >> 1), tensor w & 1
+        const int lane = tid & 63, w = tid >> 6;
+        const int blk = xcd_logical_block(blockIdx.x, p.pool_blocks);
+        const int region = 2 * blk + (w >> 1);
+        if (region >= p.B * p.R) return;
+        const int b = region / p.R, r = region - b * p.R;
+        const int tensor = w & 1;
+        const T* src = (tensor == 0 ? q : k) + static_cast<size_t>(b) * p.H * p.W * p.C;
+        const int pv = lane % nvec, tg = lane / nvec, TG = 64 / nvec;
+        double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll 8
+        for (int slot = tg; slot < p.t; slot += TG) {
+            const uint4 u =
+                *reinterpret_cast<const uint4*>(src + token_offset(p, r, slot) + pv * VEC);
+            acc[0] += bf16lo(u.x); acc[1] += bf16hi(u.x);
+            acc[2] += bf16lo(u.y); acc[3] += bf16hi(u.y);
+            acc[4] += bf16lo(u.z); acc[5] += bf16hi(u.z);
+            acc[6] += bf16lo(u.w); acc[7] += bf16hi(u.w);
+        }
+        for (int m = nvec; m < 64; m *= 2)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[e] += __shfl_xor(acc[e], m);
+        if (tg == 0) {
+            const int c = pv * 8, h = c / kHeadDim, d = c - h * kHeadDim;
+            double* dst = means + tensor * mstride +
+                          ((static_cast<size_t>(b) * p.heads + h) * p.R + r) * kHeadDim + d;
+#pragma unroll
+            for (int e = 0; e < 8; e += 2)
+                *reinterpret_cast<double2*>(dst + e) =
+                    double2{mean_of(acc[e], p.t), mean_of(acc[e + 1], p.t)};
+        }
+        return;
+    }
+
+    extern __shared__ __align__(16) unsigned char smem[];
+    T* tile = reinterpret_cast<T*>(smem);
+    const int blk = xcd_logical_block(blockIdx.x, p.pool_blocks);
+    const int b = blk / p.R, r = blk - b * p.R;
+    const size_t img = static_cast<size_t>(b) * p.H * p.W * p.C;
+    double* mimg = means + static_cast<size_t>(b) * p.heads * p.R * kHeadDim;
+    for (int tensor = 0; tensor < 2; ++tensor) {
+        const T* src = (tensor == 0 ? q : k) + img;
+        double acc[kMaxChannels / kThreads] = {};
+        for (int t0 = 0; t0 < p.t; t0 += p.pool_chunk) {
+            const int nt = min(p.pool_chunk, p.t - t0);
+            for (int i = tid; i < nt * nvec; i += kThreads) {
+                const int tt = i / nvec, pv = i - tt * nvec;
+                *reinterpret_cast<uint4*>(tile + tt * p.C + pv * VEC) =
+                    *reinterpret_cast<const uint4*>(src + token_offset(p, r, t0 + tt) + pv * VEC);
+            }
+            __syncthreads();
+#pragma unroll
+            for (int j = 0; j < kMaxChannels / kThreads; ++j) {
+                const int c = tid + j * kThreads;
+                if (c < p.C) {
+                    double s = acc[j];
+                    for (int tt = 0; tt < nt; ++tt)
+                        s += static_cast<double>(Elem<T>::f32(tile[tt * p.C + c]));
+                    acc[j] = s;
+                }
+            }
+            __syncthreads();
+        }
+#pragma unroll
+        for (int j = 0; j < kMaxChannels / kThreads; ++j) {
+            const int c = tid + j * kThreads;
+            if (c < p.C) {
+                const int h = c / kHeadDim, d = c - h * kHeadDim;
+                mimg[tensor * mstride + (static_cast<size_t>(h) * p.R + r) * kHeadDim + d] =
+                    mean_of(acc[j], p.t);
+            }
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_pool_qk(const Params& p, bool bf16, const void* q, const void* k,
+                          const float* lepe_w, double* means, uint2* lepe_table,
+                          hipStream_t stream) {
+    const int nvec = p.C / (bf16 ? 8 : 4);
+    const bool wave_path = bf16 && 64 % nvec == 0;
+    Params pp = p;
+    if (!lepe_w) pp.table_items = 0;
+    const int table_blocks = (pp.table_items + kThreads - 1) / kThreads;
+    const dim3 grid(p.pool_blocks + table_blocks), block(kThreads);
+    const int lds = wave_path ? 0 : p.pool_lds_bytes;
+#define BRA_POOL(T, HS, WS, NW, HEADS, KTOP)                                                    \
+    if (matches(Inst<T, HS, WS, NW, HEADS, KTOP>::key, p, bf16, false)) {                      \
+        hipLaunchKernelGGL((pool_qk_kernel<T, HS, WS, NW, HEADS>), grid, block, lds, stream,   \
+                           static_cast<const T*>(q), static_cast<const T*>(k), means, lepe_w,  \
+                           lepe_table, pp);                                                    \
+        return hipGetLastError();                                                              \
+    }
+    BRA_FOR_EACH_SHAPE(BRA_POOL)
+#undef BRA_POOL
+    if (bf16)
+        hipLaunchKernelGGL((pool_qk_kernel<uint16_t, 0, 0, 0, 0>), grid, block, lds, stream,
+                           static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                           means, lepe_w, lepe_table, pp);
+    else
+        hipLaunchKernelGGL((pool_qk_kernel<float, 0, 0, 0, 0>), grid, block, lds, stream,
+                           static_cast<const float*>(q), static_cast<const float*>(k), means,
+                           lepe_w, lepe_table, pp);
+    return hipGetLastError();
+}
+
+}  // namespace bra
