@@ -690,7 +690,6 @@ bool plan(Params& p, int B, int H, int W, int C, int heads, int n_win, int k, fl
     p.lstride = C + 4;
     p.lepe_items = (C / 2) * p.hs * ((p.ws + kLepeCols - 1) / kLepeCols);
     p.halo_pieces = (p.hs + 4) * (p.ws + 4) * (C / vec);
-    p.route_rows = kRouteMaxRows;
 
     long off = 0;
     auto take = [&](long bytes) {

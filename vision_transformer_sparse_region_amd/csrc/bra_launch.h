@@ -1,5 +1,5 @@
 // bra_launch.h -- internal interface between the C ABI (bra_api.cpp) and the
-// HIP kernels (bra_kernels.hip).  Not installed; the public ABI is include/bra.h.
+// HIP kernels (bra_pool.hip, bra_route.hip, bra_attend.hip).  Not installed; the public ABI is include/bra.h.
 #pragma once
 
 #include <hip/hip_runtime_api.h>
@@ -19,7 +19,6 @@ constexpr int kHaloRegs = 8;     // 16-byte halo pieces a thread keeps in flight
 constexpr int kWRegs = 2;        // 16-byte LePE weight pieces a thread keeps in flight
 constexpr int kMaxChannels = 1024;
 constexpr int kMaxRegions = 256;    // n_win <= 16
-constexpr int kRouteMaxRows = 16;   // query regions per routing workgroup
 
 // Problem geometry plus the on-chip layout of the routing/attention kernel.
 struct Params {
@@ -38,7 +37,6 @@ struct Params {
     // LDS byte offsets of the routing/attention kernel
     int off_vt, off_vh, off_l, off_w, off_idx, lds_bytes;
     int table_items; // 8-byte entries of the MFMA LePE Toeplitz operand table (0: none)
-    int route_rows;  // query regions per routing workgroup
     // region-pool kernel
     int pool_blocks; // workgroups computing means (the table follows them)
     int pool_chunk;  // staged path: tokens staged per step

@@ -15,26 +15,37 @@
 namespace bra {
 namespace {
 
+// Region-span of the affinity phase: threads tid % SPAN own region tid % SPAN,
+// SPAN = the power of two >= R (64, 128 or 256 = kMaxRegions).
+__host__ __device__ constexpr int route_span(int R) { return R <= 64 ? 64 : R <= 128 ? 128 : 256; }
+// Query rows a workgroup routes: 4 per wave for R <= 64, else 2 per wave.
+__host__ __device__ constexpr int route_rows_per_wave(int span) { return span == 64 ? 4 : 2; }
+// fp64 row stride of the affinity tile (even, so pairs of entries are 16-byte aligned).
+__host__ __device__ constexpr int route_row_stride(int R) { return (R + 1) & ~1; }
+
 __device__ __forceinline__ bool beats(double a, int ia, double b, int ib) {
     return a > b || (a == b && ia < ib);
 }
 
-// Top-k of one row by a wave-wide bitonic sort, best first (affinity
+// Top-k of NRW rows at once by wave-wide bitonic sorts, best first (affinity
 // descending, region id ascending).  Lane `lane` holds elements
-// lane * E .. lane * E + E - 1; partners within a lane swap in registers,
-// across lanes through shuffles.  Padding elements (ids >= R) carry -inf and
-// sort last.  Writes the first k ids.
-template <int E>
-__device__ __forceinline__ void wave_topk_bitonic(const double* row, int R, int k,
-                                                  int32_t* __restrict__ dst) {
+// lane * E .. lane * E + E - 1 of every row; partners within a lane swap in
+// registers, across lanes through shuffles.  Padding elements (ids >= R)
+// carry -inf and sort last.  Writes the first k ids of row j to dst[j].
+template <int E, int NRW>
+__device__ __forceinline__ void wave_topk_bitonic(const double* const (&rows)[NRW], int R, int k,
+                                                  int32_t* const (&dst)[NRW], const bool (&live)[NRW]) {
     const int lane = threadIdx.x & 63;
-    double v[E];
-    int ix[E];
+    double v[NRW][E];
+    int ix[NRW][E];
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-        const int i = lane * E + e;
-        v[e] = i < R ? row[i] : -INFINITY;
-        ix[e] = i;
+    for (int r = 0; r < NRW; ++r) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const int i = lane * E + e;
+            v[r][e] = i < R ? rows[r][i] : -INFINITY;
+            ix[r][e] = i;
+        }
     }
 #pragma unroll
     for (int size = 2; size <= 64 * E; size <<= 1) {
@@ -42,47 +53,58 @@ __device__ __forceinline__ void wave_topk_bitonic(const double* row, int R, int 
         for (int j = size >> 1; j > 0; j >>= 1) {
             if (j < E) {
 #pragma unroll
-                for (int e = 0; e < E; ++e) {
-                    const int pe = e ^ j;
-                    if (pe > e) {
-                        const bool dir = ((lane * E + e) & size) == 0;
-                        if (beats(v[e], ix[e], v[pe], ix[pe]) != dir) {
-                            const double tv = v[e];
-                            v[e] = v[pe];
-                            v[pe] = tv;
-                            const int ti = ix[e];
-                            ix[e] = ix[pe];
-                            ix[pe] = ti;
+                for (int r = 0; r < NRW; ++r) {
+#pragma unroll
+                    for (int e = 0; e < E; ++e) {
+                        const int pe = e ^ j;
+                        if (pe > e) {
+                            const bool dir = ((lane * E + e) & size) == 0;
+                            if (beats(v[r][e], ix[r][e], v[r][pe], ix[r][pe]) != dir) {
+                                const double tv = v[r][e];
+                                v[r][e] = v[r][pe];
+                                v[r][pe] = tv;
+                                const int ti = ix[r][e];
+                                ix[r][e] = ix[r][pe];
+                                ix[r][pe] = ti;
+                            }
                         }
                     }
                 }
             } else {
                 const int lj = j / E;
 #pragma unroll
-                for (int e = 0; e < E; ++e) {
-                    const double ov = __shfl_xor(v[e], lj);
-                    const int oi = __shfl_xor(ix[e], lj);
-                    const int i = lane * E + e;
-                    const bool lower = (i & j) == 0;
-                    const bool dir = (i & size) == 0;
-                    const bool mine = beats(v[e], ix[e], ov, oi);
-                    if ((lower == dir) != mine) {
-                        v[e] = ov;
-                        ix[e] = oi;
+                for (int r = 0; r < NRW; ++r) {
+#pragma unroll
+                    for (int e = 0; e < E; ++e) {
+                        const double ov = __shfl_xor(v[r][e], lj);
+                        const int oi = __shfl_xor(ix[r][e], lj);
+                        const int i = lane * E + e;
+                        const bool lower = (i & j) == 0;
+                        const bool dir = (i & size) == 0;
+                        const bool mine = beats(v[r][e], ix[r][e], ov, oi);
+                        if ((lower == dir) != mine) {
+                            v[r][e] = ov;
+                            ix[r][e] = oi;
+                        }
                     }
                 }
             }
         }
     }
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-        const int i = lane * E + e;
-        if (i < k) dst[i] = ix[e];
+    for (int r = 0; r < NRW; ++r) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const int i = lane * E + e;
+            if (live[r] && i < k) dst[r][i] = ix[r][e];
+        }
     }
 }
 
-template <int NW, int KTOP>
-__global__ __launch_bounds__(kThreads) void route_kernel(const double* __restrict__ means,
+// NW > 0 / KTOP > 0 fold the region count / k at compile time.  SPAN is
+// route_span(R).  Rows of a chunk go to waves round-robin (row = w + 4j).
+template <int NW, int KTOP, int SPAN>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))) void route_kernel(const double* __restrict__ means,
                                                          int32_t* __restrict__ idx_out,
                                                          Params p_in) {
     Params p = p_in;
@@ -91,71 +113,113 @@ __global__ __launch_bounds__(kThreads) void route_kernel(const double* __restric
         p.R = NW * NW;
     }
     if constexpr (KTOP > 0) p.k = KTOP;
-    __shared__ double sQ[kRouteMaxRows * kHeadDim];
+    constexpr int RPW = route_rows_per_wave(SPAN);
+    constexpr int ROWS = kWaves * RPW;
+    constexpr int G = kThreads / SPAN;  // row groups of the affinity phase
+    constexpr int NR = ROWS / G;        // rows per thread in the affinity phase
+    __shared__ double sQ[ROWS * kHeadDim];
     extern __shared__ __align__(16) unsigned char smem[];
-    double* sA = reinterpret_cast<double*>(smem);  // [rows][R]
+    double* sA = reinterpret_cast<double*>(smem);  // [ROWS][RS]
 
+    const int R = p.R, RS = route_row_stride(R);
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int rows = p.route_rows;
-    const int nchunk = (p.R + rows - 1) / rows;
+    const int nchunk = (R + ROWS - 1) / ROWS;
     const int bh = blockIdx.x / nchunk, chunk = blockIdx.x - bh * nchunk;
-    const int r0 = chunk * rows, nrows = min(rows, p.R - r0);
-    const size_t mstride = static_cast<size_t>(p.B) * p.heads * p.R * kHeadDim;
-    const double* qbar = means + static_cast<size_t>(bh) * p.R * kHeadDim;  // [R][32]
+    const int r0 = chunk * ROWS, nrows = min(ROWS, R - r0);
+    const size_t mstride = static_cast<size_t>(p.B) * p.heads * R * kHeadDim;
+    const double* qbar = means + static_cast<size_t>(bh) * R * kHeadDim;  // [R][32]
     const double* kbar = qbar + mstride;
 
-    for (int i = tid; i < nrows * kHeadDim / 2; i += kThreads)
-        reinterpret_cast<double2*>(sQ)[i] = reinterpret_cast<const double2*>(qbar + r0 * kHeadDim)[i];
-    __syncthreads();
-
-    // Affinity: a thread keeps one K mean in registers and takes the dot with
-    // several query rows (exact sequential order, see dot32_seq).
-    const int L = p.R <= 64 ? 64 : (p.R <= 128 ? 128 : 256);
-    const int G = kThreads / L;
-    const int s0 = tid % L, g = tid / L;
-    for (int s = s0; s < p.R; s += L) {
-        double kreg[kHeadDim];
-        const double2* src = reinterpret_cast<const double2*>(kbar + s * kHeadDim);
+    // Affinity.  Thread (s, g) keeps K mean s in registers and takes its dot
+    // with query rows g, g + G, ...; rows past the chunk read zeros.
+    const int s = tid % SPAN, g = tid / SPAN;
+    double kreg[kHeadDim];
+    {
+        const double2* src = reinterpret_cast<const double2*>(kbar + min(s, R - 1) * kHeadDim);
 #pragma unroll
         for (int d = 0; d < kHeadDim / 2; ++d) {
             const double2 x = src[d];
             kreg[2 * d] = x.x;
             kreg[2 * d + 1] = x.y;
         }
-        for (int rr = g; rr < nrows; rr += G) sA[rr * p.R + s] = dot32_seq(sQ + rr * kHeadDim, kreg);
+    }
+    for (int i = tid; i < ROWS * kHeadDim / 2; i += kThreads) {
+        const bool in = i < nrows * kHeadDim / 2;
+        reinterpret_cast<double2*>(sQ)[i] =
+            in ? reinterpret_cast<const double2*>(qbar + r0 * kHeadDim)[i] : double2{0.0, 0.0};
+    }
+    __syncthreads();
+    {
+#pragma unroll 1
+        for (int j = 0; j < NR; ++j) {
+            const int row = g + G * j;
+            const double a = dot32_seq(sQ + row * kHeadDim, kreg);
+            if (s < R && row < nrows) sA[row * RS + s] = a;
+        }
     }
     __syncthreads();
 
-    // Top-k, one wave per row.
-    for (int rr = w; rr < nrows; rr += kWaves) {
-        const double* row = sA + rr * p.R;
-        int32_t* dst = idx_out + (static_cast<size_t>(bh) * p.R + r0 + rr) * p.k;
-        if (p.k == 1) {
-            double best = -INFINITY;
-            int bs = 0x7fffffff;
-            for (int s = lane; s < p.R; s += 64) {
-                const double a = row[s];
-                if (a > best || bs == 0x7fffffff) {
-                    best = a;
-                    bs = s;
+    // Top-k, rows w, w + 4, ... of the chunk on wave w.
+    int32_t* const base = idx_out + (static_cast<size_t>(bh) * R + r0) * p.k;
+    if (p.k == 1) {
+        double best[RPW];
+        int bs[RPW];
+#pragma unroll
+        for (int j = 0; j < RPW; ++j) {
+            const double* row = sA + min(w + kWaves * j, nrows - 1) * RS;
+            best[j] = -INFINITY;
+            bs[j] = 0x7fffffff;
+            for (int x = lane; x < R; x += 64) {
+                const double a = row[x];
+                if (a > best[j] || bs[j] == 0x7fffffff) {
+                    best[j] = a;
+                    bs[j] = x;
                 }
             }
-            wave_argmax(best, bs);
-            if (lane == 0) dst[0] = bs;
-        } else {
-            const int e = (p.R + 63) / 64;
-            if constexpr (NW > 0) {
-                constexpr int RR = NW * NW;
-                constexpr int EE = RR <= 64 ? 1 : RR <= 128 ? 2 : 4;
-                wave_topk_bitonic<EE>(row, p.R, p.k, dst);
-            } else if (e <= 1) {
-                wave_topk_bitonic<1>(row, p.R, p.k, dst);
-            } else if (e <= 2) {
-                wave_topk_bitonic<2>(row, p.R, p.k, dst);
-            } else {
-                wave_topk_bitonic<4>(row, p.R, p.k, dst);  // R <= kMaxRegions = 256
+        }
+#pragma unroll
+        for (int j = 0; j < RPW; ++j) wave_argmax(best[j], bs[j]);
+#pragma unroll
+        for (int j = 0; j < RPW; ++j) {
+            const int row = w + kWaves * j;
+            if (lane == 0 && row < nrows) base[row] = bs[j];
+        }
+    } else if constexpr (SPAN == 64) {
+        // R <= 64: lane i ranks element i of each row against the whole row
+        // (broadcast reads); ranks are distinct, and rank < k places the id.
+        double mine[RPW];
+        int rank[RPW];
+#pragma unroll
+        for (int j = 0; j < RPW; ++j) {
+            const double* row = sA + min(w + kWaves * j, nrows - 1) * RS;
+            mine[j] = lane < R ? row[lane] : -INFINITY;
+            rank[j] = 0;
+        }
+        for (int x = 0; x < R; ++x) {
+#pragma unroll
+            for (int j = 0; j < RPW; ++j) {
+                const double a = sA[min(w + kWaves * j, nrows - 1) * RS + x];
+                rank[j] += (a > mine[j] || (a == mine[j] && x < lane)) ? 1 : 0;
             }
         }
+#pragma unroll
+        for (int j = 0; j < RPW; ++j) {
+            const int row = w + kWaves * j;
+            if (row < nrows && lane < R && rank[j] < p.k) base[row * p.k + rank[j]] = lane;
+        }
+    } else {
+        constexpr int E = SPAN / 64;
+        const double* rows[RPW];
+        int32_t* dst[RPW];
+        bool live[RPW];
+#pragma unroll
+        for (int j = 0; j < RPW; ++j) {
+            const int row = w + kWaves * j;
+            rows[j] = sA + min(row, nrows - 1) * RS;
+            dst[j] = base + row * p.k;
+            live[j] = row < nrows;
+        }
+        wave_topk_bitonic<E, RPW>(rows, R, p.k, dst, live);
     }
 }
 
@@ -163,17 +227,25 @@ __global__ __launch_bounds__(kThreads) void route_kernel(const double* __restric
 
 hipError_t launch_route(const Params& p, bool bf16, const double* means, int32_t* idx,
                         hipStream_t stream) {
-    const int nchunk = (p.R + p.route_rows - 1) / p.route_rows;
+    const int span = route_span(p.R);
+    const int rows = kWaves * route_rows_per_wave(span);
+    const int nchunk = (p.R + rows - 1) / rows;
     const dim3 grid(p.B * p.heads * nchunk), block(kThreads);
-    const int lds = p.route_rows * p.R * 8;
-#define BRA_ROUTE(T, HS, WS, NW, HEADS, KTOP)                                                   \
-    if (matches(Inst<T, HS, WS, NW, HEADS, KTOP>::key, p, bf16, true)) {                       \
-        hipLaunchKernelGGL((route_kernel<NW, KTOP>), grid, block, lds, stream, means, idx, p); \
-        return hipGetLastError();                                                              \
+    const int lds = rows * route_row_stride(p.R) * 8;
+#define BRA_ROUTE(T, HS, WS, NW, HEADS, KTOP)                                                \
+    if (matches(Inst<T, HS, WS, NW, HEADS, KTOP>::key, p, bf16, true)) {                    \
+        hipLaunchKernelGGL((route_kernel<NW, KTOP, route_span(NW * NW)>), grid, block, lds, \
+                           stream, means, idx, p);                                          \
+        return hipGetLastError();                                                           \
     }
     BRA_FOR_EACH_SHAPE(BRA_ROUTE)
 #undef BRA_ROUTE
-    hipLaunchKernelGGL((route_kernel<0, 0>), grid, block, lds, stream, means, idx, p);
+    if (span == 64)
+        hipLaunchKernelGGL((route_kernel<0, 0, 64>), grid, block, lds, stream, means, idx, p);
+    else if (span == 128)
+        hipLaunchKernelGGL((route_kernel<0, 0, 128>), grid, block, lds, stream, means, idx, p);
+    else
+        hipLaunchKernelGGL((route_kernel<0, 0, 256>), grid, block, lds, stream, means, idx, p);
     return hipGetLastError();
 }
 
