@@ -1,0 +1,42 @@
+"""Host-side pieces of bench.py: the byte counts the roofline divides by, the
+committed traffic summary it reads, and the refusal of more than one GPU."""
+import os
+
+import bench
+from vision_transformer_sparse_region_amd.workloads import WORKLOADS
+
+
+def test_algorithmic_bytes_stage1():
+    wl = WORKLOADS["stage1"]
+    ab = bench.algorithmic_bytes(wl)
+    S = 64 * 56 * 56 * 64 * 2
+    M = 64 * 2 * 49 * 32 * 8
+    idx = 64 * 2 * 49 * 1 * 4
+    assert ab["S"] == S
+    assert ab["pool"] == 2 * S + 2 * M
+    assert ab["route"] == 2 * M + idx
+    assert ab["attend"] == 4 * S + idx + 64 * 26 * 4
+
+
+def test_attention_flops_highres():
+    wl = WORKLOADS["highres"]
+    # 4 * tokens * heads * k * t * head_dim
+    assert bench.attention_flops(wl) == 4.0 * 8 * 128 * 128 * 2 * 16 * 64 * 32
+
+
+def test_traffic_summary_parses_and_matches_sources():
+    path = bench.traffic_summary_path("stage1")
+    if not os.path.exists(path):
+        return
+    rec = bench.read_traffic_record(path)
+    assert rec["workload"] == "stage1" and rec["kernel"] == "attend"
+    assert rec["hbm_bytes_per_launch"] > 0
+    # the stored figure is used only while the kernel sources are unchanged
+    expect = rec["hbm_bytes_per_launch"] if rec["kernel_source_sha256_16"] == \
+        bench.kernel_source_hash() else None
+    assert bench.stored_traffic("stage1") == expect
+
+
+def test_more_than_one_gpu_is_refused(capsys):
+    assert bench.main(["--gpus", "2"]) == 2
+    assert "one GPU" in capsys.readouterr().err
