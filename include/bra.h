@@ -62,7 +62,7 @@ typedef enum {
     BRA_ERR_NULL = 1,        /* a required pointer is NULL */
     BRA_ERR_SHAPE = 2,       /* sizes not positive, H or W not divisible by n_win,
                                 C not divisible by num_heads, or too large for int32 indexing */
-    BRA_ERR_UNSUPPORTED = 3, /* head_dim != 32, unknown dtype, n_win > 16,
+    BRA_ERR_UNSUPPORTED = 3, /* head_dim != 32, unknown dtype, n_win > 16, H*W >= 2^23,
                                 or a region too large for the kernels' on-chip tiles */
     BRA_ERR_HIP = 4,         /* a HIP runtime call failed (see bra_last_error) */
     BRA_ERR_NOMEM = 5,       /* device memory for the workspace could not be allocated */

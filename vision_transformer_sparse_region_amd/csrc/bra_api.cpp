@@ -23,10 +23,11 @@ struct bra_handle_s {
     int device;
     double* means;       // workspace: [2][B, heads, R, 32] fp64 region means of Q, then
                          // of K; the routing [B, heads, R, k] int32; the MFMA LePE
-                         // operand table
+                         // operand table; C zero floats (the bias when none is given)
     size_t means_bytes;
     int32_t* routing;
     uint2* lepe_table;
+    float* zero_bias;
     // per-kernel timing (events recorded by bra_forward while slots remain)
     std::vector<hipEvent_t> events;  // kEventsPerCall per recorded call
     int timing_capacity;
@@ -108,6 +109,8 @@ bra_status_t bra_create(const bra_config_t* cfg, bra_handle_t* out) {
         return fail(BRA_ERR_SHAPE, "bra_create: one image or the region grid exceeds int32 indexing");
     if (c.channels / c.num_heads != bra::kHeadDim)
         return fail(BRA_ERR_UNSUPPORTED, "bra_create: head_dim must be 32");
+    if (static_cast<double>(c.height) * c.width >= 8388608.0)  // 2^23: 24-bit token indexing
+        return fail(BRA_ERR_UNSUPPORTED, "bra_create: height * width must be below 2^23");
     if (c.dtype != BRA_F32 && c.dtype != BRA_BF16)
         return fail(BRA_ERR_UNSUPPORTED, "bra_create: dtype must be BRA_F32 or BRA_BF16");
     const int R = c.n_win * c.n_win;
@@ -133,10 +136,13 @@ bra_status_t bra_create(const bra_config_t* cfg, bra_handle_t* out) {
     const size_t mean_bytes = 2 * static_cast<size_t>(c.batch) * c.channels * R * sizeof(double);
     const size_t route_bytes =
         ((static_cast<size_t>(c.batch) * c.num_heads * R * k * sizeof(int32_t)) + 15) & ~size_t{15};
-    h->means_bytes = mean_bytes + route_bytes + static_cast<size_t>(p.table_items) * sizeof(uint2);
+    const size_t table_bytes = static_cast<size_t>(p.table_items) * sizeof(uint2);
+    const size_t zero_bytes = static_cast<size_t>(c.channels) * sizeof(float);
+    h->means_bytes = mean_bytes + route_bytes + table_bytes + zero_bytes;
     h->means = nullptr;
     h->routing = nullptr;
     h->lepe_table = nullptr;
+    h->zero_bias = nullptr;
     h->timing_capacity = 0;
     h->timing_used = 0;
     e = hipMalloc(reinterpret_cast<void**>(&h->means), h->means_bytes);
@@ -147,6 +153,14 @@ bra_status_t bra_create(const bra_config_t* cfg, bra_handle_t* out) {
     h->routing = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(h->means) + mean_bytes);
     h->lepe_table =
         reinterpret_cast<uint2*>(reinterpret_cast<char*>(h->means) + mean_bytes + route_bytes);
+    h->zero_bias = reinterpret_cast<float*>(reinterpret_cast<char*>(h->means) + mean_bytes +
+                                            route_bytes + table_bytes);
+    e = hipMemset(h->zero_bias, 0, zero_bytes);
+    if (e != hipSuccess) {
+        hipFree(h->means);
+        delete h;
+        return fail_hip(e, "bra_create: hipMemset of the zero bias");
+    }
     {
         std::lock_guard<std::mutex> lock(g_mutex);
         g_live.insert(h);
@@ -208,7 +222,7 @@ bra_status_t bra_forward(bra_handle_t h, const void* q, const void* k, const voi
     if (timed && (e = hipEventRecord(ev[2], s)) != hipSuccess)
         return fail_hip(e, "bra_forward: hipEventRecord");
     e = bra::launch_attend(h->params, h->bf16, q, k, v, routing, lepe_w, lepe_b, h->lepe_table,
-                           out, s);
+                           h->zero_bias, out, s);
     if (e != hipSuccess) return fail_hip(e, "bra_forward: attention launch");
     if (timed) {
         if ((e = hipEventRecord(ev[3], s)) != hipSuccess)

@@ -5,7 +5,7 @@
 //      (written by the routing kernel), the LePE weights or the Toeplitz LePE
 //      operands, the V window with its 2-token halo, the first job's Q
 //      operands                                                [P5 §五 ⑤]
-//   2  each wave issues the gather of its first routed K/V chunk ...
+//   2  each wave issues the gathers of its first two routed K/V chunks ...
 //   3  ... the halo goes to LDS and the 5x5 depthwise LePE of V runs while
 //      those loads are in flight                       [P5 §五 lepe, ⑧; P2 §2.2]
 //   4  token attention over the routed tokens: S^T = K Q^T and O^T += V^T P^T
@@ -63,159 +63,211 @@ struct StepRegs {
 };
 
 // Q^T operands of a job: lane (query li, group g) holds dims 8g..8g+7 of
-// query (qt0 + jq) * 16 + li of head h (zero past the window).
+// query (qt0 + jq) * 16 + li of head h.  Query slots past the window (and
+// tiles past the job's) load the window's last token instead: their score
+// columns are independent of the others and are never stored, and the load
+// stays unconditional.
 __device__ __forceinline__ void load_q_operands(const Params& p, const WaveJobs& J, int job,
                                                 const uint16_t* __restrict__ qimg, int r,
                                                 bf16x8_t (&qb)[kMaxQTiles]) {
     const int lane = threadIdx.x & 63, li = lane & 15, g = lane >> 4;
     const int h = job / J.G, grp = job - h * J.G;
     const int qt0 = grp * J.tpg;
-    const int nq = min(J.tpg, J.QT - qt0);
 #pragma unroll
     for (int jq = 0; jq < kMaxQTiles; ++jq) {
-        const int qi = (qt0 + jq) * 16 + li;
-        uint4 u = {0u, 0u, 0u, 0u};
-        if (jq < nq && qi < p.t)
-            u = *reinterpret_cast<const uint4*>(qimg + token_offset(p, r, qi) + h * kHeadDim +
-                                                8 * g);
+        const int qi = min((qt0 + jq) * 16 + li, p.t - 1);
+        const uint4 u = *reinterpret_cast<const uint4*>(qimg + token_offset(p, r, qi) +
+                                                        h * kHeadDim + 8 * g);
         qb[jq] = __builtin_bit_cast(bf16x8_t, u);
     }
 }
 
-__device__ __forceinline__ void gather_step(const Params& p, const WaveJobs& J, int w, int step,
-                                            const uint16_t* __restrict__ kimg,
-                                            const uint16_t* __restrict__ vimg, const int* sIdx,
-                                            StepRegs& g8) {
+// Gather of chunk c of local job jl into `g8`.  sOff holds, per (head, rank),
+// the element offset of the routed region's first token.  Keys past the
+// routed set (a ragged last chunk) re-read the last key: their scores are
+// masked to -inf, so they weigh nothing, and every load stays unconditional.
+__device__ __forceinline__ void gather_chunk(const Params& p, const WaveJobs& J, int w, int jl,
+                                             int c, const uint16_t* __restrict__ kimg,
+                                             const uint16_t* __restrict__ vimg, const int* sOff,
+                                             StepRegs& g8) {
     const int lane = threadIdx.x & 63, li = lane & 15, g = lane >> 4;
-    const int jl = step / J.nchunks, c = step - jl * J.nchunks;
     const int job = w + kWaves * jl;
     const int h = job / J.G;
     const int hoff = h * kHeadDim;
-    const int* idx = sIdx + h * p.k;
+    const int* off = sOff + h * p.k;
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
-        const int key = 32 * c + 8 * (li >> 2) + 4 * blk + (li & 3);
-        uint4 u = {0u, 0u, 0u, 0u};
-        if (key < p.nkeys) {
-            const int j = key / p.t, slot = key - j * p.t;
-            u = *reinterpret_cast<const uint4*>(kimg + token_offset(p, idx[j], slot) + hoff +
-                                                8 * g);
-        }
-        g8.ka[blk] = __builtin_bit_cast(bf16x8_t, u);
+        const int key = min(32 * c + 8 * (li >> 2) + 4 * blk + (li & 3), p.nkeys - 1);
+        const int j = key / p.t, slot = key - j * p.t;
+        g8.ka[blk] = __builtin_bit_cast(
+            bf16x8_t, *reinterpret_cast<const uint4*>(kimg + off[j] + slot_offset(p, slot) +
+                                                      hoff + 8 * g));
     }
 #pragma unroll
     for (int pp = 0; pp < 2; ++pp) {
         const int pc = lane + 64 * pp;
-        const int key = 32 * c + (pc >> 2);
-        uint4 u = {0u, 0u, 0u, 0u};
-        if (key < p.nkeys) {
-            const int j = key / p.t, slot = key - j * p.t;
-            u = *reinterpret_cast<const uint4*>(vimg + token_offset(p, idx[j], slot) + hoff +
-                                                8 * (pc & 3));
-        }
-        g8.vv[pp] = u;
+        const int key = min(32 * c + (pc >> 2), p.nkeys - 1);
+        const int j = key / p.t, slot = key - j * p.t;
+        g8.vv[pp] = *reinterpret_cast<const uint4*>(vimg + off[j] + slot_offset(p, slot) + hoff +
+                                                    8 * (pc & 3));
     }
 }
 
+// Chunk `ch` (0 or 1) of pair u of local job jl, if it exists.
+__device__ __forceinline__ bool pair_chunk(const WaveJobs& J, int u, int ch) {
+    return 2 * u + ch < J.nchunks;
+}
+
+// V chunk (in registers, one 16-byte piece per lane and half) through the
+// wave's LDS buffer, read back as the two V^T operands of O^T += V^T P^T.
+__device__ __forceinline__ void v_transpose(const StepRegs& cur, uint16_t* sVt,
+                                            bf16x8_t (&va)[2]) {
+    const int lane = threadIdx.x & 63, li = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int pp = 0; pp < 2; ++pp) {
+        const int pc = lane + 64 * pp;
+        uint2* dst = reinterpret_cast<uint2*>(sVt + (pc >> 2) * kVtStride + 8 * (pc & 3));
+        dst[0] = uint2{cur.vv[pp].x, cur.vv[pp].y};
+        dst[1] = uint2{cur.vv[pp].z, cur.vv[pp].w};
+    }
+    // A wave's LDS operations complete in order; the fences keep the
+    // compiler from moving the transposed reads above the writes, or the
+    // next chunk's writes above these reads.
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int db = 0; db < 2; ++db) {
+        u16x8_t t8;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) t8[e] = sVt[(8 * g + e) * kVtStride + li + 16 * db];
+        va[db] = __builtin_bit_cast(bf16x8_t, t8);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Token attention of one wave's jobs.  Keys are taken 64 at a time (a pair
+// of 32-key chunks, held in the two register sets of `ring`): scores of both
+// chunks, one max and one exponent pass, then both P.V products.  When a
+// job's routed keys fit in 64 (every BiFormer stage), this is a plain
+// softmax with no rescaling; longer key lists carry an online softmax across
+// pairs.  The next pair's gathers are issued as soon as this pair's K and V
+// registers are consumed.
 __device__ __forceinline__ void attend_mfma(const Params& p, const WaveJobs& J, const uint16_t* __restrict__ qimg,
                             const uint16_t* __restrict__ kimg, const uint16_t* __restrict__ vimg,
-                            int r, uint16_t* sVt_all, float* sL, const int* sIdx, StepRegs& cur,
-                            bf16x8_t (&qb)[kMaxQTiles]) {
+                            int r, uint16_t* sVt_all, float* sL, const int* sOff,
+                            StepRegs (&ring)[2], bf16x8_t (&qb)[kMaxQTiles]) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int li = lane & 15, g = lane >> 4;
     uint16_t* sVt = sVt_all + w * 32 * kVtStride;
+    const int npair = (J.nchunks + 1) / 2;
+    const int njl = J.nchunks > 0 ? J.nsteps / J.nchunks : 0;  // this wave's jobs
 
     float m[kMaxQTiles], l[kMaxQTiles];
     f32x4_t o0[kMaxQTiles], o1[kMaxQTiles];
-    for (int s = 0; s < J.nsteps; ++s) {
-        const int jl = s / J.nchunks, c = s - jl * J.nchunks;
+    for (int ss = 0; ss < njl * npair; ++ss) {
+        const int jl = ss / npair, u = ss - jl * npair;
         const int job = w + kWaves * jl;
         const int h = job / J.G, grp = job - h * J.G;
         const int qt0 = grp * J.tpg;
         const int nq = min(J.tpg, J.QT - qt0);
         const int hoff = h * kHeadDim;
-        if (c == 0) {
-            // the first job's operands were loaded with its first gather
-            if (s > 0) load_q_operands(p, J, job, qimg, r, qb);
-#pragma unroll
-            for (int jq = 0; jq < kMaxQTiles; ++jq) {
-                m[jq] = -INFINITY;
-                l[jq] = 0.f;
-                o0[jq] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-                o1[jq] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-            }
-        }
-        StepRegs nxt;
-        if (s + 1 < J.nsteps) gather_step(p, J, w, s + 1, kimg, vimg, sIdx, nxt);
+        const bool two = pair_chunk(J, u, 1);
+        // the first job's Q operands were loaded with its first gathers
+        if (u == 0 && jl > 0) load_q_operands(p, J, job, qimg, r, qb);
 
-        // This step's V chunk into the wave's LDS buffer, read back transposed.
-#pragma unroll
-        for (int pp = 0; pp < 2; ++pp) {
-            const int pc = lane + 64 * pp;
-            uint2* dst = reinterpret_cast<uint2*>(sVt + (pc >> 2) * kVtStride + 8 * (pc & 3));
-            dst[0] = uint2{cur.vv[pp].x, cur.vv[pp].y};
-            dst[1] = uint2{cur.vv[pp].z, cur.vv[pp].w};
-        }
-        // A wave's LDS operations complete in order; the fences keep the
-        // compiler from moving the transposed reads above the writes.
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        bf16x8_t va[2];
-#pragma unroll
-        for (int db = 0; db < 2; ++db) {
-            u16x8_t t8;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) t8[e] = sVt[(8 * g + e) * kVtStride + li + 16 * db];
-            va[db] = __builtin_bit_cast(bf16x8_t, t8);
-        }
+        bf16x8_t va[2][2];
+        v_transpose(ring[0], sVt, va[0]);
+        if (two) v_transpose(ring[1], sVt, va[1]);
 
-        const int kbase = 32 * c + 8 * g;
 #pragma unroll
         for (int jq = 0; jq < kMaxQTiles; ++jq) {
             if (jq >= nq) break;
-            const f32x4_t z4 = {0.f, 0.f, 0.f, 0.f};
-            const f32x4_t s0 =
-                __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur.ka[0], qb[jq], z4, 0, 0, 0);
-            const f32x4_t s1 =
-                __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur.ka[1], qb[jq], z4, 0, 0, 0);
-            // raw scores; the running max m is kept in raw units and the
-            // scale * log2(e) factor enters each exponent through one FMA
-            float x[8];
+            // scores of both chunks: S^T = K Q^T, keys 64u + 32ch + 8g + e on
+            // this lane
+            f32x4_t sc[2][2];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                x[e] = s0[e];
-                x[4 + e] = s1[e];
+            for (int ch = 0; ch < 2; ++ch) {
+                if (ch == 1 && !two) break;
+                const f32x4_t z4 = {0.f, 0.f, 0.f, 0.f};
+                sc[ch][0] =
+                    __builtin_amdgcn_mfma_f32_16x16x32_bf16(ring[ch].ka[0], qb[jq], z4, 0, 0, 0);
+                sc[ch][1] =
+                    __builtin_amdgcn_mfma_f32_16x16x32_bf16(ring[ch].ka[1], qb[jq], z4, 0, 0, 0);
             }
-            if (kbase + 8 > p.nkeys) {
+            // after the last tile's scores the K and V registers are consumed:
+            // the next pair's gathers go out now
+            if (jq == nq - 1) {
+                const int nss = ss + 1, njl2 = nss / npair, nu = nss - njl2 * npair;
+                if (njl2 < njl) {
+                    gather_chunk(p, J, w, njl2, 2 * nu, kimg, vimg, sOff, ring[0]);
+                    if (pair_chunk(J, nu, 1))
+                        gather_chunk(p, J, w, njl2, 2 * nu + 1, kimg, vimg, sOff, ring[1]);
+                }
+            }
+            // raw scores; the running max is kept in raw units and the
+            // scale * log2(e) factor enters each exponent through one FMA
+            float x[2][8];
+#pragma unroll
+            for (int ch = 0; ch < 2; ++ch) {
+                const int kbase = 64 * u + 32 * ch + 8 * g;
+                if (ch == 1 && !two) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) x[ch][e] = -INFINITY;
+                    continue;
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    x[ch][e] = sc[ch][0][e];
+                    x[ch][4 + e] = sc[ch][1][e];
+                }
+                if (kbase + 8 > p.nkeys) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        if (kbase + e >= p.nkeys) x[ch][e] = -INFINITY;
+                }
+            }
+            float mx = x[0][0];
+#pragma unroll
+            for (int ch = 0; ch < 2; ++ch)
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
-                    if (kbase + e >= p.nkeys) x[e] = -INFINITY;
-            }
-            const float mx = group4_max(fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
-                                              fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7]))));
-            const float mnew = fmaxf(m[jq], mx);
-            const float alpha = __builtin_amdgcn_exp2f((m[jq] - mnew) * p.scale_log2e);
+                    if (ch | e) mx = max_f(mx, x[ch][e]);
+            mx = group4_max(mx);
+            const float mnew = u == 0 ? mx : max_f(m[jq], mx);
             const float mb = mnew * p.scale_log2e;
             float psum = 0.f;
-            bf16x8_t pb;
+            bf16x8_t pb[2];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float pe = __builtin_amdgcn_exp2f(fmaf(x[e], p.scale_log2e, -mb));
-                psum += pe;
-                pb[e] = static_cast<__bf16>(pe);
+            for (int ch = 0; ch < 2; ++ch)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float pe = __builtin_amdgcn_exp2f(fmaf(x[ch][e], p.scale_log2e, -mb));
+                    psum += pe;
+                    pb[ch][e] = static_cast<__bf16>(pe);
+                }
+            if (u == 0) {
+                l[jq] = psum;
+                o0[jq] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                o1[jq] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            } else {
+                const float alpha = __builtin_amdgcn_exp2f((m[jq] - mnew) * p.scale_log2e);
+                l[jq] = l[jq] * alpha + psum;
+                o0[jq] *= alpha;
+                o1[jq] *= alpha;
             }
-            l[jq] = l[jq] * alpha + psum;
             m[jq] = mnew;
-            o0[jq] *= alpha;
-            o1[jq] *= alpha;
-            o0[jq] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[0], pb, o0[jq], 0, 0, 0);
-            o1[jq] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[1], pb, o1[jq], 0, 0, 0);
+            o0[jq] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[0][0], pb[0], o0[jq], 0, 0, 0);
+            o1[jq] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[0][1], pb[0], o1[jq], 0, 0, 0);
+            if (two) {
+                o0[jq] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[1][0], pb[1], o0[jq], 0, 0, 0);
+                o1[jq] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[1][1], pb[1], o1[jq], 0, 0, 0);
+            }
         }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
 
-        if (c == J.nchunks - 1) {
+        if (u == npair - 1) {
 #pragma unroll
             for (int jq = 0; jq < kMaxQTiles; ++jq) {
                 if (jq >= nq) break;
@@ -230,7 +282,6 @@ __device__ __forceinline__ void attend_mfma(const Params& p, const WaveJobs& J, 
                 }
             }
         }
-        if (s + 1 < J.nsteps) cur = nxt;
     }
 }
 
@@ -239,23 +290,23 @@ __device__ __forceinline__ void attend_mfma(const Params& p, const WaveJobs& J, 
 // flight while the current one is processed; fp32 throughout.
 __device__ __forceinline__ void attend_valu(const Params& p, const float* __restrict__ qimg,
                             const float* __restrict__ kimg, const float* __restrict__ vimg, int r,
-                            float* sL, const int* sIdx) {
+                            float* sL, const int* sOff) {
     const int sub = threadIdx.x & 7;
     for (int item = threadIdx.x >> 3; item < p.t * p.heads; item += kThreads / 8) {
         const int h = item / p.t, slot = item - h * p.t;
         const int hoff = h * kHeadDim + 4 * sub;
         const float4 qv = *reinterpret_cast<const float4*>(qimg + token_offset(p, r, slot) + hoff);
-        const int* idx = sIdx + h * p.k;
+        const int* roff = sOff + h * p.k;
         float m = -INFINITY, l = 0.f;
         float4 acc = {0.f, 0.f, 0.f, 0.f};
-        int off = token_offset(p, idx[0], 0) + hoff;
+        int off = roff[0] + hoff;
         float4 kv = *reinterpret_cast<const float4*>(kimg + off);
         float4 vv = *reinterpret_cast<const float4*>(vimg + off);
         for (int key = 0; key < p.nkeys; ++key) {
             float4 kn = kv, vn = vv;
             if (key + 1 < p.nkeys) {
                 const int j = (key + 1) / p.t, ks = key + 1 - j * p.t;
-                const int o2 = token_offset(p, idx[j], ks) + hoff;
+                const int o2 = roff[j] + slot_offset(p, ks) + hoff;
                 kn = *reinterpret_cast<const float4*>(kimg + o2);
                 vn = *reinterpret_cast<const float4*>(vimg + o2);
             }
@@ -394,22 +445,21 @@ struct LepeOperands {
     float bias[LepeMfmaShape<HS, WS, HEADS>::GPW];
 };
 
+// `bias` is never NULL (a zero vector stands in for a missing bias); groups
+// past the last one re-read the last group (they are never used).
 template <int HS, int WS, int HEADS>
 __device__ __forceinline__ void lepe_mfma_load(const uint2* __restrict__ table,
-                                               const float* __restrict__ lepe_b,
+                                               const float* __restrict__ bias,
                                                LepeOperands<HS, WS, HEADS>& o) {
     using S = LepeMfmaShape<HS, WS, HEADS>;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
 #pragma unroll
     for (int g = 0; g < S::GPW; ++g) {
-        const int cg = w + kWaves * g;
-        o.bias[g] = 0.f;
-        if (cg < S::NG) {
-            const uint4* src = reinterpret_cast<const uint4*>(table + (cg * 64 + lane) * 10);
+        const int cg = min(w + kWaves * g, S::NG - 1);
+        const uint4* src = reinterpret_cast<const uint4*>(table + (cg * 64 + lane) * 10);
 #pragma unroll
-            for (int e = 0; e < 5; ++e) o.tb[g][e] = src[e];
-            if (lepe_b) o.bias[g] = lepe_b[16 * cg + (lane >> 2)];
-        }
+        for (int e = 0; e < 5; ++e) o.tb[g][e] = src[e];
+        o.bias[g] = bias[16 * cg + (lane >> 2)];
     }
 }
 
@@ -430,7 +480,8 @@ __device__ __forceinline__ void lepe_mfma_compute(const Params& p, const uint16_
             for (int ty = 0; ty < S::TY; ++ty)
 #pragma unroll
                 for (int tx = 0; tx < S::TX; ++tx) {
-                    f32x4_t d = {0.f, 0.f, 0.f, 0.f};
+                    // the accumulator starts at the channel's bias
+                    f32x4_t d = {o.bias[g], o.bias[g], o.bias[g], o.bias[g]};
 #pragma unroll
                     for (int i = 0; i < 5; ++i)
 #pragma unroll
@@ -459,7 +510,7 @@ __device__ __forceinline__ void lepe_mfma_compute(const Params& p, const uint16_
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
                         sL[((4 * ty + e) * WS + 4 * tx + n) * p.lstride + c] =
-                            dacc[g][ty * S::TX + tx][e] + o.bias[g];
+                            dacc[g][ty * S::TX + tx][e];
         }
     }
     __syncthreads();
@@ -473,14 +524,14 @@ template <typename T, int HS, int WS, int NW, int HEADS, int KTOP>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))) void
 attend_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
               const int32_t* __restrict__ routing, const float* __restrict__ lepe_w,
-              const float* __restrict__ lepe_b, const uint2* __restrict__ lepe_table,
-              T* __restrict__ out, Params p_in) {
+              const float* __restrict__ lepe_b, const float* __restrict__ lepe_bias,
+              const uint2* __restrict__ lepe_table, T* __restrict__ out, Params p_in) {
     const Params p = fold_geometry<HS, WS, NW, HEADS, KTOP, Elem<T>::kVec>(p_in);
     extern __shared__ __align__(16) unsigned char smem[];
     T* sVh = reinterpret_cast<T*>(smem + p.off_vh);
     float* sL = reinterpret_cast<float*>(smem + p.off_l);
     float* sW = reinterpret_cast<float*>(smem + p.off_w);
-    int* sIdx = reinterpret_cast<int*>(smem + p.off_idx);
+    int* sOff = reinterpret_cast<int*>(smem + p.off_idx);  // routed region bases
     const bool w_in_lds = p.off_w >= 0;
 
     constexpr int VEC = Elem<T>::kVec;
@@ -493,62 +544,72 @@ attend_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restr
     const int nvec = p.C / VEC;
     const int hw = p.ws + 4;
 
-    // 1. Issue every load that does not depend on the routing first.
+    // 1. Issue every load that does not depend on the routing first.  The
+    //    loads are unconditional (clamped, in-bounds addresses) and nothing
+    //    reads a loaded value until all of them are issued: a value consumed
+    //    inside a branch makes the wave wait for it there, serialising the
+    //    loads behind it.
     //    LePE weights and bias (nw + nb 16-byte pieces, VALU LePE with
     //    weights in LDS): the first kWRegs pieces of each thread ride in
     //    registers and are stored once all loads are issued.
     const int nw = p.C * 25 / 4, nb = lepe_b ? p.C / 4 : 0;
     const bool stage_w = !kLepeMfma && w_in_lds && p.has_lepe;
     float4 wreg[kWRegs];
+    if (stage_w) {
 #pragma unroll
-    for (int u = 0; u < kWRegs; ++u) {
-        const int i = tid + u * kThreads;
-        if (stage_w && i < nw + nb)
+        for (int u = 0; u < kWRegs; ++u) {
+            const int i = min(tid + u * kThreads, nw + nb - 1);
             wreg[u] = i < nw ? reinterpret_cast<const float4*>(lepe_w)[i]
                              : reinterpret_cast<const float4*>(lepe_b)[i - nw];
+        }
     }
-    // the routed region ids of this region, one per (head, rank)
-    int ridx = 0;
-    if (tid < p.heads * p.k) {
-        const int h = tid / p.k, j = tid - h * p.k;
+    // the routed region ids of this region, one per (head, rank); lanes past
+    // heads * k re-read the last one
+    const int nhk = p.heads * p.k;
+    int ridx;
+    {
+        const int i = min(tid, nhk - 1);
+        const int h = i / p.k, j = i - h * p.k;
         ridx = routing[((static_cast<size_t>(b) * p.heads + h) * p.R + r) * p.k + j];
     }
     LepeOperands<kLepeMfma ? HS : 4, kLepeMfma ? WS : 4, kLepeMfma ? HEADS : 1> lop;
-    if constexpr (kLepeMfma) {
-        if (p.has_lepe) lepe_mfma_load<HS, WS, HEADS>(lepe_table, lepe_b, lop);
-    }
+    if constexpr (kLepeMfma) lepe_mfma_load<HS, WS, HEADS>(lepe_table, lepe_bias, lop);
     // halo pieces kept in registers: all of them for a fixed shape (when they
-    // fit kHaloRegs per thread), kHaloRegs otherwise
+    // fit kHaloRegs per thread), kHaloRegs otherwise.  Cells outside the map
+    // load a clamped in-map cell and are zeroed when staged (bit u of hvalid).
     constexpr int kHaloFixed =
         (HS > 0 && WS > 0 && HEADS > 0)
             ? ((HS + 4) * (WS + 4) * (HEADS * kHeadDim / VEC) + kThreads - 1) / kThreads
             : kHaloRegs;
     constexpr int kHR = kHaloFixed < kHaloRegs ? kHaloFixed : kHaloRegs;
     uint4 hreg[kHR];
+    unsigned hvalid = 0;
 #pragma unroll
     for (int u = 0; u < kHR; ++u) {
         const int i = tid + u * kThreads;
-        hreg[u] = uint4{0u, 0u, 0u, 0u};
-        if (p.has_lepe && i < p.halo_pieces) {
-            const int cell = i / nvec, pv = i - cell * nvec;
-            const int hy = cell / hw, hx = cell - hy * hw;
-            const int y = y0 + hy - 2, x = x0 + hx - 2;
-            if (y >= 0 && y < p.H && x >= 0 && x < p.W)
-                hreg[u] = *reinterpret_cast<const uint4*>(v + img + (y * p.W + x) * p.C + pv * VEC);
-        }
+        const int ic = min(i, p.halo_pieces - 1);
+        const int cell = ic / nvec, pv = ic - cell * nvec;
+        const int hy = cell / hw, hx = cell - hy * hw;
+        const int y = y0 + hy - 2, x = x0 + hx - 2;
+        const int yc = min(max(y, 0), p.H - 1), xc = min(max(x, 0), p.W - 1);
+        hreg[u] = *reinterpret_cast<const uint4*>(v + img + (yc * p.W + xc) * p.C + pv * VEC);
+        if (i < p.halo_pieces && y == yc && x == xc) hvalid |= 1u << u;
     }
     WaveJobs J(p, w);
     bf16x8_t qb[kMaxQTiles];
-    if constexpr (VEC == 8) {
-        if (J.nsteps > 0) load_q_operands(p, J, w, reinterpret_cast<const uint16_t*>(q) + img, r, qb);
-    }
-    // Region ids are clamped into range, so a routing buffer holding
-    // garbage (non-finite inputs) cannot send the gather outside the image.
-    if (tid < p.heads * p.k) sIdx[tid] = min(max(ridx, 0), p.R - 1);
-    for (int i = tid + kThreads; i < p.heads * p.k; i += kThreads) {
+    if constexpr (VEC == 8)
+        load_q_operands(p, J, min(w, J.njobs - 1), reinterpret_cast<const uint16_t*>(q) + img, r,
+                        qb);
+    // The element offset of each routed region's first token goes to LDS.
+    // Region ids are clamped into range, so a routing buffer holding garbage
+    // (non-finite inputs) cannot send the gather outside the image.  (Every
+    // thread stores: those past heads * k rewrite the last entry with the
+    // value it already gets, so the store needs no branch.)
+    sOff[min(tid, nhk - 1)] = region_base(p, min(max(ridx, 0), p.R - 1));
+    for (int i = tid + kThreads; i < nhk; i += kThreads) {
         const int h = i / p.k, j = i - h * p.k;
         const int x = routing[((static_cast<size_t>(b) * p.heads + h) * p.R + r) * p.k + j];
-        sIdx[i] = min(max(x, 0), p.R - 1);
+        sOff[i] = region_base(p, min(max(x, 0), p.R - 1));
     }
     if (stage_w) {
 #pragma unroll
@@ -588,7 +649,11 @@ attend_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restr
 #pragma unroll
             for (int u = 0; u < kHR; ++u) {
                 const int i = tid + u * kThreads;
-                if (i < p.halo_pieces) halo_store(i, hreg[u]);
+                // cells outside the map are zero (a mask, not a branch)
+                const unsigned mk = 0u - ((hvalid >> u) & 1u);
+                if (i < p.halo_pieces)
+                    halo_store(i, uint4{hreg[u].x & mk, hreg[u].y & mk, hreg[u].z & mk,
+                                        hreg[u].w & mk});
             }
             for (int i = tid + kHR * kThreads; i < p.halo_pieces; i += kThreads) {
                 const int cell = i / nvec, pv = i - cell * nvec;
@@ -608,13 +673,17 @@ attend_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restr
         lepe_phase<T>(p, sVh, sL, wsrc, bsrc);
     }
 
-    // 3. Each wave issues the gather of its first (job, chunk) step; the LePE
-    //    runs while it is in flight.
-    StepRegs cur;
+    // 3. Each wave issues the gathers of its first two (job, chunk) steps;
+    //    the LePE runs while they are in flight.
+    StepRegs ring[2];
     if constexpr (VEC == 8) {
-        if (J.nsteps > 0)
-            gather_step(p, J, w, 0, reinterpret_cast<const uint16_t*>(k) + img,
-                        reinterpret_cast<const uint16_t*>(v) + img, sIdx, cur);
+        if (J.nsteps > 0) {
+#pragma unroll
+            for (int ch = 0; ch < 2; ++ch)
+                if (ch < J.nchunks)
+                    gather_chunk(p, J, w, 0, ch, reinterpret_cast<const uint16_t*>(k) + img,
+                                 reinterpret_cast<const uint16_t*>(v) + img, sOff, ring[ch]);
+        }
     }
     if (!early_lepe) {
         stage_halo();
@@ -636,11 +705,11 @@ attend_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restr
         attend_mfma(p, J, reinterpret_cast<const uint16_t*>(q) + img,
                     reinterpret_cast<const uint16_t*>(k) + img,
                     reinterpret_cast<const uint16_t*>(v) + img, r,
-                    reinterpret_cast<uint16_t*>(smem + p.off_vt), sL, sIdx, cur, qb);
+                    reinterpret_cast<uint16_t*>(smem + p.off_vt), sL, sOff, ring, qb);
     } else {
         attend_valu(p, reinterpret_cast<const float*>(q) + img,
                     reinterpret_cast<const float*>(k) + img,
-                    reinterpret_cast<const float*>(v) + img, r, sL, sIdx);
+                    reinterpret_cast<const float*>(v) + img, r, sL, sOff);
     }
     __syncthreads();
 
@@ -737,17 +806,20 @@ bool plan(Params& p, int B, int H, int W, int C, int heads, int n_win, int k, fl
 
 hipError_t launch_attend(const Params& p, bool bf16, const void* q, const void* k, const void* v,
                          const int32_t* routing, const float* lepe_w, const float* lepe_b,
-                         const uint2* lepe_table, void* out, hipStream_t stream) {
+                         const uint2* lepe_table, const float* zero_bias, void* out,
+                         hipStream_t stream) {
     Params pp = p;
     pp.has_lepe = lepe_w != nullptr;
     if (!pp.has_lepe) lepe_b = nullptr;
+    // the MFMA LePE loads its bias unconditionally: a zero vector stands in
+    const float* lepe_bias = lepe_b ? lepe_b : zero_bias;
     const dim3 grid(p.B * p.R), block(kThreads);
 #define BRA_ATTEND(T, HS, WS, NW, HEADS, KTOP)                                                 \
     if (matches(Inst<T, HS, WS, NW, HEADS, KTOP>::key, p, bf16, true)) {                       \
         hipLaunchKernelGGL((attend_kernel<T, HS, WS, NW, HEADS, KTOP>), grid, block,           \
                            p.lds_bytes, stream, static_cast<const T*>(q),                      \
                            static_cast<const T*>(k), static_cast<const T*>(v), routing,        \
-                           lepe_w, lepe_b, lepe_table, static_cast<T*>(out), pp);              \
+                           lepe_w, lepe_b, lepe_bias, lepe_table, static_cast<T*>(out), pp);   \
         return hipGetLastError();                                                              \
     }
     BRA_FOR_EACH_SHAPE(BRA_ATTEND)
@@ -756,12 +828,13 @@ hipError_t launch_attend(const Params& p, bool bf16, const void* q, const void* 
         hipLaunchKernelGGL((attend_kernel<uint16_t, 0, 0, 0, 0, 0>), grid, block, p.lds_bytes,
                            stream, static_cast<const uint16_t*>(q),
                            static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
-                           routing, lepe_w, lepe_b, lepe_table, static_cast<uint16_t*>(out), pp);
+                           routing, lepe_w, lepe_b, lepe_bias, lepe_table,
+                           static_cast<uint16_t*>(out), pp);
     else
         hipLaunchKernelGGL((attend_kernel<float, 0, 0, 0, 0, 0>), grid, block, p.lds_bytes,
                            stream, static_cast<const float*>(q), static_cast<const float*>(k),
-                           static_cast<const float*>(v), routing, lepe_w, lepe_b, lepe_table,
-                           static_cast<float*>(out), pp);
+                           static_cast<const float*>(v), routing, lepe_w, lepe_b, lepe_bias,
+                           lepe_table, static_cast<float*>(out), pp);
     return hipGetLastError();
 }
 

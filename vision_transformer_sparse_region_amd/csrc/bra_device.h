@@ -60,6 +60,12 @@ __device__ __forceinline__ int xcd_logical_block(int bid, int nblocks) {
     return (bid & 7) * (full >> 3) + (bid >> 3);
 }
 
+// max(a, b) for non-NaN operands as one v_med3_f32 (the median of a, b and
+// +inf); fmaxf would first quiet each operand that the compiler cannot prove
+// canonical, an extra instruction per operand.
+__device__ __forceinline__ float max_f(float a, float b) {
+    return __builtin_amdgcn_fmed3f(a, b, INFINITY);
+}
 // Max and sum over the four lanes l, l^16, l^32, l^48 -- in the MFMA
 // attention these hold the four key groups of one query.  v_permlane16_swap
 // and v_permlane32_swap exchange rows of 16 and halves of 32 lanes in VALU
@@ -68,10 +74,10 @@ __device__ __forceinline__ int xcd_logical_block(int bid, int nblocks) {
 __device__ __forceinline__ float group4_max(float x) {
     const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x),
                                                     false, false);
-    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    x = max_f(__uint_as_float(a[0]), __uint_as_float(a[1]));
     const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
                                                     false, false);
-    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+    return max_f(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 __device__ __forceinline__ float group4_sum(float x) {
     const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x),
@@ -87,11 +93,20 @@ __device__ __forceinline__ double mean_of(double sum, int t) {
     return (t & (t - 1)) == 0 ? sum * (1.0 / static_cast<double>(t)) : sum / static_cast<double>(t);
 }
 
-// Token offset (elements) of slot `slot` of region `reg` inside one image.
-__device__ __forceinline__ int token_offset(const Params& p, int reg, int slot) {
+// Element offset, inside one image, of the first token of region `reg`, and
+// of slot `slot` relative to it; a token's offset is their sum.  Every factor
+// is below 2^24 (an image has fewer than 2^31 elements), so the products are
+// 24-bit multiplies.
+__device__ __forceinline__ int region_base(const Params& p, int reg) {
     const int ri = reg / p.n, rj = reg - ri * p.n;
+    return __mul24(__mul24(__mul24(ri, p.hs), p.W) + __mul24(rj, p.ws), p.C);
+}
+__device__ __forceinline__ int slot_offset(const Params& p, int slot) {
     const int u = slot / p.ws, w = slot - u * p.ws;
-    return ((ri * p.hs + u) * p.W + rj * p.ws + w) * p.C;
+    return __mul24(__mul24(u, p.W) + w, p.C);
+}
+__device__ __forceinline__ int token_offset(const Params& p, int reg, int slot) {
+    return region_base(p, reg) + slot_offset(p, slot);
 }
 
 // Window geometry as compile-time constants.  A kernel instantiated with

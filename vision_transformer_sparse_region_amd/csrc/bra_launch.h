@@ -57,8 +57,10 @@ hipError_t launch_pool_qk(const Params& p, bool bf16, const void* q, const void*
                           hipStream_t stream);
 hipError_t launch_route(const Params& p, bool bf16, const double* means, int32_t* routing,
                         hipStream_t stream);
+//   zero_bias: C zero floats (device), used when lepe_b is NULL.
 hipError_t launch_attend(const Params& p, bool bf16, const void* q, const void* k, const void* v,
                          const int32_t* routing, const float* lepe_w, const float* lepe_b,
-                         const uint2* lepe_table, void* out, hipStream_t stream);
+                         const uint2* lepe_table, const float* zero_bias, void* out,
+                         hipStream_t stream);
 
 }  // namespace bra
