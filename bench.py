@@ -45,12 +45,19 @@ def kernel_source_hash() -> str:
 
 def algorithmic_bytes(wl) -> dict:
     """Bytes each kernel must move once per launch (unique bytes; the k-fold
-    re-reads of routed K/V and of the LePE halo are cache traffic)."""
+    re-reads of routed K/V, of the LePE halo and of the K means are cache
+    traffic).  Maps of at most 64 regions with at most 4 heads are routed
+    inside the attention kernel, which then also reads the means and writes
+    the ids."""
     es = 2 if wl.dtype == "bf16" else 4
     S = wl.tokens * wl.channels * es                     # one [B,H,W,C] tensor
     M = wl.batch * wl.channels * wl.regions * 8          # one fp64 [B,heads,R,32] mean array
     idx = wl.batch * wl.num_heads * wl.regions * wl.topk_effective * 4
     lepe = wl.channels * 26 * 4
+    if wl.regions <= 64 and wl.num_heads <= 4:
+        # routed inside the attention kernel: it reads the means, writes the ids
+        return {"pool": 2 * S + 2 * M, "route": 0, "attend": 4 * S + 2 * M + idx + lepe,
+                "S": S}
     return {
         "pool": 2 * S + 2 * M,                           # read q, k; write both means
         "route": 2 * M + idx,                            # read both means; write the ids

@@ -14,6 +14,17 @@ def test_algorithmic_bytes_stage1():
     idx = 64 * 2 * 49 * 1 * 4
     assert ab["S"] == S
     assert ab["pool"] == 2 * S + 2 * M
+    # 49 regions, 2 heads: routed inside the attention kernel
+    assert ab["route"] == 0
+    assert ab["attend"] == 4 * S + 2 * M + idx + 64 * 26 * 4
+
+
+def test_algorithmic_bytes_highres_separate_route():
+    wl = WORKLOADS["highres"]
+    ab = bench.algorithmic_bytes(wl)
+    S = 8 * 128 * 128 * 64 * 2
+    M = 8 * 2 * 256 * 32 * 8
+    idx = 8 * 2 * 256 * 16 * 4
     assert ab["route"] == 2 * M + idx
     assert ab["attend"] == 4 * S + idx + 64 * 26 * 4
 

@@ -217,12 +217,15 @@ bra_status_t bra_forward(bra_handle_t h, const void* q, const void* k, const voi
         return fail_hip(e, "bra_forward: hipEventRecord");
     // the routing goes to the caller's buffer when one is given
     int32_t* routing = routing_idx ? routing_idx : h->routing;
-    e = bra::launch_route(h->params, h->bf16, h->means, routing, s);
-    if (e != hipSuccess) return fail_hip(e, "bra_forward: routing launch");
+    // small region grids are routed inside the attention kernel
+    if (!bra::route_in_attend(h->params)) {
+        e = bra::launch_route(h->params, h->bf16, h->means, routing, s);
+        if (e != hipSuccess) return fail_hip(e, "bra_forward: routing launch");
+    }
     if (timed && (e = hipEventRecord(ev[2], s)) != hipSuccess)
         return fail_hip(e, "bra_forward: hipEventRecord");
-    e = bra::launch_attend(h->params, h->bf16, q, k, v, routing, lepe_w, lepe_b, h->lepe_table,
-                           h->zero_bias, out, s);
+    e = bra::launch_attend(h->params, h->bf16, q, k, v, h->means, routing, lepe_w, lepe_b,
+                           h->lepe_table, h->zero_bias, out, s);
     if (e != hipSuccess) return fail_hip(e, "bra_forward: attention launch");
     if (timed) {
         if ((e = hipEventRecord(ev[3], s)) != hipSuccess)

@@ -517,13 +517,63 @@ __device__ __forceinline__ void lepe_mfma_compute(const Params& p, const uint16_
 }
 
 // ---------------------------------------------------------------------------
+// Routing of one (image, head, query region) row on one wave, R <= 64
+// [P4 §1.2; P1 §2.1 TopkRouting; P5 §五 ③-④].  Lane s holds the K mean of
+// region s; the row's Q mean is wave-uniform (scalar loads).  A[s] is the
+// sequential 32-term fp64 sum of dot32_seq.  k = 1: a wave arg-max; k > 1:
+// lane s counts the entries that beat its own (greater, or equal with a
+// lower id) through the wave's LDS scratch row -- the counts are distinct,
+// and count < k places id s at that rank.  Writes each routed region's
+// base offset to off[rank] (LDS) and its id to out[rank] (global).
+__device__ __forceinline__ void route_row_wave(const Params& p, const double* __restrict__ qrow,
+                                               const double (&kreg)[kHeadDim], double* scratch,
+                                               int* off, int32_t* __restrict__ out) {
+    const int lane = threadIdx.x & 63;
+    const double a = dot32_seq(qrow, kreg);
+    // (Non-finite affinities leave the routing undefined, but every offset
+    // the gather uses stays inside the map: the arg-max is clamped, and the
+    // ranks' offsets are pre-filled with region 0 in case NaNs leave a rank
+    // unclaimed.)
+    if (p.k == 1) {
+        double best = lane < p.R ? a : -INFINITY;
+        int bs = lane < p.R ? lane : 0x7fffffff;
+        wave_argmax(best, bs);
+        if (lane == 0) {
+            bs = min(max(bs, 0), p.R - 1);
+            off[0] = region_base(p, bs);
+            out[0] = bs;
+        }
+    } else {
+        if (lane < p.k) off[lane] = 0;
+        scratch[lane] = a;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        int rank = 0;
+        for (int x = 0; x < p.R; ++x) {
+            const double o = scratch[x];
+            rank += (o > a || (o == a && x < lane)) ? 1 : 0;
+        }
+        if (lane < p.R && rank < p.k) {
+            off[rank] = region_base(p, lane);
+            out[rank] = lane;
+        }
+        // the next row's writes must not pass this row's reads
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Fixed shapes whose LePE runs on MFMA need little LDS; all instances are
 // compiled for four waves per SIMD (more waves per SIMD did not pay: the
 // extra register pressure spills).
-template <typename T, int HS, int WS, int NW, int HEADS, int KTOP>
+template <typename T, int HS, int WS, int NW, int HEADS, int KTOP, bool FUSED>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))) void
 attend_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
-              const int32_t* __restrict__ routing, const float* __restrict__ lepe_w,
+              const double* __restrict__ means, int32_t* __restrict__ routing,
+              const float* __restrict__ lepe_w,
               const float* __restrict__ lepe_b, const float* __restrict__ lepe_bias,
               const uint2* __restrict__ lepe_table, T* __restrict__ out, Params p_in) {
     const Params p = fold_geometry<HS, WS, NW, HEADS, KTOP, Elem<T>::kVec>(p_in);
@@ -563,17 +613,38 @@ attend_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restr
                              : reinterpret_cast<const float4*>(lepe_b)[i - nw];
         }
     }
-    // the routed region ids of this region, one per (head, rank); lanes past
-    // heads * k re-read the last one
     const int nhk = p.heads * p.k;
-    int ridx;
-    {
+    const int wu = __builtin_amdgcn_readfirstlane(w);  // w, known wave-uniform
+    const size_t mstride = static_cast<size_t>(p.B) * p.heads * p.R * kHeadDim;
+    int ridx = 0;
+    double kreg[kHeadDim];
+    if constexpr (FUSED) {
+        // In-kernel routing (R <= 64, heads <= 4): wave w routes this region
+        // for head w; lane s holds the K mean of region s, loaded now with
+        // everything else.
+        if (wu < p.heads) {
+            const double2* src = reinterpret_cast<const double2*>(
+                means + mstride +
+                ((static_cast<size_t>(b) * p.heads + wu) * p.R + min(tid & 63, p.R - 1)) *
+                    kHeadDim);
+#pragma unroll
+            for (int d = 0; d < kHeadDim / 2; ++d) {
+                const double2 x = src[d];
+                kreg[2 * d] = x.x;
+                kreg[2 * d + 1] = x.y;
+            }
+        }
+    } else {
+        // the routed region ids of this region, one per (head, rank); lanes
+        // past heads * k re-read the last one
         const int i = min(tid, nhk - 1);
         const int h = i / p.k, j = i - h * p.k;
         ridx = routing[((static_cast<size_t>(b) * p.heads + h) * p.R + r) * p.k + j];
     }
+    // (with in-kernel routing the LePE operands load after it: the K means
+    // hold 64 registers until then)
     LepeOperands<kLepeMfma ? HS : 4, kLepeMfma ? WS : 4, kLepeMfma ? HEADS : 1> lop;
-    if constexpr (kLepeMfma) lepe_mfma_load<HS, WS, HEADS>(lepe_table, lepe_bias, lop);
+    if constexpr (kLepeMfma && !FUSED) lepe_mfma_load<HS, WS, HEADS>(lepe_table, lepe_bias, lop);
     // halo pieces kept in registers: all of them for a fixed shape (when they
     // fit kHaloRegs per thread), kHaloRegs otherwise.  Cells outside the map
     // load a clamped in-map cell and are zeroed when staged (bit u of hvalid).
@@ -605,11 +676,21 @@ attend_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restr
     // (non-finite inputs) cannot send the gather outside the image.  (Every
     // thread stores: those past heads * k rewrite the last entry with the
     // value it already gets, so the store needs no branch.)
-    sOff[min(tid, nhk - 1)] = region_base(p, min(max(ridx, 0), p.R - 1));
-    for (int i = tid + kThreads; i < nhk; i += kThreads) {
-        const int h = i / p.k, j = i - h * p.k;
-        const int x = routing[((static_cast<size_t>(b) * p.heads + h) * p.R + r) * p.k + j];
-        sOff[i] = region_base(p, min(max(x, 0), p.R - 1));
+    if constexpr (FUSED) {
+        if (wu < p.heads) {
+            const size_t row = (static_cast<size_t>(b) * p.heads + wu) * p.R + r;
+            route_row_wave(p, means + row * kHeadDim, kreg,
+                           reinterpret_cast<double*>(smem + p.off_vt) + wu * 64, sOff + wu * p.k,
+                           routing + row * p.k);
+        }
+        if constexpr (kLepeMfma) lepe_mfma_load<HS, WS, HEADS>(lepe_table, lepe_bias, lop);
+    } else {
+        sOff[min(tid, nhk - 1)] = region_base(p, min(max(ridx, 0), p.R - 1));
+        for (int i = tid + kThreads; i < nhk; i += kThreads) {
+            const int h = i / p.k, j = i - h * p.k;
+            const int x = routing[((static_cast<size_t>(b) * p.heads + h) * p.R + r) * p.k + j];
+            sOff[i] = region_base(p, min(max(x, 0), p.R - 1));
+        }
     }
     if (stage_w) {
 #pragma unroll
@@ -767,7 +848,10 @@ bool plan(Params& p, int B, int H, int W, int C, int heads, int n_win, int k, fl
         return static_cast<int>(o);
     };
     const long t = p.t;
-    p.off_vt = take(bf16 ? static_cast<long>(kWaves) * 32 * kVtStride * 2 : 0);
+    // per-wave V^T staging (bf16 attention), also the per-wave scratch row of
+    // the in-kernel routing (64 doubles)
+    p.off_vt = take(std::max(bf16 ? static_cast<long>(kWaves) * 32 * kVtStride * 2 : 0L,
+                             static_cast<long>(kWaves) * 64 * 8));
     // The fixed bf16 shapes whose windows tile by 4x4 run LePE on MFMA with a
     // channel-planar halo; the others on VALU with an NHWC halo.
     p.lepe_mfma = bf16 && is_fixed_shape(p, bf16) && lepe_mfma_fits(p.hs, p.ws, heads);
@@ -805,36 +889,43 @@ bool plan(Params& p, int B, int H, int W, int C, int heads, int n_win, int k, fl
 }
 
 hipError_t launch_attend(const Params& p, bool bf16, const void* q, const void* k, const void* v,
-                         const int32_t* routing, const float* lepe_w, const float* lepe_b,
-                         const uint2* lepe_table, const float* zero_bias, void* out,
-                         hipStream_t stream) {
+                         const double* means, int32_t* routing, const float* lepe_w,
+                         const float* lepe_b, const uint2* lepe_table, const float* zero_bias,
+                         void* out, hipStream_t stream) {
     Params pp = p;
     pp.has_lepe = lepe_w != nullptr;
     if (!pp.has_lepe) lepe_b = nullptr;
     // the MFMA LePE loads its bias unconditionally: a zero vector stands in
     const float* lepe_bias = lepe_b ? lepe_b : zero_bias;
     const dim3 grid(p.B * p.R), block(kThreads);
-#define BRA_ATTEND(T, HS, WS, NW, HEADS, KTOP)                                                 \
-    if (matches(Inst<T, HS, WS, NW, HEADS, KTOP>::key, p, bf16, true)) {                       \
-        hipLaunchKernelGGL((attend_kernel<T, HS, WS, NW, HEADS, KTOP>), grid, block,           \
-                           p.lds_bytes, stream, static_cast<const T*>(q),                      \
-                           static_cast<const T*>(k), static_cast<const T*>(v), routing,        \
-                           lepe_w, lepe_b, lepe_bias, lepe_table, static_cast<T*>(out), pp);   \
-        return hipGetLastError();                                                              \
+    const bool fused = route_in_attend(p);
+#define BRA_ATTEND(T, HS, WS, NW, HEADS, KTOP)                                                  \
+    if (matches(Inst<T, HS, WS, NW, HEADS, KTOP>::key, p, bf16, true)) {                        \
+        hipLaunchKernelGGL((attend_kernel<T, HS, WS, NW, HEADS, KTOP, route_fused(NW * NW, HEADS)>), \
+                           grid, block, p.lds_bytes, stream, static_cast<const T*>(q),          \
+                           static_cast<const T*>(k), static_cast<const T*>(v), means, routing,  \
+                           lepe_w, lepe_b, lepe_bias, lepe_table, static_cast<T*>(out), pp);    \
+        return hipGetLastError();                                                               \
     }
     BRA_FOR_EACH_SHAPE(BRA_ATTEND)
 #undef BRA_ATTEND
-    if (bf16)
-        hipLaunchKernelGGL((attend_kernel<uint16_t, 0, 0, 0, 0, 0>), grid, block, p.lds_bytes,
-                           stream, static_cast<const uint16_t*>(q),
-                           static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
-                           routing, lepe_w, lepe_b, lepe_bias, lepe_table,
-                           static_cast<uint16_t*>(out), pp);
-    else
-        hipLaunchKernelGGL((attend_kernel<float, 0, 0, 0, 0, 0>), grid, block, p.lds_bytes,
-                           stream, static_cast<const float*>(q), static_cast<const float*>(k),
-                           static_cast<const float*>(v), routing, lepe_w, lepe_b, lepe_bias,
-                           lepe_table, static_cast<float*>(out), pp);
+#define BRA_GENERIC(T, F)                                                                       \
+    hipLaunchKernelGGL((attend_kernel<T, 0, 0, 0, 0, 0, F>), grid, block, p.lds_bytes, stream,  \
+                       static_cast<const T*>(q), static_cast<const T*>(k),                      \
+                       static_cast<const T*>(v), means, routing, lepe_w, lepe_b, lepe_bias,     \
+                       lepe_table, static_cast<T*>(out), pp)
+    if (bf16) {
+        if (fused)
+            BRA_GENERIC(uint16_t, true);
+        else
+            BRA_GENERIC(uint16_t, false);
+    } else {
+        if (fused)
+            BRA_GENERIC(float, true);
+        else
+            BRA_GENERIC(float, false);
+    }
+#undef BRA_GENERIC
     return hipGetLastError();
 }
 

@@ -57,10 +57,19 @@ hipError_t launch_pool_qk(const Params& p, bool bf16, const void* q, const void*
                           hipStream_t stream);
 hipError_t launch_route(const Params& p, bool bf16, const double* means, int32_t* routing,
                         hipStream_t stream);
+// Maps of at most 64 regions and at most one head per wave are routed inside
+// the attention kernel (one region per lane, one head per wave); others by
+// the routing kernel.
+constexpr bool route_fused(int R, int heads) {
+    return R <= 64 && heads <= kWaves;
+}
+inline bool route_in_attend(const Params& p) { return route_fused(p.R, p.heads); }
+
+//   routing: read when the routing kernel ran, written when route_in_attend.
 //   zero_bias: C zero floats (device), used when lepe_b is NULL.
 hipError_t launch_attend(const Params& p, bool bf16, const void* q, const void* k, const void* v,
-                         const int32_t* routing, const float* lepe_w, const float* lepe_b,
-                         const uint2* lepe_table, const float* zero_bias, void* out,
-                         hipStream_t stream);
+                         const double* means, int32_t* routing, const float* lepe_w,
+                         const float* lepe_b, const uint2* lepe_table, const float* zero_bias,
+                         void* out, hipStream_t stream);
 
 }  // namespace bra
