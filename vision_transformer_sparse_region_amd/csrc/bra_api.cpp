@@ -21,8 +21,8 @@ struct bra_handle_s {
     bra::Params params;
     bool bf16;
     int device;
-    double* means;       // workspace: [2][B, heads, R, 32] fp64 region means of Q, then
-                         // of K; the routing [B, heads, R, k] int32; the MFMA LePE
+    double* means;       // workspace: fp64 region means of Q [B, heads, R, 32], then of
+                         // K [B, heads, 32, R]; the routing [B, heads, R, k] int32; the MFMA LePE
                          // operand table; C zero floats (the bias when none is given)
     size_t means_bytes;
     int32_t* routing;

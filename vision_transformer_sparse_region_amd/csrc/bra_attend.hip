@@ -615,25 +615,13 @@ attend_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restr
     }
     const int nhk = p.heads * p.k;
     const int wu = __builtin_amdgcn_readfirstlane(w);  // w, known wave-uniform
-    const size_t mstride = static_cast<size_t>(p.B) * p.heads * p.R * kHeadDim;
     int ridx = 0;
     double kreg[kHeadDim];
     if constexpr (FUSED) {
         // In-kernel routing (R <= 64, heads <= 4): wave w routes this region
         // for head w; lane s holds the K mean of region s, loaded now with
         // everything else.
-        if (wu < p.heads) {
-            const double2* src = reinterpret_cast<const double2*>(
-                means + mstride +
-                ((static_cast<size_t>(b) * p.heads + wu) * p.R + min(tid & 63, p.R - 1)) *
-                    kHeadDim);
-#pragma unroll
-            for (int d = 0; d < kHeadDim / 2; ++d) {
-                const double2 x = src[d];
-                kreg[2 * d] = x.x;
-                kreg[2 * d + 1] = x.y;
-            }
-        }
+        if (wu < p.heads) load_kmean(p, means, b * p.heads + wu, min(tid & 63, p.R - 1), kreg);
     } else {
         // the routed region ids of this region, one per (head, rank); lanes
         // past heads * k re-read the last one
@@ -679,7 +667,7 @@ attend_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restr
     if constexpr (FUSED) {
         if (wu < p.heads) {
             const size_t row = (static_cast<size_t>(b) * p.heads + wu) * p.R + r;
-            route_row_wave(p, means + row * kHeadDim, kreg,
+            route_row_wave(p, means + qmean_index(p, b * p.heads + wu, r, 0), kreg,
                            reinterpret_cast<double*>(smem + p.off_vt) + wu * 64, sOff + wu * p.k,
                            routing + row * p.k);
         }

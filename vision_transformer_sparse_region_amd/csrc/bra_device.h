@@ -88,6 +88,24 @@ __device__ __forceinline__ float group4_sum(float x) {
     return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// Layout of the fp64 region means in the workspace: Q means row-major
+// [B][heads][R][32] (a row is read whole, as wave-uniform scalar loads), then
+// K means dim-major [B][heads][32][R] (lane s of a wave reads region s, so
+// every load of a dim is one contiguous run).
+__device__ __forceinline__ size_t qmean_index(const Params& p, int bh, int r, int d) {
+    return (static_cast<size_t>(bh) * p.R + r) * kHeadDim + d;
+}
+__device__ __forceinline__ size_t kmean_index(const Params& p, int bh, int d, int s) {
+    return static_cast<size_t>(p.B) * p.heads * p.R * kHeadDim +
+           (static_cast<size_t>(bh) * kHeadDim + d) * p.R + s;
+}
+// The K mean of region s, head bh, into registers (32 coalesced loads).
+__device__ __forceinline__ void load_kmean(const Params& p, const double* __restrict__ means,
+                                           int bh, int s, double (&kreg)[kHeadDim]) {
+#pragma unroll
+    for (int d = 0; d < kHeadDim; ++d) kreg[d] = means[kmean_index(p, bh, d, s)];
+}
+
 // mean = sum / t, as a multiplication when t is a power of two (exact then).
 __device__ __forceinline__ double mean_of(double sum, int t) {
     return (t & (t - 1)) == 0 ? sum * (1.0 / static_cast<double>(t)) : sum / static_cast<double>(t);

@@ -48,7 +48,7 @@ bool plan(Params& p, int B, int H, int W, int C, int heads, int n_win, int k, fl
           bool bf16);
 
 // Kernel launches on `stream`; return the launch status.
-//   means: [2][B][heads][R][32] fp64 -- region means of Q, then of K.
+//   means: fp64 region means, Q as [B][heads][R][32], then K as [B][heads][32][R].
 //   lepe_table: p.table_items 8-byte entries (written by the pool kernel when
 //   lepe_w is given and the shape runs LePE on MFMA).
 //   routing: [B][heads][R][k] int32 region ids.

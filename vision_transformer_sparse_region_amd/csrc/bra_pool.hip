@@ -37,7 +37,6 @@ __global__ __launch_bounds__(kThreads) void pool_qk_kernel(const T* __restrict__
         if (it < p.table_items) lepe_table[it] = lepe_toeplitz_entry(lepe_w, it);
         return;
     }
-    const size_t mstride = static_cast<size_t>(p.B) * p.heads * p.R * kHeadDim;
     const int nvec = p.C / VEC;
 
     if (VEC == 8 && 64 % nvec == 0) {
@@ -65,12 +64,17 @@ __global__ __launch_bounds__(kThreads) void pool_qk_kernel(const T* __restrict__
             for (int e = 0; e < 8; ++e) acc[e] += __shfl_xor(acc[e], m);
         if (tg == 0) {
             const int c = pv * 8, h = c / kHeadDim, d = c - h * kHeadDim;
-            double* dst = means + tensor * mstride +
-                          ((static_cast<size_t>(b) * p.heads + h) * p.R + r) * kHeadDim + d;
+            const int bh = b * p.heads + h;
+            if (tensor == 0) {
+                double* dst = means + qmean_index(p, bh, r, d);
 #pragma unroll
-            for (int e = 0; e < 8; e += 2)
-                *reinterpret_cast<double2*>(dst + e) =
-                    double2{mean_of(acc[e], p.t), mean_of(acc[e + 1], p.t)};
+                for (int e = 0; e < 8; e += 2)
+                    *reinterpret_cast<double2*>(dst + e) =
+                        double2{mean_of(acc[e], p.t), mean_of(acc[e + 1], p.t)};
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) means[kmean_index(p, bh, d + e, r)] = mean_of(acc[e], p.t);
+            }
         }
         return;
     }
@@ -80,7 +84,6 @@ __global__ __launch_bounds__(kThreads) void pool_qk_kernel(const T* __restrict__
     const int blk = xcd_logical_block(blockIdx.x, p.pool_blocks);
     const int b = blk / p.R, r = blk - b * p.R;
     const size_t img = static_cast<size_t>(b) * p.H * p.W * p.C;
-    double* mimg = means + static_cast<size_t>(b) * p.heads * p.R * kHeadDim;
     for (int tensor = 0; tensor < 2; ++tensor) {
         const T* src = (tensor == 0 ? q : k) + img;
         double acc[kMaxChannels / kThreads] = {};
@@ -109,7 +112,8 @@ __global__ __launch_bounds__(kThreads) void pool_qk_kernel(const T* __restrict__
             const int c = tid + j * kThreads;
             if (c < p.C) {
                 const int h = c / kHeadDim, d = c - h * kHeadDim;
-                mimg[tensor * mstride + (static_cast<size_t>(h) * p.R + r) * kHeadDim + d] =
+                const int bh = b * p.heads + h;
+                means[tensor == 0 ? qmean_index(p, bh, r, d) : kmean_index(p, bh, d, r)] =
                     mean_of(acc[j], p.t);
             }
         }

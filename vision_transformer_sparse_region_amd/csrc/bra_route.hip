@@ -126,23 +126,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
     const int nchunk = (R + ROWS - 1) / ROWS;
     const int bh = blockIdx.x / nchunk, chunk = blockIdx.x - bh * nchunk;
     const int r0 = chunk * ROWS, nrows = min(ROWS, R - r0);
-    const size_t mstride = static_cast<size_t>(p.B) * p.heads * R * kHeadDim;
-    const double* qbar = means + static_cast<size_t>(bh) * R * kHeadDim;  // [R][32]
-    const double* kbar = qbar + mstride;
+    const double* qbar = means + qmean_index(p, bh, 0, 0);  // [R][32]
 
     // Affinity.  Thread (s, g) keeps K mean s in registers and takes its dot
     // with query rows g, g + G, ...; rows past the chunk read zeros.
     const int s = tid % SPAN, g = tid / SPAN;
     double kreg[kHeadDim];
-    {
-        const double2* src = reinterpret_cast<const double2*>(kbar + min(s, R - 1) * kHeadDim);
-#pragma unroll
-        for (int d = 0; d < kHeadDim / 2; ++d) {
-            const double2 x = src[d];
-            kreg[2 * d] = x.x;
-            kreg[2 * d + 1] = x.y;
-        }
-    }
+    load_kmean(p, means, bh, min(s, R - 1), kreg);
     for (int i = tid; i < ROWS * kHeadDim / 2; i += kThreads) {
         const bool in = i < nrows * kHeadDim / 2;
         reinterpret_cast<double2*>(sQ)[i] =
