@@ -103,6 +103,20 @@ bra_status_t bra_forward(bra_handle_t h, const void* q, const void* k, const voi
                          const float* lepe_w, const float* lepe_b, void* out,
                          int32_t* routing_idx, void* stream);
 
+/* Attention and LePE with a routing the caller supplies: steps 4-5 above on
+ * the regions routing_idx names, without computing the region means or the
+ * routing (for reusing one routing across several calls, the reuse the pages
+ * suggest for consecutive slices [P2 §4.2]).
+ *   routing_idx   device [B,heads,R,k] int32, required; row (b,h,r) lists the
+ *                 k regions whose tokens the queries of region r attend to
+ *                 (any order; a region listed twice counts twice).  Ids are
+ *                 clamped into [0, R) before use.
+ *   the other arguments and the checks are those of bra_forward.
+ * Enqueued on `stream` without synchronising or allocating. */
+bra_status_t bra_forward_routed(bra_handle_t h, const void* q, const void* k, const void* v,
+                                const float* lepe_w, const float* lepe_b,
+                                const int32_t* routing_idx, void* out, void* stream);
+
 /* Release the workspace and the handle.  NULL is a no-op (BRA_OK); a handle
  * that is not live gives BRA_ERR_BAD_HANDLE. */
 bra_status_t bra_destroy(bra_handle_t h);

@@ -64,6 +64,8 @@ def test_dead_handles(lib):
     assert lib.bra_destroy(None) == bra.BRA_OK
     assert lib.bra_destroy(fake) == bra.BRA_ERR_BAD_HANDLE
     assert bra.bra_forward_status(fake, 16, 16, 16, None, None, 32) == bra.BRA_ERR_BAD_HANDLE
+    assert bra.bra_forward_routed_status(fake, 16, 16, 16, None, None, 16, 32) == \
+        bra.BRA_ERR_BAD_HANDLE
     assert lib.bra_topk_effective(fake) == -1
     assert lib.bra_timing_enable(fake, 4) == bra.BRA_ERR_BAD_HANDLE
     buf = (ctypes.c_float * 2)()

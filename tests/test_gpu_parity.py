@@ -102,7 +102,8 @@ def test_handle_reuse_and_argument_checks():
         bra.bra_timing_enable(h.handle, 2)
         h.forward(q, k, v, w, b)
         times = bra.bra_timing_read(h.handle, 2)
-        assert len(times) == 1 and times[0][0] > 0 and times[0][1] > 0
+        # (shapes routed inside the attention kernel record ~0 for the routing)
+        assert len(times) == 1 and times[0][0] > 0 and times[0][1] >= 0 and times[0][2] > 0
     finally:
         h.close()
     assert bra.load_library().bra_forward(h.handle, None, None, None, None, None, None, None,

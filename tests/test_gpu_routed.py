@@ -1,0 +1,118 @@
+"""GPU parity of bra_forward_routed (attention + LePE on a caller-supplied
+routing) through the C ABI, against the oracle's attention with the same
+routing: arbitrary ids (unsorted, repeated), ids out of range (clamped into
+[0, R) by the library, so the oracle gets the clamped ids), the fused-routing
+shapes (whose forward routes inside the attention kernel, so this entry runs
+the other kernel instance), and agreement with bra_forward when given
+bra_forward's own routing.  Same bar as tests/parity.py."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from parity import TOL, max_rel_err, oracle_cfg, run_gpu, say
+from vision_transformer_sparse_region_amd import bra
+from vision_transformer_sparse_region_amd.workloads import WORKLOADS, Workload, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    WORKLOADS["stage1"].with_(batch=4, seed=201),
+    WORKLOADS["stage2"].with_(batch=4, seed=202),
+    WORKLOADS["stage3"].with_(batch=4, seed=203),
+    Workload("routed_ragged", 2, 12, 20, 64, 2, 4, 3, "bf16", 204, lepe_bias=True),
+    Workload("routed_f32", 2, 28, 28, 64, 2, 7, 4, "f32", 205, lepe_bias=True),
+    WORKLOADS["highres"].with_(batch=1, seed=206),
+]
+
+
+def random_routing(wl: Workload, seed: int, lo: int = 0, hi: int | None = None) -> np.ndarray:
+    rng = np.random.default_rng(seed)
+    hi = wl.regions if hi is None else hi
+    return rng.integers(lo, hi, size=(wl.batch, wl.num_heads, wl.regions, wl.topk_effective),
+                        dtype=np.int64).astype(np.int32)
+
+
+def run_routed(wl: Workload, inp: dict, idx: np.ndarray) -> torch.Tensor:
+    dev = torch.device("cuda:0")
+    q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
+    w, b = inp["lepe_w"].to(dev), inp["lepe_b"].to(dev)
+    h = bra.BRA(wl.batch, wl.height, wl.width, wl.channels, wl.num_heads, wl.n_win, wl.topk,
+                wl.dtype)
+    try:
+        out = h.forward_routed(q, k, v, torch.from_numpy(idx).to(dev), w, b)
+        torch.cuda.synchronize()
+    finally:
+        h.close()
+    return out.cpu()
+
+
+def oracle_routed(wl: Workload, inp: dict, idx: np.ndarray) -> np.ndarray:
+    f = {n: inp[n].double().numpy() for n in ("q", "k", "v", "lepe_w", "lepe_b")}
+    return oracle.attend_with_routing(oracle_cfg(wl), f["q"], f["k"], f["v"], f["lepe_w"],
+                                      f["lepe_b"], idx)
+
+
+@pytest.mark.parametrize("wl", CASES, ids=[w.name for w in CASES])
+def test_given_routing_matches_oracle(wl):
+    inp = make_inputs(wl)
+    idx = random_routing(wl, wl.seed)
+    say(f"[gpu] routed {wl.name}: B={wl.batch} {wl.height}x{wl.width} C={wl.channels} "
+        f"heads={wl.num_heads} n_win={wl.n_win} k={wl.topk_effective} {wl.dtype}")
+    out = run_routed(wl, inp, idx)
+    err = max_rel_err(out, oracle_routed(wl, inp, idx))
+    say(f"[gpu] routed {wl.name}: max rel err {err:.3e} (bound {TOL[wl.dtype]:g})")
+    assert err <= TOL[wl.dtype]
+
+
+def test_out_of_range_ids_are_clamped():
+    wl = WORKLOADS["stage2"].with_(batch=2, seed=207)
+    inp = make_inputs(wl)
+    idx = random_routing(wl, 207, lo=-8, hi=wl.regions + 8)
+    say("[gpu] routed out-of-range ids")
+    out = run_routed(wl, inp, idx)
+    err = max_rel_err(out, oracle_routed(wl, inp, np.clip(idx, 0, wl.regions - 1)))
+    say(f"[gpu] routed out-of-range ids: max rel err {err:.3e}")
+    assert err <= TOL[wl.dtype]
+
+
+@pytest.mark.parametrize("name", ["stage1", "stage3"])
+def test_own_routing_reproduces_forward(name):
+    """With bra_forward's routing, bra_forward_routed gives bra_forward's
+    output: bitwise where both use the same attention instance (stage 3 is
+    routed by the routing kernel), to 1e-6 of the output scale where the
+    forward routed inside the kernel (stage 1)."""
+    wl = WORKLOADS[name].with_(batch=4, seed=208)
+    inp = make_inputs(wl)
+    say(f"[gpu] routed vs forward {name}")
+    ref, idx = run_gpu(wl, inp)
+    out = run_routed(wl, inp, idx)
+    if name == "stage3":
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+    else:
+        d = (out.double() - ref.double()).abs().max().item() / ref.double().abs().max().item()
+        say(f"[gpu] routed vs forward {name}: max rel diff {d:.3e}")
+        assert d <= 1e-6
+
+
+def test_routed_argument_checks():
+    wl = WORKLOADS["stage1"].with_(batch=1, seed=209)
+    inp = make_inputs(wl)
+    dev = torch.device("cuda:0")
+    q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
+    out = torch.empty_like(q)
+    h = bra.BRA(wl.batch, wl.height, wl.width, wl.channels, wl.num_heads, wl.n_win, wl.topk)
+    try:
+        say("[gpu] routed argument checks")
+        idx = torch.zeros((1, 2, 49, 1), dtype=torch.int32, device=dev)
+        assert bra.bra_forward_routed_status(h.handle, q, k, v, None, None, None, out) == \
+            bra.BRA_ERR_NULL
+        assert bra.bra_forward_routed_status(h.handle, q, k, v, None, None, idx, q) == \
+            bra.BRA_ERR_ALIAS
+        assert bra.bra_forward_routed_status(h.handle, q, k, v, None, None,
+                                             idx.data_ptr() + 2, out) == bra.BRA_ERR_ALIGN
+        assert bra.bra_forward_routed_status(h.handle, q, k, v, None, None, idx, out) == \
+            bra.BRA_OK
+        torch.cuda.synchronize()
+    finally:
+        h.close()

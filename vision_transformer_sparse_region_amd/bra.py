@@ -67,6 +67,7 @@ def load_library(path: str = LIB_PATH):
     vp, i32 = ctypes.c_void_p, ctypes.c_int32
     lib.bra_create.argtypes = [ctypes.POINTER(BraConfig), ctypes.POINTER(vp)]
     lib.bra_forward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.bra_forward_routed.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.bra_destroy.argtypes = [vp]
     lib.bra_topk_effective.argtypes = [vp]
     lib.bra_topk_effective.restype = i32
@@ -76,8 +77,8 @@ def load_library(path: str = LIB_PATH):
     lib.bra_last_error.restype = ctypes.c_char_p
     lib.bra_timing_enable.argtypes = [vp, i32]
     lib.bra_timing_read.argtypes = [vp, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(i32)]
-    for name in ("bra_create", "bra_forward", "bra_destroy", "bra_timing_enable",
-                 "bra_timing_read"):
+    for name in ("bra_create", "bra_forward", "bra_forward_routed", "bra_destroy",
+                 "bra_timing_enable", "bra_timing_read"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -153,6 +154,20 @@ def bra_forward_status(h, q, k, v, lepe_w, lepe_b, out, routing_idx=None, stream
                                       _ptr(out), _ptr(routing_idx), stream)
 
 
+def bra_forward_routed(h: int, q, k, v, lepe_w, lepe_b, routing_idx, out, stream=None):
+    """Enqueue attention + LePE on a given routing (torch's current stream by default)."""
+    st = load_library().bra_forward_routed(h, _ptr(q), _ptr(k), _ptr(v), _ptr(lepe_w),
+                                           _ptr(lepe_b), _ptr(routing_idx), _ptr(out),
+                                           _stream(stream))
+    _check(st, "bra_forward_routed")
+
+
+def bra_forward_routed_status(h, q, k, v, lepe_w, lepe_b, routing_idx, out, stream=0) -> int:
+    """Raw status of bra_forward_routed (for tests of the argument checks)."""
+    return load_library().bra_forward_routed(h, _ptr(q), _ptr(k), _ptr(v), _ptr(lepe_w),
+                                             _ptr(lepe_b), _ptr(routing_idx), _ptr(out), stream)
+
+
 def bra_destroy(h) -> None:
     _check(load_library().bra_destroy(h), "bra_destroy")
 
@@ -215,6 +230,25 @@ class BRA:
             routing_idx = None
         bra_forward(self.handle, q, k, v, lepe_w, lepe_b, out, routing_idx, stream)
         return out, routing_idx
+
+    def forward_routed(self, q, k, v, routing_idx, lepe_w=None, lepe_b=None, out=None,
+                       stream=None):
+        """Attention + LePE over the regions `routing_idx` ([B, heads, R, k] int32) names."""
+        import torch
+        c = self.cfg
+        want = torch.bfloat16 if self.dtype == "bf16" else torch.float32
+        shape = (c.batch, c.height, c.width, c.channels)
+        for name, t in (("q", q), ("k", k), ("v", v)):
+            if t.dtype != want or tuple(t.shape) != shape or not t.is_contiguous() or not t.is_cuda:
+                raise ValueError(f"{name}: expected a contiguous {want} CUDA tensor {shape}")
+        rshape = (c.batch, c.num_heads, c.n_win * c.n_win, self.k)
+        if (routing_idx.dtype != torch.int32 or tuple(routing_idx.shape) != rshape or
+                not routing_idx.is_contiguous() or not routing_idx.is_cuda):
+            raise ValueError(f"routing_idx: expected a contiguous int32 CUDA tensor {rshape}")
+        if out is None:
+            out = torch.empty_like(q)
+        bra_forward_routed(self.handle, q, k, v, lepe_w, lepe_b, routing_idx, out, stream)
+        return out
 
     def close(self):
         if self.handle:

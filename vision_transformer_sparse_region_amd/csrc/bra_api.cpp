@@ -187,24 +187,38 @@ int32_t bra_topk_effective(bra_handle_t h) {
     return h->params.k;
 }
 
-bra_status_t bra_forward(bra_handle_t h, const void* q, const void* k, const void* v,
-                         const float* lepe_w, const float* lepe_b, void* out,
-                         int32_t* routing_idx, void* stream) {
-    if (!is_live(h)) return fail(BRA_ERR_BAD_HANDLE, "bra_forward: not a live handle");
-    if (!q || !k || !v || !out) return fail(BRA_ERR_NULL, "bra_forward: q, k, v and out are required");
+// The argument checks shared by both forward entry points (`what` names the
+// caller in messages).
+static bra_status_t check_forward_args(bra_handle_t h, const char* what, const void* q,
+                                       const void* k, const void* v, const float* lepe_w,
+                                       const float* lepe_b, const void* out,
+                                       const int32_t* routing_idx) {
+    const std::string w(what);
+    if (!is_live(h)) return fail(BRA_ERR_BAD_HANDLE, w + ": not a live handle");
+    if (!q || !k || !v || !out) return fail(BRA_ERR_NULL, w + ": q, k, v and out are required");
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16))
-        return fail(BRA_ERR_ALIGN, "bra_forward: q, k, v and out must be 16-byte aligned");
+        return fail(BRA_ERR_ALIGN, w + ": q, k, v and out must be 16-byte aligned");
     if (!aligned(lepe_w, 4) || !aligned(lepe_b, 4) || !aligned(routing_idx, 4))
-        return fail(BRA_ERR_ALIGN, "bra_forward: lepe_w, lepe_b and routing_idx must be 4-byte aligned");
+        return fail(BRA_ERR_ALIGN, w + ": lepe_w, lepe_b and routing_idx must be 4-byte aligned");
     const bra_config_t& c = h->cfg;
     const size_t bytes = static_cast<size_t>(c.batch) * c.height * c.width * c.channels *
                          (h->bf16 ? 2 : 4);
     if (overlaps(out, q, bytes) || overlaps(out, k, bytes) || overlaps(out, v, bytes))
-        return fail(BRA_ERR_ALIAS, "bra_forward: out must not overlap q, k or v");
+        return fail(BRA_ERR_ALIAS, w + ": out must not overlap q, k or v");
     int dev = -1;
     hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return fail_hip(e, "bra_forward: hipGetDevice");
-    if (dev != h->device) return fail(BRA_ERR_DEVICE, "bra_forward: wrong current device");
+    if (e != hipSuccess) return fail_hip(e, (w + ": hipGetDevice").c_str());
+    if (dev != h->device) return fail(BRA_ERR_DEVICE, w + ": wrong current device");
+    return BRA_OK;
+}
+
+bra_status_t bra_forward(bra_handle_t h, const void* q, const void* k, const void* v,
+                         const float* lepe_w, const float* lepe_b, void* out,
+                         int32_t* routing_idx, void* stream) {
+    bra_status_t st = check_forward_args(h, "bra_forward", q, k, v, lepe_w, lepe_b, out,
+                                         routing_idx);
+    if (st != BRA_OK) return st;
+    hipError_t e;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     const bool timed = h->timing_used < h->timing_capacity;
@@ -224,14 +238,38 @@ bra_status_t bra_forward(bra_handle_t h, const void* q, const void* k, const voi
     }
     if (timed && (e = hipEventRecord(ev[2], s)) != hipSuccess)
         return fail_hip(e, "bra_forward: hipEventRecord");
-    e = bra::launch_attend(h->params, h->bf16, q, k, v, h->means, routing, lepe_w, lepe_b,
-                           h->lepe_table, h->zero_bias, out, s);
+    e = bra::launch_attend(h->params, h->bf16, q, k, v, h->means, routing,
+                           !bra::route_in_attend(h->params), lepe_w, lepe_b, h->lepe_table,
+                           h->zero_bias, out, s);
     if (e != hipSuccess) return fail_hip(e, "bra_forward: attention launch");
     if (timed) {
         if ((e = hipEventRecord(ev[3], s)) != hipSuccess)
             return fail_hip(e, "bra_forward: hipEventRecord");
         ++h->timing_used;
     }
+    return BRA_OK;
+}
+
+bra_status_t bra_forward_routed(bra_handle_t h, const void* q, const void* k, const void* v,
+                                const float* lepe_w, const float* lepe_b,
+                                const int32_t* routing_idx, void* out, void* stream) {
+    if (!routing_idx && is_live(h))
+        return fail(BRA_ERR_NULL, "bra_forward_routed: routing_idx is required");
+    bra_status_t st = check_forward_args(h, "bra_forward_routed", q, k, v, lepe_w, lepe_b, out,
+                                         routing_idx);
+    if (st != BRA_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = hipSuccess;
+    // the MFMA LePE operand table is the region-pool kernel's side product:
+    // build it alone (no means) when this shape uses it
+    if (lepe_w && h->params.table_items > 0) {
+        e = bra::launch_lepe_table(h->params, lepe_w, h->lepe_table, s);
+        if (e != hipSuccess) return fail_hip(e, "bra_forward_routed: LePE table launch");
+    }
+    e = bra::launch_attend(h->params, h->bf16, q, k, v, h->means,
+                           const_cast<int32_t*>(routing_idx), true, lepe_w, lepe_b,
+                           h->lepe_table, h->zero_bias, out, s);
+    if (e != hipSuccess) return fail_hip(e, "bra_forward_routed: attention launch");
     return BRA_OK;
 }
 

@@ -877,26 +877,36 @@ bool plan(Params& p, int B, int H, int W, int C, int heads, int n_win, int k, fl
 }
 
 hipError_t launch_attend(const Params& p, bool bf16, const void* q, const void* k, const void* v,
-                         const double* means, int32_t* routing, const float* lepe_w,
-                         const float* lepe_b, const uint2* lepe_table, const float* zero_bias,
-                         void* out, hipStream_t stream) {
+                         const double* means, int32_t* routing, bool use_routing,
+                         const float* lepe_w, const float* lepe_b, const uint2* lepe_table,
+                         const float* zero_bias, void* out, hipStream_t stream) {
     Params pp = p;
     pp.has_lepe = lepe_w != nullptr;
     if (!pp.has_lepe) lepe_b = nullptr;
     // the MFMA LePE loads its bias unconditionally: a zero vector stands in
     const float* lepe_bias = lepe_b ? lepe_b : zero_bias;
     const dim3 grid(p.B * p.R), block(kThreads);
-    const bool fused = route_in_attend(p);
+    const bool fused = !use_routing && route_in_attend(p);
+#define BRA_ATTEND_F(T, HS, WS, NW, HEADS, KTOP, F)                                             \
+    hipLaunchKernelGGL((attend_kernel<T, HS, WS, NW, HEADS, KTOP, F>), grid, block,             \
+                       p.lds_bytes, stream, static_cast<const T*>(q), static_cast<const T*>(k), \
+                       static_cast<const T*>(v), means, routing, lepe_w, lepe_b, lepe_bias,    \
+                       lepe_table, static_cast<T*>(out), pp)
 #define BRA_ATTEND(T, HS, WS, NW, HEADS, KTOP)                                                  \
     if (matches(Inst<T, HS, WS, NW, HEADS, KTOP>::key, p, bf16, true)) {                        \
-        hipLaunchKernelGGL((attend_kernel<T, HS, WS, NW, HEADS, KTOP, route_fused(NW * NW, HEADS)>), \
-                           grid, block, p.lds_bytes, stream, static_cast<const T*>(q),          \
-                           static_cast<const T*>(k), static_cast<const T*>(v), means, routing,  \
-                           lepe_w, lepe_b, lepe_bias, lepe_table, static_cast<T*>(out), pp);    \
+        if constexpr (route_fused(NW * NW, HEADS)) {                                            \
+            if (fused)                                                                          \
+                BRA_ATTEND_F(T, HS, WS, NW, HEADS, KTOP, true);                                 \
+            else                                                                                \
+                BRA_ATTEND_F(T, HS, WS, NW, HEADS, KTOP, false);                                \
+        } else {                                                                                \
+            BRA_ATTEND_F(T, HS, WS, NW, HEADS, KTOP, false);                                    \
+        }                                                                                       \
         return hipGetLastError();                                                               \
     }
     BRA_FOR_EACH_SHAPE(BRA_ATTEND)
 #undef BRA_ATTEND
+#undef BRA_ATTEND_F
 #define BRA_GENERIC(T, F)                                                                       \
     hipLaunchKernelGGL((attend_kernel<T, 0, 0, 0, 0, 0, F>), grid, block, p.lds_bytes, stream,  \
                        static_cast<const T*>(q), static_cast<const T*>(k),                      \

@@ -65,11 +65,17 @@ constexpr bool route_fused(int R, int heads) {
 }
 inline bool route_in_attend(const Params& p) { return route_fused(p.R, p.heads); }
 
-//   routing: read when the routing kernel ran, written when route_in_attend.
+//   use_routing: read the routing from `routing` (written by the routing
+//   kernel or given by the caller); otherwise route in the kernel (needs
+//   route_in_attend) and write the ids to `routing`.
 //   zero_bias: C zero floats (device), used when lepe_b is NULL.
 hipError_t launch_attend(const Params& p, bool bf16, const void* q, const void* k, const void* v,
-                         const double* means, int32_t* routing, const float* lepe_w,
-                         const float* lepe_b, const uint2* lepe_table, const float* zero_bias,
-                         void* out, hipStream_t stream);
+                         const double* means, int32_t* routing, bool use_routing,
+                         const float* lepe_w, const float* lepe_b, const uint2* lepe_table,
+                         const float* zero_bias, void* out, hipStream_t stream);
+// The MFMA LePE operand table alone (the region-pool kernel's trailing
+// workgroups), for the entry point that skips the region means.
+hipError_t launch_lepe_table(const Params& p, const float* lepe_w, uint2* lepe_table,
+                             hipStream_t stream);
 
 }  // namespace bra

@@ -122,6 +122,24 @@ __global__ __launch_bounds__(kThreads) void pool_qk_kernel(const T* __restrict__
 
 }  // namespace
 
+namespace {
+__global__ __launch_bounds__(kThreads) void lepe_table_kernel(const float* __restrict__ lepe_w,
+                                                              uint2* __restrict__ lepe_table,
+                                                              int items) {
+    const int it = blockIdx.x * kThreads + threadIdx.x;
+    if (it < items) lepe_table[it] = lepe_toeplitz_entry(lepe_w, it);
+}
+}  // namespace
+
+hipError_t launch_lepe_table(const Params& p, const float* lepe_w, uint2* lepe_table,
+                             hipStream_t stream) {
+    if (p.table_items <= 0) return hipSuccess;
+    const dim3 grid((p.table_items + kThreads - 1) / kThreads), block(kThreads);
+    hipLaunchKernelGGL(lepe_table_kernel, grid, block, 0, stream, lepe_w, lepe_table,
+                       p.table_items);
+    return hipGetLastError();
+}
+
 hipError_t launch_pool_qk(const Params& p, bool bf16, const void* q, const void* k,
                           const float* lepe_w, double* means, uint2* lepe_table,
                           hipStream_t stream) {
