@@ -112,10 +112,12 @@ class OracleLib:
         lib.oracle_attend_with_routing.argtypes = [cp, _DP, _DP, _DP, _DP, _DP, _IP, _DP]
         lib.oracle_bra_forward.argtypes = [cp, _DP, _DP, _DP, _DP, _DP, _DP, _IP, _DP, _DP,
                                            _DP]
+        lib.oracle_route_shared.argtypes = [cp, _DP, _DP, _DP, _IP]
+        lib.oracle_bra_forward_shared.argtypes = [cp, _DP, _DP, _DP, _DP, _DP, _DP, _IP, _DP]
         lib.oracle_num_threads.argtypes = []
         for name in ("oracle_region_means", "oracle_route", "oracle_attend", "oracle_lepe",
-                     "oracle_attend_with_routing", "oracle_bra_forward",
-                     "oracle_num_threads"):
+                     "oracle_attend_with_routing", "oracle_bra_forward", "oracle_route_shared",
+                     "oracle_bra_forward_shared", "oracle_num_threads"):
             getattr(lib, name).restype = ctypes.c_int
         self.lib = lib
         self.path = path
@@ -146,6 +148,40 @@ class OracleLib:
         _check(self.lib.oracle_route(ctypes.byref(c), qp, kp, _ptr(aff),
                                      idx.ctypes.data_as(_IP)), "route")
         return (idx, aff) if want_aff else idx
+
+    def route_shared(self, cfg: OracleConfig, qbar, kbar, want_aff: bool = False):
+        """Head-shared routing: idx [B,R,k] (and the affinity [B,R,R] if want_aff)."""
+        c = cfg._c()
+        qa, qp = _f64(qbar)
+        ka, kp = _f64(kbar)
+        k = self.topk_effective(cfg)
+        idx = np.empty((cfg.batch, cfg.regions, k), np.int32)
+        aff = np.empty((cfg.batch, cfg.regions, cfg.regions), np.float64) if want_aff else None
+        _check(self.lib.oracle_route_shared(ctypes.byref(c), qp, kp, _ptr(aff),
+                                            idx.ctypes.data_as(_IP)), "route_shared")
+        return (idx, aff) if want_aff else idx
+
+    def bra_forward_shared(self, cfg: OracleConfig, q, k, v, w=None, b=None, *,
+                           want_aff=False):
+        """Whole forward with head-shared routing: dict with 'out', 'idx' [B,R,k]
+        (+ 'aff' [B,R,R])."""
+        c = cfg._c()
+        qa, qp = _f64(q)
+        ka, kp = _f64(k)
+        va, vp = _f64(v)
+        wa, wp = _f64(w)
+        ba, bp = _f64(b)
+        kk = self.topk_effective(cfg)
+        out = np.empty(_map_shape(cfg), np.float64)
+        idx = np.empty((cfg.batch, cfg.regions, kk), np.int32)
+        aff = np.empty((cfg.batch, cfg.regions, cfg.regions), np.float64) if want_aff else None
+        _check(self.lib.oracle_bra_forward_shared(ctypes.byref(c), qp, kp, vp, wp, bp,
+                                                  _ptr(out), idx.ctypes.data_as(_IP),
+                                                  _ptr(aff)), "bra_forward_shared")
+        res = {"out": out, "idx": idx}
+        if want_aff:
+            res["aff"] = aff
+        return res
 
     def attend(self, cfg: OracleConfig, q, k, v, idx) -> np.ndarray:
         c = cfg._c()
@@ -249,3 +285,11 @@ def attend_with_routing(cfg, q, k, v, w, b, idx):
 
 def bra_forward(cfg, q, k, v, w=None, b=None, *, want_aff=False, want_means=False):
     return default().bra_forward(cfg, q, k, v, w, b, want_aff=want_aff, want_means=want_means)
+
+
+def route_shared(cfg, qbar, kbar, want_aff=False):
+    return default().route_shared(cfg, qbar, kbar, want_aff)
+
+
+def bra_forward_shared(cfg, q, k, v, w=None, b=None, *, want_aff=False):
+    return default().bra_forward_shared(cfg, q, k, v, w, b, want_aff=want_aff)

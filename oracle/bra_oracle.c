@@ -92,6 +92,22 @@ int oracle_region_means(const oracle_cfg_t* c, const double* x, double* xbar) {
 
 /* ---- steps 3-4: affinity and top-k -------------------------------------- */
 
+/* Top-k of one affinity row: k passes, each keeping the largest entry not yet
+ * taken.  Strict '>' while scanning upward leaves an exact tie with the lower
+ * id.  `taken` is R bytes of scratch. */
+static void topk_row(const double* row, int R, int k, unsigned char* taken, int32_t* out) {
+    for (int s = 0; s < R; ++s) taken[s] = 0;
+    for (int j = 0; j < k; ++j) {
+        int best = -1;
+        for (int s = 0; s < R; ++s) {
+            if (taken[s]) continue;
+            if (best < 0 || row[s] > row[best]) best = s;
+        }
+        taken[best] = 1;
+        out[j] = best;
+    }
+}
+
 int oracle_route(const oracle_cfg_t* c, const double* qbar, const double* kbar,
                  double* aff, int32_t* idx) {
     if (!cfg_ok(c) || !qbar || !kbar || !idx) return -1;
@@ -112,20 +128,42 @@ int oracle_route(const oracle_cfg_t* c, const double* qbar, const double* kbar,
                 double a = 0.0;
                 for (int d = 0; d < hd; ++d) a += qr[d] * ks[d];
                 row[s] = a;
-                taken[s] = 0;
                 if (aff) aff[(size_t)rowid * R + s] = a;
             }
-            /* k passes; each keeps the largest untaken entry.  Strict '>'
-             * while scanning upward leaves an exact tie with the lower id. */
-            for (int j = 0; j < k; ++j) {
-                int best = -1;
-                for (int s = 0; s < R; ++s) {
-                    if (taken[s]) continue;
-                    if (best < 0 || row[s] > row[best]) best = s;
+            topk_row(row, R, k, taken, idx + (size_t)rowid * k);
+        }
+        free(row);
+        free(taken);
+    }
+    return 0;
+}
+
+int oracle_route_shared(const oracle_cfg_t* c, const double* qbar, const double* kbar,
+                        double* aff, int32_t* idx) {
+    if (!cfg_ok(c) || !qbar || !kbar || !idx) return -1;
+    const int H = c->num_heads, hd = c->channels / H;
+    const int R = c->n_win * c->n_win;
+    const int k = oracle_topk_effective(c);
+    const int nrows = c->batch * R;
+#pragma omp parallel
+    {
+        double* row = (double*)malloc(sizeof(double) * (size_t)R);
+        unsigned char* taken = (unsigned char*)malloc((size_t)R);
+#pragma omp for schedule(static)
+        for (int rowid = 0; rowid < nrows; ++rowid) {
+            const int b = rowid / R, r = rowid % R;
+            for (int s = 0; s < R; ++s) {
+                /* one sum over the C channels, c = h * hd + d in order */
+                double a = 0.0;
+                for (int h = 0; h < H; ++h) {
+                    const double* qh = qbar + (((size_t)b * H + h) * R + r) * hd;
+                    const double* kh = kbar + (((size_t)b * H + h) * R + s) * hd;
+                    for (int d = 0; d < hd; ++d) a += qh[d] * kh[d];
                 }
-                taken[best] = 1;
-                idx[(size_t)rowid * k + j] = best;
+                row[s] = a;
+                if (aff) aff[(size_t)rowid * R + s] = a;
             }
+            topk_row(row, R, k, taken, idx + (size_t)rowid * k);
         }
         free(row);
         free(taken);
@@ -234,6 +272,35 @@ int oracle_attend_with_routing(const oracle_cfg_t* c, const double* q, const dou
     if (rc == 0)
         for (size_t i = 0; i < n; ++i) out[i] = out[i] + L[i];
     free(L);
+    return rc;
+}
+
+int oracle_bra_forward_shared(const oracle_cfg_t* c, const double* q, const double* k,
+                              const double* v, const double* w, const double* bias,
+                              double* out, int32_t* idx, double* aff) {
+    if (!cfg_ok(c) || !q || !k || !v || !out || !idx) return -1;
+    const int H = c->num_heads, hd = c->channels / H;
+    const int R = c->n_win * c->n_win;
+    const int kk = oracle_topk_effective(c);
+    const size_t nbar = (size_t)c->batch * H * R * hd;
+    double* qb = (double*)malloc(sizeof(double) * nbar);
+    double* kb = (double*)malloc(sizeof(double) * nbar);
+    int32_t* full = (int32_t*)malloc(sizeof(int32_t) * (size_t)c->batch * H * R * kk);
+    int rc = -1;
+    if (qb && kb && full && oracle_region_means(c, q, qb) == 0 &&
+        oracle_region_means(c, k, kb) == 0 && oracle_route_shared(c, qb, kb, aff, idx) == 0) {
+        /* every head of region r attends over the same routed regions */
+        for (int b = 0; b < c->batch; ++b)
+            for (int h = 0; h < H; ++h)
+                for (int r = 0; r < R; ++r)
+                    for (int j = 0; j < kk; ++j)
+                        full[(((size_t)b * H + h) * R + r) * kk + j] =
+                            idx[((size_t)b * R + r) * kk + j];
+        rc = oracle_attend_with_routing(c, q, k, v, w, bias, full, out);
+    }
+    free(qb);
+    free(kb);
+    free(full);
     return rc;
 }
 

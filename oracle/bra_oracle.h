@@ -67,6 +67,14 @@ int oracle_region_means(const oracle_cfg_t* cfg, const double* x, double* xbar);
 int oracle_route(const oracle_cfg_t* cfg, const double* qbar, const double* kbar,
                  double* aff, int32_t* idx);
 
+/* Head-shared routing: the affinity of a region pair is one sum over all C
+ * channels (c = h*head_dim + d in order) of Qbar . Kbar -- the region means
+ * over the full channel dimension -- and one top-k per (batch, region)
+ * serves every head.  idx: [B, R, k_eff]; aff: [B, R, R] or NULL.
+ * [P1 §2.2 index without a head axis; P2 §2.1; P3 §2.1; P4 §1.2] */
+int oracle_route_shared(const oracle_cfg_t* cfg, const double* qbar, const double* kbar,
+                        double* aff, int32_t* idx);
+
 /* Token-to-token attention of every token over the tokens of its k routed
  * regions (idx as produced by oracle_route, any order).  o excludes LePE.
  * [P3 §2.2 TokenAttention; P5 §五 steps ⑤-⑦] */
@@ -88,6 +96,13 @@ int oracle_attend_with_routing(const oracle_cfg_t* cfg, const double* q, const d
 int oracle_bra_forward(const oracle_cfg_t* cfg, const double* q, const double* k,
                        const double* v, const double* lepe_w, const double* lepe_b,
                        double* out, int32_t* idx, double* aff, double* qbar, double* kbar);
+
+/* Whole forward with head-shared routing: means -> oracle_route_shared ->
+ * attend (every head over the same routed regions) -> + LePE.
+ * idx: [B, R, k_eff]; aff: [B, R, R] or NULL. */
+int oracle_bra_forward_shared(const oracle_cfg_t* cfg, const double* q, const double* k,
+                              const double* v, const double* lepe_w, const double* lepe_b,
+                              double* out, int32_t* idx, double* aff);
 
 /* Number of OpenMP threads a parallel region of the oracle uses. */
 int oracle_num_threads(void);

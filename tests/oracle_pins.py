@@ -93,10 +93,12 @@ def torch_lepe(v, w, b):
     return y.permute(0, 2, 3, 1).numpy()
 
 
-def torch_bra_recipe(cfg: OracleConfig, q, k, v, w, b):
+def torch_bra_recipe(cfg: OracleConfig, q, k, v, w, b, shared=False):
     """The pages' PyTorch recipe in float64: window partition [P3 §1], per-head
     means and affinity [P5 §五 ③], torch.topk [P5 §五 ④], torch.gather of the
-    routed windows [P5 §五 ⑤], softmax attention [P5 §五 ⑥], LePE of V added."""
+    routed windows [P5 §五 ⑤], softmax attention [P5 §五 ⑥], LePE of V added.
+    shared=True routes with the full-C means, one index for every head, as
+    P2 §2.1 and P3 §2.1 do (their affinity is [B, R, R])."""
     B, H, W, C = q.shape
     n, h = cfg.n_win, cfg.num_heads
     hd = C // h
@@ -111,8 +113,15 @@ def torch_bra_recipe(cfg: OracleConfig, q, k, v, w, b):
 
     qr, kr, vr = regions(q), regions(k), regions(v)
     t = qr.shape[3]
-    aff = qr.mean(dim=3) @ kr.mean(dim=3).transpose(-1, -2)
-    idx = aff.topk(k_eff, dim=-1).indices  # [B, h, R, k]
+    if shared:
+        # full-C region means [B, R, C] from the unsplit windows
+        qf = torch.from_numpy(np_windows(q, n)).mean(dim=2)
+        kf = torch.from_numpy(np_windows(k, n)).mean(dim=2)
+        sidx = (qf @ kf.transpose(-1, -2)).topk(k_eff, dim=-1).indices  # [B, R, k]
+        idx = sidx.unsqueeze(1).expand(B, h, R, k_eff)
+    else:
+        aff = qr.mean(dim=3) @ kr.mean(dim=3).transpose(-1, -2)
+        idx = aff.topk(k_eff, dim=-1).indices  # [B, h, R, k]
 
     def gather(x):
         xe = x.unsqueeze(2).expand(B, h, R, R, t, hd)
@@ -126,6 +135,7 @@ def torch_bra_recipe(cfg: OracleConfig, q, k, v, w, b):
     out = np_unwindows(o, n, H, W)
     if w is not None:
         out = out + torch_lepe(v, w, b)
+    idx = sidx if shared else idx
     return out, idx.numpy().astype(np.int32)
 
 
@@ -351,6 +361,77 @@ def pin_topk_clamp(orc):
         assert orc.topk_effective(OracleConfig(1, 8, 8, 4, 1, 4, topk)) == expect
 
 
+# ---- head-shared routing [P1 §2.2; P2 §2.1; P3 §2.1; P4 §1.2] --------------
+
+def pin_shared_routing_bruteforce_argsort(orc):
+    """Head-shared routing equals a stable argsort of the affinity of the
+    full-C window means, computed with numpy reshapes."""
+    for (B, H, W, heads, hd, n, topk, seed) in [
+        (2, 12, 8, 2, 8, 4, 5, 71), (1, 14, 14, 4, 8, 7, 4, 73), (3, 6, 9, 3, 4, 3, 9, 79)]:
+        cfg = OracleConfig(B, H, W, heads * hd, heads, n, topk)
+        rng = _rng(seed)
+        q, k = _rand_map(rng, cfg), _rand_map(rng, cfg)
+        res = orc.bra_forward_shared(cfg, q, k, _rand_map(rng, cfg), want_aff=True)
+        qf, kf = np_windows(q, n).mean(axis=2), np_windows(k, n).mean(axis=2)
+        aff = np.einsum("brc,bsc->brs", qf, kf)
+        np.testing.assert_allclose(res["aff"], aff, rtol=1e-12, atol=1e-14)
+        k_eff = min(topk, n * n) if topk > 0 else n * n
+        expect = np.argsort(-aff, axis=-1, kind="stable")[..., :k_eff]
+        assert (res["idx"] == expect).all()
+
+
+def pin_shared_routing_one_head_is_per_head(orc):
+    """With one head, head-shared and per-head routing coincide (bit for bit)."""
+    cfg = OracleConfig(2, 12, 12, 16, 1, 3, 4)
+    rng = _rng(83)
+    q, k, v = (_rand_map(rng, cfg) for _ in range(3))
+    w, b = _rand_lepe(rng, cfg)
+    per = orc.bra_forward(cfg, q, k, v, w, b, want_aff=True)
+    sh = orc.bra_forward_shared(cfg, q, k, v, w, b, want_aff=True)
+    assert (sh["idx"] == per["idx"][:, 0]).all()
+    np.testing.assert_array_equal(sh["aff"], per["aff"][:, 0])
+    np.testing.assert_array_equal(sh["out"], per["out"])
+
+
+def pin_shared_routing_sums_head_affinities(orc):
+    """The shared affinity is the sum of the per-head affinities (to rounding),
+    and every head attends over the shared routed set."""
+    cfg = OracleConfig(2, 8, 8, 12, 3, 4, 3)
+    rng = _rng(89)
+    q, k, v = (_rand_map(rng, cfg) for _ in range(3))
+    per = orc.bra_forward(cfg, q, k, v, want_aff=True)
+    sh = orc.bra_forward_shared(cfg, q, k, v, want_aff=True)
+    np.testing.assert_allclose(sh["aff"], per["aff"].sum(axis=1), rtol=1e-12, atol=1e-13)
+    full = np.ascontiguousarray(np.repeat(sh["idx"][:, None], 3, axis=1))
+    np.testing.assert_allclose(sh["out"], orc.attend(cfg, q, k, v, full), rtol=RTOL, atol=ATOL)
+
+
+def pin_shared_ties_go_to_lower_region(orc):
+    """Exact ties in the shared affinity go to the lower region id."""
+    cfg = OracleConfig(1, 8, 8, 8, 2, 4, 5)
+    rng = _rng(97)
+    q = _rand_map(rng, cfg)
+    tile = rng.standard_normal((2, 2, 8))
+    k = np.tile(tile, (4, 4, 1))[None]
+    res = orc.bra_forward_shared(cfg, q, k, _rand_map(rng, cfg))
+    assert (res["idx"] == np.arange(5)).all()
+
+
+def pin_shared_matches_torch_recipe(orc):
+    """The whole forward with head-shared routing equals the pages' PyTorch
+    recipe with full-C routing, in float64."""
+    for (B, H, W, heads, hd, n, topk, seed) in [
+        (2, 8, 8, 2, 8, 2, 2, 101), (1, 12, 16, 4, 8, 4, 3, 103), (2, 9, 6, 3, 4, 3, 4, 107)]:
+        cfg = OracleConfig(B, H, W, heads * hd, heads, n, topk)
+        rng = _rng(seed)
+        q, k, v = (_rand_map(rng, cfg) for _ in range(3))
+        w, b = _rand_lepe(rng, cfg)
+        res = orc.bra_forward_shared(cfg, q, k, v, w, b)
+        ref_out, ref_idx = torch_bra_recipe(cfg, q, k, v, w, b, shared=True)
+        assert (res["idx"] == ref_idx).all()
+        np.testing.assert_allclose(res["out"], ref_out, rtol=RTOL, atol=ATOL)
+
+
 ALL_PINS = [
     pin_topk_all_is_dense_attention,
     pin_one_region_is_dense_attention,
@@ -367,4 +448,9 @@ ALL_PINS = [
     pin_matches_torch_recipe,
     pin_lepe_reads_v,
     pin_topk_clamp,
+    pin_shared_routing_bruteforce_argsort,
+    pin_shared_routing_one_head_is_per_head,
+    pin_shared_routing_sums_head_affinities,
+    pin_shared_ties_go_to_lower_region,
+    pin_shared_matches_torch_recipe,
 ]

@@ -33,8 +33,13 @@ MUTANTS = [
      "for (int d = 0; d < hd - 1; ++d) a += qr[d] * ks[d];"),
     ("affinity_transposed", "const double* ks = kbar + ((size_t)bh * R + s) * hd;",
      "const double* ks = qbar + ((size_t)bh * R + s) * hd; (void)kbar;"),
-    ("k_from_q_region_means", "oracle_region_means(c, k, kb) == 0",
-     "oracle_region_means(c, q, kb) == 0"),
+    ("k_from_q_region_means", "oracle_region_means(c, k, kb) == 0 &&\n        oracle_route(",
+     "oracle_region_means(c, q, kb) == 0 &&\n        oracle_route("),
+    ("shared_head0_only", "for (int h = 0; h < H; ++h) {\n                    const double* qh",
+     "for (int h = 0; h < 1; ++h) {\n                    const double* qh"),
+    ("shared_routing_per_head0",
+     "full[(((size_t)b * H + h) * R + r) * kk + j] =\n                            idx[((size_t)b * R + r) * kk + j];",
+     "full[(((size_t)b * H + h) * R + r) * kk + j] =\n                            idx[((size_t)b * R + (h ? 0 : r)) * kk + j];"),
 ]
 
 
