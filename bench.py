@@ -43,7 +43,7 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def algorithmic_bytes(wl) -> dict:
+def algorithmic_bytes(wl, shared_routing: bool = False) -> dict:
     """Bytes each kernel must move once per launch (unique bytes; the k-fold
     re-reads of routed K/V, of the LePE halo and of the K means are cache
     traffic).  Maps of at most 64 regions with at most 4 heads are routed
@@ -52,9 +52,10 @@ def algorithmic_bytes(wl) -> dict:
     es = 2 if wl.dtype == "bf16" else 4
     S = wl.tokens * wl.channels * es                     # one [B,H,W,C] tensor
     M = wl.batch * wl.channels * wl.regions * 8          # one fp64 [B,heads,R,32] mean array
-    idx = wl.batch * wl.num_heads * wl.regions * wl.topk_effective * 4
+    idx = wl.batch * (1 if shared_routing else wl.num_heads) * wl.regions * \
+        wl.topk_effective * 4
     lepe = wl.channels * 26 * 4
-    if wl.regions <= 64 and wl.num_heads <= 4:
+    if wl.regions <= 64 and wl.num_heads <= 4 and not shared_routing:
         # routed inside the attention kernel: it reads the means, writes the ids
         return {"pool": 2 * S + 2 * M, "route": 0, "attend": 4 * S + 2 * M + idx + lepe,
                 "S": S}
@@ -95,7 +96,7 @@ def stored_traffic(workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(wl, inputs, gpu_out, target_s: float = 10.0) -> dict:
+def cpu_baseline(wl, inputs, gpu_out, target_s: float = 10.0, shared: bool = False) -> dict:
     """Time the CPU oracle on the first images of the same batch (a bounded
     sample) and check the GPU output for those images against it."""
     import numpy as np
@@ -108,7 +109,8 @@ def cpu_baseline(wl, inputs, gpu_out, target_s: float = 10.0) -> dict:
         f = {n: inputs[n][:nimg].double().numpy() for n in ("q", "k", "v")}
         w, b = inputs["lepe_w"].double().numpy(), inputs["lepe_b"].double().numpy()
         t0 = time.perf_counter()
-        res = oracle.bra_forward(cfg, f["q"], f["k"], f["v"], w, b)
+        fwd = oracle.bra_forward_shared if shared else oracle.bra_forward
+        res = fwd(cfg, f["q"], f["k"], f["v"], w, b)
         return time.perf_counter() - t0, res
 
     dt, res = run(1)
@@ -158,6 +160,8 @@ def main(argv=None) -> int:
     ap.add_argument("--buffer-sets", type=int, default=0,
                     help="input/output sets to rotate over (0: enough to exceed the MALL)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--shared-routing", action="store_true",
+                    help="one routing per region for every head (full-C region affinity)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help=f"also run a {COPY_BYTES >> 20} MiB device copy (for counter scaling)")
     args = ap.parse_args(argv)
@@ -181,12 +185,12 @@ def main(argv=None) -> int:
     for i in range(nsets):
         d = {n: host[n].to(dev) for n in ("q", "k", "v", "lepe_w", "lepe_b")}
         d["out"] = torch.empty_like(d["q"])
-        d["idx"] = torch.empty((wl.batch, wl.num_heads, wl.regions, wl.topk_effective),
-                               dtype=torch.int32, device=dev)
+        d["idx"] = torch.empty((wl.batch, 1 if args.shared_routing else wl.num_heads,
+                                wl.regions, wl.topk_effective), dtype=torch.int32, device=dev)
         sets.append(d)
 
     h = bra.BRA(wl.batch, wl.height, wl.width, wl.channels, wl.num_heads, wl.n_win, wl.topk,
-                wl.dtype)
+                wl.dtype, shared_routing=args.shared_routing)
     stream = torch.cuda.current_stream()
 
     def step(i):
@@ -226,7 +230,7 @@ def main(argv=None) -> int:
     pool_ms = sum(t[0] for t in times) / len(times)
     route_ms = sum(t[1] for t in times) / len(times)
     attn_ms = sum(t[2] for t in times) / len(times)
-    ab = algorithmic_bytes(wl)
+    ab = algorithmic_bytes(wl, args.shared_routing)
     achieved = ab["attend"] / (attn_ms * 1e-3) / 1e9
     traffic = stored_traffic(wl.name)
     line = {
@@ -247,6 +251,7 @@ def main(argv=None) -> int:
             "batch": wl.batch, "height": wl.height, "width": wl.width,
             "channels": wl.channels, "num_heads": wl.num_heads, "n_win": wl.n_win,
             "topk": wl.topk, "buffer_sets": nsets,
+            "routing": "shared by all heads" if args.shared_routing else "per head",
             "kernel_ms": {"region_pool": pool_ms, "route": route_ms, "attend": attn_ms},
             "wall_s": wall,
         },
@@ -266,7 +271,8 @@ def main(argv=None) -> int:
         },
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(wl, host, sets[(args.steps - 1) % nsets]["out"].cpu())
+        line["cpu_baseline"] = cpu_baseline(wl, host, sets[(args.steps - 1) % nsets]["out"].cpu(),
+                                            shared=args.shared_routing)
     print(json.dumps(line), flush=True)
     return 0
 

@@ -16,7 +16,9 @@
  *      [P3 §1 region_partition; P4 §1.1].  Region r = i*n_win + j holds rows
  *      i*hs.. and columns j*ws..; its tokens are numbered row-major.
  *   2. Per head, Q and K are averaged over each region [P4 §1.2; P5 §五 ③].
- *   3. Per head, A[r][s] = Qbar_r . Kbar_s (the head_dim^-0.5 factor of
+ *   3. Per head (or, with shared_routing, once over all C channels in the
+ *      order c = h*head_dim + d, one routing for every head),
+ *      A[r][s] = Qbar_r . Kbar_s (the head_dim^-0.5 factor of
  *      [P5 §五 ③] does not change the order and is not applied) and each row
  *      keeps its k largest entries, in descending order, exact ties to the
  *      lower region id [P1 §2.1 TopkRouting; P5 §五 ④].  k = min(topk, R),
@@ -36,7 +38,7 @@
  *                  (head h, dim d) is h*head_dim + d; element type = dtype
  *   lepe_w         [C, 5, 5] fp32 (a PyTorch depthwise weight [C, 1, 5, 5])
  *   lepe_b         [C] fp32
- *   routing_idx    [B, heads, R, k] int32
+ *   routing_idx    [B, heads, R, k] int32 ([B, 1, R, k] with shared_routing)
  *
  * Errors: every call returns a bra_status_t; nothing throws or aborts across
  * the ABI.  bra_last_error() gives a thread-local message for the last
@@ -81,6 +83,10 @@ typedef struct {
     int32_t topk;      /* routed regions per region; <= 0 or > n_win^2 means all */
     bra_dtype_t dtype; /* element type of q, k, v and out */
     float scale;       /* attention logit scale; <= 0 means head_dim^-0.5 */
+    int32_t shared_routing; /* 0: routing per head (the default, [P5 §五 ③-④]);
+                               1: one routing per region shared by every head,
+                               from the region means over all C channels
+                               [P1 §2.2; P2 §2.1; P3 §2.1; P4 §1.2] */
 } bra_config_t;
 
 /* Validate cfg and allocate the handle and its device workspace on the

@@ -49,6 +49,7 @@ class BraConfig(ctypes.Structure):
         ("batch", ctypes.c_int32), ("height", ctypes.c_int32), ("width", ctypes.c_int32),
         ("channels", ctypes.c_int32), ("num_heads", ctypes.c_int32), ("n_win", ctypes.c_int32),
         ("topk", ctypes.c_int32), ("dtype", ctypes.c_int), ("scale", ctypes.c_float),
+        ("shared_routing", ctypes.c_int32),
     ]
 
 
@@ -202,10 +203,12 @@ class BRA:
     """
 
     def __init__(self, batch, height, width, channels, num_heads, n_win, topk, dtype="bf16",
-                 scale=0.0):
+                 scale=0.0, shared_routing=False):
         self.cfg = BraConfig(batch, height, width, channels, num_heads, n_win, topk,
-                             BRA_BF16 if dtype == "bf16" else BRA_F32, scale)
+                             BRA_BF16 if dtype == "bf16" else BRA_F32, scale,
+                             1 if shared_routing else 0)
         self.dtype = dtype
+        self.route_heads = 1 if shared_routing else num_heads
         self.handle = bra_create(self.cfg)
         self.k = bra_topk_effective(self.handle)
 
@@ -224,7 +227,7 @@ class BRA:
         if out is None:
             out = torch.empty_like(q)
         if routing_idx is True:
-            routing_idx = torch.empty((c.batch, c.num_heads, c.n_win * c.n_win, self.k),
+            routing_idx = torch.empty((c.batch, self.route_heads, c.n_win * c.n_win, self.k),
                                       dtype=torch.int32, device=q.device)
         elif routing_idx is False:
             routing_idx = None
@@ -233,7 +236,8 @@ class BRA:
 
     def forward_routed(self, q, k, v, routing_idx, lepe_w=None, lepe_b=None, out=None,
                        stream=None):
-        """Attention + LePE over the regions `routing_idx` ([B, heads, R, k] int32) names."""
+        """Attention + LePE over the regions `routing_idx` ([B, heads, R, k] int32, or
+        [B, 1, R, k] with shared routing) names."""
         import torch
         c = self.cfg
         want = torch.bfloat16 if self.dtype == "bf16" else torch.float32
@@ -241,7 +245,7 @@ class BRA:
         for name, t in (("q", q), ("k", k), ("v", v)):
             if t.dtype != want or tuple(t.shape) != shape or not t.is_contiguous() or not t.is_cuda:
                 raise ValueError(f"{name}: expected a contiguous {want} CUDA tensor {shape}")
-        rshape = (c.batch, c.num_heads, c.n_win * c.n_win, self.k)
+        rshape = (c.batch, self.route_heads, c.n_win * c.n_win, self.k)
         if (routing_idx.dtype != torch.int32 or tuple(routing_idx.shape) != rshape or
                 not routing_idx.is_contiguous() or not routing_idx.is_cuda):
             raise ValueError(f"routing_idx: expected a contiguous int32 CUDA tensor {rshape}")

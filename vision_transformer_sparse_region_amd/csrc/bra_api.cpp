@@ -118,8 +118,10 @@ bra_status_t bra_create(const bra_config_t* cfg, bra_handle_t* out) {
     const float scale = c.scale > 0.f ? c.scale : 1.0f / std::sqrt(static_cast<float>(bra::kHeadDim));
     const bool bf16 = c.dtype == BRA_BF16;
     bra::Params p;
+    if (c.shared_routing != 0 && c.shared_routing != 1)
+        return fail(BRA_ERR_SHAPE, "bra_create: shared_routing must be 0 or 1");
     if (!bra::plan(p, c.batch, c.height, c.width, c.channels, c.num_heads, c.n_win, k, scale,
-                   bf16))
+                   bf16, c.shared_routing == 1))
         return fail(BRA_ERR_UNSUPPORTED,
                     "bra_create: a region (with its LePE halo) or the channel count is too large "
                     "for the on-chip tiles (" + std::to_string(p.lds_bytes) + " bytes of LDS)");
@@ -135,7 +137,7 @@ bra_status_t bra_create(const bra_config_t* cfg, bra_handle_t* out) {
     h->device = dev;
     const size_t mean_bytes = 2 * static_cast<size_t>(c.batch) * c.channels * R * sizeof(double);
     const size_t route_bytes =
-        ((static_cast<size_t>(c.batch) * c.num_heads * R * k * sizeof(int32_t)) + 15) & ~size_t{15};
+        ((static_cast<size_t>(c.batch) * p.rheads * R * k * sizeof(int32_t)) + 15) & ~size_t{15};
     const size_t table_bytes = static_cast<size_t>(p.table_items) * sizeof(uint2);
     const size_t zero_bytes = static_cast<size_t>(c.channels) * sizeof(float);
     h->means_bytes = mean_bytes + route_bytes + table_bytes + zero_bytes;

@@ -627,7 +627,9 @@ attend_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restr
         // past heads * k re-read the last one
         const int i = min(tid, nhk - 1);
         const int h = i / p.k, j = i - h * p.k;
-        ridx = routing[((static_cast<size_t>(b) * p.heads + h) * p.R + r) * p.k + j];
+        ridx = routing[((static_cast<size_t>(b) * p.rheads + (p.shared ? 0 : h)) * p.R + r) *
+                           p.k +
+                       j];
     }
     // (with in-kernel routing the LePE operands load after it: the K means
     // hold 64 registers until then)
@@ -676,7 +678,11 @@ attend_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restr
         sOff[min(tid, nhk - 1)] = region_base(p, min(max(ridx, 0), p.R - 1));
         for (int i = tid + kThreads; i < nhk; i += kThreads) {
             const int h = i / p.k, j = i - h * p.k;
-            const int x = routing[((static_cast<size_t>(b) * p.heads + h) * p.R + r) * p.k + j];
+            const int x = routing[((static_cast<size_t>(b) * p.rheads + (p.shared ? 0 : h)) *
+                                       p.R +
+                                   r) *
+                                      p.k +
+                                  j];
             sOff[i] = region_base(p, min(max(x, 0), p.R - 1));
         }
     }
@@ -808,7 +814,7 @@ attend_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restr
 static long align16(long x) { return (x + 15) & ~15L; }
 
 bool plan(Params& p, int B, int H, int W, int C, int heads, int n_win, int k, float scale,
-          bool bf16) {
+          bool bf16, bool shared) {
     p.B = B;
     p.H = H;
     p.W = W;
@@ -820,6 +826,8 @@ bool plan(Params& p, int B, int H, int W, int C, int heads, int n_win, int k, fl
     p.ws = W / n_win;
     p.t = p.hs * p.ws;
     p.k = k;
+    p.shared = shared ? 1 : 0;
+    p.rheads = shared ? 1 : heads;
     p.nkeys = k * p.t;
     p.scale_log2e = scale * 1.4426950408889634f;
     p.has_lepe = 0;

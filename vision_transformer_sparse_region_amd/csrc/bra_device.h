@@ -185,6 +185,14 @@ __device__ __forceinline__ double dot32_seq(const double* a, const double* b) {
     for (int d = 0; d < kHeadDim; ++d) s = s + a[d] * b[d];
     return s;
 }
+// The same 32 terms appended to a running sum s0 (a longer sequential dot).
+__device__ __forceinline__ double dot32_seq_from(double s0, const double* a, const double* b) {
+#pragma clang fp contract(off)
+    double s = s0;
+#pragma unroll
+    for (int d = 0; d < kHeadDim; ++d) s = s + a[d] * b[d];
+    return s;
+}
 
 // LePE on the 4x4x4 MFMA applies to windows whose sides are multiples of 4
 // when the per-wave accumulators (tiles x channel groups) stay small.

@@ -26,6 +26,8 @@ struct Params {
     int n, R;        // regions per side, regions per map
     int hs, ws, t;   // region height, width, tokens per region
     int k;           // routed regions per region (already clamped)
+    int shared;      // 1: one routing per region for every head (full-C affinity)
+    int rheads;      // heads of the routing buffer: 1 when shared, else heads
     int nkeys;       // k * t keys per query
     float scale_log2e;
     int has_lepe;
@@ -45,13 +47,13 @@ struct Params {
 
 // Fills the geometry and layout; returns false when a tile does not fit.
 bool plan(Params& p, int B, int H, int W, int C, int heads, int n_win, int k, float scale,
-          bool bf16);
+          bool bf16, bool shared);
 
 // Kernel launches on `stream`; return the launch status.
 //   means: fp64 region means, Q as [B][heads][R][32], then K as [B][heads][32][R].
 //   lepe_table: p.table_items 8-byte entries (written by the pool kernel when
 //   lepe_w is given and the shape runs LePE on MFMA).
-//   routing: [B][heads][R][k] int32 region ids.
+//   routing: [B][rheads][R][k] int32 region ids.
 hipError_t launch_pool_qk(const Params& p, bool bf16, const void* q, const void* k,
                           const float* lepe_w, double* means, uint2* lepe_table,
                           hipStream_t stream);
@@ -63,7 +65,7 @@ hipError_t launch_route(const Params& p, bool bf16, const double* means, int32_t
 constexpr bool route_fused(int R, int heads) {
     return R <= 64 && heads <= kWaves;
 }
-inline bool route_in_attend(const Params& p) { return route_fused(p.R, p.heads); }
+inline bool route_in_attend(const Params& p) { return !p.shared && route_fused(p.R, p.heads); }
 
 //   use_routing: read the routing from `routing` (written by the routing
 //   kernel or given by the caller); otherwise route in the kernel (needs

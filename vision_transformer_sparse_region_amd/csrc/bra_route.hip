@@ -1,10 +1,12 @@
 // bra_route.hip -- region-level routing [P4 §1.2; P1 §2.1 TopkRouting;
 // P5 §五 ③-④] (page keys in bra_device.h).
 //
-// One workgroup per (image, head, chunk of query regions): the fp64 affinity
+// One workgroup per (image, head, chunk of query regions) -- per image with
+// head-shared routing [P1 §2.2; P2 §2.1; P3 §2.1] -- : the fp64 affinity
 // A[r][s] = Qbar_r . Kbar_s of each row r of the chunk against every region
-// s, then the k largest entries of each row, in descending order with exact
-// ties to the lower region id.  The head_dim^-0.5 factor the pages apply to
+// s (over one head's 32 dims, or all C channels when shared), then the k
+// largest entries of each row, in descending order with exact ties to the
+// lower region id.  The head_dim^-0.5 factor the pages apply to
 // the affinity does not change the order and is left out.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -124,33 +126,43 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
     const int R = p.R, RS = route_row_stride(R);
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int nchunk = (R + ROWS - 1) / ROWS;
-    const int bh = blockIdx.x / nchunk, chunk = blockIdx.x - bh * nchunk;
+    // rg: the routing's (image, head) pair, or the image with shared routing
+    const int rg = blockIdx.x / nchunk, chunk = blockIdx.x - rg * nchunk;
     const int r0 = chunk * ROWS, nrows = min(ROWS, R - r0);
-    const double* qbar = means + qmean_index(p, bh, 0, 0);  // [R][32]
+    const int h0 = p.shared ? rg * p.heads : rg;          // first (image, head) summed
+    const int nh = p.shared ? p.heads : 1;                // heads summed into one affinity
 
     // Affinity.  Thread (s, g) keeps K mean s in registers and takes its dot
-    // with query rows g, g + G, ...; rows past the chunk read zeros.
+    // with query rows g, g + G, ...; rows past the chunk read zeros.  With
+    // shared routing the heads follow one another in one running sum per
+    // entry (kept in sA), so every entry is the sequential sum over all C
+    // channels in the order c = h * 32 + d.
     const int s = tid % SPAN, g = tid / SPAN;
-    double kreg[kHeadDim];
-    load_kmean(p, means, bh, min(s, R - 1), kreg);
-    for (int i = tid; i < ROWS * kHeadDim / 2; i += kThreads) {
-        const bool in = i < nrows * kHeadDim / 2;
-        reinterpret_cast<double2*>(sQ)[i] =
-            in ? reinterpret_cast<const double2*>(qbar + r0 * kHeadDim)[i] : double2{0.0, 0.0};
-    }
-    __syncthreads();
-    {
+    for (int hh = 0; hh < nh; ++hh) {
+        const int bh = h0 + hh;
+        const double* qbar = means + qmean_index(p, bh, 0, 0);  // [R][32]
+        double kreg[kHeadDim];
+        load_kmean(p, means, bh, min(s, R - 1), kreg);
+        for (int i = tid; i < ROWS * kHeadDim / 2; i += kThreads) {
+            const bool in = i < nrows * kHeadDim / 2;
+            reinterpret_cast<double2*>(sQ)[i] =
+                in ? reinterpret_cast<const double2*>(qbar + r0 * kHeadDim)[i]
+                   : double2{0.0, 0.0};
+        }
+        __syncthreads();
 #pragma unroll 1
         for (int j = 0; j < NR; ++j) {
             const int row = g + G * j;
-            const double a = dot32_seq(sQ + row * kHeadDim, kreg);
-            if (s < R && row < nrows) sA[row * RS + s] = a;
+            if (s < R && row < nrows) {
+                const double a0 = hh == 0 ? 0.0 : sA[row * RS + s];
+                sA[row * RS + s] = dot32_seq_from(a0, sQ + row * kHeadDim, kreg);
+            }
         }
+        __syncthreads();
     }
-    __syncthreads();
 
     // Top-k, rows w, w + 4, ... of the chunk on wave w.
-    int32_t* const base = idx_out + (static_cast<size_t>(bh) * R + r0) * p.k;
+    int32_t* const base = idx_out + (static_cast<size_t>(rg) * R + r0) * p.k;
     if (p.k == 1) {
         double best[RPW];
         int bs[RPW];
@@ -220,7 +232,7 @@ hipError_t launch_route(const Params& p, bool bf16, const double* means, int32_t
     const int span = route_span(p.R);
     const int rows = kWaves * route_rows_per_wave(span);
     const int nchunk = (p.R + rows - 1) / rows;
-    const dim3 grid(p.B * p.heads * nchunk), block(kThreads);
+    const dim3 grid(p.B * p.rheads * nchunk), block(kThreads);
     const int lds = rows * route_row_stride(p.R) * 8;
 #define BRA_ROUTE(T, HS, WS, NW, HEADS, KTOP)                                                \
     if (matches(Inst<T, HS, WS, NW, HEADS, KTOP>::key, p, bf16, true)) {                    \
