@@ -114,10 +114,14 @@ class OracleLib:
                                            _DP]
         lib.oracle_route_shared.argtypes = [cp, _DP, _DP, _DP, _IP]
         lib.oracle_bra_forward_shared.argtypes = [cp, _DP, _DP, _DP, _DP, _DP, _DP, _IP, _DP]
+        lib.oracle_kv_downsample.argtypes = [cp, ctypes.c_int, _DP, _DP]
+        lib.oracle_bra_forward_kvds.argtypes = [cp, ctypes.c_int, _DP, _DP, _DP, _DP, _DP, _DP,
+                                                _IP]
         lib.oracle_num_threads.argtypes = []
         for name in ("oracle_region_means", "oracle_route", "oracle_attend", "oracle_lepe",
                      "oracle_attend_with_routing", "oracle_bra_forward", "oracle_route_shared",
-                     "oracle_bra_forward_shared", "oracle_num_threads"):
+                     "oracle_bra_forward_shared", "oracle_kv_downsample",
+                     "oracle_bra_forward_kvds", "oracle_num_threads"):
             getattr(lib, name).restype = ctypes.c_int
         self.lib = lib
         self.path = path
@@ -182,6 +186,31 @@ class OracleLib:
         if want_aff:
             res["aff"] = aff
         return res
+
+    def kv_downsample(self, cfg: OracleConfig, ratio: int, x) -> np.ndarray:
+        c = cfg._c()
+        xa, xp = _f64(x)
+        out = np.empty((cfg.batch, cfg.height // ratio, cfg.width // ratio, cfg.channels),
+                       np.float64)
+        _check(self.lib.oracle_kv_downsample(ctypes.byref(c), ratio, xp, _ptr(out)),
+               "kv_downsample")
+        return out
+
+    def bra_forward_kvds(self, cfg: OracleConfig, ratio: int, q, k, v, w=None, b=None):
+        """Whole forward with KV downsampling: dict with 'out' and 'idx'."""
+        c = cfg._c()
+        qa, qp = _f64(q)
+        ka, kp = _f64(k)
+        va, vp = _f64(v)
+        wa, wp = _f64(w)
+        ba, bp = _f64(b)
+        kk = self.topk_effective(cfg)
+        out = np.empty(_map_shape(cfg), np.float64)
+        idx = np.empty((cfg.batch, cfg.num_heads, cfg.regions, kk), np.int32)
+        _check(self.lib.oracle_bra_forward_kvds(ctypes.byref(c), ratio, qp, kp, vp, wp, bp,
+                                                _ptr(out), idx.ctypes.data_as(_IP)),
+               "bra_forward_kvds")
+        return {"out": out, "idx": idx}
 
     def attend(self, cfg: OracleConfig, q, k, v, idx) -> np.ndarray:
         c = cfg._c()
@@ -293,3 +322,11 @@ def route_shared(cfg, qbar, kbar, want_aff=False):
 
 def bra_forward_shared(cfg, q, k, v, w=None, b=None, *, want_aff=False):
     return default().bra_forward_shared(cfg, q, k, v, w, b, want_aff=want_aff)
+
+
+def kv_downsample(cfg, ratio, x):
+    return default().kv_downsample(cfg, ratio, x)
+
+
+def bra_forward_kvds(cfg, ratio, q, k, v, w=None, b=None):
+    return default().bra_forward_kvds(cfg, ratio, q, k, v, w, b)

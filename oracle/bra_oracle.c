@@ -173,12 +173,16 @@ int oracle_route_shared(const oracle_cfg_t* c, const double* qbar, const double*
 
 /* ---- step 5: token attention over the routed windows -------------------- */
 
-int oracle_attend(const oracle_cfg_t* c, const double* q, const double* kk,
-                  const double* v, const int32_t* idx, double* o) {
-    if (!cfg_ok(c) || !q || !kk || !v || !idx || !o) return -1;
+/* Attention of the queries of map `c` over keys and values of map `ckv`:
+ * the same map, or its K/V downsampled (same batch, channels, heads and
+ * region grid, smaller windows). */
+static int attend_impl(const oracle_cfg_t* c, const oracle_cfg_t* ckv, const double* q,
+                       const double* kk, const double* v, const int32_t* idx, double* o) {
+    if (!cfg_ok(c) || !cfg_ok(ckv) || !q || !kk || !v || !idx || !o) return -1;
     const int hd = c->channels / c->num_heads;
     const int R = c->n_win * c->n_win;
-    const int t = (c->height / c->n_win) * (c->width / c->n_win);
+    const int tq = (c->height / c->n_win) * (c->width / c->n_win);
+    const int t = (ckv->height / ckv->n_win) * (ckv->width / ckv->n_win);
     const int k = oracle_topk_effective(c);
     const int nkeys = k * t;
     const double scale = c->scale > 0.0 ? c->scale : 1.0 / sqrt((double)hd);
@@ -198,10 +202,10 @@ int oracle_attend(const oracle_cfg_t* c, const double* q, const double* kk,
             for (int j = 0; j < k; ++j)
                 for (int slot = 0; slot < t; ++slot) {
                     int y, x;
-                    region_slot_yx(c, routed[j], slot, &y, &x);
-                    key_at[j * t + slot] = at(c, b, y, x, h * hd);
+                    region_slot_yx(ckv, routed[j], slot, &y, &x);
+                    key_at[j * t + slot] = at(ckv, b, y, x, h * hd);
                 }
-            for (int qslot = 0; qslot < t; ++qslot) {
+            for (int qslot = 0; qslot < tq; ++qslot) {
                 int qy, qx;
                 region_slot_yx(c, r, qslot, &qy, &qx);
                 const double* qv = q + at(c, b, qy, qx, h * hd);
@@ -230,6 +234,82 @@ int oracle_attend(const oracle_cfg_t* c, const double* q, const double* kk,
         free(acc);
     }
     return 0;
+}
+
+int oracle_attend(const oracle_cfg_t* c, const double* q, const double* kk,
+                  const double* v, const int32_t* idx, double* o) {
+    return attend_impl(c, c, q, kk, v, idx, o);
+}
+
+/* The map of K/V after a ratio x ratio average pool (same everything else). */
+static oracle_cfg_t kv_cfg(const oracle_cfg_t* c, int ratio) {
+    oracle_cfg_t d = *c;
+    d.height = c->height / ratio;
+    d.width = c->width / ratio;
+    return d;
+}
+
+static int ratio_ok(const oracle_cfg_t* c, int ratio) {
+    return cfg_ok(c) && ratio >= 1 && (c->height / c->n_win) % ratio == 0 &&
+           (c->width / c->n_win) % ratio == 0;
+}
+
+int oracle_kv_downsample(const oracle_cfg_t* c, int ratio, const double* x, double* xd) {
+    if (!ratio_ok(c, ratio) || !x || !xd) return -1;
+    const oracle_cfg_t d = kv_cfg(c, ratio);
+    const int n = c->batch * d.height * d.width;
+#pragma omp parallel for schedule(static)
+    for (int cell = 0; cell < n; ++cell) {
+        const int b = cell / (d.height * d.width);
+        const int yd = (cell / d.width) % d.height, xq = cell % d.width;
+        for (int ch = 0; ch < c->channels; ++ch) {
+            /* the ratio x ratio block, row-major, one plain sum, then / ratio^2 */
+            double s = 0.0;
+            for (int u = 0; u < ratio; ++u)
+                for (int w = 0; w < ratio; ++w)
+                    s += x[at(c, b, yd * ratio + u, xq * ratio + w, ch)];
+            xd[at(&d, b, yd, xq, ch)] = s / (double)(ratio * ratio);
+        }
+    }
+    return 0;
+}
+
+int oracle_bra_forward_kvds(const oracle_cfg_t* c, int ratio, const double* q,
+                            const double* k, const double* v, const double* w,
+                            const double* bias, double* out, int32_t* idx) {
+    if (!ratio_ok(c, ratio) || !q || !k || !v || !out || !idx) return -1;
+    const int hd = c->channels / c->num_heads;
+    const size_t nbar = (size_t)c->batch * c->num_heads * c->n_win * c->n_win * hd;
+    const oracle_cfg_t d = kv_cfg(c, ratio);
+    const size_t nd = (size_t)c->batch * d.height * d.width * c->channels;
+    double* qb = (double*)malloc(sizeof(double) * nbar);
+    double* kb = (double*)malloc(sizeof(double) * nbar);
+    double* kd = (double*)malloc(sizeof(double) * nd);
+    double* vd = (double*)malloc(sizeof(double) * nd);
+    double* L = w ? (double*)malloc(sizeof(double) * (size_t)c->batch * c->height * c->width *
+                                    c->channels)
+                  : NULL;
+    int rc = -1;
+    /* routing on the full-resolution region means; attention over the
+     * downsampled keys and values; LePE on the full-resolution V */
+    if (qb && kb && kd && vd && (!w || L) && oracle_region_means(c, q, qb) == 0 &&
+        oracle_region_means(c, k, kb) == 0 && oracle_route(c, qb, kb, NULL, idx) == 0 &&
+        oracle_kv_downsample(c, ratio, k, kd) == 0 &&
+        oracle_kv_downsample(c, ratio, v, vd) == 0 &&
+        attend_impl(c, &d, q, kd, vd, idx, out) == 0 &&
+        (!w || oracle_lepe(c, v, w, bias, L) == 0)) {
+        if (w) {
+            const size_t n = (size_t)c->batch * c->height * c->width * c->channels;
+            for (size_t i = 0; i < n; ++i) out[i] += L[i];
+        }
+        rc = 0;
+    }
+    free(qb);
+    free(kb);
+    free(kd);
+    free(vd);
+    free(L);
+    return rc;
 }
 
 /* ---- step 6: LePE -------------------------------------------------------- */

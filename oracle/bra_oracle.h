@@ -104,6 +104,21 @@ int oracle_bra_forward_shared(const oracle_cfg_t* cfg, const double* q, const do
                               const double* v, const double* lepe_w, const double* lepe_b,
                               double* out, int32_t* idx, double* aff);
 
+/* KV downsampling [P1 §4.1 kv_downsample_ratio, avgpool; §3.1]: K or V
+ * averaged over ratio x ratio blocks (row-major block, one plain sum, divided
+ * by ratio^2), x [B,H,W,C] -> xd [B,H/ratio,W/ratio,C].  The ratio must
+ * divide the window sides.  -1 on a bad configuration or ratio. */
+int oracle_kv_downsample(const oracle_cfg_t* cfg, int ratio, const double* x, double* xd);
+
+/* Whole forward with KV downsampling: routing on the full-resolution region
+ * means (as oracle_bra_forward), attention of every query over the
+ * downsampled K/V tokens of its routed regions ((hs/ratio)*(ws/ratio) per
+ * region, in window row-major order), + LePE of the full-resolution V.
+ * idx: [B, heads, R, k_eff]. */
+int oracle_bra_forward_kvds(const oracle_cfg_t* cfg, int ratio, const double* q,
+                            const double* k, const double* v, const double* lepe_w,
+                            const double* lepe_b, double* out, int32_t* idx);
+
 /* Number of OpenMP threads a parallel region of the oracle uses. */
 int oracle_num_threads(void);
 

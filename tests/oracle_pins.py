@@ -432,6 +432,87 @@ def pin_shared_matches_torch_recipe(orc):
         np.testing.assert_allclose(res["out"], ref_out, rtol=RTOL, atol=ATOL)
 
 
+# ---- KV downsampling [P1 §4.1 kv_downsample_ratio, avgpool] ----------------
+
+def torch_avg_pool(x, ratio):
+    """[B,H,W,C] average-pooled over ratio x ratio blocks (library avg_pool2d)."""
+    xt = torch.from_numpy(np.ascontiguousarray(x)).permute(0, 3, 1, 2)
+    return torch.nn.functional.avg_pool2d(xt, ratio).permute(0, 2, 3, 1).numpy()
+
+
+def pin_kv_downsample_matches_avg_pool(orc):
+    """The downsampled K/V equal the library's average pooling."""
+    cfg = OracleConfig(2, 16, 8, 6, 2, 2, 1)
+    rng = _rng(109)
+    x = _rand_map(rng, cfg)
+    for ratio in (1, 2, 4):
+        np.testing.assert_allclose(orc.kv_downsample(cfg, ratio, x), torch_avg_pool(x, ratio),
+                                   rtol=1e-13, atol=1e-15)
+    # a ratio that does not divide the window sides is refused
+    try:
+        orc.kv_downsample(cfg, 3, x)
+    except ValueError:
+        pass
+    else:
+        raise AssertionError("ratio 3 accepted for 8x4 windows")
+
+
+def pin_kvds_ratio_one_is_plain(orc):
+    """Ratio 1 is the plain forward, bit for bit."""
+    cfg = OracleConfig(2, 8, 8, 16, 2, 2, 2)
+    rng = _rng(113)
+    q, k, v = (_rand_map(rng, cfg) for _ in range(3))
+    w, b = _rand_lepe(rng, cfg)
+    a = orc.bra_forward(cfg, q, k, v, w, b)
+    d = orc.bra_forward_kvds(cfg, 1, q, k, v, w, b)
+    assert (a["idx"] == d["idx"]).all()
+    np.testing.assert_array_equal(a["out"], d["out"])
+
+
+def pin_kvds_all_regions_is_dense_over_pooled(orc):
+    """Every region routed: each query attends to the whole downsampled map --
+    dense attention (library SDPA) over avg-pooled K and V -- plus the LePE of
+    the full-resolution V."""
+    cfg = OracleConfig(2, 8, 8, 16, 2, 2, 4)
+    rng = _rng(127)
+    q, k, v = (_rand_map(rng, cfg) for _ in range(3))
+    w, b = _rand_lepe(rng, cfg)
+    for ratio in (2, 4):
+        kd, vd = torch_avg_pool(k, ratio), torch_avg_pool(v, ratio)
+        B, H, W, C = q.shape
+        hd = C // 2
+
+        def heads(x):
+            n = x.shape[1] * x.shape[2]
+            return torch.from_numpy(np.ascontiguousarray(x)).reshape(B, n, 2, hd).permute(0, 2, 1, 3)
+
+        o = torch.nn.functional.scaled_dot_product_attention(heads(q), heads(kd), heads(vd))
+        o = o.permute(0, 2, 1, 3).reshape(B, H, W, C).numpy()
+        res = orc.bra_forward_kvds(cfg, ratio, q, k, v, w, b)
+        np.testing.assert_allclose(res["out"], o + torch_lepe(v, w, b), rtol=RTOL, atol=ATOL)
+
+
+def pin_kvds_window_ratio_attends_region_means(orc):
+    """Ratio = window side: every routed region contributes one key and one
+    value, its mean, so each query's softmax runs over the k routed region
+    means of K (weights) and V (values) -- written out with numpy."""
+    cfg = OracleConfig(1, 8, 8, 4, 1, 2, 3)
+    rng = _rng(131)
+    q, k, v = (_rand_map(rng, cfg) for _ in range(3))
+    res = orc.bra_forward_kvds(cfg, 4, q, k, v)
+    kb, vb = np_windows(k, 2).mean(axis=2)[0], np_windows(v, 2).mean(axis=2)[0]  # [R, C]
+    qw = np_windows(q, 2)[0]  # [R, t, C]
+    idx = res["idx"][0, 0]  # [R, k]
+    out = np.empty_like(qw)
+    for r in range(4):
+        logits = qw[r] @ kb[idx[r]].T * 4 ** -0.5  # [t, k]
+        p = np.exp(logits - logits.max(axis=1, keepdims=True))
+        out[r] = (p @ vb[idx[r]]) / p.sum(axis=1, keepdims=True)
+    np.testing.assert_allclose(res["out"], np_unwindows(out[None], 2, 8, 8), rtol=RTOL,
+                               atol=ATOL)
+    assert (res["idx"] == orc.bra_forward(cfg, q, k, v)["idx"]).all()
+
+
 ALL_PINS = [
     pin_topk_all_is_dense_attention,
     pin_one_region_is_dense_attention,
@@ -453,4 +534,8 @@ ALL_PINS = [
     pin_shared_routing_sums_head_affinities,
     pin_shared_ties_go_to_lower_region,
     pin_shared_matches_torch_recipe,
+    pin_kv_downsample_matches_avg_pool,
+    pin_kvds_ratio_one_is_plain,
+    pin_kvds_all_regions_is_dense_over_pooled,
+    pin_kvds_window_ratio_attends_region_means,
 ]

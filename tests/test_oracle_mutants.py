@@ -26,8 +26,8 @@ MUTANTS = [
     ("no_softmax_scale", "logit[m] = scale * dot;", "logit[m] = dot; (void)scale;"),
     ("mean_not_divided", "xbar[(size_t)item * hd + d] = s / (double)t;",
      "xbar[(size_t)item * hd + d] = s;"),
-    ("keys_from_head0", "key_at[j * t + slot] = at(c, b, y, x, h * hd);",
-     "key_at[j * t + slot] = at(c, b, y, x, 0);"),
+    ("keys_from_head0", "key_at[j * t + slot] = at(ckv, b, y, x, h * hd);",
+     "key_at[j * t + slot] = at(ckv, b, y, x, 0);"),
     ("no_normalisation", "ov[d] = acc[d] / denom;", "ov[d] = acc[d]; (void)denom;"),
     ("affinity_short_dot", "for (int d = 0; d < hd; ++d) a += qr[d] * ks[d];",
      "for (int d = 0; d < hd - 1; ++d) a += qr[d] * ks[d];"),
@@ -35,6 +35,12 @@ MUTANTS = [
      "const double* ks = qbar + ((size_t)bh * R + s) * hd; (void)kbar;"),
     ("k_from_q_region_means", "oracle_region_means(c, k, kb) == 0 &&\n        oracle_route(",
      "oracle_region_means(c, q, kb) == 0 &&\n        oracle_route("),
+    ("kv_pool_first_only", "s += x[at(c, b, yd * ratio + u, xq * ratio + w, ch)];",
+     "s += (u | w) ? 0.0 : x[at(c, b, yd * ratio, xq * ratio, ch)] * (ratio * ratio);"),
+    ("kv_pool_not_divided", "xd[at(&d, b, yd, xq, ch)] = s / (double)(ratio * ratio);",
+     "xd[at(&d, b, yd, xq, ch)] = s;"),
+    ("kvds_without_lepe", "for (size_t i = 0; i < n; ++i) out[i] += L[i];",
+     "(void)n; (void)L;"),
     ("shared_head0_only", "for (int h = 0; h < H; ++h) {\n                    const double* qh",
      "for (int h = 0; h < 1; ++h) {\n                    const double* qh"),
     ("shared_routing_per_head0",
