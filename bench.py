@@ -43,7 +43,7 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def algorithmic_bytes(wl, shared_routing: bool = False) -> dict:
+def algorithmic_bytes(wl, shared_routing: bool = False, kv_ratio: int = 1) -> dict:
     """Bytes each kernel must move once per launch (unique bytes; the k-fold
     re-reads of routed K/V, of the LePE halo and of the K means are cache
     traffic).  Maps of at most 64 regions with at most 4 heads are routed
@@ -55,21 +55,25 @@ def algorithmic_bytes(wl, shared_routing: bool = False) -> dict:
     idx = wl.batch * (1 if shared_routing else wl.num_heads) * wl.regions * \
         wl.topk_effective * 4
     lepe = wl.channels * 26 * 4
+    r2 = max(kv_ratio, 1) ** 2
+    # with KV downsampling a pooling pass reads k and v and writes 2S/r^2; the
+    # attention then gathers the pooled K/V (2S/r^2) and still reads v for LePE
+    kvpool = 2 * S + 2 * S // r2 if r2 > 1 else 0
+    attend = (3 * S + 2 * S // r2 if r2 > 1 else 4 * S) + idx + lepe
     if wl.regions <= 64 and wl.num_heads <= 4 and not shared_routing:
         # routed inside the attention kernel: it reads the means, writes the ids
-        return {"pool": 2 * S + 2 * M, "route": 0, "attend": 4 * S + 2 * M + idx + lepe,
-                "S": S}
+        return {"pool": 2 * S + 2 * M + kvpool, "route": 0, "attend": attend + 2 * M, "S": S}
     return {
-        "pool": 2 * S + 2 * M,                           # read q, k; write both means
+        "pool": 2 * S + 2 * M + kvpool,                  # read q, k; write both means
         "route": 2 * M + idx,                            # read both means; write the ids
-        "attend": 4 * S + idx + lepe,                    # read q, k, v, ids, w; write out
+        "attend": attend,                                # read q, k, v, ids, w; write out
         "S": S,
     }
 
 
-def attention_flops(wl) -> float:
-    return 4.0 * wl.tokens * wl.num_heads * wl.topk_effective * wl.tokens_per_region * \
-        wl.head_dim
+def attention_flops(wl, kv_ratio: int = 1) -> float:
+    return 4.0 * wl.tokens * wl.num_heads * wl.topk_effective * \
+        (wl.tokens_per_region // max(kv_ratio, 1) ** 2) * wl.head_dim
 
 
 def traffic_summary_path(workload: str) -> str:
@@ -96,7 +100,8 @@ def stored_traffic(workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(wl, inputs, gpu_out, target_s: float = 10.0, shared: bool = False) -> dict:
+def cpu_baseline(wl, inputs, gpu_out, target_s: float = 10.0, shared: bool = False,
+                 kv_ratio: int = 1) -> dict:
     """Time the CPU oracle on the first images of the same batch (a bounded
     sample) and check the GPU output for those images against it."""
     import numpy as np
@@ -109,8 +114,17 @@ def cpu_baseline(wl, inputs, gpu_out, target_s: float = 10.0, shared: bool = Fal
         f = {n: inputs[n][:nimg].double().numpy() for n in ("q", "k", "v")}
         w, b = inputs["lepe_w"].double().numpy(), inputs["lepe_b"].double().numpy()
         t0 = time.perf_counter()
-        fwd = oracle.bra_forward_shared if shared else oracle.bra_forward
-        res = fwd(cfg, f["q"], f["k"], f["v"], w, b)
+        if shared and kv_ratio > 1:
+            idx = oracle.bra_forward_shared(cfg, f["q"], f["k"], f["v"])["idx"]
+            full = np.ascontiguousarray(np.repeat(idx[:, None], wl.num_heads, axis=1))
+            res = {"out": oracle.attend_kvds(cfg, kv_ratio, f["q"], f["k"], f["v"], full) +
+                   oracle.lepe(cfg, f["v"], w, b)}
+        elif kv_ratio > 1:
+            res = oracle.bra_forward_kvds(cfg, kv_ratio, f["q"], f["k"], f["v"], w, b)
+        elif shared:
+            res = oracle.bra_forward_shared(cfg, f["q"], f["k"], f["v"], w, b)
+        else:
+            res = oracle.bra_forward(cfg, f["q"], f["k"], f["v"], w, b)
         return time.perf_counter() - t0, res
 
     dt, res = run(1)
@@ -162,6 +176,8 @@ def main(argv=None) -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--shared-routing", action="store_true",
                     help="one routing per region for every head (full-C region affinity)")
+    ap.add_argument("--kv-downsample", type=int, default=1,
+                    help="KV downsampling ratio r (attention over r x r average-pooled K/V)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help=f"also run a {COPY_BYTES >> 20} MiB device copy (for counter scaling)")
     args = ap.parse_args(argv)
@@ -190,7 +206,8 @@ def main(argv=None) -> int:
         sets.append(d)
 
     h = bra.BRA(wl.batch, wl.height, wl.width, wl.channels, wl.num_heads, wl.n_win, wl.topk,
-                wl.dtype, shared_routing=args.shared_routing)
+                wl.dtype, shared_routing=args.shared_routing,
+                kv_downsample_ratio=args.kv_downsample)
     stream = torch.cuda.current_stream()
 
     def step(i):
@@ -230,7 +247,7 @@ def main(argv=None) -> int:
     pool_ms = sum(t[0] for t in times) / len(times)
     route_ms = sum(t[1] for t in times) / len(times)
     attn_ms = sum(t[2] for t in times) / len(times)
-    ab = algorithmic_bytes(wl, args.shared_routing)
+    ab = algorithmic_bytes(wl, args.shared_routing, args.kv_downsample)
     achieved = ab["attend"] / (attn_ms * 1e-3) / 1e9
     traffic = stored_traffic(wl.name)
     line = {
@@ -252,6 +269,7 @@ def main(argv=None) -> int:
             "channels": wl.channels, "num_heads": wl.num_heads, "n_win": wl.n_win,
             "topk": wl.topk, "buffer_sets": nsets,
             "routing": "shared by all heads" if args.shared_routing else "per head",
+            "kv_downsample_ratio": args.kv_downsample,
             "kernel_ms": {"region_pool": pool_ms, "route": route_ms, "attend": attn_ms},
             "wall_s": wall,
         },
@@ -264,7 +282,7 @@ def main(argv=None) -> int:
             "frac": achieved / HBM_PEAK_GBS,
             "traffic": traffic,
             "algorithmic_bytes": ab["attend"],
-            "attention_tflops": attention_flops(wl) / (attn_ms * 1e-3) / 1e12,
+            "attention_tflops": attention_flops(wl, args.kv_downsample) / (attn_ms * 1e-3) / 1e12,
             "pool_frac_hbm": ab["pool"] / (pool_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "step_frac_hbm": (ab["pool"] + ab["route"] + ab["attend"]) / (ms_per_step * 1e-3) /
             1e9 / HBM_PEAK_GBS,
@@ -272,7 +290,8 @@ def main(argv=None) -> int:
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, host, sets[(args.steps - 1) % nsets]["out"].cpu(),
-                                            shared=args.shared_routing)
+                                            shared=args.shared_routing,
+                                            kv_ratio=args.kv_downsample)
     print(json.dumps(line), flush=True)
     return 0
 

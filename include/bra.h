@@ -25,6 +25,8 @@
  *      topk <= 0 meaning every region [P5 §五 ④; P2 §3.1].
  *   4. Every token of region r attends, per head, to the k*t tokens of its
  *      routed regions: softmax(scale * q K^T) V [P3 §2.2; P5 §五 ⑤-⑦].
+ *      With kv_downsample_ratio r > 1 the keys and values are those of K and
+ *      V average-pooled over r x r blocks (k*t/r^2 keys) [P1 §4.1].
  *   5. out = attention + LePE, LePE = depthwise 5x5 convolution of V with
  *      zero padding 2 over the whole map, plus a per-channel bias
  *      [P5 §五 self.lepe and ⑧; P2 §2.2].
@@ -63,7 +65,9 @@ typedef enum {
     BRA_OK = 0,
     BRA_ERR_NULL = 1,        /* a required pointer is NULL */
     BRA_ERR_SHAPE = 2,       /* sizes not positive, H or W not divisible by n_win,
-                                C not divisible by num_heads, or too large for int32 indexing */
+                                C not divisible by num_heads, too large for int32 indexing,
+                                shared_routing not 0/1, or kv_downsample_ratio not dividing
+                                the window sides */
     BRA_ERR_UNSUPPORTED = 3, /* head_dim != 32, unknown dtype, n_win > 16, H*W >= 2^23,
                                 or a region too large for the kernels' on-chip tiles */
     BRA_ERR_HIP = 4,         /* a HIP runtime call failed (see bra_last_error) */
@@ -87,12 +91,18 @@ typedef struct {
                                1: one routing per region shared by every head,
                                from the region means over all C channels
                                [P1 §2.2; P2 §2.1; P3 §2.1; P4 §1.2] */
+    int32_t kv_downsample_ratio; /* <= 1: none.  r > 1: the attention gathers K and V
+                               average-pooled over r x r blocks (windows of
+                               (H/n_win/r) x (W/n_win/r) tokens), routing and LePE
+                               stay at full resolution [P1 §4.1]; r must divide
+                               H/n_win and W/n_win */
 } bra_config_t;
 
 /* Validate cfg and allocate the handle and its device workspace on the
  * current HIP device: the fp64 region means of Q and K (2*B*C*R*8 bytes), a
- * routing buffer (B*heads*R*k*4 bytes) and, for window shapes whose LePE
- * runs on MFMA, a C*320-byte operand table.  On success *out is a live
+ * routing buffer (B*heads*R*k*4 bytes), for window shapes whose LePE runs on
+ * MFMA a C*320-byte operand table, and with KV downsampling the pooled K and
+ * V (2*B*H*W*C*sizeof(dtype)/r^2 bytes).  On success *out is a live
  * handle; on failure *out is left NULL. */
 bra_status_t bra_create(const bra_config_t* cfg, bra_handle_t* out);
 

@@ -117,11 +117,12 @@ class OracleLib:
         lib.oracle_kv_downsample.argtypes = [cp, ctypes.c_int, _DP, _DP]
         lib.oracle_bra_forward_kvds.argtypes = [cp, ctypes.c_int, _DP, _DP, _DP, _DP, _DP, _DP,
                                                 _IP]
+        lib.oracle_attend_kvds.argtypes = [cp, ctypes.c_int, _DP, _DP, _DP, _IP, _DP]
         lib.oracle_num_threads.argtypes = []
         for name in ("oracle_region_means", "oracle_route", "oracle_attend", "oracle_lepe",
                      "oracle_attend_with_routing", "oracle_bra_forward", "oracle_route_shared",
                      "oracle_bra_forward_shared", "oracle_kv_downsample",
-                     "oracle_bra_forward_kvds", "oracle_num_threads"):
+                     "oracle_bra_forward_kvds", "oracle_attend_kvds", "oracle_num_threads"):
             getattr(lib, name).restype = ctypes.c_int
         self.lib = lib
         self.path = path
@@ -194,6 +195,17 @@ class OracleLib:
                        np.float64)
         _check(self.lib.oracle_kv_downsample(ctypes.byref(c), ratio, xp, _ptr(out)),
                "kv_downsample")
+        return out
+
+    def attend_kvds(self, cfg: OracleConfig, ratio: int, q, k, v, idx) -> np.ndarray:
+        c = cfg._c()
+        qa, qp = _f64(q)
+        ka, kp = _f64(k)
+        va, vp = _f64(v)
+        ia, ip = _i32(idx)
+        out = np.empty(_map_shape(cfg), np.float64)
+        _check(self.lib.oracle_attend_kvds(ctypes.byref(c), ratio, qp, kp, vp, ip, _ptr(out)),
+               "attend_kvds")
         return out
 
     def bra_forward_kvds(self, cfg: OracleConfig, ratio: int, q, k, v, w=None, b=None):
@@ -330,3 +342,7 @@ def kv_downsample(cfg, ratio, x):
 
 def bra_forward_kvds(cfg, ratio, q, k, v, w=None, b=None):
     return default().bra_forward_kvds(cfg, ratio, q, k, v, w, b)
+
+
+def attend_kvds(cfg, ratio, q, k, v, idx):
+    return default().attend_kvds(cfg, ratio, q, k, v, idx)

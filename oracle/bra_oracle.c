@@ -274,6 +274,22 @@ int oracle_kv_downsample(const oracle_cfg_t* c, int ratio, const double* x, doub
     return 0;
 }
 
+int oracle_attend_kvds(const oracle_cfg_t* c, int ratio, const double* q, const double* k,
+                       const double* v, const int32_t* idx, double* o) {
+    if (!ratio_ok(c, ratio) || !q || !k || !v || !idx || !o) return -1;
+    const oracle_cfg_t d = kv_cfg(c, ratio);
+    const size_t nd = (size_t)c->batch * d.height * d.width * c->channels;
+    double* kd = (double*)malloc(sizeof(double) * nd);
+    double* vd = (double*)malloc(sizeof(double) * nd);
+    int rc = -1;
+    if (kd && vd && oracle_kv_downsample(c, ratio, k, kd) == 0 &&
+        oracle_kv_downsample(c, ratio, v, vd) == 0)
+        rc = attend_impl(c, &d, q, kd, vd, idx, o);
+    free(kd);
+    free(vd);
+    return rc;
+}
+
 int oracle_bra_forward_kvds(const oracle_cfg_t* c, int ratio, const double* q,
                             const double* k, const double* v, const double* w,
                             const double* bias, double* out, int32_t* idx) {

@@ -110,6 +110,11 @@ int oracle_bra_forward_shared(const oracle_cfg_t* cfg, const double* q, const do
  * divide the window sides.  -1 on a bad configuration or ratio. */
 int oracle_kv_downsample(const oracle_cfg_t* cfg, int ratio, const double* x, double* xd);
 
+/* Attention (no LePE) of every query over the downsampled K/V tokens of the
+ * regions idx names ([B, heads, R, k_eff], any order). */
+int oracle_attend_kvds(const oracle_cfg_t* cfg, int ratio, const double* q, const double* k,
+                       const double* v, const int32_t* idx, double* o);
+
 /* Whole forward with KV downsampling: routing on the full-resolution region
  * means (as oracle_bra_forward), attention of every query over the
  * downsampled K/V tokens of its routed regions ((hs/ratio)*(ws/ratio) per

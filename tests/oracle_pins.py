@@ -492,6 +492,20 @@ def pin_kvds_all_regions_is_dense_over_pooled(orc):
         np.testing.assert_allclose(res["out"], o + torch_lepe(v, w, b), rtol=RTOL, atol=ATOL)
 
 
+def pin_attend_kvds_matches_forward(orc):
+    """Attention over the downsampled K/V with the forward's own routing, plus
+    LePE, is the KV-downsampled forward; ratio 1 is the plain attention."""
+    cfg = OracleConfig(2, 8, 8, 16, 2, 2, 2)
+    rng = _rng(137)
+    q, k, v = (_rand_map(rng, cfg) for _ in range(3))
+    w, b = _rand_lepe(rng, cfg)
+    res = orc.bra_forward_kvds(cfg, 2, q, k, v, w, b)
+    o = orc.attend_kvds(cfg, 2, q, k, v, res["idx"])
+    np.testing.assert_allclose(o + orc.lepe(cfg, v, w, b), res["out"], rtol=RTOL, atol=ATOL)
+    np.testing.assert_array_equal(orc.attend_kvds(cfg, 1, q, k, v, res["idx"]),
+                                  orc.attend(cfg, q, k, v, res["idx"]))
+
+
 def pin_kvds_window_ratio_attends_region_means(orc):
     """Ratio = window side: every routed region contributes one key and one
     value, its mean, so each query's softmax runs over the k routed region
@@ -538,4 +552,5 @@ ALL_PINS = [
     pin_kvds_ratio_one_is_plain,
     pin_kvds_all_regions_is_dense_over_pooled,
     pin_kvds_window_ratio_attends_region_means,
+    pin_attend_kvds_matches_forward,
 ]

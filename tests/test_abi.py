@@ -48,6 +48,7 @@ def _cfg(**kw):
      bra.BRA_ERR_UNSUPPORTED),                     # one 65536-token region does not fit on chip
     (dict(height=65536, width=65536, n_win=1, channels=32, num_heads=1), bra.BRA_ERR_SHAPE),
     (dict(shared_routing=2), bra.BRA_ERR_SHAPE),   # a flag: 0 or 1
+    (dict(kv_downsample_ratio=3), bra.BRA_ERR_SHAPE),  # 3 does not divide the 4x4 windows
     (dict(height=4096, width=4096, n_win=256, channels=32, num_heads=1),
      bra.BRA_ERR_UNSUPPORTED),                     # H*W = 2^24 tokens: beyond 24-bit indexing
     (dict(height=34, width=34, n_win=17, channels=32, num_heads=1),

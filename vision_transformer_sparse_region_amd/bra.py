@@ -49,7 +49,7 @@ class BraConfig(ctypes.Structure):
         ("batch", ctypes.c_int32), ("height", ctypes.c_int32), ("width", ctypes.c_int32),
         ("channels", ctypes.c_int32), ("num_heads", ctypes.c_int32), ("n_win", ctypes.c_int32),
         ("topk", ctypes.c_int32), ("dtype", ctypes.c_int), ("scale", ctypes.c_float),
-        ("shared_routing", ctypes.c_int32),
+        ("shared_routing", ctypes.c_int32), ("kv_downsample_ratio", ctypes.c_int32),
     ]
 
 
@@ -203,10 +203,10 @@ class BRA:
     """
 
     def __init__(self, batch, height, width, channels, num_heads, n_win, topk, dtype="bf16",
-                 scale=0.0, shared_routing=False):
+                 scale=0.0, shared_routing=False, kv_downsample_ratio=1):
         self.cfg = BraConfig(batch, height, width, channels, num_heads, n_win, topk,
                              BRA_BF16 if dtype == "bf16" else BRA_F32, scale,
-                             1 if shared_routing else 0)
+                             1 if shared_routing else 0, kv_downsample_ratio)
         self.dtype = dtype
         self.route_heads = 1 if shared_routing else num_heads
         self.handle = bra_create(self.cfg)

@@ -28,6 +28,8 @@ struct bra_handle_s {
     int32_t* routing;
     uint2* lepe_table;
     float* zero_bias;
+    void* kd;  // downsampled K and V [B, H/r, W/r, C] (KV downsampling), else NULL
+    void* vd;
     // per-kernel timing (events recorded by bra_forward while slots remain)
     std::vector<hipEvent_t> events;  // kEventsPerCall per recorded call
     int timing_capacity;
@@ -120,8 +122,12 @@ bra_status_t bra_create(const bra_config_t* cfg, bra_handle_t* out) {
     bra::Params p;
     if (c.shared_routing != 0 && c.shared_routing != 1)
         return fail(BRA_ERR_SHAPE, "bra_create: shared_routing must be 0 or 1");
+    const int kv_ratio = c.kv_downsample_ratio <= 1 ? 1 : c.kv_downsample_ratio;
+    if ((c.height / c.n_win) % kv_ratio || (c.width / c.n_win) % kv_ratio)
+        return fail(BRA_ERR_SHAPE,
+                    "bra_create: kv_downsample_ratio must divide the window height and width");
     if (!bra::plan(p, c.batch, c.height, c.width, c.channels, c.num_heads, c.n_win, k, scale,
-                   bf16, c.shared_routing == 1))
+                   bf16, c.shared_routing == 1, kv_ratio))
         return fail(BRA_ERR_UNSUPPORTED,
                     "bra_create: a region (with its LePE halo) or the channel count is too large "
                     "for the on-chip tiles (" + std::to_string(p.lds_bytes) + " bytes of LDS)");
@@ -139,12 +145,19 @@ bra_status_t bra_create(const bra_config_t* cfg, bra_handle_t* out) {
     const size_t route_bytes =
         ((static_cast<size_t>(c.batch) * p.rheads * R * k * sizeof(int32_t)) + 15) & ~size_t{15};
     const size_t table_bytes = static_cast<size_t>(p.table_items) * sizeof(uint2);
-    const size_t zero_bytes = static_cast<size_t>(c.channels) * sizeof(float);
-    h->means_bytes = mean_bytes + route_bytes + table_bytes + zero_bytes;
+    const size_t zero_bytes = ((static_cast<size_t>(c.channels) * sizeof(float)) + 15) &
+                              ~size_t{15};
+    // downsampled K and V (KV downsampling only)
+    const size_t kv_bytes = p.kv_ratio > 1 ? static_cast<size_t>(c.batch) * p.kH * p.kW *
+                                                 c.channels * (bf16 ? 2 : 4)
+                                           : 0;
+    h->means_bytes = mean_bytes + route_bytes + table_bytes + zero_bytes + 2 * kv_bytes;
     h->means = nullptr;
     h->routing = nullptr;
     h->lepe_table = nullptr;
     h->zero_bias = nullptr;
+    h->kd = nullptr;
+    h->vd = nullptr;
     h->timing_capacity = 0;
     h->timing_used = 0;
     e = hipMalloc(reinterpret_cast<void**>(&h->means), h->means_bytes);
@@ -157,6 +170,8 @@ bra_status_t bra_create(const bra_config_t* cfg, bra_handle_t* out) {
         reinterpret_cast<uint2*>(reinterpret_cast<char*>(h->means) + mean_bytes + route_bytes);
     h->zero_bias = reinterpret_cast<float*>(reinterpret_cast<char*>(h->means) + mean_bytes +
                                             route_bytes + table_bytes);
+    h->kd = kv_bytes ? reinterpret_cast<char*>(h->zero_bias) + zero_bytes : nullptr;
+    h->vd = kv_bytes ? static_cast<char*>(h->kd) + kv_bytes : nullptr;
     e = hipMemset(h->zero_bias, 0, zero_bytes);
     if (e != hipSuccess) {
         hipFree(h->means);
@@ -229,6 +244,10 @@ bra_status_t bra_forward(bra_handle_t h, const void* q, const void* k, const voi
         return fail_hip(e, "bra_forward: hipEventRecord");
     e = bra::launch_pool_qk(h->params, h->bf16, q, k, lepe_w, h->means, h->lepe_table, s);
     if (e != hipSuccess) return fail_hip(e, "bra_forward: region-pool launch");
+    if (h->kd) {
+        e = bra::launch_kv_pool(h->params, h->bf16, k, v, h->kd, h->vd, s);
+        if (e != hipSuccess) return fail_hip(e, "bra_forward: K/V downsampling launch");
+    }
     if (timed && (e = hipEventRecord(ev[1], s)) != hipSuccess)
         return fail_hip(e, "bra_forward: hipEventRecord");
     // the routing goes to the caller's buffer when one is given
@@ -240,9 +259,9 @@ bra_status_t bra_forward(bra_handle_t h, const void* q, const void* k, const voi
     }
     if (timed && (e = hipEventRecord(ev[2], s)) != hipSuccess)
         return fail_hip(e, "bra_forward: hipEventRecord");
-    e = bra::launch_attend(h->params, h->bf16, q, k, v, h->means, routing,
-                           !bra::route_in_attend(h->params), lepe_w, lepe_b, h->lepe_table,
-                           h->zero_bias, out, s);
+    e = bra::launch_attend(h->params, h->bf16, q, v, h->kd ? h->kd : k, h->vd ? h->vd : v,
+                           h->means, routing, !bra::route_in_attend(h->params), lepe_w, lepe_b,
+                           h->lepe_table, h->zero_bias, out, s);
     if (e != hipSuccess) return fail_hip(e, "bra_forward: attention launch");
     if (timed) {
         if ((e = hipEventRecord(ev[3], s)) != hipSuccess)
@@ -268,8 +287,12 @@ bra_status_t bra_forward_routed(bra_handle_t h, const void* q, const void* k, co
         e = bra::launch_lepe_table(h->params, lepe_w, h->lepe_table, s);
         if (e != hipSuccess) return fail_hip(e, "bra_forward_routed: LePE table launch");
     }
-    e = bra::launch_attend(h->params, h->bf16, q, k, v, h->means,
-                           const_cast<int32_t*>(routing_idx), true, lepe_w, lepe_b,
+    if (h->kd) {
+        e = bra::launch_kv_pool(h->params, h->bf16, k, v, h->kd, h->vd, s);
+        if (e != hipSuccess) return fail_hip(e, "bra_forward_routed: K/V downsampling launch");
+    }
+    e = bra::launch_attend(h->params, h->bf16, q, v, h->kd ? h->kd : k, h->vd ? h->vd : v,
+                           h->means, const_cast<int32_t*>(routing_idx), true, lepe_w, lepe_b,
                            h->lepe_table, h->zero_bias, out, s);
     if (e != hipSuccess) return fail_hip(e, "bra_forward_routed: attention launch");
     return BRA_OK;

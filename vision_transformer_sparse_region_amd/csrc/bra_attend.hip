@@ -98,18 +98,18 @@ __device__ __forceinline__ void gather_chunk(const Params& p, const WaveJobs& J,
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
         const int key = min(32 * c + 8 * (li >> 2) + 4 * blk + (li & 3), p.nkeys - 1);
-        const int j = key / p.t, slot = key - j * p.t;
+        const int j = key / p.kt, slot = key - j * p.kt;
         g8.ka[blk] = __builtin_bit_cast(
-            bf16x8_t, *reinterpret_cast<const uint4*>(kimg + off[j] + slot_offset(p, slot) +
+            bf16x8_t, *reinterpret_cast<const uint4*>(kimg + off[j] + slot_offset_kv(p, slot) +
                                                       hoff + 8 * g));
     }
 #pragma unroll
     for (int pp = 0; pp < 2; ++pp) {
         const int pc = lane + 64 * pp;
         const int key = min(32 * c + (pc >> 2), p.nkeys - 1);
-        const int j = key / p.t, slot = key - j * p.t;
-        g8.vv[pp] = *reinterpret_cast<const uint4*>(vimg + off[j] + slot_offset(p, slot) + hoff +
-                                                    8 * (pc & 3));
+        const int j = key / p.kt, slot = key - j * p.kt;
+        g8.vv[pp] = *reinterpret_cast<const uint4*>(vimg + off[j] + slot_offset_kv(p, slot) +
+                                                    hoff + 8 * (pc & 3));
     }
 }
 
@@ -305,8 +305,8 @@ __device__ __forceinline__ void attend_valu(const Params& p, const float* __rest
         for (int key = 0; key < p.nkeys; ++key) {
             float4 kn = kv, vn = vv;
             if (key + 1 < p.nkeys) {
-                const int j = (key + 1) / p.t, ks = key + 1 - j * p.t;
-                const int o2 = roff[j] + slot_offset(p, ks) + hoff;
+                const int j = (key + 1) / p.kt, ks = key + 1 - j * p.kt;
+                const int o2 = roff[j] + slot_offset_kv(p, ks) + hoff;
                 kn = *reinterpret_cast<const float4*>(kimg + o2);
                 vn = *reinterpret_cast<const float4*>(vimg + o2);
             }
@@ -540,11 +540,11 @@ __device__ __forceinline__ void route_row_wave(const Params& p, const double* __
         wave_argmax(best, bs);
         if (lane == 0) {
             bs = min(max(bs, 0), p.R - 1);
-            off[0] = region_base(p, bs);
+            off[0] = region_base_kv(p, bs);
             out[0] = bs;
         }
     } else {
-        if (lane < p.k) off[lane] = 0;
+        if (lane < p.k) off[lane] = 0;  // region 0's base in either map
         scratch[lane] = a;
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
@@ -555,7 +555,7 @@ __device__ __forceinline__ void route_row_wave(const Params& p, const double* __
             rank += (o > a || (o == a && x < lane)) ? 1 : 0;
         }
         if (lane < p.R && rank < p.k) {
-            off[rank] = region_base(p, lane);
+            off[rank] = region_base_kv(p, lane);
             out[rank] = lane;
         }
         // the next row's writes must not pass this row's reads
@@ -571,8 +571,9 @@ __device__ __forceinline__ void route_row_wave(const Params& p, const double* __
 // extra register pressure spills).
 template <typename T, int HS, int WS, int NW, int HEADS, int KTOP, bool FUSED>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))) void
-attend_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
-              const double* __restrict__ means, int32_t* __restrict__ routing,
+attend_kernel(const T* __restrict__ q, const T* __restrict__ v, const T* __restrict__ kg,
+              const T* __restrict__ vg, const double* __restrict__ means,
+              int32_t* __restrict__ routing,
               const float* __restrict__ lepe_w,
               const float* __restrict__ lepe_b, const float* __restrict__ lepe_bias,
               const uint2* __restrict__ lepe_table, T* __restrict__ out, Params p_in) {
@@ -591,6 +592,7 @@ attend_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restr
     const int b = blk / p.R, r = blk - b * p.R;
     const int y0 = (r / p.n) * p.hs, x0 = (r % p.n) * p.ws;
     const size_t img = static_cast<size_t>(b) * p.H * p.W * p.C;
+    const size_t kimg = static_cast<size_t>(b) * p.kH * p.kW * p.C;  // gathered K/V map
     const int nvec = p.C / VEC;
     const int hw = p.ws + 4;
 
@@ -675,7 +677,7 @@ attend_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restr
         }
         if constexpr (kLepeMfma) lepe_mfma_load<HS, WS, HEADS>(lepe_table, lepe_bias, lop);
     } else {
-        sOff[min(tid, nhk - 1)] = region_base(p, min(max(ridx, 0), p.R - 1));
+        sOff[min(tid, nhk - 1)] = region_base_kv(p, min(max(ridx, 0), p.R - 1));
         for (int i = tid + kThreads; i < nhk; i += kThreads) {
             const int h = i / p.k, j = i - h * p.k;
             const int x = routing[((static_cast<size_t>(b) * p.rheads + (p.shared ? 0 : h)) *
@@ -683,7 +685,7 @@ attend_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restr
                                    r) *
                                       p.k +
                                   j];
-            sOff[i] = region_base(p, min(max(x, 0), p.R - 1));
+            sOff[i] = region_base_kv(p, min(max(x, 0), p.R - 1));
         }
     }
     if (stage_w) {
@@ -756,8 +758,8 @@ attend_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restr
 #pragma unroll
             for (int ch = 0; ch < 2; ++ch)
                 if (ch < J.nchunks)
-                    gather_chunk(p, J, w, 0, ch, reinterpret_cast<const uint16_t*>(k) + img,
-                                 reinterpret_cast<const uint16_t*>(v) + img, sOff, ring[ch]);
+                    gather_chunk(p, J, w, 0, ch, reinterpret_cast<const uint16_t*>(kg) + kimg,
+                                 reinterpret_cast<const uint16_t*>(vg) + kimg, sOff, ring[ch]);
         }
     }
     if (!early_lepe) {
@@ -778,13 +780,13 @@ attend_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restr
     // 4. Token attention over the routed tokens, added into sL.
     if constexpr (VEC == 8) {
         attend_mfma(p, J, reinterpret_cast<const uint16_t*>(q) + img,
-                    reinterpret_cast<const uint16_t*>(k) + img,
-                    reinterpret_cast<const uint16_t*>(v) + img, r,
+                    reinterpret_cast<const uint16_t*>(kg) + kimg,
+                    reinterpret_cast<const uint16_t*>(vg) + kimg, r,
                     reinterpret_cast<uint16_t*>(smem + p.off_vt), sL, sOff, ring, qb);
     } else {
         attend_valu(p, reinterpret_cast<const float*>(q) + img,
-                    reinterpret_cast<const float*>(k) + img,
-                    reinterpret_cast<const float*>(v) + img, r, sL, sOff);
+                    reinterpret_cast<const float*>(kg) + kimg,
+                    reinterpret_cast<const float*>(vg) + kimg, r, sL, sOff);
     }
     __syncthreads();
 
@@ -814,7 +816,7 @@ attend_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restr
 static long align16(long x) { return (x + 15) & ~15L; }
 
 bool plan(Params& p, int B, int H, int W, int C, int heads, int n_win, int k, float scale,
-          bool bf16, bool shared) {
+          bool bf16, bool shared, int kv_ratio) {
     p.B = B;
     p.H = H;
     p.W = W;
@@ -828,7 +830,13 @@ bool plan(Params& p, int B, int H, int W, int C, int heads, int n_win, int k, fl
     p.k = k;
     p.shared = shared ? 1 : 0;
     p.rheads = shared ? 1 : heads;
-    p.nkeys = k * p.t;
+    p.kv_ratio = kv_ratio;
+    p.kH = H / kv_ratio;
+    p.kW = W / kv_ratio;
+    p.khs = p.hs / kv_ratio;
+    p.kws = p.ws / kv_ratio;
+    p.kt = p.khs * p.kws;
+    p.nkeys = k * p.kt;
     p.scale_log2e = scale * 1.4426950408889634f;
     p.has_lepe = 0;
     const long es = bf16 ? 2 : 4;
@@ -884,10 +892,11 @@ bool plan(Params& p, int B, int H, int W, int C, int heads, int n_win, int k, fl
     return off <= kMaxLdsBytes && C <= kMaxChannels && C % 32 == 0 && p.R <= kMaxRegions;
 }
 
-hipError_t launch_attend(const Params& p, bool bf16, const void* q, const void* k, const void* v,
-                         const double* means, int32_t* routing, bool use_routing,
-                         const float* lepe_w, const float* lepe_b, const uint2* lepe_table,
-                         const float* zero_bias, void* out, hipStream_t stream) {
+hipError_t launch_attend(const Params& p, bool bf16, const void* q, const void* v,
+                         const void* kg, const void* vg, const double* means, int32_t* routing,
+                         bool use_routing, const float* lepe_w, const float* lepe_b,
+                         const uint2* lepe_table, const float* zero_bias, void* out,
+                         hipStream_t stream) {
     Params pp = p;
     pp.has_lepe = lepe_w != nullptr;
     if (!pp.has_lepe) lepe_b = nullptr;
@@ -897,11 +906,11 @@ hipError_t launch_attend(const Params& p, bool bf16, const void* q, const void* 
     const bool fused = !use_routing && route_in_attend(p);
 #define BRA_ATTEND_F(T, HS, WS, NW, HEADS, KTOP, F)                                             \
     hipLaunchKernelGGL((attend_kernel<T, HS, WS, NW, HEADS, KTOP, F>), grid, block,             \
-                       p.lds_bytes, stream, static_cast<const T*>(q), static_cast<const T*>(k), \
-                       static_cast<const T*>(v), means, routing, lepe_w, lepe_b, lepe_bias,    \
-                       lepe_table, static_cast<T*>(out), pp)
+                       p.lds_bytes, stream, static_cast<const T*>(q), static_cast<const T*>(v), \
+                       static_cast<const T*>(kg), static_cast<const T*>(vg), means, routing,   \
+                       lepe_w, lepe_b, lepe_bias, lepe_table, static_cast<T*>(out), pp)
 #define BRA_ATTEND(T, HS, WS, NW, HEADS, KTOP)                                                  \
-    if (matches(Inst<T, HS, WS, NW, HEADS, KTOP>::key, p, bf16, true)) {                        \
+    if (p.kv_ratio == 1 && matches(Inst<T, HS, WS, NW, HEADS, KTOP>::key, p, bf16, true)) {     \
         if constexpr (route_fused(NW * NW, HEADS)) {                                            \
             if (fused)                                                                          \
                 BRA_ATTEND_F(T, HS, WS, NW, HEADS, KTOP, true);                                 \
@@ -917,9 +926,9 @@ hipError_t launch_attend(const Params& p, bool bf16, const void* q, const void* 
 #undef BRA_ATTEND_F
 #define BRA_GENERIC(T, F)                                                                       \
     hipLaunchKernelGGL((attend_kernel<T, 0, 0, 0, 0, 0, F>), grid, block, p.lds_bytes, stream,  \
-                       static_cast<const T*>(q), static_cast<const T*>(k),                      \
-                       static_cast<const T*>(v), means, routing, lepe_w, lepe_b, lepe_bias,     \
-                       lepe_table, static_cast<T*>(out), pp)
+                       static_cast<const T*>(q), static_cast<const T*>(v),                      \
+                       static_cast<const T*>(kg), static_cast<const T*>(vg), means, routing,    \
+                       lepe_w, lepe_b, lepe_bias, lepe_table, static_cast<T*>(out), pp)
     if (bf16) {
         if (fused)
             BRA_GENERIC(uint16_t, true);

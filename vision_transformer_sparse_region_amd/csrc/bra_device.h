@@ -126,6 +126,15 @@ __device__ __forceinline__ int slot_offset(const Params& p, int slot) {
 __device__ __forceinline__ int token_offset(const Params& p, int reg, int slot) {
     return region_base(p, reg) + slot_offset(p, slot);
 }
+// The same in the K/V map the attention gathers from (downsampled or not).
+__device__ __forceinline__ int region_base_kv(const Params& p, int reg) {
+    const int ri = reg / p.n, rj = reg - ri * p.n;
+    return __mul24(__mul24(__mul24(ri, p.khs), p.kW) + __mul24(rj, p.kws), p.C);
+}
+__device__ __forceinline__ int slot_offset_kv(const Params& p, int slot) {
+    const int u = slot / p.kws, w = slot - u * p.kws;
+    return __mul24(__mul24(u, p.kW) + w, p.C);
+}
 
 // Window geometry as compile-time constants.  A kernel instantiated with
 // nonzero HS, WS, NW, HEADS, KTOP replaces the matching runtime fields (the
@@ -151,6 +160,13 @@ __device__ __forceinline__ Params fold_geometry(const Params& in) {
         p.t = HS * WS;
         p.k = KTOP;
         p.nkeys = KTOP * HS * WS;
+        // fixed shapes run without KV downsampling
+        p.kv_ratio = 1;
+        p.kH = p.H;
+        p.kW = p.W;
+        p.khs = HS;
+        p.kws = WS;
+        p.kt = HS * WS;
         p.lepe_items = (HEADS * kHeadDim / 2) * HS * ((WS + kLepeCols - 1) / kLepeCols);
         p.lepe_alias = p.lepe_items <= kThreads;
         p.halo_pieces = (HS + 4) * (WS + 4) * (HEADS * kHeadDim / VEC);

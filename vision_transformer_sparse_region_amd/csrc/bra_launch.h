@@ -28,7 +28,10 @@ struct Params {
     int k;           // routed regions per region (already clamped)
     int shared;      // 1: one routing per region for every head (full-C affinity)
     int rheads;      // heads of the routing buffer: 1 when shared, else heads
-    int nkeys;       // k * t keys per query
+    int nkeys;       // k * kt keys per query
+    // the K/V map the attention gathers from: the input map, or its K/V
+    // average-pooled over kv_ratio x kv_ratio blocks (KV downsampling)
+    int kv_ratio, kH, kW, khs, kws, kt;
     float scale_log2e;
     int has_lepe;
     int lstride;     // floats per staged output row (C plus 16 bytes)
@@ -47,7 +50,7 @@ struct Params {
 
 // Fills the geometry and layout; returns false when a tile does not fit.
 bool plan(Params& p, int B, int H, int W, int C, int heads, int n_win, int k, float scale,
-          bool bf16, bool shared);
+          bool bf16, bool shared, int kv_ratio);
 
 // Kernel launches on `stream`; return the launch status.
 //   means: fp64 region means, Q as [B][heads][R][32], then K as [B][heads][32][R].
@@ -67,14 +70,21 @@ constexpr bool route_fused(int R, int heads) {
 }
 inline bool route_in_attend(const Params& p) { return !p.shared && route_fused(p.R, p.heads); }
 
+//   kg, vg: the K and V the attention gathers from -- k and v, or their
+//   downsampled copies ([B, kH, kW, C]) when kv_ratio > 1; v still feeds LePE.
 //   use_routing: read the routing from `routing` (written by the routing
 //   kernel or given by the caller); otherwise route in the kernel (needs
 //   route_in_attend) and write the ids to `routing`.
 //   zero_bias: C zero floats (device), used when lepe_b is NULL.
-hipError_t launch_attend(const Params& p, bool bf16, const void* q, const void* k, const void* v,
-                         const double* means, int32_t* routing, bool use_routing,
-                         const float* lepe_w, const float* lepe_b, const uint2* lepe_table,
-                         const float* zero_bias, void* out, hipStream_t stream);
+hipError_t launch_attend(const Params& p, bool bf16, const void* q, const void* v,
+                         const void* kg, const void* vg, const double* means, int32_t* routing,
+                         bool use_routing, const float* lepe_w, const float* lepe_b,
+                         const uint2* lepe_table, const float* zero_bias, void* out,
+                         hipStream_t stream);
+// KV downsampling: k and v averaged over kv_ratio x kv_ratio blocks into
+// kd, vd ([B, kH, kW, C], the input dtype; fp32 sums, one rounding).
+hipError_t launch_kv_pool(const Params& p, bool bf16, const void* k, const void* v, void* kd,
+                          void* vd, hipStream_t stream);
 // The MFMA LePE operand table alone (the region-pool kernel's trailing
 // workgroups), for the entry point that skips the region means.
 hipError_t launch_lepe_table(const Params& p, const float* lepe_w, uint2* lepe_table,

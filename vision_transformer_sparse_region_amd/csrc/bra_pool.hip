@@ -131,6 +131,80 @@ __global__ __launch_bounds__(kThreads) void lepe_table_kernel(const float* __res
 }
 }  // namespace
 
+// ---------------------------------------------------------------------------
+// KV downsampling [P1 §4.1 kv_downsample_ratio, avgpool]: one thread per
+// (tensor, image, pooled token, VEC-channel piece) sums the kv_ratio^2 input
+// tokens of its block in fp32 (block row-major), scales by 1/kv_ratio^2 and
+// rounds once to the I/O type.  Reads K and V once, writes 2/kv_ratio^2 of
+// them.
+namespace {
+template <typename T>
+__global__ __launch_bounds__(kThreads) void kv_pool_kernel(const T* __restrict__ k,
+                                                           const T* __restrict__ v,
+                                                           T* __restrict__ kd,
+                                                           T* __restrict__ vd, Params p) {
+    constexpr int VEC = Elem<T>::kVec;
+    const int nvec = p.C / VEC;
+    const long per = static_cast<long>(p.B) * p.kH * p.kW * nvec;  // pieces per tensor
+    const long it = static_cast<long>(blockIdx.x) * kThreads + threadIdx.x;
+    if (it >= 2 * per) return;
+    const int tensor = it >= per;
+    const long i = it - tensor * per;
+    const int pv = static_cast<int>(i % nvec);
+    const long cell = i / nvec;
+    const int xd = static_cast<int>(cell % p.kW);
+    const long rest = cell / p.kW;
+    const int yd = static_cast<int>(rest % p.kH), b = static_cast<int>(rest / p.kH);
+    const T* src = (tensor ? v : k) + static_cast<size_t>(b) * p.H * p.W * p.C + pv * VEC;
+    float acc[VEC];
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
+    for (int u = 0; u < p.kv_ratio; ++u)
+        for (int w = 0; w < p.kv_ratio; ++w) {
+            const size_t tok = static_cast<size_t>(yd * p.kv_ratio + u) * p.W +
+                               (xd * p.kv_ratio + w);
+            const uint4 x = *reinterpret_cast<const uint4*>(src + tok * p.C);
+            if constexpr (VEC == 8) {
+                acc[0] += bf16lo(x.x); acc[1] += bf16hi(x.x);
+                acc[2] += bf16lo(x.y); acc[3] += bf16hi(x.y);
+                acc[4] += bf16lo(x.z); acc[5] += bf16hi(x.z);
+                acc[6] += bf16lo(x.w); acc[7] += bf16hi(x.w);
+            } else {
+                acc[0] += __uint_as_float(x.x); acc[1] += __uint_as_float(x.y);
+                acc[2] += __uint_as_float(x.z); acc[3] += __uint_as_float(x.w);
+            }
+        }
+    const float inv = 1.0f / static_cast<float>(p.kv_ratio * p.kv_ratio);
+    T* dst = (tensor ? vd : kd) + static_cast<size_t>(cell) * p.C + pv * VEC;
+    uint4 o;
+    if constexpr (VEC == 8) {
+        o.x = f32_to_bf16(acc[0] * inv) | (f32_to_bf16(acc[1] * inv) << 16);
+        o.y = f32_to_bf16(acc[2] * inv) | (f32_to_bf16(acc[3] * inv) << 16);
+        o.z = f32_to_bf16(acc[4] * inv) | (f32_to_bf16(acc[5] * inv) << 16);
+        o.w = f32_to_bf16(acc[6] * inv) | (f32_to_bf16(acc[7] * inv) << 16);
+    } else {
+        o = uint4{__float_as_uint(acc[0] * inv), __float_as_uint(acc[1] * inv),
+                  __float_as_uint(acc[2] * inv), __float_as_uint(acc[3] * inv)};
+    }
+    *reinterpret_cast<uint4*>(dst) = o;
+}
+}  // namespace
+
+hipError_t launch_kv_pool(const Params& p, bool bf16, const void* k, const void* v, void* kd,
+                          void* vd, hipStream_t stream) {
+    const long per = static_cast<long>(p.B) * p.kH * p.kW * (p.C / (bf16 ? 8 : 4));
+    const dim3 grid(static_cast<unsigned>((2 * per + kThreads - 1) / kThreads)), block(kThreads);
+    if (bf16)
+        hipLaunchKernelGGL(kv_pool_kernel<uint16_t>, grid, block, 0, stream,
+                           static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
+                           static_cast<uint16_t*>(kd), static_cast<uint16_t*>(vd), p);
+    else
+        hipLaunchKernelGGL(kv_pool_kernel<float>, grid, block, 0, stream,
+                           static_cast<const float*>(k), static_cast<const float*>(v),
+                           static_cast<float*>(kd), static_cast<float*>(vd), p);
+    return hipGetLastError();
+}
+
 hipError_t launch_lepe_table(const Params& p, const float* lepe_w, uint2* lepe_table,
                              hipStream_t stream) {
     if (p.table_items <= 0) return hipSuccess;
