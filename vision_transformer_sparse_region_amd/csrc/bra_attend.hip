@@ -803,9 +803,13 @@ attend_kernel(const T* __restrict__ q, const T* __restrict__ v, const T* __restr
             u.y = f32_to_bf16(a.z) | (f32_to_bf16(a.w) << 16);
             u.z = f32_to_bf16(c.x) | (f32_to_bf16(c.y) << 16);
             u.w = f32_to_bf16(c.z) | (f32_to_bf16(c.w) << 16);
-            *reinterpret_cast<uint4*>(dst) = u;
+            // streaming store: the output is not re-read, so it should not sit
+            // dirty in L2 for the next kernel to write back
+            __builtin_nontemporal_store(u32x4_t{u.x, u.y, u.z, u.w},
+                                        reinterpret_cast<u32x4_t*>(dst));
         } else {
-            *reinterpret_cast<float4*>(dst) = *reinterpret_cast<const float4*>(src);
+            __builtin_nontemporal_store(*reinterpret_cast<const f32x4_t*>(src),
+                                        reinterpret_cast<f32x4_t*>(dst));
         }
     }
 }
