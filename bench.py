@@ -43,12 +43,32 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
+def route_in_attend(wl, shared_routing: bool = False) -> bool:
+    """Maps of at most 64 regions with at most 4 heads are routed inside the
+    attention kernel (per-head routing)."""
+    return wl.regions <= 64 and wl.num_heads <= 4 and not shared_routing
+
+
+def qmean_in_attend(wl, shared_routing: bool = False) -> bool:
+    """bf16 maps routed inside the attention kernel whose query tiles fit the
+    four waves' first jobs: the attention kernel sums the Q means itself and
+    the pool kernel reads only K.  (The split of a region's 16-query tiles
+    over the waves: at most 2 tiles per job, spare waves take extra groups.)"""
+    if wl.dtype != "bf16" or not route_in_attend(wl, shared_routing):
+        return False
+    qt = (wl.tokens_per_region + 15) // 16
+    spread = min(max(1, 4 // wl.num_heads), qt)
+    groups = max(spread, (qt + 1) // 2)
+    per_group = (qt + groups - 1) // groups
+    return wl.num_heads * ((qt + per_group - 1) // per_group) <= 4
+
+
 def algorithmic_bytes(wl, shared_routing: bool = False, kv_ratio: int = 1) -> dict:
     """Bytes each kernel must move once per launch (unique bytes; the k-fold
     re-reads of routed K/V, of the LePE halo and of the K means are cache
-    traffic).  Maps of at most 64 regions with at most 4 heads are routed
-    inside the attention kernel, which then also reads the means and writes
-    the ids."""
+    traffic).  When the routing runs inside the attention kernel, that kernel
+    also reads the means and writes the ids; when it also sums the Q means,
+    only the K means are written and read."""
     es = 2 if wl.dtype == "bf16" else 4
     S = wl.tokens * wl.channels * es                     # one [B,H,W,C] tensor
     M = wl.batch * wl.channels * wl.regions * 8          # one fp64 [B,heads,R,32] mean array
@@ -60,8 +80,9 @@ def algorithmic_bytes(wl, shared_routing: bool = False, kv_ratio: int = 1) -> di
     # attention then gathers the pooled K/V (2S/r^2) and still reads v for LePE
     kvpool = 2 * S + 2 * S // r2 if r2 > 1 else 0
     attend = (3 * S + 2 * S // r2 if r2 > 1 else 4 * S) + idx + lepe
-    if wl.regions <= 64 and wl.num_heads <= 4 and not shared_routing:
-        # routed inside the attention kernel: it reads the means, writes the ids
+    if qmean_in_attend(wl, shared_routing):
+        return {"pool": S + M + kvpool, "route": 0, "attend": attend + M, "S": S}
+    if route_in_attend(wl, shared_routing):
         return {"pool": 2 * S + 2 * M + kvpool, "route": 0, "attend": attend + 2 * M, "S": S}
     return {
         "pool": 2 * S + 2 * M + kvpool,                  # read q, k; write both means
@@ -245,7 +266,10 @@ def main(argv=None) -> int:
     ms_per_step = gpu_ms / args.steps
     tokens_per_s = wl.tokens / (ms_per_step * 1e-3)
     pool_ms = sum(t[0] for t in times) / len(times)
-    route_ms = sum(t[1] for t in times) / len(times)
+    # (no routing kernel runs when the attention kernel routes: the interval
+    # between its two events is empty)
+    route_ms = sum(t[1] for t in times) / len(times) \
+        if not route_in_attend(wl, args.shared_routing) else None
     attn_ms = sum(t[2] for t in times) / len(times)
     ab = algorithmic_bytes(wl, args.shared_routing, args.kv_downsample)
     achieved = ab["attend"] / (attn_ms * 1e-3) / 1e9

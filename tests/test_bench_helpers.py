@@ -13,10 +13,25 @@ def test_algorithmic_bytes_stage1():
     M = 64 * 2 * 49 * 32 * 8
     idx = 64 * 2 * 49 * 1 * 4
     assert ab["S"] == S
-    assert ab["pool"] == 2 * S + 2 * M
-    # 49 regions, 2 heads: routed inside the attention kernel
+    # 49 regions, 2 heads: routed inside the attention kernel, which also sums
+    # the Q means; the pool kernel reads k and writes the K means only
+    assert ab["pool"] == S + M
     assert ab["route"] == 0
-    assert ab["attend"] == 4 * S + 2 * M + idx + 64 * 26 * 4
+    assert ab["attend"] == 4 * S + M + idx + 64 * 26 * 4
+
+
+def test_q_means_summed_in_attention_kernel():
+    # every query tile of a region is some wave's first job (at most 4 jobs)
+    assert bench.qmean_in_attend(WORKLOADS["stage1"])       # 2 heads x 2 groups of 2 tiles
+    assert bench.qmean_in_attend(WORKLOADS["stage2"])       # 4 heads x 1 tile
+    assert not bench.qmean_in_attend(WORKLOADS["stage3"])   # 8 heads: routed separately
+    assert not bench.qmean_in_attend(WORKLOADS["tiny_f32"])  # fp32
+    assert not bench.qmean_in_attend(WORKLOADS["stage1"], shared_routing=True)
+    base = WORKLOADS["stage1"]
+    assert bench.qmean_in_attend(base.with_(height=56, width=42))       # t = 48: 2 + 1 tiles
+    assert not bench.qmean_in_attend(base.with_(height=42, width=42,    # t = 36, 3 heads:
+                                                 channels=96, num_heads=3, n_win=7))  # 6 jobs
+    assert not bench.qmean_in_attend(base.with_(height=70, width=70))   # t = 100: 8 jobs
 
 
 def test_algorithmic_bytes_highres_separate_route():

@@ -34,6 +34,12 @@ SMALL = [
     Workload("stage2_shape_bias", 2, 28, 28, 128, 4, 7, 4, "bf16", 117, lepe_bias=True),
     Workload("highres_shape_bias", 1, 128, 128, 64, 2, 16, 16, "bf16", 118, smooth=True,
              lepe_bias=True),
+    # in-kernel routing with the Q means summed from the waves' Q operands:
+    # two query groups per head (the sums meet across waves), uneven groups,
+    # and one head spread over four waves
+    Workload("t32_two_groups", 2, 56, 28, 64, 2, 7, 2, "bf16", 119),
+    Workload("t48_uneven_groups", 2, 56, 42, 64, 2, 7, 3, "bf16", 120, lepe_bias=True),
+    Workload("one_head_four_groups", 2, 56, 56, 32, 1, 7, 3, "bf16", 121),
     Workload("f32_stage2_shape", 4, 28, 28, 128, 4, 7, 4, "f32", 109),
     Workload("f32_ragged_bias", 2, 12, 20, 64, 2, 4, 3, "f32", 110, lepe_bias=True),
 ]

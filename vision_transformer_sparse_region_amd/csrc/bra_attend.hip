@@ -43,12 +43,11 @@ namespace {
 struct WaveJobs {
     int QT, G, tpg, njobs, nchunks, nsteps;
     __device__ __forceinline__ WaveJobs(const Params& p, int w) {
-        QT = (p.t + 15) / 16;
-        const int wph = max(1, kWaves / p.heads);
-        const int g0 = max(min(wph, QT), (QT + kMaxQTiles - 1) / kMaxQTiles);
-        tpg = (QT + g0 - 1) / g0;
-        G = (QT + tpg - 1) / tpg;  // every group non-empty
-        njobs = p.heads * G;
+        const JobShape js = job_shape(p.t, p.heads);
+        QT = js.QT;
+        tpg = js.tpg;
+        G = js.G;
+        njobs = js.njobs;
         nchunks = (p.nkeys + 31) / 32;
         const int mine = w < njobs ? (njobs - 1 - w) / kWaves + 1 : 0;
         nsteps = mine * nchunks;
@@ -517,19 +516,51 @@ __device__ __forceinline__ void lepe_mfma_compute(const Params& p, const uint16_
 }
 
 // ---------------------------------------------------------------------------
+// Region Q mean from the Q operands [P4 §1.2; P2 §2.1; P5 §五 ③].  When every
+// job is some wave's first job, the first Q operands of the waves hold each
+// query of the region once: wave w (< njobs) sums, in fp64, the queries of
+// its job (job w) for dims 8g..8g+7 of the job's head on lane row g, and
+// stores the 32 sums at sQp[w][..].  Every partial sum of bf16 values is an
+// exact fp64 number, so neither this split nor the order of the additions
+// can change the total: it equals the pool kernel's and the plain loop's.
+__device__ __forceinline__ void qmean_partial(const Params& p, const WaveJobs& J, int w,
+                                              const bf16x8_t (&qb)[kMaxQTiles], double* sQp) {
+    const int lane = threadIdx.x & 63, li = lane & 15, g = lane >> 4;
+    const int grp = w - (w / J.G) * J.G;
+    const int qt0 = grp * J.tpg, nq = min(J.tpg, J.QT - qt0);
+    double* dst = sQp + w * kHeadDim + 8 * g;
+    // one dim at a time (the K means are in flight in most of the registers)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        double acc = 0.0;
+#pragma unroll
+        for (int jq = 0; jq < kMaxQTiles; ++jq) {
+            // tiles past the job's and slots past the window hold duplicates
+            const bool in = jq < nq && (qt0 + jq) * 16 + li < p.t;
+            const u16x8_t u = __builtin_bit_cast(u16x8_t, qb[jq]);
+            acc += in ? static_cast<double>(__uint_as_float(static_cast<uint32_t>(u[e]) << 16))
+                      : 0.0;
+        }
+        acc = row16_sum_exact(acc);
+        if (li == 0) dst[e] = acc;
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Routing of one (image, head, query region) row on one wave, R <= 64
 // [P4 §1.2; P1 §2.1 TopkRouting; P5 §五 ③-④].  Lane s holds the K mean of
-// region s; the row's Q mean is wave-uniform (scalar loads).  A[s] is the
-// sequential 32-term fp64 sum of dot32_seq.  k = 1: a wave arg-max; k > 1:
+// region s; lane d (and d + 32) holds dim d of the row's Q mean, read back
+// wave-uniform.  A[s] is the sequential 32-term fp64 sum of dot32_seq_lanes.  k = 1: a wave arg-max; k > 1:
 // lane s counts the entries that beat its own (greater, or equal with a
 // lower id) through the wave's LDS scratch row -- the counts are distinct,
 // and count < k places id s at that rank.  Writes each routed region's
 // base offset to off[rank] (LDS) and its id to out[rank] (global).
-__device__ __forceinline__ void route_row_wave(const Params& p, const double* __restrict__ qrow,
+__device__ __forceinline__ void route_row_wave(const Params& p, double qmean_lane,
                                                const double (&kreg)[kHeadDim], double* scratch,
                                                int* off, int32_t* __restrict__ out) {
     const int lane = threadIdx.x & 63;
-    const double a = dot32_seq(qrow, kreg);
+    const double a = dot32_seq_lanes(qmean_lane, kreg);
     // (Non-finite affinities leave the routing undefined, but every offset
     // the gather uses stays inside the map: the arg-max is clamped, and the
     // ranks' offsets are pre-filled with region 0 in case NaNs leave a rank
@@ -617,13 +648,28 @@ attend_kernel(const T* __restrict__ q, const T* __restrict__ v, const T* __restr
     }
     const int nhk = p.heads * p.k;
     const int wu = __builtin_amdgcn_readfirstlane(w);  // w, known wave-uniform
+    WaveJobs J(p, w);
+    bf16x8_t qb[kMaxQTiles];
+    // In-kernel routing on bf16 maps whose jobs are all first jobs: the Q
+    // means come from the first Q operands, which therefore load first.
+    constexpr bool kFixed = HS > 0 && WS > 0 && NW > 0 && HEADS > 0 && KTOP > 0;
+    const bool qm_here =
+        FUSED && VEC == 8 &&
+        (kFixed ? qmean_in_attend(true, true, HS * WS, HEADS) : p.qmean_attend != 0);
+    if constexpr (FUSED && VEC == 8)
+        load_q_operands(p, J, min(w, J.njobs - 1), reinterpret_cast<const uint16_t*>(q) + img, r,
+                        qb);
     int ridx = 0;
     double kreg[kHeadDim];
+    double qmean_lane = 0.0;  // routing waves: dim lane & 31 of the region's Q mean
     if constexpr (FUSED) {
         // In-kernel routing (R <= 64, heads <= 4): wave w routes this region
         // for head w; lane s holds the K mean of region s, loaded now with
         // everything else.
-        if (wu < p.heads) load_kmean(p, means, b * p.heads + wu, min(tid & 63, p.R - 1), kreg);
+        if (wu < p.heads) {
+            load_kmean(p, means, b * p.heads + wu, min(tid & 63, p.R - 1), kreg);
+            if (!qm_here) qmean_lane = means[qmean_index(p, b * p.heads + wu, r, tid & 31)];
+        }
     } else {
         // the routed region ids of this region, one per (head, rank); lanes
         // past heads * k re-read the last one
@@ -658,9 +704,7 @@ attend_kernel(const T* __restrict__ q, const T* __restrict__ v, const T* __restr
         hreg[u] = *reinterpret_cast<const uint4*>(v + img + (yc * p.W + xc) * p.C + pv * VEC);
         if (i < p.halo_pieces && y == yc && x == xc) hvalid |= 1u << u;
     }
-    WaveJobs J(p, w);
-    bf16x8_t qb[kMaxQTiles];
-    if constexpr (VEC == 8)
+    if constexpr (!FUSED && VEC == 8)
         load_q_operands(p, J, min(w, J.njobs - 1), reinterpret_cast<const uint16_t*>(q) + img, r,
                         qb);
     // The element offset of each routed region's first token goes to LDS.
@@ -669,9 +713,34 @@ attend_kernel(const T* __restrict__ q, const T* __restrict__ v, const T* __restr
     // thread stores: those past heads * k rewrite the last entry with the
     // value it already gets, so the store needs no branch.)
     if constexpr (FUSED) {
+        if (qm_here) {
+            // partial Q sums of every wave's first job, then wave h adds up
+            // those of head h's jobs (jobs h*G .. h*G + G - 1).  With one
+            // group per head, wave h's own job is head h's whole region: no
+            // other wave's sums are needed, and no workgroup barrier.
+            double* sQp = reinterpret_cast<double*>(smem + p.off_vt) + kWaves * 64;
+            const int G = kFixed ? job_shape(HS * WS, HEADS).G : J.G;
+            if (G == 1) {
+                if (wu < p.heads) {
+                    qmean_partial(p, J, wu, qb, sQp);
+                    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                    __builtin_amdgcn_wave_barrier();
+                    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+                    qmean_lane = mean_of(sQp[wu * kHeadDim + (tid & 31)], p.t);
+                }
+            } else {
+                if (wu < J.njobs) qmean_partial(p, J, wu, qb, sQp);
+                __syncthreads();
+                if (wu < p.heads) {
+                    double sum = 0.0;
+                    for (int j = 0; j < G; ++j) sum += sQp[(wu * G + j) * kHeadDim + (tid & 31)];
+                    qmean_lane = mean_of(sum, p.t);
+                }
+            }
+        }
         if (wu < p.heads) {
             const size_t row = (static_cast<size_t>(b) * p.heads + wu) * p.R + r;
-            route_row_wave(p, means + qmean_index(p, b * p.heads + wu, r, 0), kreg,
+            route_row_wave(p, qmean_lane, kreg,
                            reinterpret_cast<double*>(smem + p.off_vt) + wu * 64, sOff + wu * p.k,
                            routing + row * p.k);
         }
@@ -856,10 +925,11 @@ bool plan(Params& p, int B, int H, int W, int C, int heads, int n_win, int k, fl
         return static_cast<int>(o);
     };
     const long t = p.t;
-    // per-wave V^T staging (bf16 attention), also the per-wave scratch row of
-    // the in-kernel routing (64 doubles)
+    // per-wave V^T staging (bf16 attention); before the attention, the
+    // in-kernel routing's per-wave scratch rows (64 doubles) and the partial
+    // Q sums of each wave (32 doubles)
     p.off_vt = take(std::max(bf16 ? static_cast<long>(kWaves) * 32 * kVtStride * 2 : 0L,
-                             static_cast<long>(kWaves) * 64 * 8));
+                             static_cast<long>(kWaves) * (64 + kHeadDim) * 8));
     // The fixed bf16 shapes whose windows tile by 4x4 run LePE on MFMA with a
     // channel-planar halo; the others on VALU with an NHWC halo.
     p.lepe_mfma = bf16 && is_fixed_shape(p, bf16) && lepe_mfma_fits(p.hs, p.ws, heads);
@@ -885,10 +955,13 @@ bool plan(Params& p, int B, int H, int W, int C, int heads, int n_win, int k, fl
     }
     p.lds_bytes = static_cast<int>(off);
     p.table_items = p.lepe_mfma ? C * 40 : 0;
+    p.qmean_attend = qmean_in_attend(bf16, route_in_attend(p), p.t, heads) ? 1 : 0;
     {
+        // wave path: one wave per (region, tensor), four waves per workgroup
         const int nvec = C / vec;
         const bool wave_path = bf16 && 64 % nvec == 0;
-        p.pool_blocks = wave_path ? (B * p.R + 1) / 2 : B * p.R;
+        const int per_block = p.qmean_attend ? kWaves : kWaves / 2;
+        p.pool_blocks = wave_path ? (B * p.R + per_block - 1) / per_block : B * p.R;
     }
     p.pool_chunk = std::max(1, std::min(p.t, kPoolChunkBytes / (C * static_cast<int>(es))));
     // LDS of the pool kernel's staged path (fp32, or C/8 not dividing 64)

@@ -194,15 +194,9 @@ __device__ __forceinline__ uint2 lepe_toeplitz_entry(const float* __restrict__ l
 }
 
 // Q_r . K_s over the 32 dims of one head, left to right, each product rounded
-// before it is added -- the same IEEE operations as a plain fp64 loop.
-__device__ __forceinline__ double dot32_seq(const double* a, const double* b) {
-#pragma clang fp contract(off)
-    double s = 0.0;
-#pragma unroll
-    for (int d = 0; d < kHeadDim; ++d) s = s + a[d] * b[d];
-    return s;
-}
-// The same 32 terms appended to a running sum s0 (a longer sequential dot).
+// before it is added -- the same IEEE operations as a plain fp64 loop --
+// appended to a running sum s0 (s0 = 0 for one head; a longer sequential dot
+// over several heads otherwise).
 __device__ __forceinline__ double dot32_seq_from(double s0, const double* a, const double* b) {
 #pragma clang fp contract(off)
     double s = s0;
@@ -269,6 +263,52 @@ __device__ __forceinline__ void argmax_swap(double& best, int& bs) {
     best = a;
     bs = ia;
 }
+// Sum of x over the 16 lanes of each DPP row (partners lane ^ 1, lane ^ 2,
+// the other quad, the other half).  For exact sums only -- fp64 sums of bf16
+// values -- where the pairing cannot change the result; every lane of the
+// row ends with the same value.
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double x) {
+    const int2 u = __builtin_bit_cast(int2, x);
+    int2 o;
+    o.x = __builtin_amdgcn_mov_dpp(u.x, CTRL, 0xf, 0xf, false);
+    o.y = __builtin_amdgcn_mov_dpp(u.y, CTRL, 0xf, 0xf, false);
+    return __builtin_bit_cast(double, o);
+}
+__device__ __forceinline__ double row16_sum_exact(double x) {
+    x += dpp_f64<0xB1>(x);
+    x += dpp_f64<0x4E>(x);
+    x += dpp_f64<0x141>(x);
+    x += dpp_f64<0x140>(x);
+    return x;
+}
+// x of lane ^ J (J = 1, 2, 4, 8) by DPP row permutations: quad_perm for 1
+// and 2; for 4, the quad reversal (lane ^ 3) after row_half_mirror (lane ^ 7);
+// for 8, row_mirror (lane ^ 15) after row_half_mirror.
+template <int J>
+__device__ __forceinline__ int lane_xor_dpp(int x) {
+    static_assert(J == 1 || J == 2 || J == 4 || J == 8, "DPP partners within a row of 16");
+    if constexpr (J == 1) return __builtin_amdgcn_mov_dpp(x, 0xB1, 0xf, 0xf, false);
+    if constexpr (J == 2) return __builtin_amdgcn_mov_dpp(x, 0x4E, 0xf, 0xf, false);
+    const int m7 = __builtin_amdgcn_mov_dpp(x, 0x141, 0xf, 0xf, false);
+    if constexpr (J == 4) return __builtin_amdgcn_mov_dpp(m7, 0x1B, 0xf, 0xf, false);
+    return __builtin_amdgcn_mov_dpp(m7, 0x140, 0xf, 0xf, false);
+}
+// Lane `src`'s x, wave-uniform.
+__device__ __forceinline__ double readlane_f64(double x, int src) {
+    const int2 u = __builtin_bit_cast(int2, x);
+    return __builtin_bit_cast(double, int2{__builtin_amdgcn_readlane(u.x, src),
+                                           __builtin_amdgcn_readlane(u.y, src)});
+}
+// dot32_seq_from(0, a, b) with a spread over lanes: lane d holds a[d].
+__device__ __forceinline__ double dot32_seq_lanes(double a_lane, const double (&b)[kHeadDim]) {
+#pragma clang fp contract(off)
+    double s = 0.0;
+#pragma unroll
+    for (int d = 0; d < kHeadDim; ++d) s = s + readlane_f64(a_lane, d) * b[d];
+    return s;
+}
+
 __device__ __forceinline__ void wave_argmax(double& best, int& bs) {
     argmax_dpp<0xB1>(best, bs);   // quad_perm [1,0,3,2]: lane ^ 1
     argmax_dpp<0x4E>(best, bs);   // quad_perm [2,3,0,1]: lane ^ 2

@@ -44,6 +44,8 @@ struct Params {
     int table_items; // 8-byte entries of the MFMA LePE Toeplitz operand table (0: none)
     // region-pool kernel
     int pool_blocks; // workgroups computing means (the table follows them)
+    int qmean_attend; // 1: the attention kernel sums the Q means itself; the
+                      // pool kernel then computes only the K means
     int pool_chunk;  // staged path: tokens staged per step
     int pool_lds_bytes;
 };
@@ -69,6 +71,32 @@ constexpr bool route_fused(int R, int heads) {
     return R <= 64 && heads <= kWaves;
 }
 inline bool route_in_attend(const Params& p) { return !p.shared && route_fused(p.R, p.heads); }
+
+// How the attention kernel splits a region's queries into wave jobs: QT tiles
+// of 16 queries per head, in G groups of tpg tiles (at most kMaxQTiles); a
+// job is one (head, group), heads * G jobs in all, dealt to the waves
+// round-robin.  Heads with fewer than kWaves waves between them split their
+// tiles over the spare waves.
+struct JobShape {
+    int QT, tpg, G, njobs;
+};
+constexpr JobShape job_shape(int t, int heads) {
+    const int QT = (t + 15) / 16;
+    const int wph = kWaves / heads > 1 ? kWaves / heads : 1;
+    const int g_spread = wph < QT ? wph : QT;
+    const int g_fit = (QT + kMaxQTiles - 1) / kMaxQTiles;
+    const int g0 = g_spread > g_fit ? g_spread : g_fit;
+    const int tpg = (QT + g0 - 1) / g0;
+    const int G = (QT + tpg - 1) / tpg;  // every group non-empty
+    return JobShape{QT, tpg, G, heads * G};
+}
+// bf16 maps routed inside the attention kernel whose jobs are each some
+// wave's first job hold every query of the region in the waves' first Q
+// operands, so the kernel sums the Q means from them (exactly, in fp64) and
+// the pool kernel reads only K.
+constexpr bool qmean_in_attend(bool bf16, bool fused, int t, int heads) {
+    return bf16 && fused && job_shape(t, heads).njobs <= kWaves;
+}
 
 //   kg, vg: the K and V the attention gathers from -- k and v, or their
 //   downsampled copies ([B, kH, kW, C]) when kv_ratio > 1; v still feeds LePE.

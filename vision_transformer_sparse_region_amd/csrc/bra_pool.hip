@@ -11,7 +11,8 @@ namespace bra {
 namespace {
 
 // ---------------------------------------------------------------------------
-// Region means of Q and K (fp64).
+// Region means of Q and K (fp64); of K alone when the attention kernel sums
+// the Q means itself (p.qmean_attend).
 //  bf16, C/8 dividing 64: one wave per (region, tensor).  Lane (pv, tg) holds
 //        fp64 sums of channels 8pv..8pv+7 over every (64/(C/8))-th token of the
 //        window; the lanes of one pv are then combined with shuffles.  A bf16
@@ -40,13 +41,14 @@ __global__ __launch_bounds__(kThreads) void pool_qk_kernel(const T* __restrict__
     const int nvec = p.C / VEC;
 
     if (VEC == 8 && 64 % nvec == 0) {
-        // two regions per workgroup: wave w -> region 2*blk + (w >> 1), tensor w & 1
+        // Q and K: two regions per workgroup, wave w -> region 2*blk + (w >> 1),
+        // tensor w & 1; K alone: four regions, wave w -> region 4*blk + w
         const int lane = tid & 63, w = tid >> 6;
         const int blk = xcd_logical_block(blockIdx.x, p.pool_blocks);
-        const int region = 2 * blk + (w >> 1);
+        const int region = p.qmean_attend ? kWaves * blk + w : 2 * blk + (w >> 1);
         if (region >= p.B * p.R) return;
         const int b = region / p.R, r = region - b * p.R;
-        const int tensor = w & 1;
+        const int tensor = p.qmean_attend ? 1 : w & 1;
         const T* src = (tensor == 0 ? q : k) + static_cast<size_t>(b) * p.H * p.W * p.C;
         const int pv = lane % nvec, tg = lane / nvec, TG = 64 / nvec;
         double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
@@ -84,7 +86,7 @@ __global__ __launch_bounds__(kThreads) void pool_qk_kernel(const T* __restrict__
     const int blk = xcd_logical_block(blockIdx.x, p.pool_blocks);
     const int b = blk / p.R, r = blk - b * p.R;
     const size_t img = static_cast<size_t>(b) * p.H * p.W * p.C;
-    for (int tensor = 0; tensor < 2; ++tensor) {
+    for (int tensor = p.qmean_attend ? 1 : 0; tensor < 2; ++tensor) {
         const T* src = (tensor == 0 ? q : k) + img;
         double acc[kMaxChannels / kThreads] = {};
         for (int t0 = 0; t0 < p.t; t0 += p.pool_chunk) {

@@ -1,13 +1,25 @@
 // bra_route.hip -- region-level routing [P4 §1.2; P1 §2.1 TopkRouting;
 // P5 §五 ③-④] (page keys in bra_device.h).
 //
-// One workgroup per (image, head, chunk of query regions) -- per image with
-// head-shared routing [P1 §2.2; P2 §2.1; P3 §2.1] -- : the fp64 affinity
-// A[r][s] = Qbar_r . Kbar_s of each row r of the chunk against every region
-// s (over one head's 32 dims, or all C channels when shared), then the k
-// largest entries of each row, in descending order with exact ties to the
-// lower region id.  The head_dim^-0.5 factor the pages apply to
-// the affinity does not change the order and is left out.
+// For each (image, head) -- each image with head-shared routing [P1 §2.2;
+// P2 §2.1; P3 §2.1] -- and each query region r: the fp64 affinity
+// A[r][s] = Qbar_r . Kbar_s against every region s (over one head's 32 dims,
+// or all C channels when shared), then the k largest entries of the row, in
+// descending order with exact ties to the lower region id.  The
+// head_dim^-0.5 factor the pages apply to the affinity does not change the
+// order and is left out.
+//
+// Every entry is the sequential fp64 sum of dot32_seq_from (with shared
+// routing the heads follow one another in one running sum, c = h * 32 + d).
+// A lane holds the K mean of one region s in registers, the query rows are
+// wave-uniform (scalar loads), and kRouteChains rows run as independent
+// chains.
+//   R <= 64: a wave owns kRouteChains rows from the affinity to the routed
+//            ids, in registers: the arg-max (k = 1), or a bitonic sort of
+//            each row over the wave's lanes (k > 1).  No LDS, no barrier.
+//   R > 64:  the lanes of a row span SPAN/64 waves; the rows go through LDS
+//            to one wave each, which keeps the k best by a bitonic sort whose
+//            cross-lane partners come from DPP and permlane swaps.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -17,26 +29,124 @@
 namespace bra {
 namespace {
 
-// Region-span of the affinity phase: threads tid % SPAN own region tid % SPAN,
-// SPAN = the power of two >= R (64, 128 or 256 = kMaxRegions).
+constexpr int kRouteChains = 4;  // query rows whose dots run interleaved
+
+// Region-span of the large-map kernel: threads tid % SPAN own region tid % SPAN,
+// SPAN = the power of two >= R (128 or 256 = kMaxRegions).
 __host__ __device__ constexpr int route_span(int R) { return R <= 64 ? 64 : R <= 128 ? 128 : 256; }
-// Query rows a workgroup routes: 4 per wave for R <= 64, else 2 per wave.
-__host__ __device__ constexpr int route_rows_per_wave(int span) { return span == 64 ? 4 : 2; }
+// Query rows a workgroup routes: kRouteChains per wave for R <= 64, else 2 per wave.
+__host__ __device__ constexpr int route_rows(int span) {
+    return span == 64 ? kWaves * kRouteChains : kWaves * 2;
+}
 // fp64 row stride of the affinity tile (even, so pairs of entries are 16-byte aligned).
 __host__ __device__ constexpr int route_row_stride(int R) { return (R + 1) & ~1; }
 
+// (a, ia) ranks before (b, ib): a larger value, or an equal one with a lower
+// id.  Bitwise, not short-circuit: no branch per comparison.
 __device__ __forceinline__ bool beats(double a, int ia, double b, int ib) {
-    return a > b || (a == b && ia < ib);
+    return (a > b) | ((a == b) & (ia < ib));
 }
 
-// Top-k of NRW rows at once by wave-wide bitonic sorts, best first (affinity
-// descending, region id ascending).  Lane `lane` holds elements
-// lane * E .. lane * E + E - 1 of every row; partners within a lane swap in
-// registers, across lanes through shuffles.  Padding elements (ids >= R)
-// carry -inf and sort last.  Writes the first k ids of row j to dst[j].
+// acc[j] += q[j] . k over the 32 dims of one head, left to right, each
+// product rounded before it is added (dot32_seq_from, N rows at once).
+template <int N>
+__device__ __forceinline__ void dots_seq(double (&acc)[N], const double* const (&q)[N],
+                                         const double (&k)[kHeadDim]) {
+#pragma clang fp contract(off)
+#pragma unroll
+    for (int d = 0; d < kHeadDim; ++d)
+#pragma unroll
+        for (int j = 0; j < N; ++j) acc[j] = acc[j] + q[j][d] * k[d];
+}
+
+// ---------------------------------------------------------------------------
+// Bitonic top-k of NRW rows at once, best first (affinity descending, region
+// id ascending).  Lane `lane` holds elements lane * E .. lane * E + E - 1 of
+// every row; partners within a lane swap in registers, partners across lanes
+// come from DPP (lane ^ 1 .. lane ^ 8) or a permlane swap (lane ^ 16, ^ 32).
+// Padding elements (ids >= R) carry -inf and sort last.
+
+// This lane's pair {own, partner at lane ^ LJ} as (a, ia), (b, ib); the
+// permlane swaps return the two in an order that depends on the lane, which
+// a compare-exchange does not need.
+template <int LJ>
+__device__ __forceinline__ void lane_pair(double v, int ix, double& a, int& ia, double& b,
+                                          int& ib) {
+    const int2 u = __builtin_bit_cast(int2, v);
+    if constexpr (LJ < 16) {
+        a = v;
+        ia = ix;
+        b = __builtin_bit_cast(double, int2{lane_xor_dpp<LJ>(u.x), lane_xor_dpp<LJ>(u.y)});
+        ib = lane_xor_dpp<LJ>(ix);
+    } else {
+        const auto lo = LJ == 16 ? __builtin_amdgcn_permlane16_swap(u.x, u.x, false, false)
+                                 : __builtin_amdgcn_permlane32_swap(u.x, u.x, false, false);
+        const auto hi = LJ == 16 ? __builtin_amdgcn_permlane16_swap(u.y, u.y, false, false)
+                                 : __builtin_amdgcn_permlane32_swap(u.y, u.y, false, false);
+        const auto ii = LJ == 16 ? __builtin_amdgcn_permlane16_swap(ix, ix, false, false)
+                                 : __builtin_amdgcn_permlane32_swap(ix, ix, false, false);
+        a = __builtin_bit_cast(double, int2{static_cast<int>(lo[0]), static_cast<int>(hi[0])});
+        ia = static_cast<int>(ii[0]);
+        b = __builtin_bit_cast(double, int2{static_cast<int>(lo[1]), static_cast<int>(hi[1])});
+        ib = static_cast<int>(ii[1]);
+    }
+}
+
+// One half-cleaner step of distance J inside bitonic blocks of SIZE
+// elements, then the steps J/2 .. 1.  Position i keeps the better of the
+// pair when (i & J) == 0 and (i & SIZE) == 0 agree, else the worse.
+template <int E, int NRW, int SIZE, int J>
+__device__ __forceinline__ void bitonic_steps(double (&v)[NRW][E], int (&ix)[NRW][E], int lane) {
+    if constexpr (J < E) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const int pe = e ^ J;
+            if (pe > e) {
+                const bool dir = ((lane * E + e) & SIZE) == 0;
+#pragma unroll
+                for (int r = 0; r < NRW; ++r) {
+                    if (beats(v[r][e], ix[r][e], v[r][pe], ix[r][pe]) != dir) {
+                        const double tv = v[r][e];
+                        v[r][e] = v[r][pe];
+                        v[r][pe] = tv;
+                        const int ti = ix[r][e];
+                        ix[r][e] = ix[r][pe];
+                        ix[r][pe] = ti;
+                    }
+                }
+            }
+        }
+    } else {
+        constexpr int LJ = J / E;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const int i = lane * E + e;
+            const bool keep_better = ((i & J) == 0) == ((i & SIZE) == 0);
+#pragma unroll
+            for (int r = 0; r < NRW; ++r) {
+                double a, b;
+                int ia, ib;
+                lane_pair<LJ>(v[r][e], ix[r][e], a, ia, b, ib);
+                const bool take_a = beats(a, ia, b, ib) == keep_better;
+                v[r][e] = take_a ? a : b;
+                ix[r][e] = take_a ? ia : ib;
+            }
+        }
+    }
+    if constexpr (J > 1) bitonic_steps<E, NRW, SIZE, J / 2>(v, ix, lane);
+}
+
+template <int E, int NRW, int SIZE>
+__device__ __forceinline__ void bitonic_sort(double (&v)[NRW][E], int (&ix)[NRW][E], int lane) {
+    bitonic_steps<E, NRW, SIZE, SIZE / 2>(v, ix, lane);
+    if constexpr (SIZE < 64 * E) bitonic_sort<E, NRW, SIZE * 2>(v, ix, lane);
+}
+
+// Writes the first k ids of row r to dst[r] (rows with live[r]).
 template <int E, int NRW>
 __device__ __forceinline__ void wave_topk_bitonic(const double* const (&rows)[NRW], int R, int k,
-                                                  int32_t* const (&dst)[NRW], const bool (&live)[NRW]) {
+                                                  int32_t* const (&dst)[NRW],
+                                                  const bool (&live)[NRW]) {
     const int lane = threadIdx.x & 63;
     double v[NRW][E];
     int ix[NRW][E];
@@ -49,50 +159,7 @@ __device__ __forceinline__ void wave_topk_bitonic(const double* const (&rows)[NR
             ix[r][e] = i;
         }
     }
-#pragma unroll
-    for (int size = 2; size <= 64 * E; size <<= 1) {
-#pragma unroll
-        for (int j = size >> 1; j > 0; j >>= 1) {
-            if (j < E) {
-#pragma unroll
-                for (int r = 0; r < NRW; ++r) {
-#pragma unroll
-                    for (int e = 0; e < E; ++e) {
-                        const int pe = e ^ j;
-                        if (pe > e) {
-                            const bool dir = ((lane * E + e) & size) == 0;
-                            if (beats(v[r][e], ix[r][e], v[r][pe], ix[r][pe]) != dir) {
-                                const double tv = v[r][e];
-                                v[r][e] = v[r][pe];
-                                v[r][pe] = tv;
-                                const int ti = ix[r][e];
-                                ix[r][e] = ix[r][pe];
-                                ix[r][pe] = ti;
-                            }
-                        }
-                    }
-                }
-            } else {
-                const int lj = j / E;
-#pragma unroll
-                for (int r = 0; r < NRW; ++r) {
-#pragma unroll
-                    for (int e = 0; e < E; ++e) {
-                        const double ov = __shfl_xor(v[r][e], lj);
-                        const int oi = __shfl_xor(ix[r][e], lj);
-                        const int i = lane * E + e;
-                        const bool lower = (i & j) == 0;
-                        const bool dir = (i & size) == 0;
-                        const bool mine = beats(v[r][e], ix[r][e], ov, oi);
-                        if ((lower == dir) != mine) {
-                            v[r][e] = ov;
-                            ix[r][e] = oi;
-                        }
-                    }
-                }
-            }
-        }
-    }
+    bitonic_sort<E, NRW, 2>(v, ix, lane);
 #pragma unroll
     for (int r = 0; r < NRW; ++r) {
 #pragma unroll
@@ -103,65 +170,136 @@ __device__ __forceinline__ void wave_topk_bitonic(const double* const (&rows)[NR
     }
 }
 
-// NW > 0 / KTOP > 0 fold the region count / k at compile time.  SPAN is
-// route_span(R).  Rows of a chunk go to waves round-robin (row = w + 4j).
-template <int NW, int KTOP, int SPAN>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))) void route_kernel(const double* __restrict__ means,
-                                                         int32_t* __restrict__ idx_out,
-                                                         Params p_in) {
+// ---------------------------------------------------------------------------
+// R <= 64.  Wave w of workgroup (routing group rg, chunk) routes rows
+// r0 .. r0 + kRouteChains - 1, r0 = (chunk * kWaves + w) * kRouteChains.
+template <int NW, int KTOP>
+__global__ __launch_bounds__(kThreads) void route_small_kernel(const double* __restrict__ means,
+                                                               int32_t* __restrict__ idx_out,
+                                                               Params p_in) {
     Params p = p_in;
     if constexpr (NW > 0) {
         p.n = NW;
         p.R = NW * NW;
     }
     if constexpr (KTOP > 0) p.k = KTOP;
-    constexpr int RPW = route_rows_per_wave(SPAN);
-    constexpr int ROWS = kWaves * RPW;
-    constexpr int G = kThreads / SPAN;  // row groups of the affinity phase
+    constexpr int ROWS = route_rows(64);
+    const int R = p.R, lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int nchunk = (R + ROWS - 1) / ROWS;
+    // rg: the routing's (image, head) pair, or the image with shared routing
+    const int rg = blockIdx.x / nchunk, chunk = blockIdx.x - rg * nchunk;
+    const int r0 = chunk * ROWS + w * kRouteChains;
+    if (r0 >= R) return;  // wave-uniform; nothing below synchronises waves
+    const int h0 = p.shared ? rg * p.heads : rg;  // first (image, head) summed
+    const int nh = p.shared ? p.heads : 1;        // heads summed into one affinity
+
+    double acc[kRouteChains];
+#pragma unroll
+    for (int j = 0; j < kRouteChains; ++j) acc[j] = 0.0;
+    for (int hh = 0; hh < nh; ++hh) {
+        const int bh = h0 + hh;
+        double kreg[kHeadDim];
+        load_kmean(p, means, bh, min(lane, R - 1), kreg);
+        // rows past the map repeat the last one (never written)
+        const double* q[kRouteChains];
+#pragma unroll
+        for (int j = 0; j < kRouteChains; ++j) q[j] = means + qmean_index(p, bh, min(r0 + j, R - 1), 0);
+        dots_seq<kRouteChains>(acc, q, kreg);
+    }
+
+    int32_t* const base = idx_out + (static_cast<size_t>(rg) * R + r0) * p.k;
+    const int nrows = min(kRouteChains, R - r0);
+    if (p.k == 1) {
+        // (a NaN row leaves the arg-max undefined; the id is clamped into range)
+#pragma unroll
+        for (int j = 0; j < kRouteChains; ++j) {
+            double best = lane < R ? acc[j] : -INFINITY;
+            int bs = lane < R ? lane : 0x7fffffff;
+            wave_argmax(best, bs);
+            if (lane == 0 && j < nrows) base[j] = min(max(bs, 0), R - 1);
+        }
+    } else {
+        // one bitonic sort per row, lane s holding entry s
+        double v[kRouteChains][1];
+        int ix[kRouteChains][1];
+#pragma unroll
+        for (int j = 0; j < kRouteChains; ++j) {
+            v[j][0] = lane < R ? acc[j] : -INFINITY;
+            ix[j][0] = lane;
+        }
+        bitonic_sort<1, kRouteChains, 2>(v, ix, lane);
+#pragma unroll
+        for (int j = 0; j < kRouteChains; ++j)
+            if (j < nrows && lane < p.k) base[j * p.k + lane] = ix[j][0];
+    }
+}
+
+// ---------------------------------------------------------------------------
+// R > 64 (SPAN = 128 or 256).  Affinity: thread (s, g) = (tid % SPAN,
+// tid / SPAN) keeps K mean s in registers and takes its dots with query rows
+// g, g + G, ... of the chunk (G = kThreads / SPAN row groups; g is
+// wave-uniform), kRouteChains at a time; the entries go to LDS.  Top-k: wave
+// w takes rows w and w + kWaves.
+template <int NW, int KTOP, int SPAN>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))) void
+route_large_kernel(const double* __restrict__ means, int32_t* __restrict__ idx_out, Params p_in) {
+    Params p = p_in;
+    if constexpr (NW > 0) {
+        p.n = NW;
+        p.R = NW * NW;
+    }
+    if constexpr (KTOP > 0) p.k = KTOP;
+    constexpr int ROWS = route_rows(SPAN);
+    constexpr int RPW = ROWS / kWaves;  // top-k rows per wave
+    constexpr int G = kThreads / SPAN;
     constexpr int NR = ROWS / G;        // rows per thread in the affinity phase
-    __shared__ double sQ[ROWS * kHeadDim];
+    static_assert(NR % kRouteChains == 0, "rows per thread come in whole chain groups");
     extern __shared__ __align__(16) unsigned char smem[];
     double* sA = reinterpret_cast<double*>(smem);  // [ROWS][RS]
 
     const int R = p.R, RS = route_row_stride(R);
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int nchunk = (R + ROWS - 1) / ROWS;
-    // rg: the routing's (image, head) pair, or the image with shared routing
     const int rg = blockIdx.x / nchunk, chunk = blockIdx.x - rg * nchunk;
     const int r0 = chunk * ROWS, nrows = min(ROWS, R - r0);
-    const int h0 = p.shared ? rg * p.heads : rg;          // first (image, head) summed
-    const int nh = p.shared ? p.heads : 1;                // heads summed into one affinity
+    const int h0 = p.shared ? rg * p.heads : rg;
+    const int nh = p.shared ? p.heads : 1;
 
-    // Affinity.  Thread (s, g) keeps K mean s in registers and takes its dot
-    // with query rows g, g + G, ...; rows past the chunk read zeros.  With
-    // shared routing the heads follow one another in one running sum per
-    // entry (kept in sA), so every entry is the sequential sum over all C
-    // channels in the order c = h * 32 + d.
-    const int s = tid % SPAN, g = tid / SPAN;
+    const int s = tid % SPAN;
+    const int g = __builtin_amdgcn_readfirstlane(tid / SPAN);
+    double acc[NR];
+#pragma unroll
+    for (int j = 0; j < NR; ++j) acc[j] = 0.0;
     for (int hh = 0; hh < nh; ++hh) {
         const int bh = h0 + hh;
-        const double* qbar = means + qmean_index(p, bh, 0, 0);  // [R][32]
         double kreg[kHeadDim];
         load_kmean(p, means, bh, min(s, R - 1), kreg);
-        for (int i = tid; i < ROWS * kHeadDim / 2; i += kThreads) {
-            const bool in = i < nrows * kHeadDim / 2;
-            reinterpret_cast<double2*>(sQ)[i] =
-                in ? reinterpret_cast<const double2*>(qbar + r0 * kHeadDim)[i]
-                   : double2{0.0, 0.0};
+#pragma unroll
+        for (int c = 0; c < NR / kRouteChains; ++c) {
+            const double* q[kRouteChains];
+            double part[kRouteChains];
+#pragma unroll
+            for (int j = 0; j < kRouteChains; ++j) {
+                const int row = g + G * (c * kRouteChains + j);
+                q[j] = means + qmean_index(p, bh, min(r0 + row, R - 1), 0);
+                part[j] = acc[c * kRouteChains + j];
+            }
+            dots_seq<kRouteChains>(part, q, kreg);
+#pragma unroll
+            for (int j = 0; j < kRouteChains; ++j) acc[c * kRouteChains + j] = part[j];
         }
-        __syncthreads();
-#pragma unroll 1
+    }
+    if (s < R) {
+#pragma unroll
         for (int j = 0; j < NR; ++j) {
             const int row = g + G * j;
-            if (s < R && row < nrows) {
-                const double a0 = hh == 0 ? 0.0 : sA[row * RS + s];
-                sA[row * RS + s] = dot32_seq_from(a0, sQ + row * kHeadDim, kreg);
-            }
+            if (row < nrows) sA[row * RS + s] = acc[j];
         }
-        __syncthreads();
     }
+    __syncthreads();
 
-    // Top-k, rows w, w + 4, ... of the chunk on wave w.
     int32_t* const base = idx_out + (static_cast<size_t>(rg) * R + r0) * p.k;
     if (p.k == 1) {
         double best[RPW];
@@ -184,30 +322,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
 #pragma unroll
         for (int j = 0; j < RPW; ++j) {
             const int row = w + kWaves * j;
-            if (lane == 0 && row < nrows) base[row] = bs[j];
-        }
-    } else if constexpr (SPAN == 64) {
-        // R <= 64: lane i ranks element i of each row against the whole row
-        // (broadcast reads); ranks are distinct, and rank < k places the id.
-        double mine[RPW];
-        int rank[RPW];
-#pragma unroll
-        for (int j = 0; j < RPW; ++j) {
-            const double* row = sA + min(w + kWaves * j, nrows - 1) * RS;
-            mine[j] = lane < R ? row[lane] : -INFINITY;
-            rank[j] = 0;
-        }
-        for (int x = 0; x < R; ++x) {
-#pragma unroll
-            for (int j = 0; j < RPW; ++j) {
-                const double a = sA[min(w + kWaves * j, nrows - 1) * RS + x];
-                rank[j] += (a > mine[j] || (a == mine[j] && x < lane)) ? 1 : 0;
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < RPW; ++j) {
-            const int row = w + kWaves * j;
-            if (row < nrows && lane < R && rank[j] < p.k) base[row * p.k + rank[j]] = lane;
+            if (lane == 0 && row < nrows) base[row] = min(max(bs[j], 0), R - 1);
         }
     } else {
         constexpr int E = SPAN / 64;
@@ -225,29 +340,45 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
     }
 }
 
+template <int NW, int KTOP>
+void launch_route_shape(const Params& p, const double* means, int32_t* idx, hipStream_t stream) {
+    const int span = route_span(p.R);
+    const int rows = route_rows(span);
+    const int nchunk = (p.R + rows - 1) / rows;
+    const dim3 grid(p.B * p.rheads * nchunk), block(kThreads);
+    const int lds = rows * route_row_stride(p.R) * 8;
+    // a fixed shape instantiates only its own span
+    constexpr int kSpan = NW > 0 ? route_span(NW * NW) : 0;
+    if constexpr (kSpan == 0 || kSpan == 64)
+        if (span == 64) {
+            hipLaunchKernelGGL((route_small_kernel<NW, KTOP>), grid, block, 0, stream, means,
+                               idx, p);
+            return;
+        }
+    if constexpr (kSpan == 0 || kSpan == 128)
+        if (span == 128) {
+            hipLaunchKernelGGL((route_large_kernel<NW, KTOP, 128>), grid, block, lds, stream,
+                               means, idx, p);
+            return;
+        }
+    if constexpr (kSpan == 0 || kSpan == 256)
+        if (span == 256)
+            hipLaunchKernelGGL((route_large_kernel<NW, KTOP, 256>), grid, block, lds, stream,
+                               means, idx, p);
+}
+
 }  // namespace
 
 hipError_t launch_route(const Params& p, bool bf16, const double* means, int32_t* idx,
                         hipStream_t stream) {
-    const int span = route_span(p.R);
-    const int rows = kWaves * route_rows_per_wave(span);
-    const int nchunk = (p.R + rows - 1) / rows;
-    const dim3 grid(p.B * p.rheads * nchunk), block(kThreads);
-    const int lds = rows * route_row_stride(p.R) * 8;
-#define BRA_ROUTE(T, HS, WS, NW, HEADS, KTOP)                                                \
-    if (matches(Inst<T, HS, WS, NW, HEADS, KTOP>::key, p, bf16, true)) {                    \
-        hipLaunchKernelGGL((route_kernel<NW, KTOP, route_span(NW * NW)>), grid, block, lds, \
-                           stream, means, idx, p);                                          \
-        return hipGetLastError();                                                           \
+#define BRA_ROUTE(T, HS, WS, NW, HEADS, KTOP)                             \
+    if (matches(Inst<T, HS, WS, NW, HEADS, KTOP>::key, p, bf16, true)) { \
+        launch_route_shape<NW, KTOP>(p, means, idx, stream);             \
+        return hipGetLastError();                                        \
     }
     BRA_FOR_EACH_SHAPE(BRA_ROUTE)
 #undef BRA_ROUTE
-    if (span == 64)
-        hipLaunchKernelGGL((route_kernel<0, 0, 64>), grid, block, lds, stream, means, idx, p);
-    else if (span == 128)
-        hipLaunchKernelGGL((route_kernel<0, 0, 128>), grid, block, lds, stream, means, idx, p);
-    else
-        hipLaunchKernelGGL((route_kernel<0, 0, 256>), grid, block, lds, stream, means, idx, p);
+    launch_route_shape<0, 0>(p, means, idx, stream);
     return hipGetLastError();
 }
 
