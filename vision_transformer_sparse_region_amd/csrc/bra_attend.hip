@@ -551,20 +551,18 @@ __device__ __forceinline__ void qmean_partial(const Params& p, const WaveJobs& J
 // Routing of one (image, head, query region) row on one wave, R <= 64
 // [P4 §1.2; P1 §2.1 TopkRouting; P5 §五 ③-④].  Lane s holds the K mean of
 // region s; lane d (and d + 32) holds dim d of the row's Q mean, read back
-// wave-uniform.  A[s] is the sequential 32-term fp64 sum of dot32_seq_lanes.  k = 1: a wave arg-max; k > 1:
-// lane s counts the entries that beat its own (greater, or equal with a
-// lower id) through the wave's LDS scratch row -- the counts are distinct,
-// and count < k places id s at that rank.  Writes each routed region's
-// base offset to off[rank] (LDS) and its id to out[rank] (global).
+// wave-uniform.  A[s] is the sequential 32-term fp64 sum of dot32_seq_lanes.
+// k = 1: a wave arg-max; k > 1: a bitonic sort of the row over the wave, in
+// registers (affinity descending, exact ties to the lower id).  Writes each
+// routed region's base offset to off[rank] (LDS) and its id to out[rank]
+// (global).
 __device__ __forceinline__ void route_row_wave(const Params& p, double qmean_lane,
-                                               const double (&kreg)[kHeadDim], double* scratch,
-                                               int* off, int32_t* __restrict__ out) {
+                                               const double (&kreg)[kHeadDim], int* off,
+                                               int32_t* __restrict__ out) {
     const int lane = threadIdx.x & 63;
     const double a = dot32_seq_lanes(qmean_lane, kreg);
     // (Non-finite affinities leave the routing undefined, but every offset
-    // the gather uses stays inside the map: the arg-max is clamped, and the
-    // ranks' offsets are pre-filled with region 0 in case NaNs leave a rank
-    // unclaimed.)
+    // the gather uses stays inside the map: the ids are clamped.)
     if (p.k == 1) {
         double best = lane < p.R ? a : -INFINITY;
         int bs = lane < p.R ? lane : 0x7fffffff;
@@ -575,24 +573,16 @@ __device__ __forceinline__ void route_row_wave(const Params& p, double qmean_lan
             out[0] = bs;
         }
     } else {
-        if (lane < p.k) off[lane] = 0;  // region 0's base in either map
-        scratch[lane] = a;
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        int rank = 0;
-        for (int x = 0; x < p.R; ++x) {
-            const double o = scratch[x];
-            rank += (o > a || (o == a && x < lane)) ? 1 : 0;
+        // a bitonic sort of the row over the wave (lane s holds entry s,
+        // lanes past R -inf); lane j < k then holds the id of rank j
+        double v[1][1] = {{lane < p.R ? a : -INFINITY}};
+        int ix[1][1] = {{lane}};
+        bitonic_sort<1, 1, 2>(v, ix, lane);
+        if (lane < p.k) {
+            const int id = min(max(ix[0][0], 0), p.R - 1);
+            off[lane] = region_base_kv(p, id);
+            out[lane] = id;
         }
-        if (lane < p.R && rank < p.k) {
-            off[rank] = region_base_kv(p, lane);
-            out[rank] = lane;
-        }
-        // the next row's writes must not pass this row's reads
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
 }
 
@@ -718,7 +708,7 @@ attend_kernel(const T* __restrict__ q, const T* __restrict__ v, const T* __restr
             // those of head h's jobs (jobs h*G .. h*G + G - 1).  With one
             // group per head, wave h's own job is head h's whole region: no
             // other wave's sums are needed, and no workgroup barrier.
-            double* sQp = reinterpret_cast<double*>(smem + p.off_vt) + kWaves * 64;
+            double* sQp = reinterpret_cast<double*>(smem + p.off_vt);  // [kWaves][32]
             const int G = kFixed ? job_shape(HS * WS, HEADS).G : J.G;
             if (G == 1) {
                 if (wu < p.heads) {
@@ -740,9 +730,7 @@ attend_kernel(const T* __restrict__ q, const T* __restrict__ v, const T* __restr
         }
         if (wu < p.heads) {
             const size_t row = (static_cast<size_t>(b) * p.heads + wu) * p.R + r;
-            route_row_wave(p, qmean_lane, kreg,
-                           reinterpret_cast<double*>(smem + p.off_vt) + wu * 64, sOff + wu * p.k,
-                           routing + row * p.k);
+            route_row_wave(p, qmean_lane, kreg, sOff + wu * p.k, routing + row * p.k);
         }
         if constexpr (kLepeMfma) lepe_mfma_load<HS, WS, HEADS>(lepe_table, lepe_bias, lop);
     } else {
@@ -926,10 +914,9 @@ bool plan(Params& p, int B, int H, int W, int C, int heads, int n_win, int k, fl
     };
     const long t = p.t;
     // per-wave V^T staging (bf16 attention); before the attention, the
-    // in-kernel routing's per-wave scratch rows (64 doubles) and the partial
-    // Q sums of each wave (32 doubles)
+    // partial Q sums of each wave (32 doubles)
     p.off_vt = take(std::max(bf16 ? static_cast<long>(kWaves) * 32 * kVtStride * 2 : 0L,
-                             static_cast<long>(kWaves) * (64 + kHeadDim) * 8));
+                             static_cast<long>(kWaves) * kHeadDim * 8));
     // The fixed bf16 shapes whose windows tile by 4x4 run LePE on MFMA with a
     // channel-planar halo; the others on VALU with an NHWC halo.
     p.lepe_mfma = bf16 && is_fixed_shape(p, bf16) && lepe_mfma_fits(p.hs, p.ws, heads);

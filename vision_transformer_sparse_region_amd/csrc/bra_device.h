@@ -318,5 +318,93 @@ __device__ __forceinline__ void wave_argmax(double& best, int& bs) {
     argmax_swap<false>(best, bs);
 }
 
+// (a, ia) ranks before (b, ib): a larger value, or an equal one with a lower
+// id.  Bitwise, not short-circuit: no branch per comparison.
+__device__ __forceinline__ bool beats(double a, int ia, double b, int ib) {
+    return (a > b) | ((a == b) & (ia < ib));
+}
+
+// ---------------------------------------------------------------------------
+// Bitonic sort of NRW rows at once, best first (affinity descending, region
+// id ascending), for the top-k selections of the routing.  Lane `lane` holds elements lane * E .. lane * E + E - 1 of
+// every row; partners within a lane swap in registers, partners across lanes
+// come from DPP (lane ^ 1 .. lane ^ 8) or a permlane swap (lane ^ 16, ^ 32).
+// Padding elements (ids >= R) carry -inf and sort last.
+
+// This lane's pair {own, partner at lane ^ LJ} as (a, ia), (b, ib); the
+// permlane swaps return the two in an order that depends on the lane, which
+// a compare-exchange does not need.
+template <int LJ>
+__device__ __forceinline__ void lane_pair(double v, int ix, double& a, int& ia, double& b,
+                                          int& ib) {
+    const int2 u = __builtin_bit_cast(int2, v);
+    if constexpr (LJ < 16) {
+        a = v;
+        ia = ix;
+        b = __builtin_bit_cast(double, int2{lane_xor_dpp<LJ>(u.x), lane_xor_dpp<LJ>(u.y)});
+        ib = lane_xor_dpp<LJ>(ix);
+    } else {
+        const auto lo = LJ == 16 ? __builtin_amdgcn_permlane16_swap(u.x, u.x, false, false)
+                                 : __builtin_amdgcn_permlane32_swap(u.x, u.x, false, false);
+        const auto hi = LJ == 16 ? __builtin_amdgcn_permlane16_swap(u.y, u.y, false, false)
+                                 : __builtin_amdgcn_permlane32_swap(u.y, u.y, false, false);
+        const auto ii = LJ == 16 ? __builtin_amdgcn_permlane16_swap(ix, ix, false, false)
+                                 : __builtin_amdgcn_permlane32_swap(ix, ix, false, false);
+        a = __builtin_bit_cast(double, int2{static_cast<int>(lo[0]), static_cast<int>(hi[0])});
+        ia = static_cast<int>(ii[0]);
+        b = __builtin_bit_cast(double, int2{static_cast<int>(lo[1]), static_cast<int>(hi[1])});
+        ib = static_cast<int>(ii[1]);
+    }
+}
+
+// One half-cleaner step of distance J inside bitonic blocks of SIZE
+// elements, then the steps J/2 .. 1.  Position i keeps the better of the
+// pair when (i & J) == 0 and (i & SIZE) == 0 agree, else the worse.
+template <int E, int NRW, int SIZE, int J>
+__device__ __forceinline__ void bitonic_steps(double (&v)[NRW][E], int (&ix)[NRW][E], int lane) {
+    if constexpr (J < E) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const int pe = e ^ J;
+            if (pe > e) {
+                const bool dir = ((lane * E + e) & SIZE) == 0;
+#pragma unroll
+                for (int r = 0; r < NRW; ++r) {
+                    if (beats(v[r][e], ix[r][e], v[r][pe], ix[r][pe]) != dir) {
+                        const double tv = v[r][e];
+                        v[r][e] = v[r][pe];
+                        v[r][pe] = tv;
+                        const int ti = ix[r][e];
+                        ix[r][e] = ix[r][pe];
+                        ix[r][pe] = ti;
+                    }
+                }
+            }
+        }
+    } else {
+        constexpr int LJ = J / E;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const int i = lane * E + e;
+            const bool keep_better = ((i & J) == 0) == ((i & SIZE) == 0);
+#pragma unroll
+            for (int r = 0; r < NRW; ++r) {
+                double a, b;
+                int ia, ib;
+                lane_pair<LJ>(v[r][e], ix[r][e], a, ia, b, ib);
+                const bool take_a = beats(a, ia, b, ib) == keep_better;
+                v[r][e] = take_a ? a : b;
+                ix[r][e] = take_a ? ia : ib;
+            }
+        }
+    }
+    if constexpr (J > 1) bitonic_steps<E, NRW, SIZE, J / 2>(v, ix, lane);
+}
+
+template <int E, int NRW, int SIZE>
+__device__ __forceinline__ void bitonic_sort(double (&v)[NRW][E], int (&ix)[NRW][E], int lane) {
+    bitonic_steps<E, NRW, SIZE, SIZE / 2>(v, ix, lane);
+    if constexpr (SIZE < 64 * E) bitonic_sort<E, NRW, SIZE * 2>(v, ix, lane);
+}
 
 }  // namespace bra
