@@ -40,6 +40,17 @@ SMALL = [
     Workload("t32_two_groups", 2, 56, 28, 64, 2, 7, 2, "bf16", 119),
     Workload("t48_uneven_groups", 2, 56, 42, 64, 2, 7, 3, "bf16", 120, lepe_bias=True),
     Workload("one_head_four_groups", 2, 56, 56, 32, 1, 7, 3, "bf16", 121),
+    # the routing kernel: 65..128 regions (two entries per lane in the
+    # bitonic sort), the arg-max over more than 64 regions, the generic
+    # 256-region instance, more than four heads with k = 1, and a map of 9
+    # regions (waves past the last row leave early)
+    Workload("r100_topk1", 2, 40, 40, 64, 2, 10, 1, "bf16", 122),
+    Workload("r100_topk7_ragged", 2, 30, 50, 96, 3, 10, 7, "bf16", 123, lepe_bias=True),
+    Workload("r121_f32", 1, 44, 44, 64, 2, 11, 5, "f32", 124),
+    Workload("r256_topk1_generic", 1, 64, 64, 64, 2, 16, 1, "bf16", 125, smooth=True),
+    Workload("r256_topk5_generic", 1, 64, 64, 64, 2, 16, 5, "bf16", 126, smooth=True),
+    Workload("eight_heads_topk1", 2, 28, 28, 256, 8, 7, 1, "bf16", 127),
+    Workload("r9_eight_heads", 3, 12, 12, 256, 8, 3, 2, "bf16", 128),
     Workload("f32_stage2_shape", 4, 28, 28, 128, 4, 7, 4, "f32", 109),
     Workload("f32_ragged_bias", 2, 12, 20, 64, 2, 4, 3, "f32", 110, lepe_bias=True),
 ]

@@ -23,6 +23,7 @@ CASES = [
     Workload("shared_sixteen_heads", 2, 7, 7, 512, 16, 7, 49, "bf16", 306),
     Workload("shared_three_heads_t36", 2, 24, 24, 96, 3, 4, 5, "bf16", 307),
     Workload("shared_f32", 2, 28, 28, 64, 2, 7, 4, "f32", 308, lepe_bias=True),
+    Workload("shared_r100", 2, 40, 40, 128, 4, 10, 3, "bf16", 310),
 ]
 
 
