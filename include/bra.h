@@ -107,8 +107,11 @@ typedef struct {
 bra_status_t bra_create(const bra_config_t* cfg, bra_handle_t* out);
 
 /* Enqueue the forward pass on `stream` (a hipStream_t; NULL = the null
- * stream) as three kernels -- region means, routing, attention + LePE -- and
- * return without synchronising.  No allocation happens here.
+ * stream) and return without synchronising.  The kernels are the region
+ * means, then (with KV downsampling) the pooled K/V, then the routing unless
+ * the attention kernel routes by itself (at most 64 regions, at most 4
+ * heads, per-head routing), then attention + LePE: two to four launches.  No
+ * allocation happens here.
  *   q, k, v       device, [B,H,W,C], dtype, 16-byte aligned
  *   lepe_w        device [C,5,5] fp32, or NULL for no LePE term (lepe_b is then ignored)
  *   lepe_b        device [C] fp32, or NULL for a zero bias
@@ -147,12 +150,13 @@ const char* bra_status_string(bra_status_t s);
 const char* bra_last_error(void);
 
 /* Per-kernel timing for profiling.  bra_timing_enable(h, n) makes the next n
- * calls of bra_forward record HIP events around each of its three kernels on
- * the call's stream (n = 0 turns recording off).  bra_timing_read waits for
- * the recorded events and writes, for each recorded call i < *count,
- * ms[3*i] = region-pool kernel, ms[3*i+1] = routing kernel and
+ * calls of bra_forward record HIP events around each of its steps on the
+ * call's stream (n = 0 turns recording off).  bra_timing_read waits for the
+ * recorded events and writes, for each recorded call i < *count,
+ * ms[3*i] = region means (and KV downsampling), ms[3*i+1] = routing kernel and
  * ms[3*i+2] = attention/LePE kernel time (milliseconds), then clears the
- * record.  `ms` holds at least 3*n floats. */
+ * record.  When the attention kernel routes, ms[3*i+1] measures only the gap
+ * between two back-to-back events.  `ms` holds at least 3*n floats. */
 bra_status_t bra_timing_enable(bra_handle_t h, int32_t n);
 bra_status_t bra_timing_read(bra_handle_t h, float* ms, int32_t* count);
 

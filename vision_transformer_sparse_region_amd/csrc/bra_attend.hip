@@ -157,15 +157,23 @@ __device__ __forceinline__ void v_transpose(const StepRegs& cur, uint16_t* sVt,
 __device__ __forceinline__ void attend_mfma(const Params& p, const WaveJobs& J, const uint16_t* __restrict__ qimg,
                             const uint16_t* __restrict__ kimg, const uint16_t* __restrict__ vimg,
                             int r, uint16_t* sVt_all, float* sL, const int* sOff,
-                            StepRegs (&ring)[2], bf16x8_t (&qb)[kMaxQTiles]) {
+                            StepRegs (&ring)[2], bf16x8_t (&qb)[kMaxQTiles], bool sum_mfma) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int li = lane & 15, g = lane >> 4;
     uint16_t* sVt = sVt_all + w * 32 * kVtStride;
     const int npair = (J.nchunks + 1) / 2;
     const int njl = J.nchunks > 0 ? J.nsteps / J.nchunks : 0;  // this wave's jobs
 
-    float m[kMaxQTiles], l[kMaxQTiles];
-    f32x4_t o0[kMaxQTiles], o1[kMaxQTiles];
+    // Softmax denominator.  sum_mfma (long key lists, where the VALU softmax
+    // is the bound): an all-ones A operand sums P over a chunk's 32 keys on
+    // the MFMA (every row of the product is that sum; element 0 is kept and
+    // rescaled).  Otherwise (one pair of chunks: latency matters more than
+    // VALU slots) each lane adds up its 16 exponentials and the four lane
+    // groups are summed at the end.
+    const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, u32x4_t{0x3f803f80u, 0x3f803f80u,
+                                                              0x3f803f80u, 0x3f803f80u});
+    float m[kMaxQTiles];
+    f32x4_t o0[kMaxQTiles], o1[kMaxQTiles], l[kMaxQTiles];
     for (int ss = 0; ss < njl * npair; ++ss) {
         const int jl = ss / npair, u = ss - jl * npair;
         const int job = w + kWaves * jl;
@@ -237,32 +245,36 @@ __device__ __forceinline__ void attend_mfma(const Params& p, const WaveJobs& J, 
             mx = group4_max(mx);
             const float mnew = u == 0 ? mx : max_f(m[jq], mx);
             const float mb = mnew * p.scale_log2e;
-            float psum = 0.f;
             bf16x8_t pb[2];
+            float psum = 0.f;
 #pragma unroll
             for (int ch = 0; ch < 2; ++ch)
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const float pe = __builtin_amdgcn_exp2f(fmaf(x[ch][e], p.scale_log2e, -mb));
-                    psum += pe;
+                    if (!sum_mfma) psum += pe;
                     pb[ch][e] = static_cast<__bf16>(pe);
                 }
             if (u == 0) {
-                l[jq] = psum;
+                l[jq] = f32x4_t{sum_mfma ? 0.f : psum, 0.f, 0.f, 0.f};
                 o0[jq] = f32x4_t{0.f, 0.f, 0.f, 0.f};
                 o1[jq] = f32x4_t{0.f, 0.f, 0.f, 0.f};
             } else {
                 const float alpha = __builtin_amdgcn_exp2f((m[jq] - mnew) * p.scale_log2e);
-                l[jq] = l[jq] * alpha + psum;
+                l[jq][0] = sum_mfma ? l[jq][0] * alpha : fmaf(l[jq][0], alpha, psum);
                 o0[jq] *= alpha;
                 o1[jq] *= alpha;
             }
             m[jq] = mnew;
             o0[jq] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[0][0], pb[0], o0[jq], 0, 0, 0);
             o1[jq] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[0][1], pb[0], o1[jq], 0, 0, 0);
+            if (sum_mfma)
+                l[jq] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[0], l[jq], 0, 0, 0);
             if (two) {
                 o0[jq] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[1][0], pb[1], o0[jq], 0, 0, 0);
                 o1[jq] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[1][1], pb[1], o1[jq], 0, 0, 0);
+                if (sum_mfma)
+                    l[jq] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[1], l[jq], 0, 0, 0);
             }
         }
 
@@ -270,7 +282,8 @@ __device__ __forceinline__ void attend_mfma(const Params& p, const WaveJobs& J, 
 #pragma unroll
             for (int jq = 0; jq < kMaxQTiles; ++jq) {
                 if (jq >= nq) break;
-                const float inv = __builtin_amdgcn_rcpf(group4_sum(l[jq]));
+                const float inv =
+                    __builtin_amdgcn_rcpf(sum_mfma ? l[jq][0] : group4_sum(l[jq][0]));
                 const int qi = (qt0 + jq) * 16 + li;
                 if (qi < p.t) {
                     float* dst = sL + qi * p.lstride + hoff + 4 * g;
@@ -836,10 +849,13 @@ attend_kernel(const T* __restrict__ q, const T* __restrict__ v, const T* __restr
 
     // 4. Token attention over the routed tokens, added into sL.
     if constexpr (VEC == 8) {
+        // the denominator on the MFMA for key lists longer than one pair of chunks
+        constexpr bool kFixedKeys = HS > 0 && WS > 0 && KTOP > 0;
+        const bool sum_mfma = kFixedKeys ? KTOP * HS * WS > 64 : p.nkeys > 64;
         attend_mfma(p, J, reinterpret_cast<const uint16_t*>(q) + img,
                     reinterpret_cast<const uint16_t*>(kg) + kimg,
                     reinterpret_cast<const uint16_t*>(vg) + kimg, r,
-                    reinterpret_cast<uint16_t*>(smem + p.off_vt), sL, sOff, ring, qb);
+                    reinterpret_cast<uint16_t*>(smem + p.off_vt), sL, sOff, ring, qb, sum_mfma);
     } else {
         attend_valu(p, reinterpret_cast<const float*>(q) + img,
                     reinterpret_cast<const float*>(kg) + kimg,
