@@ -28,7 +28,8 @@ from .build import LIB_PATH, build_oracle
 
 __all__ = [
     "OracleConfig", "OracleLib", "topk_effective", "region_means", "route", "attend", "lepe",
-    "attend_with_routing", "bra_forward", "num_threads", "default",
+    "attend_with_routing", "bra_forward", "num_threads", "default", "round_to", "linear",
+    "bra_forward_proj",
 ]
 
 
@@ -119,10 +120,16 @@ class OracleLib:
                                                 _IP]
         lib.oracle_attend_kvds.argtypes = [cp, ctypes.c_int, _DP, _DP, _DP, _IP, _DP]
         lib.oracle_num_threads.argtypes = []
+        lib.oracle_round.argtypes = [ctypes.c_int, ctypes.c_int64, _DP, _DP]
+        lib.oracle_linear.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_int, _DP, _DP, _DP,
+                                      ctypes.c_int, _DP]
+        lib.oracle_bra_forward_proj.argtypes = [cp, ctypes.c_int, _DP, _DP, _DP, _DP, _DP, _DP,
+                                                _DP, _DP, _IP, _DP]
         for name in ("oracle_region_means", "oracle_route", "oracle_attend", "oracle_lepe",
                      "oracle_attend_with_routing", "oracle_bra_forward", "oracle_route_shared",
                      "oracle_bra_forward_shared", "oracle_kv_downsample",
-                     "oracle_bra_forward_kvds", "oracle_attend_kvds", "oracle_num_threads"):
+                     "oracle_bra_forward_kvds", "oracle_attend_kvds", "oracle_num_threads",
+                     "oracle_round", "oracle_linear", "oracle_bra_forward_proj"):
             getattr(lib, name).restype = ctypes.c_int
         self.lib = lib
         self.path = path
@@ -283,6 +290,47 @@ class OracleLib:
         return res
 
 
+    # ---- projections (round: 0 none, 1 bf16, 2 fp32) -----------------------
+    ROUND = {"f64": 0, "bf16": 1, "f32": 2}
+
+    def round_to(self, x, round_mode: int):
+        xa, xp = _f64(x)
+        y = np.empty_like(xa)
+        _check(self.lib.oracle_round(int(round_mode), xa.size, xp, _ptr(y)), "round")
+        return y
+
+    def linear(self, x, w, b=None, round_mode: int = 0):
+        """y[..., o] = x[..., :] . w[o, :] + b[o] (w a Linear weight [out, in])."""
+        xa, xp = _f64(x)
+        wa, wp = _f64(w)
+        ba, bp = _f64(b)
+        out_f, in_f = wa.shape
+        rows = xa.size // in_f
+        y = np.empty(xa.shape[:-1] + (out_f,), np.float64)
+        _check(self.lib.oracle_linear(rows, in_f, out_f, xp, wp, bp, int(round_mode), _ptr(y)),
+               "linear")
+        return y
+
+    def bra_forward_proj(self, cfg: OracleConfig, round_mode: int, x, w_qkv, b_qkv, lepe_w,
+                         lepe_b, w_o, b_o, *, want_qkv=False):
+        """Projections + forward; returns a dict with 'out', 'idx' (+ 'qkv')."""
+        c = cfg._c()
+        arrs = [_f64(a) for a in (x, w_qkv, b_qkv, lepe_w, lepe_b, w_o, b_o)]
+        kk = self.topk_effective(cfg)
+        out = np.empty(_map_shape(cfg), np.float64)
+        idx = np.empty((cfg.batch, cfg.num_heads, cfg.regions, kk), np.int32)
+        qkv = np.empty(_map_shape(cfg)[:-1] + (3 * cfg.channels,), np.float64) \
+            if want_qkv else None
+        _check(self.lib.oracle_bra_forward_proj(ctypes.byref(c), int(round_mode),
+                                                *[p for _, p in arrs], _ptr(out),
+                                                idx.ctypes.data_as(_IP), _ptr(qkv)),
+               "bra_forward_proj")
+        res = {"out": out, "idx": idx}
+        if want_qkv:
+            res["qkv"] = qkv
+        return res
+
+
 _default = None
 
 
@@ -346,3 +394,17 @@ def bra_forward_kvds(cfg, ratio, q, k, v, w=None, b=None):
 
 def attend_kvds(cfg, ratio, q, k, v, idx):
     return default().attend_kvds(cfg, ratio, q, k, v, idx)
+
+
+def round_to(x, round_mode):
+    return default().round_to(x, round_mode)
+
+
+def linear(x, w, b=None, round_mode=0):
+    return default().linear(x, w, b, round_mode)
+
+
+def bra_forward_proj(cfg, round_mode, x, w_qkv, b_qkv, lepe_w, lepe_b, w_o, b_o, *,
+                     want_qkv=False):
+    return default().bra_forward_proj(cfg, round_mode, x, w_qkv, b_qkv, lepe_w, lepe_b, w_o,
+                                      b_o, want_qkv=want_qkv)

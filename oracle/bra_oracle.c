@@ -416,3 +416,81 @@ int oracle_bra_forward(const oracle_cfg_t* c, const double* q, const double* k,
     if (!kbar) free(kb);
     return rc;
 }
+
+/* ---- the projections either side of the path ------------------------------
+ * [P5 §五 ① qkv = Linear(dim, 3*dim) of the input, ⑧ proj = Linear(dim, dim) of
+ * the attention output; P4 §1.1 the 1x1 projections around the attention] */
+
+/* Nearest bf16 value of x (ties to even), as a double.  bf16 keeps 8
+ * significant bits: within the binade [2^(e-1), 2^e) its spacing is
+ * 2^(e-8), and below the smallest normal (2^-126) it is 2^-133; rint rounds
+ * to nearest even in the default rounding mode.  Beyond the largest finite
+ * bf16 ((2 - 2^-7) * 2^127) the result is +-inf. */
+static double round_bf16(double x) {
+    if (!isfinite(x) || x == 0.0) return x;
+    int e;
+    frexp(x, &e); /* x = m * 2^e with 0.5 <= |m| < 1 */
+    if (e < -125) e = -125;
+    const double r = ldexp(rint(ldexp(x, 8 - e)), e - 8);
+    return fabs(r) > 3.3895313892515355e38 ? copysign(INFINITY, x) : r;
+}
+
+static double round_to(double x, int round) {
+    if (round == 1) return round_bf16(x);
+    if (round == 2) return (double)(float)x;
+    return x;
+}
+
+int oracle_round(int round, int64_t n, const double* x, double* y) {
+    if (round < 0 || round > 2 || n < 0 || (n > 0 && (!x || !y))) return -1;
+    for (int64_t i = 0; i < n; ++i) y[i] = round_to(x[i], round);
+    return 0;
+}
+
+int oracle_linear(int64_t rows, int in_f, int out_f, const double* x, const double* w,
+                  const double* b, int round, double* y) {
+    if (rows < 0 || in_f <= 0 || out_f <= 0 || round < 0 || round > 2 || !x || !w || !y)
+        return -1;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < rows; ++i)
+        for (int o = 0; o < out_f; ++o) {
+            double s = 0.0;
+            for (int ci = 0; ci < in_f; ++ci) s += x[i * in_f + ci] * w[(size_t)o * in_f + ci];
+            if (b) s += b[o];
+            y[i * out_f + o] = round_to(s, round);
+        }
+    return 0;
+}
+
+int oracle_bra_forward_proj(const oracle_cfg_t* c, int round, const double* x,
+                            const double* w_qkv, const double* b_qkv, const double* lepe_w,
+                            const double* lepe_b, const double* w_o, const double* b_o,
+                            double* out, int32_t* idx, double* qkv) {
+    if (!cfg_ok(c) || round < 0 || round > 2 || !x || !w_qkv || !w_o || !out || !idx) return -1;
+    const int C = c->channels;
+    const int64_t N = (int64_t)c->batch * c->height * c->width;
+    double* P = qkv ? qkv : (double*)malloc(sizeof(double) * (size_t)N * 3 * C);
+    double* q = (double*)malloc(sizeof(double) * (size_t)N * C);
+    double* k = (double*)malloc(sizeof(double) * (size_t)N * C);
+    double* v = (double*)malloc(sizeof(double) * (size_t)N * C);
+    double* y = (double*)malloc(sizeof(double) * (size_t)N * C);
+    int rc = -1;
+    if (P && q && k && v && y && oracle_linear(N, C, 3 * C, x, w_qkv, b_qkv, round, P) == 0) {
+        /* q, k, v are the three C-channel blocks of each token's 3C outputs */
+        for (int64_t i = 0; i < N; ++i)
+            for (int ci = 0; ci < C; ++ci) {
+                q[i * C + ci] = P[i * 3 * C + ci];
+                k[i * C + ci] = P[i * 3 * C + C + ci];
+                v[i * C + ci] = P[i * 3 * C + 2 * C + ci];
+            }
+        if (oracle_bra_forward(c, q, k, v, lepe_w, lepe_b, y, idx, NULL, NULL, NULL) == 0 &&
+            oracle_linear(N, C, C, y, w_o, b_o, 0, out) == 0)
+            rc = 0;
+    }
+    if (!qkv) free(P);
+    free(q);
+    free(k);
+    free(v);
+    free(y);
+    return rc;
+}

@@ -124,6 +124,29 @@ int oracle_bra_forward_kvds(const oracle_cfg_t* cfg, int ratio, const double* q,
                             const double* k, const double* v, const double* lepe_w,
                             const double* lepe_b, double* out, int32_t* idx);
 
+/* The projections either side of the path [P5 §五 ① qkv Linear(dim, 3*dim),
+ * ⑧ proj Linear(dim, dim); P4 §1.1].
+ *
+ * oracle_round: y[i] = x[i] rounded to the I/O type: round 0 = none (fp64),
+ * 1 = bf16 (nearest, ties to even), 2 = fp32.
+ *
+ * oracle_linear: y[i][o] = (sum_c x[i][c] * w[o][c]) + b[o], then rounded as
+ * oracle_round; x [rows, in_f], w [out_f, in_f] (a PyTorch Linear weight),
+ * b [out_f] or NULL, y [rows, out_f].
+ *
+ * oracle_bra_forward_proj: qkv = linear(x, w_qkv [3C, C], b_qkv [3C] or NULL)
+ * rounded to the I/O type (`round`), q, k, v = its channel blocks [0, C),
+ * [C, 2C), [2C, 3C); y = oracle_bra_forward(q, k, v, lepe) kept in fp64;
+ * out = linear(y, w_o [C, C], b_o [C] or NULL) in fp64.  qkv ([B*H*W, 3C],
+ * the rounded projections) may be NULL. */
+int oracle_round(int round, int64_t n, const double* x, double* y);
+int oracle_linear(int64_t rows, int in_f, int out_f, const double* x, const double* w,
+                  const double* b, int round, double* y);
+int oracle_bra_forward_proj(const oracle_cfg_t* cfg, int round, const double* x,
+                            const double* w_qkv, const double* b_qkv, const double* lepe_w,
+                            const double* lepe_b, const double* w_o, const double* b_o,
+                            double* out, int32_t* idx, double* qkv);
+
 /* Number of OpenMP threads a parallel region of the oracle uses. */
 int oracle_num_threads(void);
 

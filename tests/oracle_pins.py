@@ -527,6 +527,76 @@ def pin_kvds_window_ratio_attends_region_means(orc):
     assert (res["idx"] == orc.bra_forward(cfg, q, k, v)["idx"]).all()
 
 
+# ---- the projections either side of the path [P5 §五 ① and ⑧; P4 §1.1] ----
+def pin_round_bf16_matches_torch(orc):
+    """Rounding to bf16 agrees with torch's float32 -> bfloat16 conversion
+    (round to nearest, ties to even) on float32 inputs, ties, subnormals and
+    the overflow edge."""
+    rng = _rng(201)
+    x = (rng.standard_normal(4096) * np.exp(rng.uniform(-30, 30, 4096))).astype(np.float32)
+    specials = np.array([1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -(1.0 + 2 ** -8), 2 ** -130,
+                         3 * 2 ** -134, 3.3895313892515355e38, 3.3961775292304e38, 0.0, -0.0,
+                         1e-45], dtype=np.float32)
+    x = np.concatenate([x, specials])
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+    got = orc.round_to(x.astype(np.float64), 1)
+    np.testing.assert_array_equal(got, ref)
+    np.testing.assert_array_equal(orc.round_to(np.array([0.1, 1 / 3]), 2),
+                                  np.array([0.1, 1 / 3], dtype=np.float32).astype(np.float64))
+
+
+def pin_linear_matches_numpy(orc):
+    """linear(x, w, b) is x w^T + b (numpy matmul, float64), for a PyTorch
+    Linear weight [out, in]."""
+    rng = _rng(202)
+    x = rng.standard_normal((37, 48))
+    w = rng.standard_normal((20, 48))
+    b = rng.standard_normal(20)
+    np.testing.assert_allclose(orc.linear(x, w, b), x @ w.T + b, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(orc.linear(x, w), x @ w.T, rtol=1e-12, atol=1e-12)
+
+
+def pin_proj_identity_is_plain_forward(orc):
+    """With w_qkv = [I; I; I], no qkv bias, w_o = I and no output bias, the
+    projected forward of x is the plain forward of (x, x, x), bit for bit."""
+    cfg = OracleConfig(2, 8, 8, 32, 1, 2, 2)
+    rng = _rng(203)
+    x = _rand_map(rng, cfg)
+    w, b = _rand_lepe(rng, cfg)
+    eye = np.eye(cfg.channels)
+    a = orc.bra_forward_proj(cfg, 0, x, np.vstack([eye, eye, eye]), None, w, b, eye, None)
+    d = orc.bra_forward(cfg, x, x, x, w, b)
+    assert (a["idx"] == d["idx"]).all()
+    np.testing.assert_array_equal(a["out"], d["out"])
+
+
+def pin_proj_composes_linear_and_forward(orc):
+    """The projected forward is linear(forward(split(round(linear(x)))))
+    with every piece from numpy/torch: the qkv projection by numpy matmul and
+    torch's bf16 conversion, the channel split, the plain forward, and the
+    output projection by numpy matmul."""
+    cfg = OracleConfig(2, 12, 8, 64, 2, 4, 3)
+    rng = _rng(204)
+    x = torch.from_numpy(_rand_map(rng, cfg)).to(torch.bfloat16).double().numpy()
+    C = cfg.channels
+    wq = rng.standard_normal((3 * C, C)) / math.sqrt(C)
+    bq = rng.standard_normal(3 * C) * 0.1
+    wo = rng.standard_normal((C, C)) / math.sqrt(C)
+    bo = rng.standard_normal(C) * 0.1
+    lw, lb = _rand_lepe(rng, cfg)
+    res = orc.bra_forward_proj(cfg, 1, x, wq, bq, lw, lb, wo, bo, want_qkv=True)
+    qkv = torch.from_numpy(x @ wq.T + bq).float().to(torch.bfloat16).double().numpy()
+    # numpy's matmul sums in another order: a bf16 rounding may flip by one
+    # step in rare halfway cases; all others agree exactly
+    same = res["qkv"] == qkv
+    assert same.mean() > 0.999, same.mean()
+    qkv = res["qkv"]
+    q, k, v = qkv[..., :C], qkv[..., C:2 * C], qkv[..., 2 * C:]
+    plain = orc.bra_forward(cfg, q, k, v, lw, lb)
+    assert (plain["idx"] == res["idx"]).all()
+    np.testing.assert_allclose(res["out"], plain["out"] @ wo.T + bo, rtol=1e-12, atol=1e-12)
+
+
 ALL_PINS = [
     pin_topk_all_is_dense_attention,
     pin_one_region_is_dense_attention,
@@ -553,4 +623,8 @@ ALL_PINS = [
     pin_kvds_all_regions_is_dense_over_pooled,
     pin_kvds_window_ratio_attends_region_means,
     pin_attend_kvds_matches_forward,
+    pin_round_bf16_matches_torch,
+    pin_linear_matches_numpy,
+    pin_proj_identity_is_plain_forward,
+    pin_proj_composes_linear_and_forward,
 ]

@@ -46,6 +46,14 @@ MUTANTS = [
     ("shared_routing_per_head0",
      "full[(((size_t)b * H + h) * R + r) * kk + j] =\n                            idx[((size_t)b * R + r) * kk + j];",
      "full[(((size_t)b * H + h) * R + r) * kk + j] =\n                            idx[((size_t)b * R + (h ? 0 : r)) * kk + j];"),
+    ("linear_weight_transposed", "s += x[i * in_f + ci] * w[(size_t)o * in_f + ci];",
+     "s += x[i * in_f + ci] * w[(size_t)ci * out_f + o];"),
+    ("proj_no_rounding", "y[i * out_f + o] = round_to(s, round);",
+     "y[i * out_f + o] = s; (void)round;"),
+    ("proj_k_block_is_q", "k[i * C + ci] = P[i * 3 * C + C + ci];",
+     "k[i * C + ci] = P[i * 3 * C + ci];"),
+    ("bf16_ties_away", "const double r = ldexp(rint(ldexp(x, 8 - e)), e - 8);",
+     "const double r = ldexp(round(ldexp(x, 8 - e)), e - 8);"),
 ]
 
 
