@@ -66,10 +66,11 @@ typedef enum {
     BRA_ERR_NULL = 1,        /* a required pointer is NULL */
     BRA_ERR_SHAPE = 2,       /* sizes not positive, H or W not divisible by n_win,
                                 C not divisible by num_heads, too large for int32 indexing,
-                                shared_routing not 0/1, or kv_downsample_ratio not dividing
-                                the window sides */
+                                shared_routing or projections not 0/1, or
+                                kv_downsample_ratio not dividing the window sides */
     BRA_ERR_UNSUPPORTED = 3, /* head_dim != 32, unknown dtype, n_win > 16, H*W >= 2^23,
-                                or a region too large for the kernels' on-chip tiles */
+                                a region too large for the kernels' on-chip tiles, or
+                                projections with fp32 (or on a handle without them) */
     BRA_ERR_HIP = 4,         /* a HIP runtime call failed (see bra_last_error) */
     BRA_ERR_NOMEM = 5,       /* device memory for the workspace could not be allocated */
     BRA_ERR_BAD_HANDLE = 6,  /* not a live handle (never created, or destroyed) */
@@ -96,14 +97,19 @@ typedef struct {
                                (H/n_win/r) x (W/n_win/r) tokens), routing and LePE
                                stay at full resolution [P1 §4.1]; r must divide
                                H/n_win and W/n_win */
+    int32_t projections;    /* 1: the handle also runs bra_forward_proj (the
+                               module's qkv and output projections around the
+                               path, [P5 §五 ① and ⑧]); its workspace then holds
+                               the projected q, k, v.  bf16 only.  0: none */
 } bra_config_t;
 
 /* Validate cfg and allocate the handle and its device workspace on the
  * current HIP device: the fp64 region means of Q and K (2*B*C*R*8 bytes), a
  * routing buffer (B*heads*R*k*4 bytes), for window shapes whose LePE runs on
- * MFMA a C*320-byte operand table, and with KV downsampling the pooled K and
- * V (2*B*H*W*C*sizeof(dtype)/r^2 bytes).  On success *out is a live
- * handle; on failure *out is left NULL. */
+ * MFMA a C*320-byte operand table, with KV downsampling the pooled K and V
+ * (2*B*H*W*C*sizeof(dtype)/r^2 bytes), and with projections the projected
+ * q, k, v (3*B*H*W*C*2 bytes).  On success *out is a live handle; on failure
+ * *out is left NULL. */
 bra_status_t bra_create(const bra_config_t* cfg, bra_handle_t* out);
 
 /* Enqueue the forward pass on `stream` (a hipStream_t; NULL = the null
@@ -135,6 +141,30 @@ bra_status_t bra_forward(bra_handle_t h, const void* q, const void* k, const voi
 bra_status_t bra_forward_routed(bra_handle_t h, const void* q, const void* k, const void* v,
                                 const float* lepe_w, const float* lepe_b,
                                 const int32_t* routing_idx, void* out, void* stream);
+
+/* The path with the module's projections on either side [P5 §五 ① qkv =
+ * Linear(dim, 3*dim), ⑧ proj = Linear(dim, dim); P4 §1.1], for handles created
+ * with projections = 1:
+ *   q|k|v = x w_qkv^T + b_qkv, each rounded once to bf16 (channel blocks
+ *           [0,C), [C,2C), [2C,3C) of the 3C outputs)
+ *   y     = the bra_forward result of (q, k, v, lepe_w, lepe_b), kept in fp32
+ *   out   = y w_o^T + b_o, rounded once to bf16
+ *   x             device [B,H,W,C] bf16, 16-byte aligned
+ *   w_qkv         device [3C, C] bf16 (a PyTorch Linear weight), 16-byte aligned
+ *   b_qkv         device [3C] fp32, or NULL for none
+ *   w_o           device [C, C] bf16 (Linear weight), 16-byte aligned
+ *   b_o           device [C] fp32, or NULL for none
+ *   lepe_w, lepe_b, routing_idx, stream: as bra_forward; out: [B,H,W,C] bf16,
+ *   must not overlap x.
+ * The qkv projection runs on MFMA with the region means of the projected q
+ * and k computed in the same pass; the output projection runs in the
+ * attention kernel's epilogue, so y never goes to memory.  Enqueued without
+ * synchronising or allocating.  BRA_ERR_UNSUPPORTED for a handle created
+ * without projections. */
+bra_status_t bra_forward_proj(bra_handle_t h, const void* x, const void* w_qkv,
+                              const float* b_qkv, const float* lepe_w, const float* lepe_b,
+                              const void* w_o, const float* b_o, void* out,
+                              int32_t* routing_idx, void* stream);
 
 /* Release the workspace and the handle.  NULL is a no-op (BRA_OK); a handle
  * that is not live gives BRA_ERR_BAD_HANDLE. */

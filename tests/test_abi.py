@@ -48,6 +48,8 @@ def _cfg(**kw):
      bra.BRA_ERR_UNSUPPORTED),                     # one 65536-token region does not fit on chip
     (dict(height=65536, width=65536, n_win=1, channels=32, num_heads=1), bra.BRA_ERR_SHAPE),
     (dict(shared_routing=2), bra.BRA_ERR_SHAPE),   # a flag: 0 or 1
+    (dict(projections=2), bra.BRA_ERR_SHAPE),      # a flag: 0 or 1
+    (dict(projections=1, dtype=bra.BRA_F32), bra.BRA_ERR_UNSUPPORTED),  # bf16 only
     (dict(kv_downsample_ratio=3), bra.BRA_ERR_SHAPE),  # 3 does not divide the 4x4 windows
     (dict(height=4096, width=4096, n_win=256, channels=32, num_heads=1),
      bra.BRA_ERR_UNSUPPORTED),                     # H*W = 2^24 tokens: beyond 24-bit indexing
@@ -71,6 +73,8 @@ def test_dead_handles(lib):
     assert lib.bra_destroy(fake) == bra.BRA_ERR_BAD_HANDLE
     assert bra.bra_forward_status(fake, 16, 16, 16, None, None, 32) == bra.BRA_ERR_BAD_HANDLE
     assert bra.bra_forward_routed_status(fake, 16, 16, 16, None, None, 16, 32) == \
+        bra.BRA_ERR_BAD_HANDLE
+    assert bra.bra_forward_proj_status(fake, 16, 16, None, None, None, 16, None, 32) == \
         bra.BRA_ERR_BAD_HANDLE
     assert lib.bra_topk_effective(fake) == -1
     assert lib.bra_timing_enable(fake, 4) == bra.BRA_ERR_BAD_HANDLE

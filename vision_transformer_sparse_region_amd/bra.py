@@ -50,6 +50,7 @@ class BraConfig(ctypes.Structure):
         ("channels", ctypes.c_int32), ("num_heads", ctypes.c_int32), ("n_win", ctypes.c_int32),
         ("topk", ctypes.c_int32), ("dtype", ctypes.c_int), ("scale", ctypes.c_float),
         ("shared_routing", ctypes.c_int32), ("kv_downsample_ratio", ctypes.c_int32),
+        ("projections", ctypes.c_int32),
     ]
 
 
@@ -69,6 +70,7 @@ def load_library(path: str = LIB_PATH):
     lib.bra_create.argtypes = [ctypes.POINTER(BraConfig), ctypes.POINTER(vp)]
     lib.bra_forward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.bra_forward_routed.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.bra_forward_proj.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.bra_destroy.argtypes = [vp]
     lib.bra_topk_effective.argtypes = [vp]
     lib.bra_topk_effective.restype = i32
@@ -78,7 +80,8 @@ def load_library(path: str = LIB_PATH):
     lib.bra_last_error.restype = ctypes.c_char_p
     lib.bra_timing_enable.argtypes = [vp, i32]
     lib.bra_timing_read.argtypes = [vp, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(i32)]
-    for name in ("bra_create", "bra_forward", "bra_forward_routed", "bra_destroy",
+    for name in ("bra_create", "bra_forward", "bra_forward_routed", "bra_forward_proj",
+                 "bra_destroy",
                  "bra_timing_enable", "bra_timing_read"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
@@ -169,6 +172,23 @@ def bra_forward_routed_status(h, q, k, v, lepe_w, lepe_b, routing_idx, out, stre
                                              _ptr(lepe_b), _ptr(routing_idx), _ptr(out), stream)
 
 
+def bra_forward_proj(h: int, x, w_qkv, b_qkv, lepe_w, lepe_b, w_o, b_o, out,
+                     routing_idx=None, stream=None):
+    """Enqueue the projected forward (handles created with projections)."""
+    st = load_library().bra_forward_proj(h, _ptr(x), _ptr(w_qkv), _ptr(b_qkv), _ptr(lepe_w),
+                                         _ptr(lepe_b), _ptr(w_o), _ptr(b_o), _ptr(out),
+                                         _ptr(routing_idx), _stream(stream))
+    _check(st, "bra_forward_proj")
+
+
+def bra_forward_proj_status(h, x, w_qkv, b_qkv, lepe_w, lepe_b, w_o, b_o, out,
+                            routing_idx=None, stream=0) -> int:
+    """Raw status of bra_forward_proj (for tests of the argument checks)."""
+    return load_library().bra_forward_proj(h, _ptr(x), _ptr(w_qkv), _ptr(b_qkv), _ptr(lepe_w),
+                                           _ptr(lepe_b), _ptr(w_o), _ptr(b_o), _ptr(out),
+                                           _ptr(routing_idx), stream)
+
+
 def bra_destroy(h) -> None:
     _check(load_library().bra_destroy(h), "bra_destroy")
 
@@ -203,10 +223,11 @@ class BRA:
     """
 
     def __init__(self, batch, height, width, channels, num_heads, n_win, topk, dtype="bf16",
-                 scale=0.0, shared_routing=False, kv_downsample_ratio=1):
+                 scale=0.0, shared_routing=False, kv_downsample_ratio=1, projections=False):
         self.cfg = BraConfig(batch, height, width, channels, num_heads, n_win, topk,
                              BRA_BF16 if dtype == "bf16" else BRA_F32, scale,
-                             1 if shared_routing else 0, kv_downsample_ratio)
+                             1 if shared_routing else 0, kv_downsample_ratio,
+                             1 if projections else 0)
         self.dtype = dtype
         self.route_heads = 1 if shared_routing else num_heads
         self.handle = bra_create(self.cfg)
@@ -253,6 +274,33 @@ class BRA:
             out = torch.empty_like(q)
         bra_forward_routed(self.handle, q, k, v, lepe_w, lepe_b, routing_idx, out, stream)
         return out
+
+    def forward_proj(self, x, w_qkv, w_o, b_qkv=None, b_o=None, lepe_w=None, lepe_b=None,
+                     out=None, routing_idx=True, stream=None):
+        """The path with the module's projections on either side (bf16; handle
+        created with projections=True): returns ``(out, routing_idx)``."""
+        import torch
+        c = self.cfg
+        shape = (c.batch, c.height, c.width, c.channels)
+        if x.dtype != torch.bfloat16 or tuple(x.shape) != shape or not x.is_contiguous() or \
+                not x.is_cuda:
+            raise ValueError(f"x: expected a contiguous bfloat16 CUDA tensor {shape}")
+        for name, t, ws in (("w_qkv", w_qkv, (3 * c.channels, c.channels)),
+                            ("w_o", w_o, (c.channels, c.channels))):
+            if t.dtype != torch.bfloat16 or tuple(t.shape) != ws or not t.is_contiguous() or \
+                    not t.is_cuda:
+                raise ValueError(f"{name}: expected a contiguous bfloat16 CUDA tensor {ws}")
+        if out is None:
+            out = torch.empty_like(x)
+        idx = None
+        if routing_idx is True:
+            idx = torch.empty((c.batch, self.route_heads, c.n_win * c.n_win, self.k),
+                              dtype=torch.int32, device=x.device)
+        elif routing_idx is not None and routing_idx is not False:
+            idx = routing_idx
+        bra_forward_proj(self.handle, x, w_qkv, b_qkv, lepe_w, lepe_b, w_o, b_o, out, idx,
+                         stream)
+        return out, idx
 
     def close(self):
         if self.handle:

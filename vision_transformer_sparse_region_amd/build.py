@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG, "libbra.so")
 SOURCES = [os.path.join(CSRC, n) for n in
-           ("bra_pool.hip", "bra_route.hip", "bra_attend.hip", "bra_api.cpp")]
+           ("bra_pool.hip", "bra_route.hip", "bra_attend.hip", "bra_proj.hip", "bra_api.cpp")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

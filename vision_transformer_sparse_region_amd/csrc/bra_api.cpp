@@ -30,6 +30,9 @@ struct bra_handle_s {
     float* zero_bias;
     void* kd;  // downsampled K and V [B, H/r, W/r, C] (KV downsampling), else NULL
     void* vd;
+    void* qs;  // projected q, k, v [B, H, W, C] (handles created with projections), else NULL
+    void* ks;
+    void* vs;
     // per-kernel timing (events recorded by bra_forward while slots remain)
     std::vector<hipEvent_t> events;  // kEventsPerCall per recorded call
     int timing_capacity;
@@ -122,6 +125,10 @@ bra_status_t bra_create(const bra_config_t* cfg, bra_handle_t* out) {
     bra::Params p;
     if (c.shared_routing != 0 && c.shared_routing != 1)
         return fail(BRA_ERR_SHAPE, "bra_create: shared_routing must be 0 or 1");
+    if (c.projections != 0 && c.projections != 1)
+        return fail(BRA_ERR_SHAPE, "bra_create: projections must be 0 or 1");
+    if (c.projections && !bf16)
+        return fail(BRA_ERR_UNSUPPORTED, "bra_create: projections need dtype BRA_BF16");
     const int kv_ratio = c.kv_downsample_ratio <= 1 ? 1 : c.kv_downsample_ratio;
     if ((c.height / c.n_win) % kv_ratio || (c.width / c.n_win) % kv_ratio)
         return fail(BRA_ERR_SHAPE,
@@ -151,13 +158,19 @@ bra_status_t bra_create(const bra_config_t* cfg, bra_handle_t* out) {
     const size_t kv_bytes = p.kv_ratio > 1 ? static_cast<size_t>(c.batch) * p.kH * p.kW *
                                                  c.channels * (bf16 ? 2 : 4)
                                            : 0;
-    h->means_bytes = mean_bytes + route_bytes + table_bytes + zero_bytes + 2 * kv_bytes;
+    // projected q, k, v (projections only)
+    const size_t map_bytes = static_cast<size_t>(c.batch) * c.height * c.width * c.channels *
+                             (bf16 ? 2 : 4);
+    const size_t proj_bytes = c.projections ? 3 * map_bytes : 0;
+    h->means_bytes = mean_bytes + route_bytes + table_bytes + zero_bytes + 2 * kv_bytes +
+                     proj_bytes;
     h->means = nullptr;
     h->routing = nullptr;
     h->lepe_table = nullptr;
     h->zero_bias = nullptr;
     h->kd = nullptr;
     h->vd = nullptr;
+    h->qs = h->ks = h->vs = nullptr;
     h->timing_capacity = 0;
     h->timing_used = 0;
     e = hipMalloc(reinterpret_cast<void**>(&h->means), h->means_bytes);
@@ -172,6 +185,11 @@ bra_status_t bra_create(const bra_config_t* cfg, bra_handle_t* out) {
                                             route_bytes + table_bytes);
     h->kd = kv_bytes ? reinterpret_cast<char*>(h->zero_bias) + zero_bytes : nullptr;
     h->vd = kv_bytes ? static_cast<char*>(h->kd) + kv_bytes : nullptr;
+    if (proj_bytes) {
+        h->qs = reinterpret_cast<char*>(h->zero_bias) + zero_bytes + 2 * kv_bytes;
+        h->ks = static_cast<char*>(h->qs) + map_bytes;
+        h->vs = static_cast<char*>(h->ks) + map_bytes;
+    }
     e = hipMemset(h->zero_bias, 0, zero_bytes);
     if (e != hipSuccess) {
         hipFree(h->means);
@@ -229,46 +247,86 @@ static bra_status_t check_forward_args(bra_handle_t h, const char* what, const v
     return BRA_OK;
 }
 
+// The forward steps on stream s.  With x (projections), the qkv projection
+// writes the handle's q, k, v (and the region means), and the attention
+// kernel applies the output projection w_o, b_o; otherwise the pool kernel
+// reads the caller's q and k.
+static bra_status_t enqueue_forward(bra_handle_t h, const char* what, const void* x,
+                                    const void* w_qkv, const float* b_qkv, const void* q,
+                                    const void* k, const void* v, const float* lepe_w,
+                                    const float* lepe_b, const void* w_o, const float* b_o,
+                                    void* out, int32_t* routing_idx, hipStream_t s) {
+    const std::string wh(what);
+    hipError_t e;
+    const bool timed = h->timing_used < h->timing_capacity;
+    hipEvent_t* ev = timed ? &h->events[kEventsPerCall * h->timing_used] : nullptr;
+    if (timed && (e = hipEventRecord(ev[0], s)) != hipSuccess)
+        return fail_hip(e, (wh + ": hipEventRecord").c_str());
+    if (x) {
+        e = bra::launch_proj_qkv(h->params, x, w_qkv, b_qkv, h->qs, h->ks, h->vs, h->means,
+                                 lepe_w, h->lepe_table, s);
+        if (e != hipSuccess) return fail_hip(e, (wh + ": qkv projection launch").c_str());
+        q = h->qs;
+        k = h->ks;
+        v = h->vs;
+    } else {
+        e = bra::launch_pool_qk(h->params, h->bf16, q, k, lepe_w, h->means, h->lepe_table, s);
+        if (e != hipSuccess) return fail_hip(e, (wh + ": region-pool launch").c_str());
+    }
+    if (h->kd) {
+        e = bra::launch_kv_pool(h->params, h->bf16, k, v, h->kd, h->vd, s);
+        if (e != hipSuccess) return fail_hip(e, (wh + ": K/V downsampling launch").c_str());
+    }
+    if (timed && (e = hipEventRecord(ev[1], s)) != hipSuccess)
+        return fail_hip(e, (wh + ": hipEventRecord").c_str());
+    // the routing goes to the caller's buffer when one is given
+    int32_t* routing = routing_idx ? routing_idx : h->routing;
+    // small region grids are routed inside the attention kernel
+    if (!bra::route_in_attend(h->params)) {
+        e = bra::launch_route(h->params, h->bf16, h->means, routing, s);
+        if (e != hipSuccess) return fail_hip(e, (wh + ": routing launch").c_str());
+    }
+    if (timed && (e = hipEventRecord(ev[2], s)) != hipSuccess)
+        return fail_hip(e, (wh + ": hipEventRecord").c_str());
+    e = bra::launch_attend(h->params, h->bf16, q, v, h->kd ? h->kd : k, h->vd ? h->vd : v,
+                           h->means, routing, !bra::route_in_attend(h->params), lepe_w, lepe_b,
+                           h->lepe_table, h->zero_bias, w_o, b_o, out, s);
+    if (e != hipSuccess) return fail_hip(e, (wh + ": attention launch").c_str());
+    if (timed) {
+        if ((e = hipEventRecord(ev[3], s)) != hipSuccess)
+            return fail_hip(e, (wh + ": hipEventRecord").c_str());
+        ++h->timing_used;
+    }
+    return BRA_OK;
+}
+
 bra_status_t bra_forward(bra_handle_t h, const void* q, const void* k, const void* v,
                          const float* lepe_w, const float* lepe_b, void* out,
                          int32_t* routing_idx, void* stream) {
     bra_status_t st = check_forward_args(h, "bra_forward", q, k, v, lepe_w, lepe_b, out,
                                          routing_idx);
     if (st != BRA_OK) return st;
-    hipError_t e;
+    return enqueue_forward(h, "bra_forward", nullptr, nullptr, nullptr, q, k, v, lepe_w, lepe_b,
+                           nullptr, nullptr, out, routing_idx, static_cast<hipStream_t>(stream));
+}
 
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    const bool timed = h->timing_used < h->timing_capacity;
-    hipEvent_t* ev = timed ? &h->events[kEventsPerCall * h->timing_used] : nullptr;
-    if (timed && (e = hipEventRecord(ev[0], s)) != hipSuccess)
-        return fail_hip(e, "bra_forward: hipEventRecord");
-    e = bra::launch_pool_qk(h->params, h->bf16, q, k, lepe_w, h->means, h->lepe_table, s);
-    if (e != hipSuccess) return fail_hip(e, "bra_forward: region-pool launch");
-    if (h->kd) {
-        e = bra::launch_kv_pool(h->params, h->bf16, k, v, h->kd, h->vd, s);
-        if (e != hipSuccess) return fail_hip(e, "bra_forward: K/V downsampling launch");
-    }
-    if (timed && (e = hipEventRecord(ev[1], s)) != hipSuccess)
-        return fail_hip(e, "bra_forward: hipEventRecord");
-    // the routing goes to the caller's buffer when one is given
-    int32_t* routing = routing_idx ? routing_idx : h->routing;
-    // small region grids are routed inside the attention kernel
-    if (!bra::route_in_attend(h->params)) {
-        e = bra::launch_route(h->params, h->bf16, h->means, routing, s);
-        if (e != hipSuccess) return fail_hip(e, "bra_forward: routing launch");
-    }
-    if (timed && (e = hipEventRecord(ev[2], s)) != hipSuccess)
-        return fail_hip(e, "bra_forward: hipEventRecord");
-    e = bra::launch_attend(h->params, h->bf16, q, v, h->kd ? h->kd : k, h->vd ? h->vd : v,
-                           h->means, routing, !bra::route_in_attend(h->params), lepe_w, lepe_b,
-                           h->lepe_table, h->zero_bias, out, s);
-    if (e != hipSuccess) return fail_hip(e, "bra_forward: attention launch");
-    if (timed) {
-        if ((e = hipEventRecord(ev[3], s)) != hipSuccess)
-            return fail_hip(e, "bra_forward: hipEventRecord");
-        ++h->timing_used;
-    }
-    return BRA_OK;
+bra_status_t bra_forward_proj(bra_handle_t h, const void* x, const void* w_qkv,
+                              const float* b_qkv, const float* lepe_w, const float* lepe_b,
+                              const void* w_o, const float* b_o, void* out,
+                              int32_t* routing_idx, void* stream) {
+    bra_status_t st = check_forward_args(h, "bra_forward_proj", x, x, x, lepe_w, lepe_b, out,
+                                         routing_idx);
+    if (st != BRA_OK) return st;
+    if (!h->qs)
+        return fail(BRA_ERR_UNSUPPORTED,
+                    "bra_forward_proj: the handle was created without projections");
+    if (!w_qkv || !w_o) return fail(BRA_ERR_NULL, "bra_forward_proj: w_qkv and w_o are required");
+    if (!aligned(w_qkv, 16) || !aligned(w_o, 16) || !aligned(b_qkv, 4) || !aligned(b_o, 4))
+        return fail(BRA_ERR_ALIGN,
+                    "bra_forward_proj: w_qkv and w_o must be 16-byte aligned, the biases 4-byte");
+    return enqueue_forward(h, "bra_forward_proj", x, w_qkv, b_qkv, nullptr, nullptr, nullptr,
+                           lepe_w, lepe_b, w_o, b_o, out, routing_idx,
+                           static_cast<hipStream_t>(stream));
 }
 
 bra_status_t bra_forward_routed(bra_handle_t h, const void* q, const void* k, const void* v,
@@ -293,7 +351,7 @@ bra_status_t bra_forward_routed(bra_handle_t h, const void* q, const void* k, co
     }
     e = bra::launch_attend(h->params, h->bf16, q, v, h->kd ? h->kd : k, h->vd ? h->vd : v,
                            h->means, const_cast<int32_t*>(routing_idx), true, lepe_w, lepe_b,
-                           h->lepe_table, h->zero_bias, out, s);
+                           h->lepe_table, h->zero_bias, nullptr, nullptr, out, s);
     if (e != hipSuccess) return fail_hip(e, "bra_forward_routed: attention launch");
     return BRA_OK;
 }

@@ -610,7 +610,8 @@ attend_kernel(const T* __restrict__ q, const T* __restrict__ v, const T* __restr
               int32_t* __restrict__ routing,
               const float* __restrict__ lepe_w,
               const float* __restrict__ lepe_b, const float* __restrict__ lepe_bias,
-              const uint2* __restrict__ lepe_table, T* __restrict__ out, Params p_in) {
+              const uint2* __restrict__ lepe_table, const uint16_t* __restrict__ w_o,
+              const float* __restrict__ b_o, T* __restrict__ out, Params p_in) {
     const Params p = fold_geometry<HS, WS, NW, HEADS, KTOP, Elem<T>::kVec>(p_in);
     extern __shared__ __align__(16) unsigned char smem[];
     T* sVh = reinterpret_cast<T*>(smem + p.off_vh);
@@ -863,7 +864,49 @@ attend_kernel(const T* __restrict__ q, const T* __restrict__ v, const T* __restr
     }
     __syncthreads();
 
-    // 5. out = LePE + O, one rounding, 16-byte NHWC stores.
+    // 5. out = LePE + O, one rounding, 16-byte NHWC stores -- or, with the
+    //    output projection [P5 §五 ⑧ proj; P4 §1.1], out = (LePE + O) W_o^T + b_o
+    //    on MFMA: out^T tile = W_o[o0 .. o0+15, :] . Y^T, operand A row m the
+    //    Linear weight row o0 + m, operand B column n token n of the tile (its
+    //    fp32 row of LePE + O from LDS, rounded to bf16); lane (n, g) receives
+    //    output channels o0 + 4g .. o0 + 4g + 3 of token n, rounded once.
+    if constexpr (VEC == 8) {
+        if (p.out_proj) {
+            const int lane = tid & 63, n = lane & 15, g = lane >> 4;
+            const int otiles = p.C / 16, ttiles = (p.t + 15) / 16, ksteps = p.C / 32;
+            for (int job = w; job < otiles * ttiles; job += kWaves) {
+                const int tt = job / otiles, o0 = (job - tt * otiles) * 16;
+                const int tok = tt * 16 + n;
+                const float* yrow = sL + min(tok, p.t - 1) * p.lstride;
+                f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+                for (int s = 0; s < ksteps; ++s) {
+                    const uint4 a = *reinterpret_cast<const uint4*>(
+                        w_o + static_cast<size_t>(o0 + n) * p.C + 32 * s + 8 * g);
+                    const float4 y0 = *reinterpret_cast<const float4*>(yrow + 32 * s + 8 * g);
+                    const float4 y1 = *reinterpret_cast<const float4*>(yrow + 32 * s + 8 * g + 4);
+                    const u32x4_t yb = {f32_to_bf16(y0.x) | (f32_to_bf16(y0.y) << 16),
+                                        f32_to_bf16(y0.z) | (f32_to_bf16(y0.w) << 16),
+                                        f32_to_bf16(y1.x) | (f32_to_bf16(y1.y) << 16),
+                                        f32_to_bf16(y1.z) | (f32_to_bf16(y1.w) << 16)};
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, yb), acc, 0,
+                        0, 0);
+                }
+                if (tok < p.t) {
+                    const int c = o0 + 4 * g;
+                    float bo[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) bo[i] = b_o ? b_o[c + i] : 0.f;
+                    const uint32_t lo = f32_to_bf16(acc[0] + bo[0]) | (f32_to_bf16(acc[1] + bo[1]) << 16);
+                    const uint32_t hi = f32_to_bf16(acc[2] + bo[2]) | (f32_to_bf16(acc[3] + bo[3]) << 16);
+                    __builtin_nontemporal_store(
+                        u32x2_t{lo, hi},
+                        reinterpret_cast<u32x2_t*>(out + img + token_offset(p, r, tok) + c));
+                }
+            }
+            return;
+        }
+    }
     for (int i = tid; i < p.t * nvec; i += kThreads) {
         const int slot = i / nvec, pv = i - slot * nvec;
         const float* src = sL + slot * p.lstride + pv * VEC;
@@ -975,20 +1018,22 @@ bool plan(Params& p, int B, int H, int W, int C, int heads, int n_win, int k, fl
 hipError_t launch_attend(const Params& p, bool bf16, const void* q, const void* v,
                          const void* kg, const void* vg, const double* means, int32_t* routing,
                          bool use_routing, const float* lepe_w, const float* lepe_b,
-                         const uint2* lepe_table, const float* zero_bias, void* out,
-                         hipStream_t stream) {
+                         const uint2* lepe_table, const float* zero_bias, const void* w_o,
+                         const float* b_o, void* out, hipStream_t stream) {
     Params pp = p;
     pp.has_lepe = lepe_w != nullptr;
+    pp.out_proj = bf16 && w_o != nullptr;
     if (!pp.has_lepe) lepe_b = nullptr;
     // the MFMA LePE loads its bias unconditionally: a zero vector stands in
     const float* lepe_bias = lepe_b ? lepe_b : zero_bias;
     const dim3 grid(p.B * p.R), block(kThreads);
     const bool fused = !use_routing && route_in_attend(p);
+    const uint16_t* wo = static_cast<const uint16_t*>(w_o);
 #define BRA_ATTEND_F(T, HS, WS, NW, HEADS, KTOP, F)                                             \
     hipLaunchKernelGGL((attend_kernel<T, HS, WS, NW, HEADS, KTOP, F>), grid, block,             \
                        p.lds_bytes, stream, static_cast<const T*>(q), static_cast<const T*>(v), \
                        static_cast<const T*>(kg), static_cast<const T*>(vg), means, routing,   \
-                       lepe_w, lepe_b, lepe_bias, lepe_table, static_cast<T*>(out), pp)
+                       lepe_w, lepe_b, lepe_bias, lepe_table, wo, b_o, static_cast<T*>(out), pp)
 #define BRA_ATTEND(T, HS, WS, NW, HEADS, KTOP)                                                  \
     if (p.kv_ratio == 1 && matches(Inst<T, HS, WS, NW, HEADS, KTOP>::key, p, bf16, true)) {     \
         if constexpr (route_fused(NW * NW, HEADS)) {                                            \
@@ -1008,7 +1053,7 @@ hipError_t launch_attend(const Params& p, bool bf16, const void* q, const void* 
     hipLaunchKernelGGL((attend_kernel<T, 0, 0, 0, 0, 0, F>), grid, block, p.lds_bytes, stream,  \
                        static_cast<const T*>(q), static_cast<const T*>(v),                      \
                        static_cast<const T*>(kg), static_cast<const T*>(vg), means, routing,    \
-                       lepe_w, lepe_b, lepe_bias, lepe_table, static_cast<T*>(out), pp)
+                       lepe_w, lepe_b, lepe_bias, lepe_table, wo, b_o, static_cast<T*>(out), pp)
     if (bf16) {
         if (fused)
             BRA_GENERIC(uint16_t, true);

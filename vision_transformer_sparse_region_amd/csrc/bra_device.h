@@ -20,6 +20,7 @@ namespace bra {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
 typedef uint16_t u16x8_t __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) {

@@ -38,6 +38,7 @@ struct Params {
     int lepe_items;  // (channel pair, window row, 8-column block) work items
     int lepe_alias;  // 1: outputs overwrite the V halo after a single LePE round
     int lepe_mfma;   // 1: LePE on the 4x4x4 MFMA with a channel-planar halo
+    int out_proj;    // 1: the attention kernel applies the output projection (bf16)
     int halo_pieces; // 16-byte pieces of the V window with its 2-token halo
     // LDS byte offsets of the routing/attention kernel
     int off_vt, off_vh, off_l, off_w, off_idx, lds_bytes;
@@ -104,11 +105,20 @@ constexpr bool qmean_in_attend(bool bf16, bool fused, int t, int heads) {
 //   kernel or given by the caller); otherwise route in the kernel (needs
 //   route_in_attend) and write the ids to `routing`.
 //   zero_bias: C zero floats (device), used when lepe_b is NULL.
+//   w_o, b_o: the output projection (bf16 [C, C] Linear weight, fp32 [C] bias
+//   or NULL), applied in the kernel's epilogue; NULL w_o: none.
 hipError_t launch_attend(const Params& p, bool bf16, const void* q, const void* v,
                          const void* kg, const void* vg, const double* means, int32_t* routing,
                          bool use_routing, const float* lepe_w, const float* lepe_b,
-                         const uint2* lepe_table, const float* zero_bias, void* out,
-                         hipStream_t stream);
+                         const uint2* lepe_table, const float* zero_bias, const void* w_o,
+                         const float* b_o, void* out, hipStream_t stream);
+// The qkv projection [P5 §五 ①] of x (bf16 [B,H,W,C]) by w_qkv (bf16 [3C, C]
+// Linear weight) + b_qkv (fp32 [3C] or NULL) into qs, ks, vs (bf16
+// [B,H,W,C]), with the region means of the projected Q and K written to
+// `means` as launch_pool_qk does, and the MFMA LePE table when lepe_w is given.
+hipError_t launch_proj_qkv(const Params& p, const void* x, const void* w_qkv,
+                           const float* b_qkv, void* qs, void* ks, void* vs, double* means,
+                           const float* lepe_w, uint2* lepe_table, hipStream_t stream);
 // KV downsampling: k and v averaged over kv_ratio x kv_ratio blocks into
 // kd, vd ([B, kH, kW, C], the input dtype; fp32 sums, one rounding).
 hipError_t launch_kv_pool(const Params& p, bool bf16, const void* k, const void* v, void* kd,

@@ -26,7 +26,7 @@ from dataclasses import dataclass, replace
 
 import torch
 
-__all__ = ["Workload", "WORKLOADS", "make_inputs", "workload"]
+__all__ = ["Workload", "WORKLOADS", "make_inputs", "make_proj_weights", "workload"]
 
 
 @dataclass(frozen=True)
@@ -143,3 +143,19 @@ def make_inputs(wl: Workload) -> dict:
     else:
         lepe_b = torch.zeros((wl.channels,), dtype=torch.float32)
     return {"q": q, "k": k, "v": v, "lepe_w": lepe_w, "lepe_b": lepe_b}
+
+
+def make_proj_weights(wl: Workload, seed: int | None = None) -> dict:
+    """Random Linear weights of the module's projections (bf16, PyTorch [out, in]
+    layout) and fp32 biases, drawn in the order w_qkv, b_qkv, w_o, b_o from a
+    generator seeded with `seed` (default wl.seed + 1000): w ~ N(0, 1/C), so
+    a projection of N(0, 1) inputs has unit variance, and b ~ N(0, 0.02^2).
+    Synthetic stand-ins for trained weights; the draws only."""
+    gen = torch.Generator().manual_seed(wl.seed + 1000 if seed is None else seed)
+    C = wl.channels
+    std = C ** -0.5
+    w_qkv = (torch.randn((3 * C, C), generator=gen) * std).to(torch.bfloat16)
+    b_qkv = torch.randn((3 * C,), generator=gen) * 0.02
+    w_o = (torch.randn((C, C), generator=gen) * std).to(torch.bfloat16)
+    b_o = torch.randn((C,), generator=gen) * 0.02
+    return {"w_qkv": w_qkv, "b_qkv": b_qkv, "w_o": w_o, "b_o": b_o}
