@@ -63,7 +63,8 @@ def qmean_in_attend(wl, shared_routing: bool = False) -> bool:
     return wl.num_heads * ((qt + per_group - 1) // per_group) <= 4
 
 
-def algorithmic_bytes(wl, shared_routing: bool = False, kv_ratio: int = 1) -> dict:
+def algorithmic_bytes(wl, shared_routing: bool = False, kv_ratio: int = 1,
+                      projections: bool = False) -> dict:
     """Bytes each kernel must move once per launch (unique bytes; the k-fold
     re-reads of routed K/V, of the LePE halo and of the K means are cache
     traffic).  When the routing runs inside the attention kernel, that kernel
@@ -80,6 +81,15 @@ def algorithmic_bytes(wl, shared_routing: bool = False, kv_ratio: int = 1) -> di
     # attention then gathers the pooled K/V (2S/r^2) and still reads v for LePE
     kvpool = 2 * S + 2 * S // r2 if r2 > 1 else 0
     attend = (3 * S + 2 * S // r2 if r2 > 1 else 4 * S) + idx + lepe
+    if projections:
+        # the qkv projection reads x and the weights, writes q, k, v and both
+        # means; the attention kernel also reads the output weights
+        wq, wo = 3 * wl.channels * wl.channels * es, wl.channels * wl.channels * es
+        pool = S + wq + 3 * wl.channels * 4 + 3 * S + 2 * M + kvpool
+        att = attend + wo + wl.channels * 4
+        if route_in_attend(wl, shared_routing):
+            return {"pool": pool, "route": 0, "attend": att + 2 * M, "S": S}
+        return {"pool": pool, "route": 2 * M + idx, "attend": att, "S": S}
     if qmean_in_attend(wl, shared_routing):
         return {"pool": S + M + kvpool, "route": 0, "attend": attend + M, "S": S}
     if route_in_attend(wl, shared_routing):
@@ -199,6 +209,9 @@ def main(argv=None) -> int:
                     help="one routing per region for every head (full-C region affinity)")
     ap.add_argument("--kv-downsample", type=int, default=1,
                     help="KV downsampling ratio r (attention over r x r average-pooled K/V)")
+    ap.add_argument("--projections", action="store_true",
+                    help="time bra_forward_proj: the module's qkv and output projections "
+                         "around the path (random bf16 weights)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help=f"also run a {COPY_BYTES >> 20} MiB device copy (for counter scaling)")
     args = ap.parse_args(argv)
@@ -211,7 +224,8 @@ def main(argv=None) -> int:
     import torch
 
     from vision_transformer_sparse_region_amd import bra
-    from vision_transformer_sparse_region_amd.workloads import WORKLOADS, make_inputs
+    from vision_transformer_sparse_region_amd.workloads import (WORKLOADS, make_inputs,
+                                                               make_proj_weights)
 
     wl = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
@@ -228,11 +242,18 @@ def main(argv=None) -> int:
 
     h = bra.BRA(wl.batch, wl.height, wl.width, wl.channels, wl.num_heads, wl.n_win, wl.topk,
                 wl.dtype, shared_routing=args.shared_routing,
-                kv_downsample_ratio=args.kv_downsample)
+                kv_downsample_ratio=args.kv_downsample, projections=args.projections)
     stream = torch.cuda.current_stream()
+    wts = {n: t.to(dev) for n, t in make_proj_weights(wl).items()} if args.projections else None
 
     def step(i):
         d = sets[i % nsets]
+        if wts is not None:
+            # the module input x is the q set; the handle stages q, k, v
+            bra.bra_forward_proj(h.handle, d["q"], wts["w_qkv"], wts["b_qkv"], d["lepe_w"],
+                                 d["lepe_b"], wts["w_o"], wts["b_o"], d["out"], d["idx"],
+                                 stream.cuda_stream)
+            return
         bra.bra_forward(h.handle, d["q"], d["k"], d["v"], d["lepe_w"], d["lepe_b"], d["out"],
                         d["idx"], stream.cuda_stream)
 
@@ -271,7 +292,7 @@ def main(argv=None) -> int:
     route_ms = sum(t[1] for t in times) / len(times) \
         if not route_in_attend(wl, args.shared_routing) else None
     attn_ms = sum(t[2] for t in times) / len(times)
-    ab = algorithmic_bytes(wl, args.shared_routing, args.kv_downsample)
+    ab = algorithmic_bytes(wl, args.shared_routing, args.kv_downsample, args.projections)
     achieved = ab["attend"] / (attn_ms * 1e-3) / 1e9
     traffic = stored_traffic(wl.name)
     line = {
@@ -294,6 +315,7 @@ def main(argv=None) -> int:
             "topk": wl.topk, "buffer_sets": nsets,
             "routing": "shared by all heads" if args.shared_routing else "per head",
             "kv_downsample_ratio": args.kv_downsample,
+            "projections": bool(args.projections),
             "kernel_ms": {"region_pool": pool_ms, "route": route_ms, "attend": attn_ms},
             "wall_s": wall,
         },
@@ -312,7 +334,7 @@ def main(argv=None) -> int:
             1e9 / HBM_PEAK_GBS,
         },
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not args.projections:
         line["cpu_baseline"] = cpu_baseline(wl, host, sets[(args.steps - 1) % nsets]["out"].cpu(),
                                             shared=args.shared_routing,
                                             kv_ratio=args.kv_downsample)

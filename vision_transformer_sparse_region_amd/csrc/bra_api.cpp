@@ -129,6 +129,8 @@ bra_status_t bra_create(const bra_config_t* cfg, bra_handle_t* out) {
         return fail(BRA_ERR_SHAPE, "bra_create: projections must be 0 or 1");
     if (c.projections && !bf16)
         return fail(BRA_ERR_UNSUPPORTED, "bra_create: projections need dtype BRA_BF16");
+    if (c.projections && c.channels > 512)
+        return fail(BRA_ERR_UNSUPPORTED, "bra_create: projections need channels <= 512");
     const int kv_ratio = c.kv_downsample_ratio <= 1 ? 1 : c.kv_downsample_ratio;
     if ((c.height / c.n_win) % kv_ratio || (c.width / c.n_win) % kv_ratio)
         return fail(BRA_ERR_SHAPE,

@@ -874,34 +874,48 @@ attend_kernel(const T* __restrict__ q, const T* __restrict__ v, const T* __restr
         if (p.out_proj) {
             const int lane = tid & 63, n = lane & 15, g = lane >> 4;
             const int otiles = p.C / 16, ttiles = (p.t + 15) / 16, ksteps = p.C / 32;
-            for (int job = w; job < otiles * ttiles; job += kWaves) {
-                const int tt = job / otiles, o0 = (job - tt * otiles) * 16;
-                const int tok = tt * 16 + n;
-                const float* yrow = sL + min(tok, p.t - 1) * p.lstride;
-                f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-                for (int s = 0; s < ksteps; ++s) {
-                    const uint4 a = *reinterpret_cast<const uint4*>(
-                        w_o + static_cast<size_t>(o0 + n) * p.C + 32 * s + 8 * g);
-                    const float4 y0 = *reinterpret_cast<const float4*>(yrow + 32 * s + 8 * g);
-                    const float4 y1 = *reinterpret_cast<const float4*>(yrow + 32 * s + 8 * g + 4);
-                    const u32x4_t yb = {f32_to_bf16(y0.x) | (f32_to_bf16(y0.y) << 16),
-                                        f32_to_bf16(y0.z) | (f32_to_bf16(y0.w) << 16),
-                                        f32_to_bf16(y1.x) | (f32_to_bf16(y1.y) << 16),
-                                        f32_to_bf16(y1.z) | (f32_to_bf16(y1.w) << 16)};
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        __builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, yb), acc, 0,
-                        0, 0);
-                }
-                if (tok < p.t) {
-                    const int c = o0 + 4 * g;
-                    float bo[4];
+            constexpr int kMaxSteps = kMaxChannels / 32;
+            // wave w takes output tiles w, w + kWaves, ...: the tile's weight
+            // operands are loaded once and serve every token tile
+            for (int ot = w; ot < otiles; ot += kWaves) {
+                const int o0 = ot * 16, c = o0 + 4 * g;
+                uint4 a[kMaxSteps > 16 ? 16 : kMaxSteps];
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) bo[i] = b_o ? b_o[c + i] : 0.f;
-                    const uint32_t lo = f32_to_bf16(acc[0] + bo[0]) | (f32_to_bf16(acc[1] + bo[1]) << 16);
-                    const uint32_t hi = f32_to_bf16(acc[2] + bo[2]) | (f32_to_bf16(acc[3] + bo[3]) << 16);
-                    __builtin_nontemporal_store(
-                        u32x2_t{lo, hi},
-                        reinterpret_cast<u32x2_t*>(out + img + token_offset(p, r, tok) + c));
+                for (int s = 0; s < 16; ++s)
+                    if (s < ksteps)
+                        a[s] = *reinterpret_cast<const uint4*>(
+                            w_o + static_cast<size_t>(o0 + n) * p.C + 32 * s + 8 * g);
+                float bo[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) bo[i] = b_o ? b_o[c + i] : 0.f;
+                for (int tt = 0; tt < ttiles; ++tt) {
+                    const int tok = tt * 16 + n;
+                    const float* yrow = sL + min(tok, p.t - 1) * p.lstride;
+                    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int s = 0; s < 16; ++s)
+                        if (s < ksteps) {
+                            const float4 y0 =
+                                *reinterpret_cast<const float4*>(yrow + 32 * s + 8 * g);
+                            const float4 y1 =
+                                *reinterpret_cast<const float4*>(yrow + 32 * s + 8 * g + 4);
+                            const u32x4_t yb = {f32_to_bf16(y0.x) | (f32_to_bf16(y0.y) << 16),
+                                                f32_to_bf16(y0.z) | (f32_to_bf16(y0.w) << 16),
+                                                f32_to_bf16(y1.x) | (f32_to_bf16(y1.y) << 16),
+                                                f32_to_bf16(y1.z) | (f32_to_bf16(y1.w) << 16)};
+                            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                __builtin_bit_cast(bf16x8_t, a[s]),
+                                __builtin_bit_cast(bf16x8_t, yb), acc, 0, 0, 0);
+                        }
+                    if (tok < p.t) {
+                        const uint32_t lo =
+                            f32_to_bf16(acc[0] + bo[0]) | (f32_to_bf16(acc[1] + bo[1]) << 16);
+                        const uint32_t hi =
+                            f32_to_bf16(acc[2] + bo[2]) | (f32_to_bf16(acc[3] + bo[3]) << 16);
+                        __builtin_nontemporal_store(
+                            u32x2_t{lo, hi},
+                            reinterpret_cast<u32x2_t*>(out + img + token_offset(p, r, tok) + c));
+                    }
                 }
             }
             return;

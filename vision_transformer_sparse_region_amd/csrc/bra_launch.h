@@ -116,6 +116,8 @@ hipError_t launch_attend(const Params& p, bool bf16, const void* q, const void* 
 // Linear weight) + b_qkv (fp32 [3C] or NULL) into qs, ks, vs (bf16
 // [B,H,W,C]), with the region means of the projected Q and K written to
 // `means` as launch_pool_qk does, and the MFMA LePE table when lepe_w is given.
+// (C <= 512; its dynamic LDS is proj_qkv_lds_bytes, at most 64 KB)
+int proj_qkv_lds_bytes(const Params& p);
 hipError_t launch_proj_qkv(const Params& p, const void* x, const void* w_qkv,
                            const float* b_qkv, void* qs, void* ks, void* vs, double* means,
                            const float* lepe_w, uint2* lepe_table, hipStream_t stream);
