@@ -100,7 +100,9 @@ typedef struct {
     int32_t projections;    /* 1: the handle also runs bra_forward_proj (the
                                module's qkv and output projections around the
                                path, [P5 §五 ① and ⑧]); its workspace then holds
-                               the projected q, k, v.  bf16 only.  0: none */
+                               the projected q, k, v.  bf16, C <= 512, per-head
+                               routing and no KV downsampling only
+                               (BRA_ERR_UNSUPPORTED otherwise).  0: none */
 } bra_config_t;
 
 /* Validate cfg and allocate the handle and its device workspace on the

@@ -50,6 +50,9 @@ def _cfg(**kw):
     (dict(shared_routing=2), bra.BRA_ERR_SHAPE),   # a flag: 0 or 1
     (dict(projections=2), bra.BRA_ERR_SHAPE),      # a flag: 0 or 1
     (dict(projections=1, dtype=bra.BRA_F32), bra.BRA_ERR_UNSUPPORTED),  # bf16 only
+    (dict(projections=1, shared_routing=1), bra.BRA_ERR_UNSUPPORTED),  # per-head routing only
+    (dict(projections=1, kv_downsample_ratio=2), bra.BRA_ERR_UNSUPPORTED),  # no KV downsampling
+    (dict(projections=1, channels=544, num_heads=17), bra.BRA_ERR_UNSUPPORTED),  # C <= 512
     (dict(kv_downsample_ratio=3), bra.BRA_ERR_SHAPE),  # 3 does not divide the 4x4 windows
     (dict(height=4096, width=4096, n_win=256, channels=32, num_heads=1),
      bra.BRA_ERR_UNSUPPORTED),                     # H*W = 2^24 tokens: beyond 24-bit indexing

@@ -132,6 +132,9 @@ bra_status_t bra_create(const bra_config_t* cfg, bra_handle_t* out) {
     if (c.projections && c.channels > 512)
         return fail(BRA_ERR_UNSUPPORTED, "bra_create: projections need channels <= 512");
     const int kv_ratio = c.kv_downsample_ratio <= 1 ? 1 : c.kv_downsample_ratio;
+    if (c.projections && (c.shared_routing == 1 || kv_ratio > 1))
+        return fail(BRA_ERR_UNSUPPORTED,
+                    "bra_create: projections combine with neither shared_routing nor KV downsampling");
     if ((c.height / c.n_win) % kv_ratio || (c.width / c.n_win) % kv_ratio)
         return fail(BRA_ERR_SHAPE,
                     "bra_create: kv_downsample_ratio must divide the window height and width");
