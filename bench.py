@@ -49,6 +49,12 @@ def route_in_attend(wl, shared_routing: bool = False) -> bool:
     return wl.regions <= 64 and wl.num_heads <= 4 and not shared_routing
 
 
+def out_proj_in_attend(wl) -> bool:
+    """The output projection runs in the attention kernel's epilogue when
+    C <= 4 t, else as a kernel of its own over the attention output."""
+    return wl.channels <= 4 * wl.tokens_per_region
+
+
 def qmean_in_attend(wl, shared_routing: bool = False) -> bool:
     """bf16 maps routed inside the attention kernel whose query tiles fit the
     four waves' first jobs: the attention kernel sums the Q means itself and
@@ -83,7 +89,9 @@ def algorithmic_bytes(wl, shared_routing: bool = False, kv_ratio: int = 1,
     attend = (3 * S + 2 * S // r2 if r2 > 1 else 4 * S) + idx + lepe
     if projections:
         # the qkv projection reads x and the weights, writes q, k, v and both
-        # means; the attention kernel also reads the output weights
+        # means; the attention kernel also reads the output weights.  (When
+        # the output projection is a kernel of its own, the attention slot
+        # times both kernels; y's round trip between them is not counted.)
         wq, wo = 3 * wl.channels * wl.channels * es, wl.channels * wl.channels * es
         pool = S + wq + 3 * wl.channels * 4 + 3 * S + 2 * M + kvpool
         att = attend + wo + wl.channels * 4
@@ -316,6 +324,8 @@ def main(argv=None) -> int:
             "routing": "shared by all heads" if args.shared_routing else "per head",
             "kv_downsample_ratio": args.kv_downsample,
             "projections": bool(args.projections),
+            **({"output_projection": "attention epilogue" if out_proj_in_attend(wl)
+                else "own kernel"} if args.projections else {}),
             "kernel_ms": {"region_pool": pool_ms, "route": route_ms, "attend": attn_ms},
             "wall_s": wall,
         },

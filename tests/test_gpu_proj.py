@@ -50,6 +50,12 @@ CASES = [
     Workload("proj_stage3_b2", 2, 14, 14, 256, 8, 7, 16, "bf16", 403),
     Workload("proj_ragged_t15", 2, 12, 20, 64, 2, 4, 3, "bf16", 404, lepe_bias=True),
     Workload("proj_r100", 1, 40, 40, 96, 3, 10, 5, "bf16", 405),
+    # the output projection as its own kernel (C > 8 t): ragged last row slice,
+    # one head (half a channel chunk), C > 256 (32-token slices), stage 4
+    Workload("proj_out_ragged_rows", 1, 10, 10, 128, 4, 5, 3, "bf16", 408, lepe_bias=True),
+    Workload("proj_one_head_t2", 3, 8, 4, 32, 1, 4, 2, "bf16", 409),
+    Workload("proj_wide_c320", 1, 14, 14, 320, 10, 7, 4, "bf16", 410),
+    Workload("proj_stage4_b2", 2, 7, 7, 512, 16, 7, 49, "bf16", 411),
 ]
 
 
@@ -90,11 +96,16 @@ def test_projected_forward_matches_oracle(wl):
 
 
 @pytest.mark.parametrize("wl", [WORKLOADS["stage1"].with_(batch=4),
-                                Workload("eye_generic", 2, 12, 20, 64, 2, 4, 3, "bf16", 406)],
-                         ids=["stage1_b4", "generic"])
+                                Workload("eye_generic", 2, 12, 20, 64, 2, 4, 3, "bf16", 406),
+                                WORKLOADS["stage3"].with_(batch=2),
+                                Workload("eye_generic_small_t", 1, 10, 10, 128, 4, 5, 3, "bf16",
+                                         412)],
+                         ids=["stage1_b4", "generic", "stage3_b2", "generic_small_t"])
 def test_identity_projections_equal_plain_forward(wl):
     """w_qkv = [I; I; I], w_o = I, no biases: q = k = v = x exactly, and
-    out = bf16(y), the plain forward's own rounding -- bit for bit."""
+    out = bf16(y), the plain forward's own rounding -- bit for bit, with the
+    output projection in the attention epilogue (stage 1, generic) and as
+    its own kernel (stage 3, generic with small regions)."""
     inp = make_inputs(wl)
     C = wl.channels
     eye = torch.eye(C, dtype=torch.bfloat16)

@@ -33,6 +33,8 @@ struct bra_handle_s {
     void* qs;  // projected q, k, v [B, H, W, C] (handles created with projections), else NULL
     void* ks;
     void* vs;
+    void* ys;  // attention output before the output projection, when that runs as its own
+               // kernel (projections on shapes with small regions), else NULL
     // per-kernel timing (events recorded by bra_forward while slots remain)
     std::vector<hipEvent_t> events;  // kEventsPerCall per recorded call
     int timing_capacity;
@@ -166,7 +168,8 @@ bra_status_t bra_create(const bra_config_t* cfg, bra_handle_t* out) {
     // projected q, k, v (projections only)
     const size_t map_bytes = static_cast<size_t>(c.batch) * c.height * c.width * c.channels *
                              (bf16 ? 2 : 4);
-    const size_t proj_bytes = c.projections ? 3 * map_bytes : 0;
+    const bool proj_after = c.projections && !bra::out_proj_in_attend(p.t, c.channels);
+    const size_t proj_bytes = c.projections ? (proj_after ? 4 : 3) * map_bytes : 0;
     h->means_bytes = mean_bytes + route_bytes + table_bytes + zero_bytes + 2 * kv_bytes +
                      proj_bytes;
     h->means = nullptr;
@@ -175,7 +178,7 @@ bra_status_t bra_create(const bra_config_t* cfg, bra_handle_t* out) {
     h->zero_bias = nullptr;
     h->kd = nullptr;
     h->vd = nullptr;
-    h->qs = h->ks = h->vs = nullptr;
+    h->qs = h->ks = h->vs = h->ys = nullptr;
     h->timing_capacity = 0;
     h->timing_used = 0;
     e = hipMalloc(reinterpret_cast<void**>(&h->means), h->means_bytes);
@@ -194,10 +197,11 @@ bra_status_t bra_create(const bra_config_t* cfg, bra_handle_t* out) {
         h->qs = reinterpret_cast<char*>(h->zero_bias) + zero_bytes + 2 * kv_bytes;
         h->ks = static_cast<char*>(h->qs) + map_bytes;
         h->vs = static_cast<char*>(h->ks) + map_bytes;
+        if (proj_after) h->ys = static_cast<char*>(h->vs) + map_bytes;
     }
     e = hipMemset(h->zero_bias, 0, zero_bytes);
     if (e != hipSuccess) {
-        hipFree(h->means);
+        (void)hipFree(h->means);
         delete h;
         return fail_hip(e, "bra_create: hipMemset of the zero bias");
     }
@@ -293,10 +297,18 @@ static bra_status_t enqueue_forward(bra_handle_t h, const char* what, const void
     }
     if (timed && (e = hipEventRecord(ev[2], s)) != hipSuccess)
         return fail_hip(e, (wh + ": hipEventRecord").c_str());
+    // the output projection: in the attention kernel's epilogue, or over y
+    // in a kernel of its own (h->ys is set for the shapes that take that)
+    const bool proj_after = w_o && h->ys;
     e = bra::launch_attend(h->params, h->bf16, q, v, h->kd ? h->kd : k, h->vd ? h->vd : v,
                            h->means, routing, !bra::route_in_attend(h->params), lepe_w, lepe_b,
-                           h->lepe_table, h->zero_bias, w_o, b_o, out, s);
+                           h->lepe_table, h->zero_bias, proj_after ? nullptr : w_o, b_o,
+                           proj_after ? h->ys : out, s);
     if (e != hipSuccess) return fail_hip(e, (wh + ": attention launch").c_str());
+    if (proj_after) {
+        e = bra::launch_proj_out(h->params, h->ys, w_o, b_o, out, s);
+        if (e != hipSuccess) return fail_hip(e, (wh + ": output projection launch").c_str());
+    }
     if (timed) {
         if ((e = hipEventRecord(ev[3], s)) != hipSuccess)
             return fail_hip(e, (wh + ": hipEventRecord").c_str());

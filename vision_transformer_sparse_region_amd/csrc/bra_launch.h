@@ -116,11 +116,23 @@ hipError_t launch_attend(const Params& p, bool bf16, const void* q, const void* 
 // Linear weight) + b_qkv (fp32 [3C] or NULL) into qs, ks, vs (bf16
 // [B,H,W,C]), with the region means of the projected Q and K written to
 // `means` as launch_pool_qk does, and the MFMA LePE table when lepe_w is given.
-// (C <= 512; its dynamic LDS is proj_qkv_lds_bytes, at most 64 KB)
+// (C <= 512; its dynamic LDS is proj_qkv_lds_bytes, at most 45 KB)
 int proj_qkv_lds_bytes(const Params& p);
 hipError_t launch_proj_qkv(const Params& p, const void* x, const void* w_qkv,
                            const float* b_qkv, void* qs, void* ks, void* vs, double* means,
                            const float* lepe_w, uint2* lepe_table, hipStream_t stream);
+// The output projection [P5 §五 ⑧] runs in the attention kernel's epilogue
+// when a region has enough tokens to amortise the C x C weight that each
+// attention workgroup reads (C <= 4 t; measured, the epilogue saves 11 us
+// per forward at C = t, 64 x 64 tokens, and the separate kernel saves 4 us
+// at C = 8 t and 30 us at C = 64 t); otherwise the attention kernel stores y
+// (bf16) and launch_proj_out applies the projection over slices of the
+// token rows.  Both give the same bits: y rounded to bf16, the same MFMA
+// sums in the same order, one rounding.
+constexpr bool out_proj_in_attend(int t, int C) { return C <= 4 * t; }
+// out = y w_o^T + b_o over the B*H*W token rows of y (bf16 [B,H,W,C]).
+hipError_t launch_proj_out(const Params& p, const void* y, const void* w_o, const float* b_o,
+                           void* out, hipStream_t stream);
 // KV downsampling: k and v averaged over kv_ratio x kv_ratio blocks into
 // kd, vd ([B, kH, kW, C], the input dtype; fp32 sums, one rounding).
 hipError_t launch_kv_pool(const Params& p, bool bf16, const void* k, const void* v, void* kd,
