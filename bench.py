@@ -213,6 +213,8 @@ def main(argv=None) -> int:
     ap.add_argument("--buffer-sets", type=int, default=0,
                     help="input/output sets to rotate over (0: enough to exceed the MALL)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the pass that replays the forwards as one captured HIP graph")
     ap.add_argument("--shared-routing", action="store_true",
                     help="one routing per region for every head (full-C region affinity)")
     ap.add_argument("--kv-downsample", type=int, default=1,
@@ -256,14 +258,14 @@ def main(argv=None) -> int:
 
     def step(i):
         d = sets[i % nsets]
+        s = torch.cuda.current_stream().cuda_stream  # the capture stream inside a graph
         if wts is not None:
             # the module input x is the q set; the handle stages q, k, v
             bra.bra_forward_proj(h.handle, d["q"], wts["w_qkv"], wts["b_qkv"], d["lepe_w"],
-                                 d["lepe_b"], wts["w_o"], wts["b_o"], d["out"], d["idx"],
-                                 stream.cuda_stream)
+                                 d["lepe_b"], wts["w_o"], wts["b_o"], d["out"], d["idx"], s)
             return
         bra.bra_forward(h.handle, d["q"], d["k"], d["v"], d["lepe_w"], d["lepe_b"], d["out"],
-                        d["idx"], stream.cuda_stream)
+                        d["idx"], s)
 
     for i in range(args.warmup):
         step(i)
@@ -279,6 +281,24 @@ def main(argv=None) -> int:
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     gpu_ms = start.elapsed_time(end)
+    # The same forwards captured once as a HIP graph (one forward per buffer
+    # set) and replayed about K / sets times: the host's launch cost is gone.
+    graph_ms = None
+    if not args.no_graph:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=torch.cuda.Stream()):
+            for i in range(nsets):
+                step(i)
+        reps = max(1, args.steps // nsets)
+        g.replay()
+        torch.cuda.synchronize()
+        start.record(stream)
+        for _ in range(reps):
+            g.replay()
+        end.record(stream)
+        torch.cuda.synchronize()
+        graph_ms = start.elapsed_time(end) / (reps * nsets)
+        del g
     # Per-kernel breakdown: the same K forwards again, over the same buffer
     # sets, with the library recording HIP events on the launch stream before
     # the first kernel and after each of the three (event records between
@@ -344,6 +364,9 @@ def main(argv=None) -> int:
             1e9 / HBM_PEAK_GBS,
         },
     }
+    if graph_ms is not None:
+        line["graph"] = {"ms_per_step": graph_ms, "value": wl.tokens / (graph_ms * 1e-3),
+                         "unit": "tokens/s", "forwards_per_graph": nsets}
     if not args.no_cpu_baseline and not args.projections:
         line["cpu_baseline"] = cpu_baseline(wl, host, sets[(args.steps - 1) % nsets]["out"].cpu(),
                                             shared=args.shared_routing,
