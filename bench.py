@@ -49,6 +49,15 @@ def route_in_attend(wl, shared_routing: bool = False) -> bool:
     return wl.regions <= 64 and wl.num_heads <= 4 and not shared_routing
 
 
+def route_in_pool(wl, shared_routing: bool = False) -> bool:
+    """bf16 maps of at most 64 regions routed outside the attention kernel,
+    with regions of at most 16 tokens and R * t <= 256: one kernel computes
+    the region means and the routing."""
+    return (wl.dtype == "bf16" and not shared_routing and wl.regions <= 64 and
+            not route_in_attend(wl, shared_routing) and wl.tokens_per_region <= 16 and
+            wl.regions * wl.tokens_per_region <= 256)
+
+
 def out_proj_in_attend(wl) -> bool:
     """The output projection runs in the attention kernel's epilogue when
     C <= 4 t, else as a kernel of its own over the attention output."""
@@ -98,6 +107,9 @@ def algorithmic_bytes(wl, shared_routing: bool = False, kv_ratio: int = 1,
         if route_in_attend(wl, shared_routing):
             return {"pool": pool, "route": 0, "attend": att + 2 * M, "S": S}
         return {"pool": pool, "route": 2 * M + idx, "attend": att, "S": S}
+    if route_in_pool(wl, shared_routing):
+        # one kernel reads q and k and writes the ids; no mean array in HBM
+        return {"pool": 2 * S + idx + kvpool, "route": 0, "attend": attend, "S": S}
     if qmean_in_attend(wl, shared_routing):
         return {"pool": S + M + kvpool, "route": 0, "attend": attend + M, "S": S}
     if route_in_attend(wl, shared_routing):
@@ -317,8 +329,9 @@ def main(argv=None) -> int:
     pool_ms = sum(t[0] for t in times) / len(times)
     # (no routing kernel runs when the attention kernel routes: the interval
     # between its two events is empty)
-    route_ms = sum(t[1] for t in times) / len(times) \
-        if not route_in_attend(wl, args.shared_routing) else None
+    fused_route = route_in_attend(wl, args.shared_routing) or \
+        (route_in_pool(wl, args.shared_routing) and not args.projections)
+    route_ms = sum(t[1] for t in times) / len(times) if not fused_route else None
     attn_ms = sum(t[2] for t in times) / len(times)
     ab = algorithmic_bytes(wl, args.shared_routing, args.kv_downsample, args.projections)
     achieved = ab["attend"] / (attn_ms * 1e-3) / 1e9

@@ -44,6 +44,23 @@ def test_algorithmic_bytes_highres_separate_route():
     assert ab["attend"] == 4 * S + idx + 64 * 26 * 4
 
 
+def test_algorithmic_bytes_stage3_means_and_routing_in_one_kernel():
+    wl = WORKLOADS["stage3"]
+    assert bench.route_in_pool(wl)
+    ab = bench.algorithmic_bytes(wl)
+    S = 64 * 14 * 14 * 256 * 2
+    idx = 64 * 8 * 49 * 16 * 4
+    # one kernel reads q and k and writes the ids; the means stay on chip
+    assert ab["pool"] == 2 * S + idx
+    assert ab["route"] == 0
+    assert ab["attend"] == 4 * S + idx + 256 * 26 * 4
+    # the other shapes keep their kernels
+    assert not bench.route_in_pool(WORKLOADS["stage1"])    # routed in the attention kernel
+    assert not bench.route_in_pool(WORKLOADS["highres"])   # 256 regions
+    assert not bench.route_in_pool(WORKLOADS["tiny_f32"])  # fp32
+    assert not bench.route_in_pool(wl, shared_routing=True)
+
+
 def test_attention_flops_highres():
     wl = WORKLOADS["highres"]
     # 4 * tokens * heads * k * t * head_dim

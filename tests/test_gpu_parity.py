@@ -51,6 +51,12 @@ SMALL = [
     Workload("r256_topk5_generic", 1, 64, 64, 64, 2, 16, 5, "bf16", 126, smooth=True),
     Workload("eight_heads_topk1", 2, 28, 28, 256, 8, 7, 1, "bf16", 127),
     Workload("r9_eight_heads", 3, 12, 12, 256, 8, 3, 2, "bf16", 128),
+    # region means and routing in one kernel (more than four heads, regions
+    # of at most 16 tokens, R * t <= 256): 2 x 3 windows, 64 regions of 4
+    # tokens with the arg-max, 4 regions (rows of the 16-row chunk clamped)
+    Workload("pool_route_ragged", 2, 12, 18, 192, 6, 6, 5, "bf16", 129, lepe_bias=True),
+    Workload("pool_route_r64_topk1", 1, 16, 16, 160, 5, 8, 1, "bf16", 130),
+    Workload("pool_route_r4", 3, 8, 8, 192, 6, 2, 3, "bf16", 131),
     Workload("f32_stage2_shape", 4, 28, 28, 128, 4, 7, 4, "f32", 109),
     Workload("f32_ragged_bias", 2, 12, 20, 64, 2, 4, 3, "f32", 110, lepe_bias=True),
 ]
@@ -82,13 +88,17 @@ def test_routing_export_optional_and_deterministic():
     assert (ia == ib).all()
 
 
-def test_exact_ties_pick_lower_regions():
+@pytest.mark.parametrize("wl", [Workload("all_tied", 2, 28, 28, 128, 4, 7, 6, "bf16", 114),
+                                Workload("all_tied_pool_route", 2, 14, 14, 256, 8, 7, 6, "bf16",
+                                         132)],
+                         ids=["attention_kernel_routes", "pool_kernel_routes"])
+def test_exact_ties_pick_lower_regions(wl):
     """Every K window identical: all affinities of a row tie exactly, so the
     routing is regions 0..k-1 in order."""
-    wl = Workload("all_tied", 2, 28, 28, 128, 4, 7, 6, "bf16", 114)
     inp = make_inputs(wl)
-    tile = inp["k"][:, :4, :4, :].clone()
-    inp["k"] = tile.repeat(1, 7, 7, 1).contiguous()
+    hs, ws = wl.height // wl.n_win, wl.width // wl.n_win
+    tile = inp["k"][:, :hs, :ws, :].clone()
+    inp["k"] = tile.repeat(1, wl.n_win, wl.n_win, 1).contiguous()
     say("[gpu] all_tied")
     _, idx = run_gpu(wl, inp)
     assert (idx == np.arange(6, dtype=np.int32)).all()

@@ -271,6 +271,12 @@ static bra_status_t enqueue_forward(bra_handle_t h, const char* what, const void
     hipEvent_t* ev = timed ? &h->events[kEventsPerCall * h->timing_used] : nullptr;
     if (timed && (e = hipEventRecord(ev[0], s)) != hipSuccess)
         return fail_hip(e, (wh + ": hipEventRecord").c_str());
+    // the routing goes to the caller's buffer when one is given
+    int32_t* routing = routing_idx ? routing_idx : h->routing;
+    const bra::Params& P = h->params;
+    // small region grids with many heads: means and routing in one kernel
+    const bool pool_route =
+        !x && bra::route_in_pool(h->bf16, P.shared != 0, P.R, P.heads, P.t);
     if (x) {
         e = bra::launch_proj_qkv(h->params, x, w_qkv, b_qkv, h->qs, h->ks, h->vs, h->means,
                                  lepe_w, h->lepe_table, s);
@@ -278,6 +284,9 @@ static bra_status_t enqueue_forward(bra_handle_t h, const char* what, const void
         q = h->qs;
         k = h->ks;
         v = h->vs;
+    } else if (pool_route) {
+        e = bra::launch_pool_route(h->params, q, k, lepe_w, h->lepe_table, routing, s);
+        if (e != hipSuccess) return fail_hip(e, (wh + ": region-pool and routing launch").c_str());
     } else {
         e = bra::launch_pool_qk(h->params, h->bf16, q, k, lepe_w, h->means, h->lepe_table, s);
         if (e != hipSuccess) return fail_hip(e, (wh + ": region-pool launch").c_str());
@@ -288,10 +297,8 @@ static bra_status_t enqueue_forward(bra_handle_t h, const char* what, const void
     }
     if (timed && (e = hipEventRecord(ev[1], s)) != hipSuccess)
         return fail_hip(e, (wh + ": hipEventRecord").c_str());
-    // the routing goes to the caller's buffer when one is given
-    int32_t* routing = routing_idx ? routing_idx : h->routing;
     // small region grids are routed inside the attention kernel
-    if (!bra::route_in_attend(h->params)) {
+    if (!bra::route_in_attend(h->params) && !pool_route) {
         e = bra::launch_route(h->params, h->bf16, h->means, routing, s);
         if (e != hipSuccess) return fail_hip(e, (wh + ": routing launch").c_str());
     }

@@ -73,6 +73,19 @@ constexpr bool route_fused(int R, int heads) {
 }
 inline bool route_in_attend(const Params& p) { return !p.shared && route_fused(p.R, p.heads); }
 
+// Small region grids routed outside the attention kernel (per head, bf16)
+// with small regions: one kernel computes the region means and routes
+// (pool_route_kernel), staging one head's K of every region (R * t * 64
+// bytes, at most 16 KB) and Q of 16 regions (at most 16 KB) in LDS; no mean
+// array goes to HBM.
+constexpr bool route_in_pool(bool bf16, bool shared, int R, int heads, int t) {
+    return bf16 && !shared && R <= 64 && !route_fused(R, heads) && t <= 16 && R * t <= 256;
+}
+int pool_route_lds(const Params& p);
+hipError_t launch_pool_route(const Params& p, const void* q, const void* k,
+                             const float* lepe_w, uint2* lepe_table, int32_t* idx,
+                             hipStream_t stream);
+
 // How the attention kernel splits a region's queries into wave jobs: QT tiles
 // of 16 queries per head, in G groups of tpg tiles (at most kMaxQTiles); a
 // job is one (head, group), heads * G jobs in all, dealt to the waves

@@ -251,6 +251,168 @@ route_large_kernel(const double* __restrict__ means, int32_t* __restrict__ idx_o
     }
 }
 
+// ---------------------------------------------------------------------------
+// Region means and routing in one kernel, for small region grids routed
+// outside the attention kernel (R <= 64 with more than kWaves heads, bf16,
+// per head) whose K for one head fits LDS.  Workgroup (image b, head h,
+// chunk of route_rows(64) query rows):
+//   1. K of head h for all R regions (R * t tokens, 64 bytes each) and Q of
+//      the chunk's regions reach LDS by LDS DMA (global_load_lds_dwordx4: a
+//      wave instruction fills 64 consecutive 16-byte slots, lane L slot L).
+//   2. Threads take (region, dim) items: the exact fp64 sum of the t bf16
+//      values divided by t -- bit for bit the pool kernel's mean -- into
+//      K-bar [32][R] (lane s reads region s) and Q-bar [rows][32], which
+//      overlay the staged K and Q once every sum is taken.
+//   3. Each wave routes kRouteChains rows as route_small_kernel does, from
+//      the LDS means.
+// The means never go to HBM, and the routing needs no second launch.
+constexpr int kPoolRouteRows = kWaves * kRouteChains;
+
+// 16-byte slots of one head's K (R * t tokens, 4 slots each) and of the
+// chunk's Q, in whole DMA rounds of kThreads slots.
+__host__ __device__ constexpr int pr_k_rounds(int R, int t) {
+    return (R * t * 4 + kThreads - 1) / kThreads;
+}
+__host__ __device__ constexpr int pr_q_rounds(int t) {
+    return (kPoolRouteRows * t * 4 + kThreads - 1) / kThreads;
+}
+// LDS: staged K, then K-bar over it; staged Q, then Q-bar over it.
+__host__ __device__ constexpr int pr_k_bytes(int R, int t) {
+    return pr_k_rounds(R, t) * kThreads * 16 > kHeadDim * R * 8 ? pr_k_rounds(R, t) * kThreads * 16
+                                                                 : kHeadDim * R * 8;
+}
+__host__ __device__ constexpr int pr_q_bytes(int t) {
+    return pr_q_rounds(t) * kThreads * 16 > kPoolRouteRows * kHeadDim * 8
+               ? pr_q_rounds(t) * kThreads * 16
+               : kPoolRouteRows * kHeadDim * 8;
+}
+__host__ __device__ constexpr int pool_route_lds_bytes(int R, int t) {
+    return pr_k_bytes(R, t) + pr_q_bytes(t);
+}
+// (region, dim) mean items per thread: at most 64 regions of 32 dims, and
+// the chunk's 16 query rows.
+constexpr int kKMeanItems = 64 * kHeadDim / kThreads;
+constexpr int kQMeanItems = kPoolRouteRows * kHeadDim / kThreads;
+
+template <int HS, int WS, int NW, int HEADS, int KTOP>
+__global__ __launch_bounds__(kThreads) void pool_route_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, int32_t* __restrict__ idx_out,
+    const float* __restrict__ lepe_w, uint2* __restrict__ lepe_table, Params p_in) {
+    const Params p = fold_geometry<HS, WS, NW, HEADS, KTOP, 8>(p_in);
+    extern __shared__ __align__(16) unsigned char smem[];
+    const int R = p.R, t = p.t, tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int nchunk = (R + kPoolRouteRows - 1) / kPoolRouteRows;
+    const int tasks = p.B * p.heads * nchunk;
+    if (static_cast<int>(blockIdx.x) >= tasks) {
+        // trailing workgroups: the Toeplitz operands of the MFMA LePE
+        const int it = (blockIdx.x - tasks) * kThreads + tid;
+        if (it < p.table_items) lepe_table[it] = lepe_toeplitz_entry(lepe_w, it);
+        return;
+    }
+    const int krounds = pr_k_rounds(R, t), qrounds = pr_q_rounds(t);
+    uint16_t* sK = reinterpret_cast<uint16_t*>(smem);                    // [R * t][32]
+    uint16_t* sQ = reinterpret_cast<uint16_t*>(smem + pr_k_bytes(R, t));  // [rows * t][32]
+    double* sKbar = reinterpret_cast<double*>(sK);  // [32][R], over sK
+    double* sQbar = reinterpret_cast<double*>(sQ);  // [rows][32], over sQ
+    const int blk = xcd_logical_block(blockIdx.x, tasks);
+    const int bh = blk / nchunk, chunk = blk - bh * nchunk;
+    const int b = bh / p.heads, h = bh - b * p.heads;
+    const int r0 = chunk * kPoolRouteRows;
+    const size_t img = static_cast<size_t>(b) * p.H * p.W * p.C + h * kHeadDim;
+    const int wave_slot0 = __builtin_amdgcn_readfirstlane(tid & ~63);
+    // 1. DMA: slot i holds 16-byte piece i % 4 of token i / 4 (region
+    //    token / t, slot token % t); slots past the end copy the last piece
+    {
+        const int last = R * t * 4 - 1;
+        for (int j = 0; j < krounds; ++j) {
+            const int i = min(j * kThreads + tid, last);
+            const int tok = i >> 2, s = tok / t, u = tok - s * t;
+            __builtin_amdgcn_global_load_lds(
+                k + img + token_offset(p, s, u) + 8 * (i & 3),
+                (__attribute__((address_space(3))) void*)(sK + 8 * (j * kThreads + wave_slot0)),
+                16, 0, 0);
+        }
+        const int qlast = kPoolRouteRows * t * 4 - 1;
+        for (int j = 0; j < qrounds; ++j) {
+            const int i = min(j * kThreads + tid, qlast);
+            const int tok = i >> 2, row = tok / t, u = tok - row * t;
+            __builtin_amdgcn_global_load_lds(
+                q + img + token_offset(p, min(r0 + row, R - 1), u) + 8 * (i & 3),
+                (__attribute__((address_space(3))) void*)(sQ + 8 * (j * kThreads + wave_slot0)),
+                16, 0, 0);
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's DMA has landed
+    __syncthreads();
+    // 2. the means: exact fp64 sums of bf16 values (any order), then / t,
+    //    held in registers until every staged value is read
+    double km[kKMeanItems], qm[kQMeanItems];
+#pragma unroll
+    for (int j = 0; j < kKMeanItems; ++j) {
+        const int item = tid + j * kThreads, s = item / kHeadDim, d = item - s * kHeadDim;
+        double sum = 0.0;
+        if (s < R)
+            for (int u = 0; u < t; ++u)
+                sum += static_cast<double>(bf16_to_f32(sK[(s * t + u) * kHeadDim + d]));
+        km[j] = mean_of(sum, t);
+    }
+#pragma unroll
+    for (int j = 0; j < kQMeanItems; ++j) {
+        const int item = tid + j * kThreads, row = item / kHeadDim, d = item - row * kHeadDim;
+        double sum = 0.0;
+        for (int u = 0; u < t; ++u)
+            sum += static_cast<double>(bf16_to_f32(sQ[(row * t + u) * kHeadDim + d]));
+        qm[j] = mean_of(sum, t);
+    }
+    __syncthreads();  // the staged K and Q are read: the means overlay them
+#pragma unroll
+    for (int j = 0; j < kKMeanItems; ++j) {
+        const int item = tid + j * kThreads, s = item / kHeadDim, d = item - s * kHeadDim;
+        if (s < R) sKbar[d * R + s] = km[j];
+    }
+#pragma unroll
+    for (int j = 0; j < kQMeanItems; ++j) sQbar[tid + j * kThreads] = qm[j];
+    __syncthreads();
+    // 3. routing of rows r0 + w * kRouteChains ..: lane s holds K-bar s
+    const int rw = r0 + w * kRouteChains;
+    if (rw >= R) return;  // wave-uniform; no barrier follows
+    double kreg[kHeadDim];
+#pragma unroll
+    for (int d = 0; d < kHeadDim; ++d) kreg[d] = sKbar[d * R + min(lane, R - 1)];
+    double acc[kRouteChains];
+    const double* qr[kRouteChains];
+#pragma unroll
+    for (int j = 0; j < kRouteChains; ++j) {
+        acc[j] = 0.0;
+        qr[j] = sQbar + (w * kRouteChains + j) * kHeadDim;
+    }
+    dots_seq<kRouteChains>(acc, qr, kreg);
+    int32_t* const base = idx_out + (static_cast<size_t>(bh) * R + rw) * p.k;
+    const int nrows = min(kRouteChains, R - rw);
+    if (p.k == 1) {
+#pragma unroll
+        for (int j = 0; j < kRouteChains; ++j) {
+            double best = lane < R ? acc[j] : -INFINITY;
+            int bs = lane < R ? lane : 0x7fffffff;
+            wave_argmax(best, bs);
+            if (lane == 0 && j < nrows) base[j] = min(max(bs, 0), R - 1);
+        }
+    } else {
+        double v[kRouteChains][1];
+        int ix[kRouteChains][1];
+#pragma unroll
+        for (int j = 0; j < kRouteChains; ++j) {
+            v[j][0] = lane < R ? acc[j] : -INFINITY;
+            ix[j][0] = lane;
+        }
+        bitonic_sort<1, kRouteChains, 2>(v, ix, lane);
+#pragma unroll
+        for (int j = 0; j < kRouteChains; ++j)
+            if (j < nrows && lane < p.k) base[j * p.k + lane] = ix[j][0];
+    }
+}
+
 template <int NW, int KTOP>
 void launch_route_shape(const Params& p, const double* means, int32_t* idx, hipStream_t stream) {
     const int span = route_span(p.R);
@@ -279,6 +441,34 @@ void launch_route_shape(const Params& p, const double* means, int32_t* idx, hipS
 }
 
 }  // namespace
+
+int pool_route_lds(const Params& p) { return pool_route_lds_bytes(p.R, p.t); }
+
+hipError_t launch_pool_route(const Params& p, const void* q, const void* k,
+                             const float* lepe_w, uint2* lepe_table, int32_t* idx,
+                             hipStream_t stream) {
+    Params pp = p;
+    if (!lepe_w) pp.table_items = 0;
+    const int nchunk = (p.R + kPoolRouteRows - 1) / kPoolRouteRows;
+    const int table_blocks = (pp.table_items + kThreads - 1) / kThreads;
+    const dim3 grid(p.B * p.heads * nchunk + table_blocks), block(kThreads);
+    const int lds = pool_route_lds_bytes(p.R, p.t);
+    const uint16_t* qq = static_cast<const uint16_t*>(q);
+    const uint16_t* kk = static_cast<const uint16_t*>(k);
+#define BRA_POOL_ROUTE(T, HS, WS, NW, HEADS, KTOP)                                              \
+    if constexpr (sizeof(T) == 2 && NW * NW <= 64 && HEADS > kWaves) {                         \
+        if (matches(Inst<T, HS, WS, NW, HEADS, KTOP>::key, p, true, true)) {                   \
+            hipLaunchKernelGGL((pool_route_kernel<HS, WS, NW, HEADS, KTOP>), grid, block, lds,  \
+                               stream, qq, kk, idx, lepe_w, lepe_table, pp);                    \
+            return hipGetLastError();                                                          \
+        }                                                                                      \
+    }
+    BRA_FOR_EACH_SHAPE(BRA_POOL_ROUTE)
+#undef BRA_POOL_ROUTE
+    hipLaunchKernelGGL((pool_route_kernel<0, 0, 0, 0, 0>), grid, block, lds, stream, qq, kk, idx,
+                       lepe_w, lepe_table, pp);
+    return hipGetLastError();
+}
 
 hipError_t launch_route(const Params& p, bool bf16, const double* means, int32_t* idx,
                         hipStream_t stream) {
