@@ -116,10 +116,12 @@ bra_status_t bra_create(const bra_config_t* cfg, bra_handle_t* out);
 
 /* Enqueue the forward pass on `stream` (a hipStream_t; NULL = the null
  * stream) and return without synchronising.  The kernels are the region
- * means, then (with KV downsampling) the pooled K/V, then the routing unless
- * the attention kernel routes by itself (at most 64 regions, at most 4
- * heads, per-head routing), then attention + LePE: two to four launches.  No
- * allocation happens here.
+ * means, then (with KV downsampling) the pooled K/V, then the routing, then
+ * attention + LePE: two to four launches.  The attention kernel routes by
+ * itself for at most 64 regions and at most 4 heads (per-head routing); the
+ * region-mean kernel routes too for at most 64 regions, more heads, regions
+ * of at most 16 tokens and R * t <= 256 (bf16, per head).  No allocation
+ * happens here; the calls may be captured in a HIP graph.
  *   q, k, v       device, [B,H,W,C], dtype, 16-byte aligned
  *   lepe_w        device [C,5,5] fp32, or NULL for no LePE term (lepe_b is then ignored)
  *   lepe_b        device [C] fp32, or NULL for a zero bias
@@ -187,8 +189,10 @@ const char* bra_last_error(void);
  * recorded events and writes, for each recorded call i < *count,
  * ms[3*i] = region means (and KV downsampling), ms[3*i+1] = routing kernel and
  * ms[3*i+2] = attention/LePE kernel time (milliseconds), then clears the
- * record.  When the attention kernel routes, ms[3*i+1] measures only the gap
- * between two back-to-back events.  `ms` holds at least 3*n floats. */
+ * record.  When the attention or the region-mean kernel routes, ms[3*i+1]
+ * measures only the gap between two back-to-back events.  With projections
+ * the first slot is the qkv projection and the last includes the output
+ * projection.  `ms` holds at least 3*n floats. */
 bra_status_t bra_timing_enable(bra_handle_t h, int32_t n);
 bra_status_t bra_timing_read(bra_handle_t h, float* ms, int32_t* count);
 
