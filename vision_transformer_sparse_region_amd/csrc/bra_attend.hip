@@ -349,41 +349,52 @@ __device__ __forceinline__ void attend_valu(const Params& p, const float* __rest
 // One LePE work item: channels c0, c0+1 of window row y, columns xs..xs+7
 // (fewer at the window's right edge), bias + 25 taps from the LDS halo.
 // Weights come from LDS (sW, [C][25] then the bias [C]) or from global memory.
-template <typename T>
+// The 50 weights of a thread's channel pair (c0, c0 + 1), loaded in the
+// prologue when each thread has at most one LePE item and the weights are
+// not in LDS: rows c0 and c0 + 1 of the [C][25] weights.
+struct LepePairWeights {
+    float w[50];
+};
+
+// NC: output columns per item, kLepeCols, or the window width of a fixed
+// shape narrower than that (no work on columns past the window).
+template <typename T, bool PRE, int NC>
 __device__ __forceinline__ void lepe_item(const Params& p, const T* sVh, const float* wsrc,
-                                          const float* bsrc, int c0, int y, int xs, int nx,
-                                          float (&acc)[2][kLepeCols]) {
+                                          const LepePairWeights& pre, const float* bsrc, int c0,
+                                          int y, int xs, int nx, float (&acc)[2][NC]) {
     float b0 = 0.f, b1 = 0.f;
     if (p.has_lepe && bsrc) {
         b0 = bsrc[c0];
         b1 = bsrc[c0 + 1];
     }
 #pragma unroll
-    for (int x = 0; x < kLepeCols; ++x) {
+    for (int x = 0; x < NC; ++x) {
         acc[0][x] = b0;
         acc[1][x] = b1;
     }
     if (!p.has_lepe) return;
     const int hw = p.ws + 4;
-#pragma unroll 1
+    // (the rows unroll when the weights are in registers: they are indexed
+    // by the row)
+#pragma unroll(PRE ? 5 : 1)
     for (int i = 0; i < 5; ++i) {
         float w0[5], w1[5];
 #pragma unroll
         for (int j = 0; j < 5; ++j) {
-            w0[j] = wsrc[c0 * 25 + i * 5 + j];
-            w1[j] = wsrc[(c0 + 1) * 25 + i * 5 + j];
+            w0[j] = PRE ? pre.w[i * 5 + j] : wsrc[c0 * 25 + i * 5 + j];
+            w1[j] = PRE ? pre.w[25 + i * 5 + j] : wsrc[(c0 + 1) * 25 + i * 5 + j];
         }
         const T* row = sVh + ((y + i) * hw + xs) * p.C + c0;
-        float in0[kLepeCols + 4], in1[kLepeCols + 4];
+        float in0[NC + 4], in1[NC + 4];
 #pragma unroll
-        for (int xx = 0; xx < kLepeCols + 4; ++xx) {
+        for (int xx = 0; xx < NC + 4; ++xx) {
             float2 v2 = {0.f, 0.f};
             if (xx < nx + 4) v2 = Elem<T>::pair(row + xx * p.C);
             in0[xx] = v2.x;
             in1[xx] = v2.y;
         }
 #pragma unroll
-        for (int x = 0; x < kLepeCols; ++x)
+        for (int x = 0; x < NC; ++x)
 #pragma unroll
             for (int j = 0; j < 5; ++j) {
                 acc[0][x] = fmaf(w0[j], in0[x + j], acc[0][x]);
@@ -392,10 +403,11 @@ __device__ __forceinline__ void lepe_item(const Params& p, const T* sVh, const f
     }
 }
 
+template <int NC>
 __device__ __forceinline__ void store_lepe(const Params& p, float* sL, int c0, int y, int xs,
-                                           int nx, const float (&acc)[2][kLepeCols]) {
+                                           int nx, const float (&acc)[2][NC]) {
 #pragma unroll
-    for (int x = 0; x < kLepeCols; ++x)
+    for (int x = 0; x < NC; ++x)
         if (x < nx)
             *reinterpret_cast<float2*>(sL + (y * p.ws + xs + x) * p.lstride + c0) =
                 float2{acc[0][x], acc[1][x]};
@@ -404,22 +416,23 @@ __device__ __forceinline__ void store_lepe(const Params& p, float* sL, int c0, i
 // The whole LePE step: every (channel pair, row, column block) item, written
 // to sL.  In alias mode sL overlays the halo, so the items (at most one per
 // thread) are computed first and stored after a barrier.  Ends with a barrier.
-template <typename T>
-__device__ __forceinline__ void lepe_phase(const Params& p, const T* sVh, float* sL, const float* wsrc,
-                           const float* bsrc) {
+template <typename T, bool PRE, int NC>
+__device__ __forceinline__ void lepe_phase(const Params& p, const T* sVh, float* sL,
+                                           const float* wsrc, const LepePairWeights& pre,
+                                           const float* bsrc) {
     const int npairs = p.C / 2;
     const int nxb = (p.ws + kLepeCols - 1) / kLepeCols;
-    float acc[2][kLepeCols];
+    float acc[2][NC];
     int mine = -1;
     for (int it = threadIdx.x; it < p.lepe_items; it += kThreads) {
         const int cp = it % npairs, rest = it / npairs;
         const int xb = rest % nxb, y = rest / nxb;
         const int xs = xb * kLepeCols, nx = min(kLepeCols, p.ws - xs);
-        lepe_item<T>(p, sVh, wsrc, bsrc, 2 * cp, y, xs, nx, acc);
+        lepe_item<T, PRE, NC>(p, sVh, wsrc, pre, bsrc, 2 * cp, y, xs, nx, acc);
         if (p.lepe_alias)
             mine = it;
         else
-            store_lepe(p, sL, 2 * cp, y, xs, nx, acc);
+            store_lepe<NC>(p, sL, 2 * cp, y, xs, nx, acc);
     }
     if (p.lepe_alias) {
         __syncthreads();  // every halo read is done before sL overwrites it
@@ -427,7 +440,7 @@ __device__ __forceinline__ void lepe_phase(const Params& p, const T* sVh, float*
             const int cp = mine % npairs, rest = mine / npairs;
             const int xb = rest % nxb, y = rest / nxb;
             const int xs = xb * kLepeCols;
-            store_lepe(p, sL, 2 * cp, y, xs, min(kLepeCols, p.ws - xs), acc);
+            store_lepe<NC>(p, sL, 2 * cp, y, xs, min(kLepeCols, p.ws - xs), acc);
         }
     }
     __syncthreads();
@@ -650,6 +663,19 @@ attend_kernel(const T* __restrict__ q, const T* __restrict__ v, const T* __restr
                              : reinterpret_cast<const float4*>(lepe_b)[i - nw];
         }
     }
+    // VALU LePE with the weights outside LDS and at most one item per thread
+    // (fixed bf16 shapes only: elsewhere the 50 registers would spill): the
+    // thread's 50 weights load now, with everything else, rather than one
+    // tap row at a time inside the LePE
+    constexpr bool kFixedShape = HS > 0 && WS > 0 && NW > 0 && HEADS > 0 && KTOP > 0;
+    const bool pre_w = kFixedShape && VEC == 8 && !kLepeMfma && !w_in_lds && p.has_lepe &&
+                       p.lepe_items <= kThreads;
+    LepePairWeights pw;
+    if (pre_w) {
+        const int c0 = 2 * (min(tid, p.lepe_items - 1) % (p.C / 2));
+#pragma unroll
+        for (int e = 0; e < 50; ++e) pw.w[e] = lepe_w[c0 * 25 + e];
+    }
     const int nhk = p.heads * p.k;
     const int wu = __builtin_amdgcn_readfirstlane(w);  // w, known wave-uniform
     WaveJobs J(p, w);
@@ -816,9 +842,20 @@ attend_kernel(const T* __restrict__ q, const T* __restrict__ v, const T* __restr
         __syncthreads();
     };
     const bool early_lepe = !kLepeMfma && !w_in_lds;
+    // VALU LePE columns per item: a fixed window narrower than kLepeCols
+    // computes only its own columns
+    constexpr int kLepeNC = WS > 0 && WS < kLepeCols ? WS : kLepeCols;
     if (early_lepe) {
         stage_halo();
-        lepe_phase<T>(p, sVh, sL, wsrc, bsrc);
+        if constexpr (kFixedShape && VEC == 8 && !kLepeMfma) {
+            if (pre_w) {
+                lepe_phase<T, true, kLepeNC>(p, sVh, sL, wsrc, pw, bsrc);
+            } else {
+                lepe_phase<T, false, kLepeNC>(p, sVh, sL, wsrc, pw, bsrc);
+            }
+        } else {
+            lepe_phase<T, false, kLepeNC>(p, sVh, sL, wsrc, pw, bsrc);
+        }
     }
 
     // 3. Each wave issues the gathers of its first two (job, chunk) steps;
@@ -844,7 +881,7 @@ attend_kernel(const T* __restrict__ q, const T* __restrict__ v, const T* __restr
                 __syncthreads();
             }
         } else {
-            lepe_phase<T>(p, sVh, sL, wsrc, bsrc);
+            lepe_phase<T, false, kLepeNC>(p, sVh, sL, wsrc, pw, bsrc);
         }
     }
 
