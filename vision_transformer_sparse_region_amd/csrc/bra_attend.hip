@@ -613,11 +613,14 @@ __device__ __forceinline__ void route_row_wave(const Params& p, double qmean_lan
 }
 
 // ---------------------------------------------------------------------------
-// Fixed shapes whose LePE runs on MFMA need little LDS; all instances are
-// compiled for four waves per SIMD (more waves per SIMD did not pay: the
-// extra register pressure spills).
+// Fixed shapes whose LePE runs on MFMA need little LDS; the fixed instances
+// are compiled for four waves per SIMD (more waves per SIMD did not pay: the
+// extra register pressure spills), the generic ones, whose runtime sizes
+// keep more registers live, for three (at 128 registers they spilled 90 to
+// 140).
 template <typename T, int HS, int WS, int NW, int HEADS, int KTOP, bool FUSED>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))) void
+__global__ __launch_bounds__(kThreads) __attribute__((
+    amdgpu_waves_per_eu(HS > 0 && WS > 0 && NW > 0 && HEADS > 0 && KTOP > 0 ? 4 : 2, 8))) void
 attend_kernel(const T* __restrict__ q, const T* __restrict__ v, const T* __restrict__ kg,
               const T* __restrict__ vg, const double* __restrict__ means,
               int32_t* __restrict__ routing,
