@@ -92,20 +92,25 @@ __device__ __forceinline__ float group4_sum(float x) {
 
 // Layout of the fp64 region means in the workspace: Q means row-major
 // [B][heads][R][32] (a row is read whole, as wave-uniform scalar loads), then
-// K means dim-major [B][heads][32][R] (lane s of a wave reads region s, so
-// every load of a dim is one contiguous run).
+// K means in dim pairs, [B][heads][16][R][2]: lane s of a wave reads dims
+// 2j, 2j + 1 of region s as one 16-byte load, and the lanes' loads of a pair
+// are one contiguous run.
 __device__ __forceinline__ size_t qmean_index(const Params& p, int bh, int r, int d) {
     return (static_cast<size_t>(bh) * p.R + r) * kHeadDim + d;
 }
 __device__ __forceinline__ size_t kmean_index(const Params& p, int bh, int d, int s) {
     return static_cast<size_t>(p.B) * p.heads * p.R * kHeadDim +
-           (static_cast<size_t>(bh) * kHeadDim + d) * p.R + s;
+           ((static_cast<size_t>(bh) * (kHeadDim / 2) + (d >> 1)) * p.R + s) * 2 + (d & 1);
 }
-// The K mean of region s, head bh, into registers (32 coalesced loads).
+// The K mean of region s, head bh, into registers (16 coalesced 16-byte loads).
 __device__ __forceinline__ void load_kmean(const Params& p, const double* __restrict__ means,
                                            int bh, int s, double (&kreg)[kHeadDim]) {
 #pragma unroll
-    for (int d = 0; d < kHeadDim; ++d) kreg[d] = means[kmean_index(p, bh, d, s)];
+    for (int j = 0; j < kHeadDim / 2; ++j) {
+        const double2 v = *reinterpret_cast<const double2*>(means + kmean_index(p, bh, 2 * j, s));
+        kreg[2 * j] = v.x;
+        kreg[2 * j + 1] = v.y;
+    }
 }
 
 // mean = sum / t, as a multiplication when t is a power of two (exact then).
