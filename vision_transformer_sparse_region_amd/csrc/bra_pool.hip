@@ -10,6 +10,38 @@
 namespace bra {
 namespace {
 
+// x plus the x of lane l ^ M, in VALU registers: DPP row permutations for
+// M = 4 and 8, v_permlane16/32_swap for M = 16 and 32.  (The pool sums are
+// exact, so the order of the two terms is immaterial.)
+template <int M>
+__device__ __forceinline__ double xor_sum(double x) {
+    const u32x2_t u = __builtin_bit_cast(u32x2_t, x);
+    if constexpr (M == 16 || M == 32) {
+        const auto a = M == 16 ? __builtin_amdgcn_permlane16_swap(u.x, u.x, false, false)
+                               : __builtin_amdgcn_permlane32_swap(u.x, u.x, false, false);
+        const auto b = M == 16 ? __builtin_amdgcn_permlane16_swap(u.y, u.y, false, false)
+                               : __builtin_amdgcn_permlane32_swap(u.y, u.y, false, false);
+        return __builtin_bit_cast(double, u32x2_t{a[0], b[0]}) +
+               __builtin_bit_cast(double, u32x2_t{a[1], b[1]});
+    } else {
+        const int lo = lane_xor_dpp<M>(static_cast<int>(u.x));
+        const int hi = lane_xor_dpp<M>(static_cast<int>(u.y));
+        return x + __builtin_bit_cast(double, u32x2_t{static_cast<unsigned>(lo),
+                                                       static_cast<unsigned>(hi)});
+    }
+}
+
+// Sum over the lanes that share l % nvec (nvec = 4, 8, 16, 32 or 64).
+__device__ __forceinline__ void token_group_sum(double (&acc)[8], int nvec) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        if (nvec <= 4) acc[e] = xor_sum<4>(acc[e]);
+        if (nvec <= 8) acc[e] = xor_sum<8>(acc[e]);
+        if (nvec <= 16) acc[e] = xor_sum<16>(acc[e]);
+        if (nvec <= 32) acc[e] = xor_sum<32>(acc[e]);
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Region means of Q and K (fp64); of K alone when the attention kernel sums
 // the Q means itself (p.qmean_attend).
@@ -61,9 +93,7 @@ __global__ __launch_bounds__(kThreads) void pool_qk_kernel(const T* __restrict__
             acc[4] += bf16lo(u.z); acc[5] += bf16hi(u.z);
             acc[6] += bf16lo(u.w); acc[7] += bf16hi(u.w);
         }
-        for (int m = nvec; m < 64; m *= 2)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc[e] += __shfl_xor(acc[e], m);
+        token_group_sum(acc, nvec);
         if (tg == 0) {
             const int c = pv * 8, h = c / kHeadDim, d = c - h * kHeadDim;
             const int bh = b * p.heads + h;
