@@ -26,7 +26,8 @@ sys.path.insert(0, ROOT)
 
 import bench  # noqa: E402
 
-KERNELS = {"pool_qk_kernel": "region_pool", "proj_qkv_kernel": "qkv_projection",
+KERNELS = {"pool_qk_kernel": "region_pool", "pool_route_kernel": "region_pool_and_route",
+           "proj_qkv_kernel": "qkv_projection",
            "proj_out_kernel": "output_projection", "route_small_kernel": "route",
            "route_large_kernel": "route", "attend_kernel": "attend"}
 COPY_KERNELS = ("__amd_rocclr_copyBuffer",)
