@@ -719,23 +719,54 @@ attend_kernel(const T* __restrict__ q, const T* __restrict__ v, const T* __restr
     // halo pieces kept in registers: all of them for a fixed shape (when they
     // fit kHaloRegs per thread), kHaloRegs otherwise.  Cells outside the map
     // load a clamped in-map cell and are zeroed when staged (bit u of hvalid).
+    // For the MFMA LePE (channel-planar halo) a task can be 4 consecutive
+    // cells of one halo row times one 16-byte channel piece, so that each
+    // channel plane takes one 8-byte LDS write per task instead of four
+    // 2-byte ones; taken where it needs no more registers than one cell per
+    // task (stage 2: 4 either way; 8 x 8 windows would need 8 instead of 5,
+    // and measured slower).
     constexpr int kHaloFixed =
         (HS > 0 && WS > 0 && HEADS > 0)
             ? ((HS + 4) * (WS + 4) * (HEADS * kHeadDim / VEC) + kThreads - 1) / kThreads
             : kHaloRegs;
-    constexpr int kHR = kHaloFixed < kHaloRegs ? kHaloFixed : kHaloRegs;
-    uint4 hreg[kHR];
+    constexpr int kHR1 = kHaloFixed < kHaloRegs ? kHaloFixed : kHaloRegs;
+    constexpr int kHTasks4 =
+        kLepeMfma ? (HS + 4) * ((WS + 4) / 4) * (HEADS * kHeadDim / 8) : 0;
+    constexpr bool kHalo4 = kLepeMfma && 4 * ((kHTasks4 + kThreads - 1) / kThreads) <= kHR1;
+    constexpr int kHTask = kHalo4 ? 4 : 1;  // cells per task
+    constexpr int kHTasks = kHalo4 ? kHTasks4 : 0;
+    constexpr int kHR = kHalo4 ? (kHTasks + kThreads - 1) / kThreads : kHR1;
+    static_assert(kHR * kHTask <= 32, "one validity bit per halo register");
+    uint4 hreg[kHR * kHTask];
     unsigned hvalid = 0;
+    if constexpr (kHalo4) {
+        constexpr int NV = HEADS * kHeadDim / 8, GX = (WS + 4) / 4;
 #pragma unroll
-    for (int u = 0; u < kHR; ++u) {
-        const int i = tid + u * kThreads;
-        const int ic = min(i, p.halo_pieces - 1);
-        const int cell = ic / nvec, pv = ic - cell * nvec;
-        const int hy = cell / hw, hx = cell - hy * hw;
-        const int y = y0 + hy - 2, x = x0 + hx - 2;
-        const int yc = min(max(y, 0), p.H - 1), xc = min(max(x, 0), p.W - 1);
-        hreg[u] = *reinterpret_cast<const uint4*>(v + img + (yc * p.W + xc) * p.C + pv * VEC);
-        if (i < p.halo_pieces && y == yc && x == xc) hvalid |= 1u << u;
+        for (int u = 0; u < kHR; ++u) {
+            const int task = tid + u * kThreads;
+            const int tc = min(task, kHTasks - 1);
+            const int pv = tc % NV, cg = tc / NV, hy = cg / GX, gx = cg - hy * GX;
+            const int y = y0 + hy - 2, yc = min(max(y, 0), p.H - 1);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int x = x0 + 4 * gx + j - 2, xc = min(max(x, 0), p.W - 1);
+                hreg[u * 4 + j] =
+                    *reinterpret_cast<const uint4*>(v + img + (yc * p.W + xc) * p.C + pv * 8);
+                if (task < kHTasks && y == yc && x == xc) hvalid |= 1u << (u * 4 + j);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int u = 0; u < kHR; ++u) {
+            const int i = tid + u * kThreads;
+            const int ic = min(i, p.halo_pieces - 1);
+            const int cell = ic / nvec, pv = ic - cell * nvec;
+            const int hy = cell / hw, hx = cell - hy * hw;
+            const int y = y0 + hy - 2, x = x0 + hx - 2;
+            const int yc = min(max(y, 0), p.H - 1), xc = min(max(x, 0), p.W - 1);
+            hreg[u] = *reinterpret_cast<const uint4*>(v + img + (yc * p.W + xc) * p.C + pv * VEC);
+            if (i < p.halo_pieces && y == yc && x == xc) hvalid |= 1u << u;
+        }
     }
     if constexpr (!FUSED && VEC == 8)
         load_q_operands(p, J, min(w, J.njobs - 1), reinterpret_cast<const uint16_t*>(q) + img, r,
@@ -822,6 +853,44 @@ attend_kernel(const T* __restrict__ q, const T* __restrict__ v, const T* __restr
         }
     };
     auto stage_halo = [&]() {
+        if constexpr (kHalo4) {
+            // channel c = 8 pv + e of the task's 4 cells: bf16 e of each
+            // cell's piece, two cells to a 32-bit word
+            using S = LepeMfmaShape<HS, WS, HEADS>;
+            constexpr int NV = HEADS * kHeadDim / 8, GX = (WS + 4) / 4;
+            if (p.has_lepe) {
+#pragma unroll
+                for (int u = 0; u < kHR; ++u) {
+                    const int task = tid + u * kThreads;
+                    if (task < kHTasks) {
+                        const int pv = task % NV, cg = task / NV, hy = cg / GX, gx = cg - hy * GX;
+                        uint32_t wd[4][4];
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            const unsigned mk = 0u - ((hvalid >> (u * 4 + j)) & 1u);
+                            wd[j][0] = hreg[u * 4 + j].x & mk;
+                            wd[j][1] = hreg[u * 4 + j].y & mk;
+                            wd[j][2] = hreg[u * 4 + j].z & mk;
+                            wd[j][3] = hreg[u * 4 + j].w & mk;
+                        }
+                        uint16_t* base = reinterpret_cast<uint16_t*>(sVh) + pv * 8 * S::PS +
+                                         hy * S::HWP + 4 * gx;
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            const int sh = 16 * (e & 1);
+                            const uint32_t c0 = (wd[0][e >> 1] >> sh) & 0xffffu;
+                            const uint32_t c1 = (wd[1][e >> 1] >> sh) & 0xffffu;
+                            const uint32_t c2 = (wd[2][e >> 1] >> sh) & 0xffffu;
+                            const uint32_t c3 = (wd[3][e >> 1] >> sh) & 0xffffu;
+                            *reinterpret_cast<uint2*>(base + e * S::PS) =
+                                uint2{c0 | (c1 << 16), c2 | (c3 << 16)};
+                        }
+                    }
+                }
+            }
+            __syncthreads();
+            return;
+        }
         if (p.has_lepe) {
 #pragma unroll
             for (int u = 0; u < kHR; ++u) {
