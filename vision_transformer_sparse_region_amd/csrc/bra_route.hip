@@ -34,9 +34,12 @@ constexpr int kRouteChains = 4;  // query rows whose dots run interleaved
 // Region-span of the large-map kernel: threads tid % SPAN own region tid % SPAN,
 // SPAN = the power of two >= R (128 or 256 = kMaxRegions).
 __host__ __device__ constexpr int route_span(int R) { return R <= 64 ? 64 : R <= 128 ? 128 : 256; }
-// Query rows a workgroup routes: kRouteChains per wave for R <= 64, else 2 per wave.
+// Query rows a workgroup routes: kRouteChains per wave for R <= 64, 2 per
+// wave for R <= 128, 1 per wave above (more workgroups: the selection over
+// 256 entries is long, and 4 rows per workgroup measured 2.3 us faster than 8
+// on 8 x 2 x 256 rows, despite the K means being read twice as often).
 __host__ __device__ constexpr int route_rows(int span) {
-    return span == 64 ? kWaves * kRouteChains : kWaves * 2;
+    return span == 64 ? kWaves * kRouteChains : span == 256 ? kWaves : kWaves * 2;
 }
 // fp64 row stride of the affinity tile (even, so pairs of entries are 16-byte aligned).
 __host__ __device__ constexpr int route_row_stride(int R) { return (R + 1) & ~1; }
