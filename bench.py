@@ -239,7 +239,7 @@ def main(argv=None) -> int:
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs on one GPU; the forward needs no collective and "
+        print("bench.py: this implementation runs on one GPU; the forward needs no collective and "
               "its multi-GPU sharding is described but not built.", file=sys.stderr)
         return 2
 
