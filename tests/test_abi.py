@@ -54,6 +54,10 @@ def _cfg(**kw):
     (dict(projections=1, kv_downsample_ratio=2), bra.BRA_ERR_UNSUPPORTED),  # no KV downsampling
     (dict(projections=1, channels=544, num_heads=17), bra.BRA_ERR_UNSUPPORTED),  # C <= 512
     (dict(kv_downsample_ratio=3), bra.BRA_ERR_SHAPE),  # 3 does not divide the 4x4 windows
+    (dict(height=256, width=256, n_win=16, channels=32, num_heads=1),
+     bra.BRA_ERR_UNSUPPORTED),                     # 16 x 16 windows at C = 32: past the LDS tiles
+    (dict(height=110, width=110, n_win=10, channels=64, num_heads=2),
+     bra.BRA_ERR_UNSUPPORTED),                     # 11 x 11 windows at C = 64
     (dict(height=4096, width=4096, n_win=256, channels=32, num_heads=1),
      bra.BRA_ERR_UNSUPPORTED),                     # H*W = 2^24 tokens: beyond 24-bit indexing
     (dict(height=34, width=34, n_win=17, channels=32, num_heads=1),

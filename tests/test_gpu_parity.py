@@ -57,6 +57,12 @@ SMALL = [
     Workload("pool_route_ragged", 2, 12, 18, 192, 6, 6, 5, "bf16", 129, lepe_bias=True),
     Workload("pool_route_r64_topk1", 1, 16, 16, 160, 5, 8, 1, "bf16", 130),
     Workload("pool_route_r4", 3, 8, 8, 192, 6, 2, 3, "bf16", 131),
+    # the largest windows the on-chip tiles take (bra_create refuses the next
+    # size up): 15 x 15 at C = 32 with 256 regions, 10 x 10 at C = 64, 6 x 6
+    # at C = 128
+    Workload("max_window_c32_r256", 1, 240, 240, 32, 1, 16, 4, "bf16", 133),
+    Workload("max_window_c64", 1, 100, 100, 64, 2, 10, 3, "bf16", 134, lepe_bias=True),
+    Workload("max_window_c128", 2, 36, 36, 128, 4, 6, 5, "bf16", 135),
     Workload("f32_stage2_shape", 4, 28, 28, 128, 4, 7, 4, "f32", 109),
     Workload("f32_ragged_bias", 2, 12, 20, 64, 2, 4, 3, "f32", 110, lepe_bias=True),
 ]
