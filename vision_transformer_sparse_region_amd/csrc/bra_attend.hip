@@ -135,12 +135,25 @@ __device__ __forceinline__ void v_transpose(const StepRegs& cur, uint16_t* sVt,
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // ds_read_b64_tr_b16: in each 16-lane group, lane i receives element
+    // i % 4 of the 8-byte pieces that lanes i / 4, 4 + i / 4, 8 + i / 4 and
+    // 12 + i / 4 read.  Lane 4r + a of group g reads dims 16 db + 4a .. + 3 of
+    // key 8g + r (then 8g + 4 + r), so lane i gets dim 16 db + i of keys
+    // 8g .. 8g + 3 (then 8g + 4 .. 8g + 7): the operand, without repacking.
+    const int tr_r = li >> 2, tr_a = li & 3;
 #pragma unroll
     for (int db = 0; db < 2; ++db) {
-        u16x8_t t8;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) t8[e] = sVt[(8 * g + e) * kVtStride + li + 16 * db];
-        va[db] = __builtin_bit_cast(bf16x8_t, t8);
+        const uint16_t* base = sVt + (8 * g + tr_r) * kVtStride + 16 * db + 4 * tr_a;
+        const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4_t*)(base));
+        const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4_t*)(base + 4 * kVtStride));
+        va[db] = __builtin_bit_cast(
+            bf16x8_t, u32x4_t{__builtin_bit_cast(u32x2_t, lo)[0], __builtin_bit_cast(u32x2_t, lo)[1],
+                              __builtin_bit_cast(u32x2_t, hi)[0], __builtin_bit_cast(u32x2_t, hi)[1]});
+        // (unscheduled, the reads of both halves bunch up and the long-key
+        // loop spills)
+        __builtin_amdgcn_sched_barrier(0);
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -460,7 +473,6 @@ __device__ __forceinline__ void lepe_phase(const Params& p, const T* sVh, float*
 // and the lane's column: the pool kernel writes them once per forward to a
 // small table (lepe_toeplitz_entry).  Weights enter the product as bf16 (the
 // accumulation is fp32).
-typedef short s16x4_t __attribute__((ext_vector_type(4)));
 
 // The Toeplitz B operands and the bias of this lane's channel in each of the
 // wave's channel groups, loaded from the table the pool kernel built.
