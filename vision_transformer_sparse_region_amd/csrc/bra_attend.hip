@@ -2,16 +2,21 @@
 // workgroup per (image, region), all heads (page keys in bra_device.h).
 //
 //   1  issue every load at once: the routed region ids of this region
-//      (written by the routing kernel), the LePE weights or the Toeplitz LePE
-//      operands, the V window with its 2-token halo, the first job's Q
-//      operands                                                [P5 §五 ⑤]
+//      (written by a routing kernel) -- or, when this kernel routes (at most
+//      64 regions, at most 4 heads), the K means of the image --, the LePE
+//      weights or Toeplitz operands, the V window with its 2-token halo, the
+//      first job's Q operands                                  [P5 §五 ⑤]
+//   1b in-kernel routing: the Q means from the Q operands (exact fp64 sums),
+//      the fp64 affinity with every region, arg-max or bitonic top-k, wave h
+//      for head h                              [P4 §1.2; P1 §2.1; P5 §五 ③-④]
 //   2  each wave issues the gathers of its first two routed K/V chunks ...
 //   3  ... the halo goes to LDS and the 5x5 depthwise LePE of V runs while
 //      those loads are in flight                       [P5 §五 lepe, ⑧; P2 §2.2]
 //   4  token attention over the routed tokens: S^T = K Q^T and O^T += V^T P^T
 //      on bf16 MFMA (fp32 VALU for fp32 input), fp32 online softmax, the next
 //      chunk's gather in flight during each chunk         [P3 §2.2; P5 §五 ⑤-⑦]
-//   5  out = LePE + O, one rounding, 16-byte NHWC stores
+//   5  out = LePE + O, one rounding, 16-byte NHWC stores; or, with the
+//      module's output projection, (LePE + O) W_o^T + b_o on MFMA  [P5 §五 ⑧]
 // The routed K/V tokens are never copied to HBM: [P3 §4.2] and [P1 §2.2]
 // build a dense k-fold gathered tensor with torch.gather; here the routing
 // index drives the loads straight into MFMA operands.
