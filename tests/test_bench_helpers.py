@@ -80,6 +80,14 @@ def test_traffic_summary_parses_and_matches_sources():
     assert bench.stored_traffic("stage1") == expect
 
 
+def test_source_hash_ignores_comments_only():
+    a = "int f(int x) {  // one\n    return x + 1; /* two */\n}\n"
+    b = "// header\nint f(int x) {\n\n    return x + 1;\n}\n"
+    c = "int f(int x) {\n    return x + 2;\n}\n"
+    assert bench._code_only(a) == bench._code_only(b)
+    assert bench._code_only(a) != bench._code_only(c)
+
+
 def test_more_than_one_gpu_is_refused(capsys):
     assert bench.main(["--gpus", "2"]) == 2
     assert "one GPU" in capsys.readouterr().err
