@@ -620,7 +620,7 @@ __device__ __forceinline__ void route_row_wave(const Params& p, double qmean_lan
         // lanes past R -inf); lane j < k then holds the id of rank j
         double v[1][1] = {{lane < p.R ? a : -INFINITY}};
         int ix[1][1] = {{lane}};
-        bitonic_sort<1, 1, 2>(v, ix, lane);
+        route_topk<1, 1>(v, ix, lane, p.k);
         if (lane < p.k) {
             const int id = min(max(ix[0][0], 0), p.R - 1);
             off[lane] = region_base_kv(p, id);

@@ -414,4 +414,125 @@ __device__ __forceinline__ void bitonic_sort(double (&v)[NRW][E], int (&ix)[NRW]
     if constexpr (SIZE < 64 * E) bitonic_sort<E, NRW, SIZE * 2>(v, ix, lane);
 }
 
+// ---------------------------------------------------------------------------
+// The same network on fp32 keys alone (equal keys in any order): a lane
+// moves two dwords per partner instead of three, and a compare-exchange is
+// one compare and two selects instead of three compares and three selects.
+template <int LJ>
+__device__ __forceinline__ void lane_pair_f32(float v, int ix, float& a, int& ia, float& b,
+                                              int& ib) {
+    if constexpr (LJ < 16) {
+        a = v;
+        ia = ix;
+        b = __int_as_float(lane_xor_dpp<LJ>(__float_as_int(v)));
+        ib = lane_xor_dpp<LJ>(ix);
+    } else {
+        const auto vv = LJ == 16 ? __builtin_amdgcn_permlane16_swap(__float_as_uint(v),
+                                                                    __float_as_uint(v), false,
+                                                                    false)
+                                 : __builtin_amdgcn_permlane32_swap(__float_as_uint(v),
+                                                                    __float_as_uint(v), false,
+                                                                    false);
+        const auto ii = LJ == 16 ? __builtin_amdgcn_permlane16_swap(ix, ix, false, false)
+                                 : __builtin_amdgcn_permlane32_swap(ix, ix, false, false);
+        a = __uint_as_float(vv[0]);
+        ia = static_cast<int>(ii[0]);
+        b = __uint_as_float(vv[1]);
+        ib = static_cast<int>(ii[1]);
+    }
+}
+
+template <int E, int NRW, int SIZE, int J>
+__device__ __forceinline__ void bitonic_steps_f32(float (&v)[NRW][E], int (&ix)[NRW][E],
+                                                  int lane) {
+    if constexpr (J < E) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const int pe = e ^ J;
+            if (pe > e) {
+                const bool dir = ((lane * E + e) & SIZE) == 0;
+#pragma unroll
+                for (int r = 0; r < NRW; ++r) {
+                    if ((v[r][e] > v[r][pe]) != dir) {
+                        const float tv = v[r][e];
+                        v[r][e] = v[r][pe];
+                        v[r][pe] = tv;
+                        const int ti = ix[r][e];
+                        ix[r][e] = ix[r][pe];
+                        ix[r][pe] = ti;
+                    }
+                }
+            }
+        }
+    } else {
+        constexpr int LJ = J / E;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const int i = lane * E + e;
+            const bool keep_better = ((i & J) == 0) == ((i & SIZE) == 0);
+#pragma unroll
+            for (int r = 0; r < NRW; ++r) {
+                float a, b;
+                int ia, ib;
+                lane_pair_f32<LJ>(v[r][e], ix[r][e], a, ia, b, ib);
+                const bool take_a = (a > b) == keep_better;
+                v[r][e] = take_a ? a : b;
+                ix[r][e] = take_a ? ia : ib;
+            }
+        }
+    }
+    if constexpr (J > 1) bitonic_steps_f32<E, NRW, SIZE, J / 2>(v, ix, lane);
+}
+
+template <int E, int NRW, int SIZE>
+__device__ __forceinline__ void bitonic_sort_f32(float (&v)[NRW][E], int (&ix)[NRW][E],
+                                                 int lane) {
+    bitonic_steps_f32<E, NRW, SIZE, SIZE / 2>(v, ix, lane);
+    if constexpr (SIZE < 64 * E) bitonic_sort_f32<E, NRW, SIZE * 2>(v, ix, lane);
+}
+
+// The k best entries of NRW rows, best first, exactly as bitonic_sort would
+// order them (fp64 value descending, exact ties to the lower id): ix[r][e]
+// holds the id at position lane * E + e.  The rows are first sorted on fp32
+// keys (round-to-nearest is monotone).  If in every row the fp32 keys of
+// positions 0 .. k are strictly decreasing (position k when it exists), the
+// fp64 values are too, and every entry past position k - 1 has a smaller
+// fp32 key -- hence a smaller fp64 value -- than every entry before: that
+// order is the exact one.  Otherwise (fp64 values that round to one fp32
+// key, exact ties) the rows are sorted again on the fp64 values and ids.
+template <int E, int NRW>
+__device__ __forceinline__ void route_topk(double (&v)[NRW][E], int (&ix)[NRW][E], int lane,
+                                           int k) {
+    float f[NRW][E];
+    int fx[NRW][E];
+#pragma unroll
+    for (int r = 0; r < NRW; ++r)
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            f[r][e] = static_cast<float>(v[r][e]);
+            fx[r][e] = ix[r][e];
+        }
+    bitonic_sort_f32<E, NRW, 2>(f, fx, lane);
+    bool bad = false;
+#pragma unroll
+    for (int r = 0; r < NRW; ++r) {
+        // position lane * E + E is lane + 1's first entry
+        const float after = __shfl_down(f[r][0], 1);
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const int j = lane * E + e;
+            const float next = e + 1 < E ? f[r][e + 1] : after;
+            if (j < k && j + 1 < 64 * E && !(f[r][e] > next)) bad = true;
+        }
+    }
+    if (__ballot(bad) != 0ull) {  // wave-uniform
+        bitonic_sort<E, NRW, 2>(v, ix, lane);
+    } else {
+#pragma unroll
+        for (int r = 0; r < NRW; ++r)
+#pragma unroll
+            for (int e = 0; e < E; ++e) ix[r][e] = fx[r][e];
+    }
+}
+
 }  // namespace bra

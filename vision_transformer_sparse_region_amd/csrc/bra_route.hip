@@ -73,7 +73,7 @@ __device__ __forceinline__ void wave_topk_bitonic(const double* const (&rows)[NR
             ix[r][e] = i;
         }
     }
-    bitonic_sort<E, NRW, 2>(v, ix, lane);
+    route_topk<E, NRW>(v, ix, lane, k);
 #pragma unroll
     for (int r = 0; r < NRW; ++r) {
 #pragma unroll
@@ -142,7 +142,7 @@ __global__ __launch_bounds__(kThreads) void route_small_kernel(const double* __r
             v[j][0] = lane < R ? acc[j] : -INFINITY;
             ix[j][0] = lane;
         }
-        bitonic_sort<1, kRouteChains, 2>(v, ix, lane);
+        route_topk<1, kRouteChains>(v, ix, lane, p.k);
 #pragma unroll
         for (int j = 0; j < kRouteChains; ++j)
             if (j < nrows && lane < p.k) base[j * p.k + lane] = ix[j][0];
@@ -409,7 +409,7 @@ __global__ __launch_bounds__(kThreads) void pool_route_kernel(
             v[j][0] = lane < R ? acc[j] : -INFINITY;
             ix[j][0] = lane;
         }
-        bitonic_sort<1, kRouteChains, 2>(v, ix, lane);
+        route_topk<1, kRouteChains>(v, ix, lane, p.k);
 #pragma unroll
         for (int j = 0; j < kRouteChains; ++j)
             if (j < nrows && lane < p.k) base[j * p.k + lane] = ix[j][0];
