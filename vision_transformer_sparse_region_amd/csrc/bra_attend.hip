@@ -86,6 +86,9 @@ __device__ __forceinline__ void load_q_operands(const Params& p, const WaveJobs&
     }
 }
 
+// Word 3 of a raw buffer descriptor on gfx9-family chips (gfx950 included).
+constexpr int kBufferDword3 = 0x00020000;
+
 // Gather of chunk c of local job jl into `g8`.  sOff holds, per (head, rank),
 // the element offset of the routed region's first token.  Keys past the
 // routed set (a ragged last chunk) re-read the last key: their scores are
@@ -99,21 +102,29 @@ __device__ __forceinline__ void gather_chunk(const Params& p, const WaveJobs& J,
     const int h = job / J.G;
     const int hoff = h * kHeadDim;
     const int* off = sOff + h * p.k;
+    // buffer loads: a 32-bit byte offset per lane against the image's base
+    // in a buffer descriptor (no 64-bit address arithmetic per load)
+    const uint32_t map_bytes = static_cast<uint32_t>(p.kH) * p.kW * p.C * 2u;
+    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(kimg), 0, static_cast<int>(map_bytes), kBufferDword3);
+    const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(vimg), 0, static_cast<int>(map_bytes), kBufferDword3);
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
         const int key = min(32 * c + 8 * (li >> 2) + 4 * blk + (li & 3), p.nkeys - 1);
         const int j = key / p.kt, slot = key - j * p.kt;
-        g8.ka[blk] = __builtin_bit_cast(
-            bf16x8_t, *reinterpret_cast<const uint4*>(kimg + off[j] + slot_offset_kv(p, slot) +
-                                                      hoff + 8 * g));
+        const int e = off[j] + slot_offset_kv(p, slot) + hoff + 8 * g;
+        g8.ka[blk] = __builtin_bit_cast(bf16x8_t,
+                                        __builtin_amdgcn_raw_buffer_load_b128(krs, 2 * e, 0, 0));
     }
 #pragma unroll
     for (int pp = 0; pp < 2; ++pp) {
         const int pc = lane + 64 * pp;
         const int key = min(32 * c + (pc >> 2), p.nkeys - 1);
         const int j = key / p.kt, slot = key - j * p.kt;
-        g8.vv[pp] = *reinterpret_cast<const uint4*>(vimg + off[j] + slot_offset_kv(p, slot) +
-                                                    hoff + 8 * (pc & 3));
+        const int e = off[j] + slot_offset_kv(p, slot) + hoff + 8 * (pc & 3);
+        g8.vv[pp] = __builtin_bit_cast(uint4,
+                                       __builtin_amdgcn_raw_buffer_load_b128(vrs, 2 * e, 0, 0));
     }
 }
 
