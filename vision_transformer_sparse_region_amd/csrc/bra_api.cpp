@@ -22,8 +22,9 @@ struct bra_handle_s {
     bool bf16;
     int device;
     double* means;       // workspace: fp64 region means of Q [B, heads, R, 32], then of
-                         // K [B, heads, 32, R]; the routing [B, heads, R, k] int32; the MFMA LePE
-                         // operand table; C zero floats (the bias when none is given)
+                         // K [B, heads, 16, R, 2], then K in fp32 (same order); the routing
+                         // [B, heads, R, k] int32; the MFMA LePE operand table; C zero floats
+                         // (the bias when none is given)
     size_t means_bytes;
     int32_t* routing;
     uint2* lepe_table;
@@ -155,7 +156,9 @@ bra_status_t bra_create(const bra_config_t* cfg, bra_handle_t* out) {
     h->params = p;
     h->bf16 = bf16;
     h->device = dev;
-    const size_t mean_bytes = 2 * static_cast<size_t>(c.batch) * c.channels * R * sizeof(double);
+    // fp64 Q and K means, then the K means in fp32
+    const size_t mean_bytes = static_cast<size_t>(c.batch) * c.channels * R *
+                              (2 * sizeof(double) + sizeof(float));
     const size_t route_bytes =
         ((static_cast<size_t>(c.batch) * p.rheads * R * k * sizeof(int32_t)) + 15) & ~size_t{15};
     const size_t table_bytes = static_cast<size_t>(p.table_items) * sizeof(uint2);

@@ -603,23 +603,90 @@ __device__ __forceinline__ void qmean_partial(const Params& p, const WaveJobs& J
 
 // ---------------------------------------------------------------------------
 // Routing of one (image, head, query region) row on one wave, R <= 64
-// [P4 §1.2; P1 §2.1 TopkRouting; P5 §五 ③-④].  Lane s holds the K mean of
-// region s; lane d (and d + 32) holds dim d of the row's Q mean, read back
-// wave-uniform.  A[s] is the sequential 32-term fp64 sum of dot32_seq_lanes.
-// k = 1: a wave arg-max; k > 1: a bitonic sort of the row over the wave, in
-// registers (affinity descending, exact ties to the lower id).  Writes each
-// routed region's base offset to off[rank] (LDS) and its id to out[rank]
-// (global).
-__device__ __forceinline__ void route_row_wave(const Params& p, double qmean_lane,
-                                               const double (&kreg)[kHeadDim], int* off,
-                                               int32_t* __restrict__ out) {
+// [P4 §1.2; P1 §2.1 TopkRouting; P5 §五 ③-④].  Lane d (and d + 32) holds dim
+// d of the row's Q mean, read back wave-uniform; lane s routes region s.  The
+// result is the one of the fp64 affinities A[s] (sequential 32-term fp64 sum
+// of dot32_seq_lanes): affinity descending, exact ties to the lower id.
+//  1. Screen: lane s holds the fp32 K mean of region s (kf) and forms
+//     a[s] = sum of fp32 products, with a bound on |a[s] - A[s]|.  Rounding
+//     the means to fp32 moves each product by at most 2u of its size
+//     (u = 2^-24), the 32 fused multiply-adds add at most 32u of the sum of
+//     |products| S, and the fp64 sum is within 2^-47 S of the exact one: 35u
+//     of S in the normal range.  With S <= Q K1 (Q = max |q_d|, K1 = sum
+//     |k_d|), the bound taken is e = 2^-18 Q K1 (64u) plus 2^-120 (K1 + 32 Q
+//     + 64), which also covers the fp32 subnormal range (at most 2^-150 per
+//     rounding there); E is e at the row's largest K1.  Two fp32 values more
+//     than 2E apart order the fp64 affinities the same way.
+//     k = 1: if one region alone lies within 2E of the fp32 maximum, it is
+//     the fp64 arg-max.  k > 1: the fp32 values are sorted (bitonic, in
+//     registers); if each of ranks 0 .. k-1 exceeds the next rank by more
+//     than 2E, the fp64 order of the first k and the set below them agree.
+//  2. Otherwise (near or exact ties, or a non-finite value or bound): the
+//     fp64 K means are read and the exact pass decides -- a wave arg-max, or
+//     route_topk.
+// Writes each routed region's base offset to off[rank] (LDS) and its id to
+// out[rank] (global).
+// kreg holds the fp32 K mean as load_kmean32 leaves it when screening;
+// without the fp32 means (p.kmean32 = 0) it holds the fp64 K mean and only
+// the exact pass runs.
+__device__ __forceinline__ void route_row_wave(const Params& p, double qmean_lane, bool screen,
+                                               double (&kreg)[kHeadDim],
+                                               const double* __restrict__ means, int bh,
+                                               int* off, int32_t* __restrict__ out) {
     const int lane = threadIdx.x & 63;
-    const double a = dot32_seq_lanes(qmean_lane, kreg);
+    const bool in = lane < p.R;
+    if (screen) {
+        float a = 0.f, k1 = 0.f;
+        const float ql = static_cast<float>(qmean_lane);
+#pragma unroll
+        for (int d = 0; d < kHeadDim; ++d) {
+            const float qd = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ql), d));
+            const float kd = __uint_as_float(__builtin_bit_cast(u32x2_t, kreg[d >> 1])[d & 1]);
+            a = fmaf(qd, kd, a);
+            k1 += fabsf(kd);
+        }
+        const bool finite = __builtin_isfinite(a) && __builtin_isfinite(k1);
+        const bool screened = __ballot(in && !finite) == 0ull;
+        const float qinf = wave_max_f32(fabsf(ql));  // lanes d and d + 32 hold dim d
+        const float k1max = wave_max_f32(in ? k1 : 0.f);
+        // e = (2^-18 Q + 2^-120) K1 + (32 Q + 64) 2^-120, increasing in K1
+        const float band =
+            2.f * ((qinf * 0x1p-18f + 0x1p-120f) * k1max + (32.f * qinf + 64.f) * 0x1p-120f);
+        if (p.k == 1) {
+            const float mx = wave_max_f32(in ? a : -INFINITY);
+            const unsigned long long near = __ballot(in && !(a < mx - band));
+            if (screened && __popcll(near) == 1) {
+                if (lane == 0) {
+                    const int bs = __ffsll(static_cast<long long>(near)) - 1;
+                    off[0] = region_base_kv(p, bs);
+                    out[0] = bs;
+                }
+                return;
+            }
+        } else {
+            float f[1][1] = {{in ? a : -INFINITY}};
+            int fx[1][1] = {{lane}};
+            bitonic_sort_f32<1, 1, 2>(f, fx, lane);
+            const float next = __shfl_down(f[0][0], 1);
+            const bool bad = lane < p.k && lane + 1 < p.R && !(f[0][0] - next > band);
+            if (screened && __ballot(bad) == 0ull) {
+                if (lane < p.k) {
+                    const int id = min(max(fx[0][0], 0), p.R - 1);
+                    off[lane] = region_base_kv(p, id);
+                    out[lane] = id;
+                }
+                return;
+            }
+        }
+        // the exact pass needs the fp64 means (wave-uniform branch)
+        load_kmean(p, means, bh, min(lane, p.R - 1), kreg);
+    }
+    const double ad = dot32_seq_lanes(qmean_lane, kreg);
     // (Non-finite affinities leave the routing undefined, but every offset
     // the gather uses stays inside the map: the ids are clamped.)
     if (p.k == 1) {
-        double best = lane < p.R ? a : -INFINITY;
-        int bs = lane < p.R ? lane : 0x7fffffff;
+        double best = in ? ad : -INFINITY;
+        int bs = in ? lane : 0x7fffffff;
         wave_argmax(best, bs);
         if (lane == 0) {
             bs = min(max(bs, 0), p.R - 1);
@@ -627,9 +694,7 @@ __device__ __forceinline__ void route_row_wave(const Params& p, double qmean_lan
             out[0] = bs;
         }
     } else {
-        // a bitonic sort of the row over the wave (lane s holds entry s,
-        // lanes past R -inf); lane j < k then holds the id of rank j
-        double v[1][1] = {{lane < p.R ? a : -INFINITY}};
+        double v[1][1] = {{in ? ad : -INFINITY}};
         int ix[1][1] = {{lane}};
         route_topk<1, 1>(v, ix, lane, p.k);
         if (lane < p.k) {
@@ -721,14 +786,21 @@ attend_kernel(const T* __restrict__ q, const T* __restrict__ v, const T* __restr
         load_q_operands(p, J, min(w, J.njobs - 1), reinterpret_cast<const uint16_t*>(q) + img, r,
                         qb);
     int ridx = 0;
+    // routing waves: the K mean of region lane & 63, in fp32 when the
+    // routing screens with it, else in fp64
+    constexpr int kScreenFixed = kFixed ? (kmean32_pays(HS * WS) ? 1 : 0) : -1;
+    const bool screen = kScreenFixed >= 0 ? kScreenFixed == 1 : p.kmean32 != 0;
     double kreg[kHeadDim];
     double qmean_lane = 0.0;  // routing waves: dim lane & 31 of the region's Q mean
     if constexpr (FUSED) {
         // In-kernel routing (R <= 64, heads <= 4): wave w routes this region
-        // for head w; lane s holds the K mean of region s, loaded now with
-        // everything else.
+        // for head w; lane s holds the fp32 K mean of region s, loaded now
+        // with everything else (the fp64 means only if the screen needs them).
         if (wu < p.heads) {
-            load_kmean(p, means, b * p.heads + wu, min(tid & 63, p.R - 1), kreg);
+            if (screen)
+                load_kmean32(p, means, b * p.heads + wu, min(tid & 63, p.R - 1), kreg);
+            else
+                load_kmean(p, means, b * p.heads + wu, min(tid & 63, p.R - 1), kreg);
             if (!qm_here) qmean_lane = means[qmean_index(p, b * p.heads + wu, r, tid & 31)];
         }
     } else {
@@ -741,7 +813,7 @@ attend_kernel(const T* __restrict__ q, const T* __restrict__ v, const T* __restr
                        j];
     }
     // (with in-kernel routing the LePE operands load after it: the K means
-    // hold 64 registers until then)
+    // hold 32 or 64 registers until then)
     LepeOperands<kLepeMfma ? HS : 4, kLepeMfma ? WS : 4, kLepeMfma ? HEADS : 1> lop;
     if constexpr (kLepeMfma && !FUSED) lepe_mfma_load<HS, WS, HEADS>(lepe_table, lepe_bias, lop);
     // halo pieces kept in registers: all of them for a fixed shape (when they
@@ -832,7 +904,8 @@ attend_kernel(const T* __restrict__ q, const T* __restrict__ v, const T* __restr
         }
         if (wu < p.heads) {
             const size_t row = (static_cast<size_t>(b) * p.heads + wu) * p.R + r;
-            route_row_wave(p, qmean_lane, kreg, sOff + wu * p.k, routing + row * p.k);
+            route_row_wave(p, qmean_lane, screen, kreg, means, b * p.heads + wu,
+                           sOff + wu * p.k, routing + row * p.k);
         }
         if constexpr (kLepeMfma) lepe_mfma_load<HS, WS, HEADS>(lepe_table, lepe_bias, lop);
     } else {
@@ -1153,6 +1226,7 @@ bool plan(Params& p, int B, int H, int W, int C, int heads, int n_win, int k, fl
     p.lds_bytes = static_cast<int>(off);
     p.table_items = p.lepe_mfma ? C * 40 : 0;
     p.qmean_attend = qmean_in_attend(bf16, route_in_attend(p), p.t, heads) ? 1 : 0;
+    p.kmean32 = route_in_attend(p) && kmean32_pays(p.t) ? 1 : 0;
     {
         // wave path: one wave per (region, tensor), four waves per workgroup
         const int nvec = C / vec;

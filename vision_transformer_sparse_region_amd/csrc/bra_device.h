@@ -114,6 +114,44 @@ __device__ __forceinline__ void load_kmean(const Params& p, const double* __rest
     }
 }
 
+// The fp32 copy of the K means (each rounded to nearest), in the same order,
+// after the fp64 Q and K means; written when p.kmean32 is set.  The routing
+// inside the attention kernel screens with it (half the bytes of the fp64
+// means) and reads the fp64 means only where the screen cannot decide.
+__device__ __forceinline__ size_t kmean32_offset(const Params& p, int bh, int d, int s) {
+    return ((static_cast<size_t>(bh) * (kHeadDim / 2) + (d >> 1)) * p.R + s) * 2 + (d & 1);
+}
+__device__ __forceinline__ const float* kmean32_base(const Params& p, const double* means) {
+    return reinterpret_cast<const float*>(means +
+                                          2 * static_cast<size_t>(p.B) * p.heads * p.R * kHeadDim);
+}
+__device__ __forceinline__ void store_kmean(const Params& p, double* __restrict__ means, int bh,
+                                            int d, int s, double m) {
+    means[kmean_index(p, bh, d, s)] = m;
+    if (p.kmean32)
+        const_cast<float*>(kmean32_base(p, means))[kmean32_offset(p, bh, d, s)] =
+            static_cast<float>(m);
+}
+// Dims d and d + 1 (d even) of one K mean: one 16-byte and one 8-byte store.
+__device__ __forceinline__ void store_kmean_pair(const Params& p, double* __restrict__ means,
+                                                 int bh, int d, int s, double m0, double m1) {
+    *reinterpret_cast<double2*>(means + kmean_index(p, bh, d, s)) = double2{m0, m1};
+    if (p.kmean32)
+        *reinterpret_cast<float2*>(const_cast<float*>(kmean32_base(p, means)) +
+                                   kmean32_offset(p, bh, d, s)) =
+            float2{static_cast<float>(m0), static_cast<float>(m1)};
+}
+// The fp32 K mean of region s, head bh: dims 2j, 2j + 1 as the two halves
+// of kb[j], j < 16 (16 coalesced 8-byte loads; kb[16..31] untouched, so the
+// same registers can hold the fp64 mean instead).
+__device__ __forceinline__ void load_kmean32(const Params& p, const double* __restrict__ means,
+                                             int bh, int s, double (&kb)[kHeadDim]) {
+    const float* base = kmean32_base(p, means);
+#pragma unroll
+    for (int j = 0; j < kHeadDim / 2; ++j)
+        kb[j] = *reinterpret_cast<const double*>(base + kmean32_offset(p, bh, 2 * j, s));
+}
+
 // mean = sum / t, as a multiplication when t is a power of two (exact then).
 __device__ __forceinline__ double mean_of(double sum, int t) {
     return (t & (t - 1)) == 0 ? sum * (1.0 / static_cast<double>(t)) : sum / static_cast<double>(t);
@@ -191,11 +229,17 @@ __device__ __forceinline__ uint2 lepe_toeplitz_entry(const float* __restrict__ l
     const int ks = it & 1, i = (it >> 1) % 5, lane_cg = it / 10;
     const int lane = lane_cg & 63, cg = lane_cg >> 6;
     const int c = 16 * cg + (lane >> 2), n = lane & 3;
+    // the four loads go out together (clamped tap, always in the row), the
+    // taps outside the kernel are zeroed afterwards
+    float wv[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+        wv[kk] = lepe_w[c * 25 + i * 5 + min(max(4 * ks + kk - n, 0), 4)];
     uint32_t h[4];
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
         const int j = 4 * ks + kk - n;
-        h[kk] = (j >= 0 && j <= 4) ? f32_to_bf16(lepe_w[c * 25 + i * 5 + j]) : 0u;
+        h[kk] = (j >= 0 && j <= 4) ? f32_to_bf16(wv[kk]) : 0u;
     }
     return uint2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
 }
@@ -300,6 +344,19 @@ __device__ __forceinline__ int lane_xor_dpp(int x) {
     const int m7 = __builtin_amdgcn_mov_dpp(x, 0x141, 0xf, 0xf, false);
     if constexpr (J == 4) return __builtin_amdgcn_mov_dpp(m7, 0x1B, 0xf, 0xf, false);
     return __builtin_amdgcn_mov_dpp(m7, 0x140, 0xf, 0xf, false);
+}
+// Maximum over the wave (every lane ends with it), non-NaN values: DPP
+// within rows of 16, then the row swaps of group4_max.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float wave_max_f32(float x) {
+    x = max_f(x, dpp_f32<0xB1>(x));   // lane ^ 1
+    x = max_f(x, dpp_f32<0x4E>(x));   // lane ^ 2
+    x = max_f(x, dpp_f32<0x141>(x));  // the other quad of 8
+    x = max_f(x, dpp_f32<0x140>(x));  // the other 8 of 16
+    return group4_max(x);
 }
 // Lane `src`'s x, wave-uniform.
 __device__ __forceinline__ double readlane_f64(double x, int src) {

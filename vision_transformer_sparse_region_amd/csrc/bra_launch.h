@@ -47,6 +47,8 @@ struct Params {
     int pool_blocks; // workgroups computing means (the table follows them)
     int qmean_attend; // 1: the attention kernel sums the Q means itself; the
                       // pool kernel then computes only the K means
+    int kmean32;     // 1: the K means are also written in fp32 (the in-kernel
+                     // routing's first pass reads them)
     int pool_chunk;  // staged path: tokens staged per step
     int pool_lds_bytes;
 };
@@ -57,7 +59,8 @@ bool plan(Params& p, int B, int H, int W, int C, int heads, int n_win, int k, fl
 
 // Kernel launches on `stream`; return the launch status.
 //   means: fp64 region means, Q as [B][heads][R][32], then K as [B][heads][16][R][2]
-//   (kmean_index: dims in pairs).
+//   (kmean_index: dims in pairs), then K again in fp32, same order (kmean32_offset;
+//   written when p.kmean32).
 //   lepe_table: p.table_items 8-byte entries (written by the pool kernel when
 //   lepe_w is given and the shape runs LePE on MFMA).
 //   routing: [B][rheads][R][k] int32 region ids.
@@ -73,6 +76,11 @@ constexpr bool route_fused(int R, int heads) {
     return R <= 64 && heads <= kWaves;
 }
 inline bool route_in_attend(const Params& p) { return !p.shared && route_fused(p.R, p.heads); }
+// The in-kernel routing screens with fp32 K means where a mean sums at least
+// 32 tokens: the fp32 copy then adds at most 1/16 to the bytes the pool
+// kernel moves (measured: stage-1 windows of 64 tokens gain 1 us per forward,
+// 16-token windows lose 0.4).
+__host__ __device__ constexpr bool kmean32_pays(int t) { return t >= 32; }
 
 // Small region grids routed outside the attention kernel (per head, bf16)
 // with small regions: one kernel computes the region means and routes

@@ -94,18 +94,30 @@ __global__ __launch_bounds__(kThreads) void pool_qk_kernel(const T* __restrict__
             acc[6] += bf16lo(u.w); acc[7] += bf16hi(u.w);
         }
         token_group_sum(acc, nvec);
-        if (tg == 0) {
-            const int c = pv * 8, h = c / kHeadDim, d = c - h * kHeadDim;
-            const int bh = b * p.heads + h;
-            if (tensor == 0) {
+        // every lane of a channel piece now holds the piece's sums
+        const int c = pv * 8, h = c / kHeadDim, d = c - h * kHeadDim;
+        const int bh = b * p.heads + h;
+        if (tensor == 0) {
+            if (tg == 0) {
                 double* dst = means + qmean_index(p, bh, r, d);
 #pragma unroll
                 for (int e = 0; e < 8; e += 2)
                     *reinterpret_cast<double2*>(dst + e) =
                         double2{mean_of(acc[e], p.t), mean_of(acc[e + 1], p.t)};
-            } else {
+            }
+        } else {
+            // K: lane tg of the piece stores dim pair tg (pairs tg, tg + TG,
+            // .. when fewer than 4 lanes share the piece), the pair picked by
+            // selects rather than a dynamic register index
+            for (int j = tg; j < 4; j += TG) {
+                double m0 = acc[0], m1 = acc[1];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) means[kmean_index(p, bh, d + e, r)] = mean_of(acc[e], p.t);
+                for (int e = 2; e < 8; e += 2)
+                    if (j == e / 2) {
+                        m0 = acc[e];
+                        m1 = acc[e + 1];
+                    }
+                store_kmean_pair(p, means, bh, d + 2 * j, r, mean_of(m0, p.t), mean_of(m1, p.t));
             }
         }
         return;
@@ -145,8 +157,10 @@ __global__ __launch_bounds__(kThreads) void pool_qk_kernel(const T* __restrict__
             if (c < p.C) {
                 const int h = c / kHeadDim, d = c - h * kHeadDim;
                 const int bh = b * p.heads + h;
-                means[tensor == 0 ? qmean_index(p, bh, r, d) : kmean_index(p, bh, d, r)] =
-                    mean_of(acc[j], p.t);
+                if (tensor == 0)
+                    means[qmean_index(p, bh, r, d)] = mean_of(acc[j], p.t);
+                else
+                    store_kmean(p, means, bh, d, r, mean_of(acc[j], p.t));
             }
         }
     }

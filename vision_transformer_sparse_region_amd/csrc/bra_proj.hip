@@ -252,8 +252,10 @@ __global__ __launch_bounds__(kThreads) void proj_qkv_kernel(
                             sum += static_cast<double>(bf16_to_f32(sO[u * kOutRow + cc]));
                         const int c = c0 + cc, h = c / kHeadDim, d = c - h * kHeadDim;
                         const int bh = b * p.heads + h;
-                        means[which == 0 ? qmean_index(p, bh, r0 + rr, d)
-                                         : kmean_index(p, bh, d, r0 + rr)] = mean_of(sum, p.t);
+                        if (which == 0)
+                            means[qmean_index(p, bh, r0 + rr, d)] = mean_of(sum, p.t);
+                        else
+                            store_kmean(p, means, bh, d, r0 + rr, mean_of(sum, p.t));
                     }
                 } else if (pc < cw) {
                     for (int u = part; u < nt; u += kSumParts)
@@ -279,8 +281,10 @@ __global__ __launch_bounds__(kThreads) void proj_qkv_kernel(
                 for (int q = 0; q < kSumParts; ++q) sum += sP[q * kProjOut + tid];
                 const int c = c0 + tid, h = c / kHeadDim, d = c - h * kHeadDim;
                 const int bh = b * p.heads + h;
-                means[which == 0 ? qmean_index(p, bh, r0, d) : kmean_index(p, bh, d, r0)] =
-                    mean_of(sum, p.t);
+                if (which == 0)
+                    means[qmean_index(p, bh, r0, d)] = mean_of(sum, p.t);
+                else
+                    store_kmean(p, means, bh, d, r0, mean_of(sum, p.t));
             }
         }
     }
