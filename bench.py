@@ -87,13 +87,22 @@ def qmean_in_attend(wl, shared_routing: bool = False) -> bool:
     return wl.num_heads * ((qt + per_group - 1) // per_group) <= 4
 
 
+def kmean32(wl, shared_routing: bool = False) -> bool:
+    """Mirrors the library: the routing inside the attention kernel screens
+    with an fp32 copy of the K means (written next to the fp64 ones) when a
+    window holds at least 32 tokens."""
+    return route_in_attend(wl, shared_routing) and wl.tokens_per_region >= 32
+
+
 def algorithmic_bytes(wl, shared_routing: bool = False, kv_ratio: int = 1,
                       projections: bool = False) -> dict:
     """Bytes each kernel must move once per launch (unique bytes; the k-fold
     re-reads of routed K/V, of the LePE halo and of the K means are cache
     traffic).  When the routing runs inside the attention kernel, that kernel
     also reads the means and writes the ids; when it also sums the Q means,
-    only the K means are written and read."""
+    only the K means are written and read.  Where it screens with fp32 K
+    means, those are written besides the fp64 ones and read instead of them
+    (the fp64 means are read only for near ties)."""
     es = 2 if wl.dtype == "bf16" else 4
     S = wl.tokens * wl.channels * es                     # one [B,H,W,C] tensor
     M = wl.batch * wl.channels * wl.regions * 8          # one fp64 [B,heads,R,32] mean array
@@ -105,24 +114,27 @@ def algorithmic_bytes(wl, shared_routing: bool = False, kv_ratio: int = 1,
     # attention then gathers the pooled K/V (2S/r^2) and still reads v for LePE
     kvpool = 2 * S + 2 * S // r2 if r2 > 1 else 0
     attend = (3 * S + 2 * S // r2 if r2 > 1 else 4 * S) + idx + lepe
+    k32 = M // 2 if kmean32(wl, shared_routing) else 0   # fp32 K means
+    kread = k32 if k32 else M                            # K means the attention reads
     if projections:
         # the qkv projection reads x and the weights, writes q, k, v and both
         # means; the attention kernel also reads the output weights.  (When
         # the output projection is a kernel of its own, the attention slot
         # times both kernels; y's round trip between them is not counted.)
         wq, wo = 3 * wl.channels * wl.channels * es, wl.channels * wl.channels * es
-        pool = S + wq + 3 * wl.channels * 4 + 3 * S + 2 * M + kvpool
+        pool = S + wq + 3 * wl.channels * 4 + 3 * S + 2 * M + k32 + kvpool
         att = attend + wo + wl.channels * 4
         if route_in_attend(wl, shared_routing):
-            return {"pool": pool, "route": 0, "attend": att + 2 * M, "S": S}
+            return {"pool": pool, "route": 0, "attend": att + M + kread, "S": S}
         return {"pool": pool, "route": 2 * M + idx, "attend": att, "S": S}
     if route_in_pool(wl, shared_routing):
         # one kernel reads q and k and writes the ids; no mean array in HBM
         return {"pool": 2 * S + idx + kvpool, "route": 0, "attend": attend, "S": S}
     if qmean_in_attend(wl, shared_routing):
-        return {"pool": S + M + kvpool, "route": 0, "attend": attend + M, "S": S}
+        return {"pool": S + M + k32 + kvpool, "route": 0, "attend": attend + kread, "S": S}
     if route_in_attend(wl, shared_routing):
-        return {"pool": 2 * S + 2 * M + kvpool, "route": 0, "attend": attend + 2 * M, "S": S}
+        return {"pool": 2 * S + 2 * M + k32 + kvpool, "route": 0, "attend": attend + M + kread,
+                "S": S}
     return {
         "pool": 2 * S + 2 * M + kvpool,                  # read q, k; write both means
         "route": 2 * M + idx,                            # read both means; write the ids

@@ -14,10 +14,25 @@ def test_algorithmic_bytes_stage1():
     idx = 64 * 2 * 49 * 1 * 4
     assert ab["S"] == S
     # 49 regions, 2 heads: routed inside the attention kernel, which also sums
-    # the Q means; the pool kernel reads k and writes the K means only
-    assert ab["pool"] == S + M
+    # the Q means; the pool kernel reads k and writes the K means only, in
+    # fp64 and (64-token windows) in fp32, and the attention kernel reads the
+    # fp32 ones
+    assert bench.kmean32(wl)
+    assert ab["pool"] == S + M + M // 2
     assert ab["route"] == 0
-    assert ab["attend"] == 4 * S + M + idx + 64 * 26 * 4
+    assert ab["attend"] == 4 * S + M // 2 + idx + 64 * 26 * 4
+
+
+def test_fp32_k_means_only_for_windows_of_32_tokens():
+    assert not bench.kmean32(WORKLOADS["stage2"])            # 16-token windows
+    assert not bench.kmean32(WORKLOADS["stage3"])            # routed outside
+    assert not bench.kmean32(WORKLOADS["highres"])           # 256 regions
+    assert not bench.kmean32(WORKLOADS["stage1"], shared_routing=True)
+    wl = WORKLOADS["stage2"]
+    S = 64 * 28 * 28 * 128 * 2
+    M = 64 * 128 * 49 * 8
+    ab = bench.algorithmic_bytes(wl)
+    assert ab["pool"] == S + M
 
 
 def test_q_means_summed_in_attention_kernel():
