@@ -31,7 +31,9 @@
  *      zero padding 2 over the whole map, plus a per-channel bias
  *      [P5 §五 self.lepe and ⑧; P2 §2.2].
  *   Routing is computed in fp64 (region sums are exact for bf16 input), so
- *   routing_idx equals a float64 evaluation of steps 2-3.  Attention runs on
+ *   routing_idx equals a float64 evaluation of steps 2-3.  (Where a faster
+ *   fp32 pass is taken first, an error bound decides whether its order is
+ *   the fp64 one; otherwise the fp64 values decide.)  Attention runs on
  *   bf16 MFMA with fp32 accumulation and an fp32 online softmax (bf16 I/O)
  *   or in fp32 VALU arithmetic (fp32 I/O); LePE accumulates in fp32.
  *
@@ -106,7 +108,8 @@ typedef struct {
 } bra_config_t;
 
 /* Validate cfg and allocate the handle and its device workspace on the
- * current HIP device: the fp64 region means of Q and K (2*B*C*R*8 bytes), a
+ * current HIP device: the region means of Q and K (2*B*C*R*8 bytes in fp64,
+ * B*C*R*4 more for an fp32 copy of the K means), a
  * routing buffer (B*heads*R*k*4 bytes), for window shapes whose LePE runs on
  * MFMA a C*320-byte operand table, with KV downsampling the pooled K and V
  * (2*B*H*W*C*sizeof(dtype)/r^2 bytes), and with projections the projected

@@ -7,8 +7,10 @@
 //      weights or Toeplitz operands, the V window with its 2-token halo, the
 //      first job's Q operands                                  [P5 §五 ⑤]
 //   1b in-kernel routing: the Q means from the Q operands (exact fp64 sums),
-//      the fp64 affinity with every region, arg-max or bitonic top-k, wave h
-//      for head h                              [P4 §1.2; P1 §2.1; P5 §五 ③-④]
+//      the affinity with every region -- screened with fp32 K means and an
+//      error bound, the fp64 affinities where the bound cannot decide --,
+//      arg-max or bitonic top-k, wave h for head h
+//                                              [P4 §1.2; P1 §2.1; P5 §五 ③-④]
 //   2  each wave issues the gathers of its first two routed K/V chunks ...
 //   3  ... the halo goes to LDS and the 5x5 depthwise LePE of V runs while
 //      those loads are in flight                       [P5 §五 lepe, ⑧; P2 §2.2]
