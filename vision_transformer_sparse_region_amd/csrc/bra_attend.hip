@@ -724,6 +724,14 @@ attend_kernel(const T* __restrict__ q, const T* __restrict__ v, const T* __restr
               const uint2* __restrict__ lepe_table, const uint16_t* __restrict__ w_o,
               const float* __restrict__ b_o, T* __restrict__ out, Params p_in) {
     const Params p = fold_geometry<HS, WS, NW, HEADS, KTOP, Elem<T>::kVec>(p_in);
+    // Where this kernel routes windows of at least 32 tokens (fixed shapes),
+    // the prologue -- loads, Q means, routing, up to the first gathers -- runs
+    // at raised wave priority: that chain decides when the workgroup's
+    // gathers go out (stage 1: attention 36.5 -> 35.7 us; with 16-token
+    // windows it measured 0.6 us slower).
+    constexpr bool kPrioPrologue = HS > 0 && WS > 0 && NW > 0 && HEADS > 0 && KTOP > 0 &&
+                                   FUSED && kmean32_pays(HS * WS);
+    if constexpr (kPrioPrologue) __builtin_amdgcn_s_setprio(2);
     extern __shared__ __align__(16) unsigned char smem[];
     T* sVh = reinterpret_cast<T*>(smem + p.off_vh);
     float* sL = reinterpret_cast<float*>(smem + p.off_l);
@@ -1045,6 +1053,7 @@ attend_kernel(const T* __restrict__ q, const T* __restrict__ v, const T* __restr
                                  reinterpret_cast<const uint16_t*>(vg) + kimg, sOff, ring[ch]);
         }
     }
+    if constexpr (kPrioPrologue) __builtin_amdgcn_s_setprio(0);
     if (!early_lepe) {
         stage_halo();
         if constexpr (kLepeMfma) {
