@@ -125,20 +125,21 @@ __device__ __forceinline__ const float* kmean32_base(const Params& p, const doub
     return reinterpret_cast<const float*>(means +
                                           2 * static_cast<size_t>(p.B) * p.heads * p.R * kHeadDim);
 }
+__device__ __forceinline__ float* kmean32_base(const Params& p, double* means) {
+    return reinterpret_cast<float*>(means + 2 * static_cast<size_t>(p.B) * p.heads * p.R * kHeadDim);
+}
 __device__ __forceinline__ void store_kmean(const Params& p, double* __restrict__ means, int bh,
                                             int d, int s, double m) {
     means[kmean_index(p, bh, d, s)] = m;
     if (p.kmean32)
-        const_cast<float*>(kmean32_base(p, means))[kmean32_offset(p, bh, d, s)] =
-            static_cast<float>(m);
+        kmean32_base(p, means)[kmean32_offset(p, bh, d, s)] = static_cast<float>(m);
 }
 // Dims d and d + 1 (d even) of one K mean: one 16-byte and one 8-byte store.
 __device__ __forceinline__ void store_kmean_pair(const Params& p, double* __restrict__ means,
                                                  int bh, int d, int s, double m0, double m1) {
     *reinterpret_cast<double2*>(means + kmean_index(p, bh, d, s)) = double2{m0, m1};
     if (p.kmean32)
-        *reinterpret_cast<float2*>(const_cast<float*>(kmean32_base(p, means)) +
-                                   kmean32_offset(p, bh, d, s)) =
+        *reinterpret_cast<float2*>(kmean32_base(p, means) + kmean32_offset(p, bh, d, s)) =
             float2{static_cast<float>(m0), static_cast<float>(m1)};
 }
 // The fp32 K mean of region s, head bh: dims 2j, 2j + 1 as the two halves
