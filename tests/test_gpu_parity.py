@@ -63,6 +63,9 @@ SMALL = [
     Workload("max_window_c32_r256", 1, 240, 240, 32, 1, 16, 4, "bf16", 133),
     Workload("max_window_c64", 1, 100, 100, 64, 2, 10, 3, "bf16", 134, lepe_bias=True),
     Workload("max_window_c128", 2, 36, 36, 128, 4, 6, 5, "bf16", 135),
+    # the whole-image kernel (the head group's K and V resident in LDS):
+    # stage-3 geometry with a bias and a batch of 3
+    Workload("image_stage3_bias_b3", 3, 14, 14, 256, 8, 7, 16, "bf16", 150, lepe_bias=True),
     Workload("f32_stage2_shape", 4, 28, 28, 128, 4, 7, 4, "f32", 109),
     Workload("f32_ragged_bias", 2, 12, 20, 64, 2, 4, 3, "f32", 110, lepe_bias=True),
 ]
@@ -75,6 +78,10 @@ def test_small_case(wl):
 
 def test_without_lepe():
     check_parity(Workload("no_lepe", 4, 56, 56, 64, 2, 7, 1, "bf16", 111), lepe=False)
+
+
+def test_without_lepe_image_kernel():
+    check_parity(Workload("image_no_lepe", 2, 28, 28, 128, 4, 7, 4, "bf16", 151), lepe=False)
 
 
 def test_explicit_scale():
@@ -96,8 +103,13 @@ def test_routing_export_optional_and_deterministic():
 
 @pytest.mark.parametrize("wl", [Workload("all_tied", 2, 28, 28, 128, 4, 7, 6, "bf16", 114),
                                 Workload("all_tied_pool_route", 2, 14, 14, 256, 8, 7, 6, "bf16",
-                                         132)],
-                         ids=["attention_kernel_routes", "pool_kernel_routes"])
+                                         132),
+                                Workload("all_tied_image_k4", 2, 28, 28, 128, 4, 7, 4, "bf16",
+                                         152),
+                                Workload("all_tied_image_k16", 2, 14, 14, 256, 8, 7, 16, "bf16",
+                                         153)],
+                         ids=["attention_kernel_routes", "pool_kernel_routes",
+                              "image_kernel_k4", "image_kernel_k16"])
 def test_exact_ties_pick_lower_regions(wl):
     """Every K window identical: all affinities of a row tie exactly, so the
     routing is regions 0..k-1 in order."""
@@ -107,7 +119,7 @@ def test_exact_ties_pick_lower_regions(wl):
     inp["k"] = tile.repeat(1, wl.n_win, wl.n_win, 1).contiguous()
     say("[gpu] all_tied")
     _, idx = run_gpu(wl, inp)
-    assert (idx == np.arange(6, dtype=np.int32)).all()
+    assert (idx == np.arange(wl.topk, dtype=np.int32)).all()
     check_parity(wl, inp)
 
 

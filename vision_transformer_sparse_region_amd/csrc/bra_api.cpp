@@ -14,6 +14,7 @@
 #include <string>
 #include <vector>
 
+#include "bra_image.h"
 #include "bra_launch.h"
 
 struct bra_handle_s {
@@ -150,6 +151,10 @@ bra_status_t bra_create(const bra_config_t* cfg, bra_handle_t* out) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return fail_hip(e, "bra_create: hipGetDevice");
+    if (bra::image_applies(p, bf16)) {
+        e = bra::prepare_image(p);
+        if (e != hipSuccess) return fail_hip(e, "bra_create: image kernel LDS limit");
+    }
     bra_handle_t h = new (std::nothrow) bra_handle_s();
     if (!h) return fail(BRA_ERR_NOMEM, "bra_create: host allocation failed");
     h->cfg = c;
@@ -277,9 +282,11 @@ static bra_status_t enqueue_forward(bra_handle_t h, const char* what, const void
     // the routing goes to the caller's buffer when one is given
     int32_t* routing = routing_idx ? routing_idx : h->routing;
     const bra::Params& P = h->params;
+    // maps whose head-group K and V fit LDS: the whole forward in one kernel
+    const bool image = bra::image_applies(P, h->bf16);
     // small region grids with many heads: means and routing in one kernel
     const bool pool_route =
-        !x && bra::route_in_pool(h->bf16, P.shared != 0, P.R, P.heads, P.t);
+        !x && !image && bra::route_in_pool(h->bf16, P.shared != 0, P.R, P.heads, P.t);
     if (x) {
         e = bra::launch_proj_qkv(h->params, x, w_qkv, b_qkv, h->qs, h->ks, h->vs, h->means,
                                  lepe_w, h->lepe_table, s);
@@ -290,7 +297,7 @@ static bra_status_t enqueue_forward(bra_handle_t h, const char* what, const void
     } else if (pool_route) {
         e = bra::launch_pool_route(h->params, q, k, lepe_w, h->lepe_table, routing, s);
         if (e != hipSuccess) return fail_hip(e, (wh + ": region-pool and routing launch").c_str());
-    } else {
+    } else if (!image) {
         e = bra::launch_pool_qk(h->params, h->bf16, q, k, lepe_w, h->means, h->lepe_table, s);
         if (e != hipSuccess) return fail_hip(e, (wh + ": region-pool launch").c_str());
     }
@@ -301,7 +308,7 @@ static bra_status_t enqueue_forward(bra_handle_t h, const char* what, const void
     if (timed && (e = hipEventRecord(ev[1], s)) != hipSuccess)
         return fail_hip(e, (wh + ": hipEventRecord").c_str());
     // small region grids are routed inside the attention kernel
-    if (!bra::route_in_attend(h->params) && !pool_route) {
+    if (!image && !bra::route_in_attend(h->params) && !pool_route) {
         e = bra::launch_route(h->params, h->bf16, h->means, routing, s);
         if (e != hipSuccess) return fail_hip(e, (wh + ": routing launch").c_str());
     }
@@ -310,11 +317,17 @@ static bra_status_t enqueue_forward(bra_handle_t h, const char* what, const void
     // the output projection: in the attention kernel's epilogue, or over y
     // in a kernel of its own (h->ys is set for the shapes that take that)
     const bool proj_after = w_o && h->ys;
-    e = bra::launch_attend(h->params, h->bf16, q, v, h->kd ? h->kd : k, h->vd ? h->vd : v,
+    if (image) {
+        e = bra::launch_image(h->params, q, k, v, lepe_w, lepe_b, routing, false,
+                              proj_after ? h->ys : out, s);
+        if (e != hipSuccess) return fail_hip(e, (wh + ": image kernel launch").c_str());
+    } else {
+        e = bra::launch_attend(h->params, h->bf16, q, v, h->kd ? h->kd : k, h->vd ? h->vd : v,
                            h->means, routing, !bra::route_in_attend(h->params), lepe_w, lepe_b,
                            h->lepe_table, h->zero_bias, proj_after ? nullptr : w_o, b_o,
                            proj_after ? h->ys : out, s);
-    if (e != hipSuccess) return fail_hip(e, (wh + ": attention launch").c_str());
+        if (e != hipSuccess) return fail_hip(e, (wh + ": attention launch").c_str());
+    }
     if (proj_after) {
         e = bra::launch_proj_out(h->params, h->ys, w_o, b_o, out, s);
         if (e != hipSuccess) return fail_hip(e, (wh + ": output projection launch").c_str());
@@ -366,6 +379,12 @@ bra_status_t bra_forward_routed(bra_handle_t h, const void* q, const void* k, co
     if (st != BRA_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = hipSuccess;
+    if (bra::image_applies(h->params, h->bf16)) {
+        e = bra::launch_image(h->params, q, k, v, lepe_w, lepe_b,
+                              const_cast<int32_t*>(routing_idx), true, out, s);
+        if (e != hipSuccess) return fail_hip(e, "bra_forward_routed: image kernel launch");
+        return BRA_OK;
+    }
     // the MFMA LePE operand table is the region-pool kernel's side product:
     // build it alone (no means) when this shape uses it
     if (lepe_w && h->params.table_items > 0) {
