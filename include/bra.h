@@ -88,7 +88,8 @@ typedef struct {
     int32_t batch, height, width, channels, num_heads;
     int32_t n_win;     /* regions per side: H % n_win == 0 and W % n_win == 0 */
     int32_t topk;      /* routed regions per region; <= 0 or > n_win^2 means all */
-    bra_dtype_t dtype; /* element type of q, k, v and out */
+    int32_t dtype;     /* element type of q, k, v and out: a bra_dtype_t (BRA_F32 or
+                          BRA_BF16; other values are rejected) */
     float scale;       /* attention logit scale; <= 0 means head_dim^-0.5 */
     int32_t shared_routing; /* 0: routing per head (the default, [P5 §五 ③-④]);
                                1: one routing per region shared by every head,
@@ -180,8 +181,9 @@ bra_status_t bra_destroy(bra_handle_t h);
 /* k actually used by the handle (min(topk, R), or R); -1 for a bad handle. */
 int32_t bra_topk_effective(bra_handle_t h);
 
-/* Static description of a status code. */
-const char* bra_status_string(bra_status_t s);
+/* Static description of a status code ("unknown status" for any other
+ * value; taken as an int32_t so that any value can be passed). */
+const char* bra_status_string(int32_t s);
 
 /* Thread-local detail of the last failing call on this thread ("" if none). */
 const char* bra_last_error(void);
@@ -198,6 +200,19 @@ const char* bra_last_error(void);
  * projection.  `ms` holds at least 3*n floats. */
 bra_status_t bra_timing_enable(bra_handle_t h, int32_t n);
 bra_status_t bra_timing_read(bra_handle_t h, float* ms, int32_t* count);
+
+/* Testing hooks (failure handling without exhausting a device).
+ * bra_debug_inject_alloc_failure(which, n): the next n allocations of kind
+ * `which` made by bra_create fail as if memory were exhausted -- the handle
+ * itself (BRA_ALLOC_HOST) or its device workspace (BRA_ALLOC_DEVICE) --, so
+ * bra_create returns BRA_ERR_NOMEM, leaves *out NULL and frees whatever it
+ * had allocated; n = 0 disarms.  Both failures are injected before any HIP
+ * call, so they are testable without a GPU.  BRA_ERR_SHAPE for n < 0 or an
+ * unknown kind.  bra_debug_live_handles() is the number of handles created
+ * and not yet destroyed, in this process. */
+enum { BRA_ALLOC_HOST = 1, BRA_ALLOC_DEVICE = 2 };
+bra_status_t bra_debug_inject_alloc_failure(int32_t which, int32_t count);
+int32_t bra_debug_live_handles(void);
 
 #ifdef __cplusplus
 }

@@ -94,3 +94,32 @@ def test_missing_library_fails_loudly(tmp_path, monkeypatch):
     monkeypatch.setattr(bra, "_lib", None)
     with pytest.raises(bra.BraLibraryMissing):
         bra.load_library(str(tmp_path / "libbra.so"))
+
+
+@pytest.mark.parametrize("which", [bra.BRA_ALLOC_HOST, bra.BRA_ALLOC_DEVICE],
+                         ids=["handle", "workspace"])
+def test_create_reports_allocation_failure_and_leaks_nothing(lib, which):
+    """An injected allocation failure makes bra_create return BRA_ERR_NOMEM,
+    leave *out NULL and keep no handle alive; the hook disarms after its
+    count.  (The failure is injected before any HIP call, so this runs
+    without a GPU; the host-sanitizer build of the library runs it too.)"""
+    live = bra.bra_debug_live_handles()
+    assert bra.bra_debug_inject_alloc_failure(which, 2) == bra.BRA_OK
+    for _ in range(2):
+        h = ctypes.c_void_p(0x1)
+        c = _cfg()
+        assert lib.bra_create(ctypes.byref(c), ctypes.byref(h)) == bra.BRA_ERR_NOMEM
+        assert h.value is None
+        assert "out of memory" in bra.bra_last_error() or "host allocation" in bra.bra_last_error()
+        assert bra.bra_debug_live_handles() == live
+    # disarmed: the next create gets past the allocation (on a CPU host it
+    # then fails at the first HIP call, never with BRA_ERR_NOMEM)
+    st = bra.bra_create_status(_cfg())
+    assert st != bra.BRA_ERR_NOMEM
+    assert bra.bra_debug_live_handles() == live
+
+
+def test_alloc_failure_hook_arguments(lib):
+    assert bra.bra_debug_inject_alloc_failure(bra.BRA_ALLOC_HOST, -1) == bra.BRA_ERR_SHAPE
+    assert bra.bra_debug_inject_alloc_failure(7, 1) == bra.BRA_ERR_SHAPE
+    assert bra.bra_debug_inject_alloc_failure(bra.BRA_ALLOC_DEVICE, 0) == bra.BRA_OK

@@ -16,7 +16,9 @@ import os
 import re
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libbra.so")
+# BRA_LIBRARY names another build of the same ABI (the host-sanitizer build
+# the CPU tests use); a missing library fails loudly either way.
+LIB_PATH = os.environ.get("BRA_LIBRARY", os.path.join(PKG, "libbra.so"))
 HEADER = os.path.join(os.path.dirname(PKG), "include", "bra.h")
 
 BRA_OK = 0
@@ -80,8 +82,11 @@ def load_library(path: str = LIB_PATH):
     lib.bra_last_error.restype = ctypes.c_char_p
     lib.bra_timing_enable.argtypes = [vp, i32]
     lib.bra_timing_read.argtypes = [vp, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(i32)]
+    lib.bra_debug_inject_alloc_failure.argtypes = [i32, i32]
+    lib.bra_debug_live_handles.argtypes = []
+    lib.bra_debug_live_handles.restype = i32
     for name in ("bra_create", "bra_forward", "bra_forward_routed", "bra_forward_proj",
-                 "bra_destroy",
+                 "bra_destroy", "bra_debug_inject_alloc_failure",
                  "bra_timing_enable", "bra_timing_read"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
@@ -201,6 +206,19 @@ def bra_timing_enable(h, n: int) -> None:
     _check(load_library().bra_timing_enable(h, n), "bra_timing_enable")
 
 
+BRA_ALLOC_HOST, BRA_ALLOC_DEVICE = 1, 2
+
+
+def bra_debug_inject_alloc_failure(which: int, count: int) -> int:
+    """Make the next `count` allocations of kind `which` in bra_create fail
+    (a testing hook); returns the raw status."""
+    return load_library().bra_debug_inject_alloc_failure(which, count)
+
+
+def bra_debug_live_handles() -> int:
+    return int(load_library().bra_debug_live_handles())
+
+
 KERNELS = ("region_pool", "route", "attend")
 
 
@@ -233,6 +251,31 @@ class BRA:
         self.handle = bra_create(self.cfg)
         self.k = bra_topk_effective(self.handle)
 
+    # The C ABI cannot see tensor sizes: every tensor handed to it is checked
+    # here against the shape, dtype and device the call reads or writes.
+    def _check_tensor(self, name, t, dtype, shape, device):
+        if (t.dtype != dtype or tuple(t.shape) != tuple(shape) or not t.is_contiguous() or
+                not t.is_cuda or t.device != device):
+            raise ValueError(f"{name}: expected a contiguous {dtype} tensor {tuple(shape)} on "
+                             f"{device}, got {t.dtype} {tuple(t.shape)} on {t.device}")
+
+    def _check_common(self, first, lepe_w, lepe_b, out, routing_idx):
+        import torch
+        c = self.cfg
+        dev = first.device
+        if lepe_w is not None:
+            # lepe_w may be [C, 5, 5] or PyTorch's depthwise [C, 1, 5, 5]
+            shape = (c.channels, 1, 5, 5) if lepe_w.dim() == 4 else (c.channels, 5, 5)
+            self._check_tensor("lepe_w", lepe_w, torch.float32, shape, dev)
+        if lepe_b is not None:
+            self._check_tensor("lepe_b", lepe_b, torch.float32, (c.channels,), dev)
+        if out is not None:
+            self._check_tensor("out", out, first.dtype, (c.batch, c.height, c.width, c.channels),
+                               dev)
+        if routing_idx is not None and routing_idx is not True and routing_idx is not False:
+            self._check_tensor("routing_idx", routing_idx, torch.int32,
+                               (c.batch, self.route_heads, c.n_win * c.n_win, self.k), dev)
+
     def forward(self, q, k, v, lepe_w=None, lepe_b=None, out=None, routing_idx=True,
                 stream=None):
         import torch
@@ -240,11 +283,8 @@ class BRA:
         want = torch.bfloat16 if self.dtype == "bf16" else torch.float32
         shape = (c.batch, c.height, c.width, c.channels)
         for name, t in (("q", q), ("k", k), ("v", v)):
-            if t.dtype != want or tuple(t.shape) != shape or not t.is_contiguous() or not t.is_cuda:
-                raise ValueError(f"{name}: expected a contiguous {want} CUDA tensor {shape}")
-        for name, t in (("lepe_w", lepe_w), ("lepe_b", lepe_b)):
-            if t is not None and (t.dtype != torch.float32 or not t.is_contiguous() or not t.is_cuda):
-                raise ValueError(f"{name}: expected a contiguous float32 CUDA tensor")
+            self._check_tensor(name, t, want, shape, q.device)
+        self._check_common(q, lepe_w, lepe_b, out, routing_idx)
         if out is None:
             out = torch.empty_like(q)
         if routing_idx is True:
@@ -264,12 +304,10 @@ class BRA:
         want = torch.bfloat16 if self.dtype == "bf16" else torch.float32
         shape = (c.batch, c.height, c.width, c.channels)
         for name, t in (("q", q), ("k", k), ("v", v)):
-            if t.dtype != want or tuple(t.shape) != shape or not t.is_contiguous() or not t.is_cuda:
-                raise ValueError(f"{name}: expected a contiguous {want} CUDA tensor {shape}")
-        rshape = (c.batch, self.route_heads, c.n_win * c.n_win, self.k)
-        if (routing_idx.dtype != torch.int32 or tuple(routing_idx.shape) != rshape or
-                not routing_idx.is_contiguous() or not routing_idx.is_cuda):
-            raise ValueError(f"routing_idx: expected a contiguous int32 CUDA tensor {rshape}")
+            self._check_tensor(name, t, want, shape, q.device)
+        if routing_idx is None or routing_idx is True or routing_idx is False:
+            raise ValueError("routing_idx: a routing tensor is required")
+        self._check_common(q, lepe_w, lepe_b, out, routing_idx)
         if out is None:
             out = torch.empty_like(q)
         bra_forward_routed(self.handle, q, k, v, lepe_w, lepe_b, routing_idx, out, stream)
@@ -282,14 +320,14 @@ class BRA:
         import torch
         c = self.cfg
         shape = (c.batch, c.height, c.width, c.channels)
-        if x.dtype != torch.bfloat16 or tuple(x.shape) != shape or not x.is_contiguous() or \
-                not x.is_cuda:
-            raise ValueError(f"x: expected a contiguous bfloat16 CUDA tensor {shape}")
+        self._check_tensor("x", x, torch.bfloat16, shape, x.device)
         for name, t, ws in (("w_qkv", w_qkv, (3 * c.channels, c.channels)),
                             ("w_o", w_o, (c.channels, c.channels))):
-            if t.dtype != torch.bfloat16 or tuple(t.shape) != ws or not t.is_contiguous() or \
-                    not t.is_cuda:
-                raise ValueError(f"{name}: expected a contiguous bfloat16 CUDA tensor {ws}")
+            self._check_tensor(name, t, torch.bfloat16, ws, x.device)
+        for name, t, n in (("b_qkv", b_qkv, 3 * c.channels), ("b_o", b_o, c.channels)):
+            if t is not None:
+                self._check_tensor(name, t, torch.float32, (n,), x.device)
+        self._check_common(x, lepe_w, lepe_b, out, routing_idx)
         if out is None:
             out = torch.empty_like(x)
         idx = None

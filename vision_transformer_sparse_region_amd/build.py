@@ -31,11 +31,13 @@ FLAGS = [
 ]
 
 
-def build_library(out: str = LIB_PATH, extra_flags=(), verbose: bool = False) -> str:
+def build_library(out: str = LIB_PATH, extra_flags=(), verbose: bool = False,
+                  link_flags=()) -> str:
     """Compile every source and link `out`; raises CalledProcessError on failure."""
     objs = []
+    tag = os.path.splitext(os.path.basename(out))[0]
     for src in SOURCES:
-        obj = os.path.join(CSRC, os.path.basename(src) + ".o")
+        obj = os.path.join(CSRC, f"{os.path.basename(src)}.{tag}.o")
         lang = ["-x", "hip"] if src.endswith(".hip") else []
         cmd = [HIPCC, *FLAGS, *extra_flags, *lang, "-c", src, "-o", obj]
         if verbose:
@@ -43,7 +45,7 @@ def build_library(out: str = LIB_PATH, extra_flags=(), verbose: bool = False) ->
         subprocess.run(cmd, check=True, timeout=BUILD_TIMEOUT_S)
         objs.append(obj)
     tmp = out + ".tmp"
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *link_flags, *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), file=sys.stderr)
     subprocess.run(cmd, check=True, timeout=BUILD_TIMEOUT_S)

@@ -17,26 +17,35 @@
 #include "bra_image.h"
 #include "bra_launch.h"
 
-struct bra_handle_s {
-    bra_config_t cfg;
-    bra::Params params;
-    bool bf16;
-    int device;
-    double* means;       // workspace: fp64 region means of Q [B, heads, R, 32], then of
-                         // K [B, heads, 16, R, 2], then K in fp32 (same order); the routing
-                         // [B, heads, R, k] int32; the MFMA LePE operand table; C zero floats
-                         // (the bias when none is given)
-    size_t means_bytes;
+// Device workspace of the forward: the region means (fp64 Q means
+// [B, heads, R, 32], fp64 K means [B, heads, 16, R, 2], the K means again in
+// fp32), the routing [B, rheads, R, k] int32 for calls that pass no
+// routing_idx, the MFMA LePE operand table, C zero floats (the bias when none
+// is given), the K/V downsampled by kv_downsample_ratio, and the projected
+// q, k, v (and y) of the projected path.
+struct bra_workspace {
+    double* means;
     int32_t* routing;
     uint2* lepe_table;
     float* zero_bias;
     void* kd;  // downsampled K and V [B, H/r, W/r, C] (KV downsampling), else NULL
     void* vd;
-    void* qs;  // projected q, k, v [B, H, W, C] (handles created with projections), else NULL
+    void* qs;  // projected q, k, v [B, H, W, C] (projections), else NULL
     void* ks;
     void* vs;
     void* ys;  // attention output before the output projection, when that runs as its own
                // kernel (projections on shapes with small regions), else NULL
+    size_t zero_bytes;
+};
+
+struct bra_handle_s {
+    bra_config_t cfg;
+    bra::Params params;
+    bool bf16;
+    int device;
+    void* base;          // the one device allocation holding the workspace
+    size_t bytes;
+    bra_workspace ws;
     // per-kernel timing (events recorded by bra_forward while slots remain)
     std::vector<hipEvent_t> events;  // kEventsPerCall per recorded call
     int timing_capacity;
@@ -50,6 +59,18 @@ constexpr int kEventsPerCall = 4;  // before pool, route, attend; after attend
 std::mutex g_mutex;
 std::set<bra_handle_t> g_live;  // handles between create and destroy
 thread_local std::string g_last_error;
+// Allocation-failure injection (bra_debug_inject_alloc_failure): the next
+// g_fail_host handle allocations and the next g_fail_device workspace
+// allocations of bra_create fail as if out of memory.
+int g_fail_host = 0;
+int g_fail_device = 0;
+
+bool take_injected(int& counter) {
+    std::lock_guard<std::mutex> lock(g_mutex);
+    if (counter <= 0) return false;
+    --counter;
+    return true;
+}
 
 bra_status_t fail(bra_status_t s, const std::string& msg) {
     g_last_error = msg;
@@ -80,11 +101,112 @@ void release_events(bra_handle_t h) {
     h->timing_used = 0;
 }
 
+// Checks cfg; on success fills p and bf16 (the planned kernel geometry).
+bra_status_t validate_config(const bra_config_t* cfg, const char* what, bra::Params& p,
+                             bool& bf16) {
+    const std::string w(what);
+    if (!cfg) return fail(BRA_ERR_NULL, w + ": cfg is required");
+    const bra_config_t c = *cfg;
+    if (c.batch <= 0 || c.height <= 0 || c.width <= 0 || c.channels <= 0 || c.num_heads <= 0 ||
+        c.n_win <= 0)
+        return fail(BRA_ERR_SHAPE, w + ": sizes must be positive");
+    if (c.height % c.n_win || c.width % c.n_win)
+        return fail(BRA_ERR_SHAPE, w + ": height and width must be divisible by n_win");
+    if (c.channels % c.num_heads)
+        return fail(BRA_ERR_SHAPE, w + ": channels must be divisible by num_heads");
+    const double elems = static_cast<double>(c.height) * c.width * c.channels;
+    if (elems >= 2147483647.0 || static_cast<double>(c.batch) * c.n_win * c.n_win >= 2147483647.0)
+        return fail(BRA_ERR_SHAPE, w + ": one image or the region grid exceeds int32 indexing");
+    if (c.channels / c.num_heads != bra::kHeadDim)
+        return fail(BRA_ERR_UNSUPPORTED, w + ": head_dim must be 32");
+    if (static_cast<double>(c.height) * c.width >= 8388608.0)  // 2^23: 24-bit token indexing
+        return fail(BRA_ERR_UNSUPPORTED, w + ": height * width must be below 2^23");
+    if (c.dtype != BRA_F32 && c.dtype != BRA_BF16)
+        return fail(BRA_ERR_UNSUPPORTED, w + ": dtype must be BRA_F32 or BRA_BF16");
+    const int R = c.n_win * c.n_win;
+    const int k = (c.topk <= 0 || c.topk > R) ? R : c.topk;
+    const float scale =
+        c.scale > 0.f ? c.scale : 1.0f / std::sqrt(static_cast<float>(bra::kHeadDim));
+    bf16 = c.dtype == BRA_BF16;
+    if (c.shared_routing != 0 && c.shared_routing != 1)
+        return fail(BRA_ERR_SHAPE, w + ": shared_routing must be 0 or 1");
+    if (c.projections != 0 && c.projections != 1)
+        return fail(BRA_ERR_SHAPE, w + ": projections must be 0 or 1");
+    if (c.projections && !bf16)
+        return fail(BRA_ERR_UNSUPPORTED, w + ": projections need dtype BRA_BF16");
+    if (c.projections && c.channels > 512)
+        return fail(BRA_ERR_UNSUPPORTED, w + ": projections need channels <= 512");
+    const int kv_ratio = c.kv_downsample_ratio <= 1 ? 1 : c.kv_downsample_ratio;
+    if (c.projections && (c.shared_routing == 1 || kv_ratio > 1))
+        return fail(BRA_ERR_UNSUPPORTED,
+                    w + ": projections combine with neither shared_routing nor KV downsampling");
+    if ((c.height / c.n_win) % kv_ratio || (c.width / c.n_win) % kv_ratio)
+        return fail(BRA_ERR_SHAPE,
+                    w + ": kv_downsample_ratio must divide the window height and width");
+    if (!bra::plan(p, c.batch, c.height, c.width, c.channels, c.num_heads, c.n_win, k, scale,
+                   bf16, c.shared_routing == 1, kv_ratio))
+        return fail(BRA_ERR_UNSUPPORTED,
+                    w + ": a region (with its LePE halo) or the channel count is too large "
+                        "for the on-chip tiles (" + std::to_string(p.lds_bytes) + " bytes of LDS)");
+    return BRA_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t{255}; }
+
+// The workspace of a forward with config c: returns its size in bytes and,
+// when base is given, carves ws out of base.
+size_t workspace_layout(const bra_config_t& c, const bra::Params& p, bool bf16, char* base,
+                        bra_workspace* ws) {
+    const size_t R = static_cast<size_t>(p.R);
+    // fp64 Q and K means, then the K means in fp32
+    const size_t mean_bytes = align256(static_cast<size_t>(c.batch) * c.channels * R *
+                                       (2 * sizeof(double) + sizeof(float)));
+    const size_t route_bytes =
+        align256(static_cast<size_t>(c.batch) * p.rheads * R * p.k * sizeof(int32_t));
+    const size_t table_bytes = align256(static_cast<size_t>(p.table_items) * sizeof(uint2));
+    const size_t zero_bytes = align256(static_cast<size_t>(c.channels) * sizeof(float));
+    // downsampled K and V (KV downsampling only)
+    const size_t kv_bytes =
+        p.kv_ratio > 1
+            ? align256(static_cast<size_t>(c.batch) * p.kH * p.kW * c.channels * (bf16 ? 2 : 4))
+            : 0;
+    // projected q, k, v (projections only)
+    const size_t map_bytes = align256(static_cast<size_t>(c.batch) * c.height * c.width *
+                                      c.channels * (bf16 ? 2 : 4));
+    const bool proj_after = c.projections && !bra::out_proj_in_attend(p.t, c.channels);
+    const size_t proj_bytes = c.projections ? (proj_after ? 4 : 3) * map_bytes : 0;
+    const size_t total =
+        mean_bytes + route_bytes + table_bytes + zero_bytes + 2 * kv_bytes + proj_bytes;
+    if (base && ws) {
+        char* at = base;
+        ws->means = reinterpret_cast<double*>(at);
+        at += mean_bytes;
+        ws->routing = reinterpret_cast<int32_t*>(at);
+        at += route_bytes;
+        ws->lepe_table = reinterpret_cast<uint2*>(at);
+        at += table_bytes;
+        ws->zero_bias = reinterpret_cast<float*>(at);
+        ws->zero_bytes = zero_bytes;
+        at += zero_bytes;
+        ws->kd = kv_bytes ? at : nullptr;
+        ws->vd = kv_bytes ? at + kv_bytes : nullptr;
+        at += 2 * kv_bytes;
+        ws->qs = ws->ks = ws->vs = ws->ys = nullptr;
+        if (proj_bytes) {
+            ws->qs = at;
+            ws->ks = at + map_bytes;
+            ws->vs = at + 2 * map_bytes;
+            if (proj_after) ws->ys = at + 3 * map_bytes;
+        }
+    }
+    return total;
+}
+
 }  // namespace
 
 extern "C" {
 
-const char* bra_status_string(bra_status_t s) {
+const char* bra_status_string(int32_t s) {
     switch (s) {
         case BRA_OK: return "ok";
         case BRA_ERR_NULL: return "a required pointer is NULL";
@@ -105,111 +227,47 @@ const char* bra_last_error(void) { return g_last_error.c_str(); }
 bra_status_t bra_create(const bra_config_t* cfg, bra_handle_t* out) {
     if (!cfg || !out) return fail(BRA_ERR_NULL, "bra_create: cfg and out are required");
     *out = nullptr;
-    const bra_config_t c = *cfg;
-    if (c.batch <= 0 || c.height <= 0 || c.width <= 0 || c.channels <= 0 || c.num_heads <= 0 ||
-        c.n_win <= 0)
-        return fail(BRA_ERR_SHAPE, "bra_create: sizes must be positive");
-    if (c.height % c.n_win || c.width % c.n_win)
-        return fail(BRA_ERR_SHAPE, "bra_create: height and width must be divisible by n_win");
-    if (c.channels % c.num_heads)
-        return fail(BRA_ERR_SHAPE, "bra_create: channels must be divisible by num_heads");
-    const double elems = static_cast<double>(c.height) * c.width * c.channels;
-    if (elems >= 2147483647.0 || static_cast<double>(c.batch) * c.n_win * c.n_win >= 2147483647.0)
-        return fail(BRA_ERR_SHAPE, "bra_create: one image or the region grid exceeds int32 indexing");
-    if (c.channels / c.num_heads != bra::kHeadDim)
-        return fail(BRA_ERR_UNSUPPORTED, "bra_create: head_dim must be 32");
-    if (static_cast<double>(c.height) * c.width >= 8388608.0)  // 2^23: 24-bit token indexing
-        return fail(BRA_ERR_UNSUPPORTED, "bra_create: height * width must be below 2^23");
-    if (c.dtype != BRA_F32 && c.dtype != BRA_BF16)
-        return fail(BRA_ERR_UNSUPPORTED, "bra_create: dtype must be BRA_F32 or BRA_BF16");
-    const int R = c.n_win * c.n_win;
-    const int k = (c.topk <= 0 || c.topk > R) ? R : c.topk;
-    const float scale = c.scale > 0.f ? c.scale : 1.0f / std::sqrt(static_cast<float>(bra::kHeadDim));
-    const bool bf16 = c.dtype == BRA_BF16;
     bra::Params p;
-    if (c.shared_routing != 0 && c.shared_routing != 1)
-        return fail(BRA_ERR_SHAPE, "bra_create: shared_routing must be 0 or 1");
-    if (c.projections != 0 && c.projections != 1)
-        return fail(BRA_ERR_SHAPE, "bra_create: projections must be 0 or 1");
-    if (c.projections && !bf16)
-        return fail(BRA_ERR_UNSUPPORTED, "bra_create: projections need dtype BRA_BF16");
-    if (c.projections && c.channels > 512)
-        return fail(BRA_ERR_UNSUPPORTED, "bra_create: projections need channels <= 512");
-    const int kv_ratio = c.kv_downsample_ratio <= 1 ? 1 : c.kv_downsample_ratio;
-    if (c.projections && (c.shared_routing == 1 || kv_ratio > 1))
-        return fail(BRA_ERR_UNSUPPORTED,
-                    "bra_create: projections combine with neither shared_routing nor KV downsampling");
-    if ((c.height / c.n_win) % kv_ratio || (c.width / c.n_win) % kv_ratio)
-        return fail(BRA_ERR_SHAPE,
-                    "bra_create: kv_downsample_ratio must divide the window height and width");
-    if (!bra::plan(p, c.batch, c.height, c.width, c.channels, c.num_heads, c.n_win, k, scale,
-                   bf16, c.shared_routing == 1, kv_ratio))
-        return fail(BRA_ERR_UNSUPPORTED,
-                    "bra_create: a region (with its LePE halo) or the channel count is too large "
-                    "for the on-chip tiles (" + std::to_string(p.lds_bytes) + " bytes of LDS)");
-
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return fail_hip(e, "bra_create: hipGetDevice");
-    if (bra::image_applies(p, bf16)) {
-        e = bra::prepare_image(p);
-        if (e != hipSuccess) return fail_hip(e, "bra_create: image kernel LDS limit");
-    }
-    bra_handle_t h = new (std::nothrow) bra_handle_s();
+    bool bf16 = false;
+    bra_status_t st = validate_config(cfg, "bra_create", p, bf16);
+    if (st != BRA_OK) return st;
+    bra_handle_t h = take_injected(g_fail_host) ? nullptr : new (std::nothrow) bra_handle_s();
     if (!h) return fail(BRA_ERR_NOMEM, "bra_create: host allocation failed");
-    h->cfg = c;
+    h->cfg = *cfg;
     h->params = p;
     h->bf16 = bf16;
-    h->device = dev;
-    // fp64 Q and K means, then the K means in fp32
-    const size_t mean_bytes = static_cast<size_t>(c.batch) * c.channels * R *
-                              (2 * sizeof(double) + sizeof(float));
-    const size_t route_bytes =
-        ((static_cast<size_t>(c.batch) * p.rheads * R * k * sizeof(int32_t)) + 15) & ~size_t{15};
-    const size_t table_bytes = static_cast<size_t>(p.table_items) * sizeof(uint2);
-    const size_t zero_bytes = ((static_cast<size_t>(c.channels) * sizeof(float)) + 15) &
-                              ~size_t{15};
-    // downsampled K and V (KV downsampling only)
-    const size_t kv_bytes = p.kv_ratio > 1 ? static_cast<size_t>(c.batch) * p.kH * p.kW *
-                                                 c.channels * (bf16 ? 2 : 4)
-                                           : 0;
-    // projected q, k, v (projections only)
-    const size_t map_bytes = static_cast<size_t>(c.batch) * c.height * c.width * c.channels *
-                             (bf16 ? 2 : 4);
-    const bool proj_after = c.projections && !bra::out_proj_in_attend(p.t, c.channels);
-    const size_t proj_bytes = c.projections ? (proj_after ? 4 : 3) * map_bytes : 0;
-    h->means_bytes = mean_bytes + route_bytes + table_bytes + zero_bytes + 2 * kv_bytes +
-                     proj_bytes;
-    h->means = nullptr;
-    h->routing = nullptr;
-    h->lepe_table = nullptr;
-    h->zero_bias = nullptr;
-    h->kd = nullptr;
-    h->vd = nullptr;
-    h->qs = h->ks = h->vs = h->ys = nullptr;
     h->timing_capacity = 0;
     h->timing_used = 0;
-    e = hipMalloc(reinterpret_cast<void**>(&h->means), h->means_bytes);
+    h->bytes = workspace_layout(*cfg, p, bf16, nullptr, nullptr);
+    h->base = nullptr;
+    if (take_injected(g_fail_device)) {
+        delete h;
+        return fail(BRA_ERR_NOMEM, "bra_create: hipMalloc of the workspace: out of memory "
+                                   "(injected)");
+    }
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) {
+        delete h;
+        return fail_hip(e, "bra_create: hipGetDevice");
+    }
+    h->device = dev;
+    if (bra::image_applies(p, bf16)) {
+        e = bra::prepare_image(p);
+        if (e != hipSuccess) {
+            delete h;
+            return fail_hip(e, "bra_create: image kernel LDS limit");
+        }
+    }
+    e = hipMalloc(&h->base, h->bytes);
     if (e != hipSuccess) {
         delete h;
         return fail_hip(e, "bra_create: hipMalloc of the workspace");
     }
-    h->routing = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(h->means) + mean_bytes);
-    h->lepe_table =
-        reinterpret_cast<uint2*>(reinterpret_cast<char*>(h->means) + mean_bytes + route_bytes);
-    h->zero_bias = reinterpret_cast<float*>(reinterpret_cast<char*>(h->means) + mean_bytes +
-                                            route_bytes + table_bytes);
-    h->kd = kv_bytes ? reinterpret_cast<char*>(h->zero_bias) + zero_bytes : nullptr;
-    h->vd = kv_bytes ? static_cast<char*>(h->kd) + kv_bytes : nullptr;
-    if (proj_bytes) {
-        h->qs = reinterpret_cast<char*>(h->zero_bias) + zero_bytes + 2 * kv_bytes;
-        h->ks = static_cast<char*>(h->qs) + map_bytes;
-        h->vs = static_cast<char*>(h->ks) + map_bytes;
-        if (proj_after) h->ys = static_cast<char*>(h->vs) + map_bytes;
-    }
-    e = hipMemset(h->zero_bias, 0, zero_bytes);
+    workspace_layout(*cfg, p, bf16, static_cast<char*>(h->base), &h->ws);
+    e = hipMemset(h->ws.zero_bias, 0, h->ws.zero_bytes);
     if (e != hipSuccess) {
-        (void)hipFree(h->means);
+        (void)hipFree(h->base);
         delete h;
         return fail_hip(e, "bra_create: hipMemset of the zero bias");
     }
@@ -228,7 +286,7 @@ bra_status_t bra_destroy(bra_handle_t h) {
         if (!g_live.erase(h)) return fail(BRA_ERR_BAD_HANDLE, "bra_destroy: not a live handle");
     }
     release_events(h);
-    hipError_t e = hipFree(h->means);
+    hipError_t e = hipFree(h->base);
     delete h;
     if (e != hipSuccess) return fail_hip(e, "bra_destroy: hipFree");
     return BRA_OK;
@@ -239,24 +297,37 @@ int32_t bra_topk_effective(bra_handle_t h) {
     return h->params.k;
 }
 
-// The argument checks shared by both forward entry points (`what` names the
-// caller in messages).
+// The pointer checks of the forward entry points (`what` names the caller in
+// messages); `bytes` is the size of one [B,H,W,C] map.
+static bra_status_t check_pointers(const char* what, size_t bytes, const void* q, const void* k,
+                                   const void* v, const float* lepe_w, const float* lepe_b,
+                                   const void* out, const int32_t* routing_idx) {
+    const std::string w(what);
+    if (!q || !k || !v || !out) return fail(BRA_ERR_NULL, w + ": q, k, v and out are required");
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16))
+        return fail(BRA_ERR_ALIGN, w + ": q, k, v and out must be 16-byte aligned");
+    if (!aligned(lepe_w, 4) || !aligned(lepe_b, 4) || !aligned(routing_idx, 4))
+        return fail(BRA_ERR_ALIGN, w + ": lepe_w, lepe_b and routing_idx must be 4-byte aligned");
+    if (overlaps(out, q, bytes) || overlaps(out, k, bytes) || overlaps(out, v, bytes))
+        return fail(BRA_ERR_ALIAS, w + ": out must not overlap q, k or v");
+    return BRA_OK;
+}
+
+static size_t map_bytes(const bra_config_t& c) {
+    return static_cast<size_t>(c.batch) * c.height * c.width * c.channels *
+           (c.dtype == BRA_BF16 ? 2 : 4);
+}
+
+// The argument checks of the handle entry points.
 static bra_status_t check_forward_args(bra_handle_t h, const char* what, const void* q,
                                        const void* k, const void* v, const float* lepe_w,
                                        const float* lepe_b, const void* out,
                                        const int32_t* routing_idx) {
     const std::string w(what);
     if (!is_live(h)) return fail(BRA_ERR_BAD_HANDLE, w + ": not a live handle");
-    if (!q || !k || !v || !out) return fail(BRA_ERR_NULL, w + ": q, k, v and out are required");
-    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16))
-        return fail(BRA_ERR_ALIGN, w + ": q, k, v and out must be 16-byte aligned");
-    if (!aligned(lepe_w, 4) || !aligned(lepe_b, 4) || !aligned(routing_idx, 4))
-        return fail(BRA_ERR_ALIGN, w + ": lepe_w, lepe_b and routing_idx must be 4-byte aligned");
-    const bra_config_t& c = h->cfg;
-    const size_t bytes = static_cast<size_t>(c.batch) * c.height * c.width * c.channels *
-                         (h->bf16 ? 2 : 4);
-    if (overlaps(out, q, bytes) || overlaps(out, k, bytes) || overlaps(out, v, bytes))
-        return fail(BRA_ERR_ALIAS, w + ": out must not overlap q, k or v");
+    bra_status_t st =
+        check_pointers(what, map_bytes(h->cfg), q, k, v, lepe_w, lepe_b, out, routing_idx);
+    if (st != BRA_OK) return st;
     int dev = -1;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return fail_hip(e, (w + ": hipGetDevice").c_str());
@@ -264,80 +335,90 @@ static bra_status_t check_forward_args(bra_handle_t h, const char* what, const v
     return BRA_OK;
 }
 
-// The forward steps on stream s.  With x (projections), the qkv projection
-// writes the handle's q, k, v (and the region means), and the attention
-// kernel applies the output projection w_o, b_o; otherwise the pool kernel
-// reads the caller's q and k.
-static bra_status_t enqueue_forward(bra_handle_t h, const char* what, const void* x,
+// The forward steps on stream s, with the workspace ws.  With x
+// (projections), the qkv projection writes the workspace's q, k, v (and the
+// region means), and the attention kernel applies the output projection
+// w_o, b_o; otherwise the pool kernel reads the caller's q and k.  ev: NULL,
+// or kEventsPerCall events to record around the steps.
+static bra_status_t enqueue_forward(const bra::Params& P, bool bf16, const bra_workspace& ws,
+                                    hipEvent_t* ev, const char* what, const void* x,
                                     const void* w_qkv, const float* b_qkv, const void* q,
                                     const void* k, const void* v, const float* lepe_w,
                                     const float* lepe_b, const void* w_o, const float* b_o,
                                     void* out, int32_t* routing_idx, hipStream_t s) {
     const std::string wh(what);
     hipError_t e;
-    const bool timed = h->timing_used < h->timing_capacity;
-    hipEvent_t* ev = timed ? &h->events[kEventsPerCall * h->timing_used] : nullptr;
-    if (timed && (e = hipEventRecord(ev[0], s)) != hipSuccess)
+    if (ev && (e = hipEventRecord(ev[0], s)) != hipSuccess)
         return fail_hip(e, (wh + ": hipEventRecord").c_str());
     // the routing goes to the caller's buffer when one is given
-    int32_t* routing = routing_idx ? routing_idx : h->routing;
-    const bra::Params& P = h->params;
+    int32_t* routing = routing_idx ? routing_idx : ws.routing;
     // maps whose head-group K and V fit LDS: the whole forward in one kernel
-    const bool image = bra::image_applies(P, h->bf16);
+    const bool image = bra::image_applies(P, bf16);
     // small region grids with many heads: means and routing in one kernel
     const bool pool_route =
-        !x && !image && bra::route_in_pool(h->bf16, P.shared != 0, P.R, P.heads, P.t);
+        !x && !image && bra::route_in_pool(bf16, P.shared != 0, P.R, P.heads, P.t);
     if (x) {
-        e = bra::launch_proj_qkv(h->params, x, w_qkv, b_qkv, h->qs, h->ks, h->vs, h->means,
-                                 lepe_w, h->lepe_table, s);
+        e = bra::launch_proj_qkv(P, x, w_qkv, b_qkv, ws.qs, ws.ks, ws.vs, ws.means, lepe_w,
+                                 ws.lepe_table, s);
         if (e != hipSuccess) return fail_hip(e, (wh + ": qkv projection launch").c_str());
-        q = h->qs;
-        k = h->ks;
-        v = h->vs;
+        q = ws.qs;
+        k = ws.ks;
+        v = ws.vs;
     } else if (pool_route) {
-        e = bra::launch_pool_route(h->params, q, k, lepe_w, h->lepe_table, routing, s);
+        e = bra::launch_pool_route(P, q, k, lepe_w, ws.lepe_table, routing, s);
         if (e != hipSuccess) return fail_hip(e, (wh + ": region-pool and routing launch").c_str());
     } else if (!image) {
-        e = bra::launch_pool_qk(h->params, h->bf16, q, k, lepe_w, h->means, h->lepe_table, s);
+        e = bra::launch_pool_qk(P, bf16, q, k, lepe_w, ws.means, ws.lepe_table, s);
         if (e != hipSuccess) return fail_hip(e, (wh + ": region-pool launch").c_str());
     }
-    if (h->kd) {
-        e = bra::launch_kv_pool(h->params, h->bf16, k, v, h->kd, h->vd, s);
+    if (ws.kd) {
+        e = bra::launch_kv_pool(P, bf16, k, v, ws.kd, ws.vd, s);
         if (e != hipSuccess) return fail_hip(e, (wh + ": K/V downsampling launch").c_str());
     }
-    if (timed && (e = hipEventRecord(ev[1], s)) != hipSuccess)
+    if (ev && (e = hipEventRecord(ev[1], s)) != hipSuccess)
         return fail_hip(e, (wh + ": hipEventRecord").c_str());
     // small region grids are routed inside the attention kernel
-    if (!image && !bra::route_in_attend(h->params) && !pool_route) {
-        e = bra::launch_route(h->params, h->bf16, h->means, routing, s);
+    if (!image && !bra::route_in_attend(P) && !pool_route) {
+        e = bra::launch_route(P, bf16, ws.means, routing, s);
         if (e != hipSuccess) return fail_hip(e, (wh + ": routing launch").c_str());
     }
-    if (timed && (e = hipEventRecord(ev[2], s)) != hipSuccess)
+    if (ev && (e = hipEventRecord(ev[2], s)) != hipSuccess)
         return fail_hip(e, (wh + ": hipEventRecord").c_str());
     // the output projection: in the attention kernel's epilogue, or over y
-    // in a kernel of its own (h->ys is set for the shapes that take that)
-    const bool proj_after = w_o && h->ys;
+    // in a kernel of its own (ws.ys is set for the shapes that take that)
+    const bool proj_after = w_o && ws.ys;
     if (image) {
-        e = bra::launch_image(h->params, q, k, v, lepe_w, lepe_b, routing, false,
-                              proj_after ? h->ys : out, s);
+        e = bra::launch_image(P, q, k, v, lepe_w, lepe_b, routing, false,
+                              proj_after ? ws.ys : out, s);
         if (e != hipSuccess) return fail_hip(e, (wh + ": image kernel launch").c_str());
     } else {
-        e = bra::launch_attend(h->params, h->bf16, q, v, h->kd ? h->kd : k, h->vd ? h->vd : v,
-                           h->means, routing, !bra::route_in_attend(h->params), lepe_w, lepe_b,
-                           h->lepe_table, h->zero_bias, proj_after ? nullptr : w_o, b_o,
-                           proj_after ? h->ys : out, s);
+        e = bra::launch_attend(P, bf16, q, v, ws.kd ? ws.kd : k, ws.vd ? ws.vd : v, ws.means,
+                               routing, !bra::route_in_attend(P), lepe_w, lepe_b, ws.lepe_table,
+                               ws.zero_bias, proj_after ? nullptr : w_o, b_o,
+                               proj_after ? ws.ys : out, s);
         if (e != hipSuccess) return fail_hip(e, (wh + ": attention launch").c_str());
     }
     if (proj_after) {
-        e = bra::launch_proj_out(h->params, h->ys, w_o, b_o, out, s);
+        e = bra::launch_proj_out(P, ws.ys, w_o, b_o, out, s);
         if (e != hipSuccess) return fail_hip(e, (wh + ": output projection launch").c_str());
     }
-    if (timed) {
-        if ((e = hipEventRecord(ev[3], s)) != hipSuccess)
-            return fail_hip(e, (wh + ": hipEventRecord").c_str());
-        ++h->timing_used;
-    }
+    if (ev && (e = hipEventRecord(ev[3], s)) != hipSuccess)
+        return fail_hip(e, (wh + ": hipEventRecord").c_str());
     return BRA_OK;
+}
+
+// enqueue_forward with the handle's workspace and timing slots.
+static bra_status_t enqueue_handle(bra_handle_t h, const char* what, const void* x,
+                                   const void* w_qkv, const float* b_qkv, const void* q,
+                                   const void* k, const void* v, const float* lepe_w,
+                                   const float* lepe_b, const void* w_o, const float* b_o,
+                                   void* out, int32_t* routing_idx, hipStream_t s) {
+    const bool timed = h->timing_used < h->timing_capacity;
+    hipEvent_t* ev = timed ? &h->events[kEventsPerCall * h->timing_used] : nullptr;
+    bra_status_t st = enqueue_forward(h->params, h->bf16, h->ws, ev, what, x, w_qkv, b_qkv, q,
+                                      k, v, lepe_w, lepe_b, w_o, b_o, out, routing_idx, s);
+    if (st == BRA_OK && timed) ++h->timing_used;
+    return st;
 }
 
 bra_status_t bra_forward(bra_handle_t h, const void* q, const void* k, const void* v,
@@ -346,8 +427,8 @@ bra_status_t bra_forward(bra_handle_t h, const void* q, const void* k, const voi
     bra_status_t st = check_forward_args(h, "bra_forward", q, k, v, lepe_w, lepe_b, out,
                                          routing_idx);
     if (st != BRA_OK) return st;
-    return enqueue_forward(h, "bra_forward", nullptr, nullptr, nullptr, q, k, v, lepe_w, lepe_b,
-                           nullptr, nullptr, out, routing_idx, static_cast<hipStream_t>(stream));
+    return enqueue_handle(h, "bra_forward", nullptr, nullptr, nullptr, q, k, v, lepe_w, lepe_b,
+                          nullptr, nullptr, out, routing_idx, static_cast<hipStream_t>(stream));
 }
 
 bra_status_t bra_forward_proj(bra_handle_t h, const void* x, const void* w_qkv,
@@ -357,16 +438,16 @@ bra_status_t bra_forward_proj(bra_handle_t h, const void* x, const void* w_qkv,
     bra_status_t st = check_forward_args(h, "bra_forward_proj", x, x, x, lepe_w, lepe_b, out,
                                          routing_idx);
     if (st != BRA_OK) return st;
-    if (!h->qs)
+    if (!h->ws.qs)
         return fail(BRA_ERR_UNSUPPORTED,
                     "bra_forward_proj: the handle was created without projections");
     if (!w_qkv || !w_o) return fail(BRA_ERR_NULL, "bra_forward_proj: w_qkv and w_o are required");
     if (!aligned(w_qkv, 16) || !aligned(w_o, 16) || !aligned(b_qkv, 4) || !aligned(b_o, 4))
         return fail(BRA_ERR_ALIGN,
                     "bra_forward_proj: w_qkv and w_o must be 16-byte aligned, the biases 4-byte");
-    return enqueue_forward(h, "bra_forward_proj", x, w_qkv, b_qkv, nullptr, nullptr, nullptr,
-                           lepe_w, lepe_b, w_o, b_o, out, routing_idx,
-                           static_cast<hipStream_t>(stream));
+    return enqueue_handle(h, "bra_forward_proj", x, w_qkv, b_qkv, nullptr, nullptr, nullptr,
+                          lepe_w, lepe_b, w_o, b_o, out, routing_idx,
+                          static_cast<hipStream_t>(stream));
 }
 
 bra_status_t bra_forward_routed(bra_handle_t h, const void* q, const void* k, const void* v,
@@ -387,17 +468,18 @@ bra_status_t bra_forward_routed(bra_handle_t h, const void* q, const void* k, co
     }
     // the MFMA LePE operand table is the region-pool kernel's side product:
     // build it alone (no means) when this shape uses it
+    const bra_workspace& ws = h->ws;
     if (lepe_w && h->params.table_items > 0) {
-        e = bra::launch_lepe_table(h->params, lepe_w, h->lepe_table, s);
+        e = bra::launch_lepe_table(h->params, lepe_w, ws.lepe_table, s);
         if (e != hipSuccess) return fail_hip(e, "bra_forward_routed: LePE table launch");
     }
-    if (h->kd) {
-        e = bra::launch_kv_pool(h->params, h->bf16, k, v, h->kd, h->vd, s);
+    if (ws.kd) {
+        e = bra::launch_kv_pool(h->params, h->bf16, k, v, ws.kd, ws.vd, s);
         if (e != hipSuccess) return fail_hip(e, "bra_forward_routed: K/V downsampling launch");
     }
-    e = bra::launch_attend(h->params, h->bf16, q, v, h->kd ? h->kd : k, h->vd ? h->vd : v,
-                           h->means, const_cast<int32_t*>(routing_idx), true, lepe_w, lepe_b,
-                           h->lepe_table, h->zero_bias, nullptr, nullptr, out, s);
+    e = bra::launch_attend(h->params, h->bf16, q, v, ws.kd ? ws.kd : k, ws.vd ? ws.vd : v,
+                           ws.means, const_cast<int32_t*>(routing_idx), true, lepe_w, lepe_b,
+                           ws.lepe_table, ws.zero_bias, nullptr, nullptr, out, s);
     if (e != hipSuccess) return fail_hip(e, "bra_forward_routed: attention launch");
     return BRA_OK;
 }
@@ -438,6 +520,23 @@ bra_status_t bra_timing_read(bra_handle_t h, float* ms, int32_t* count) {
     *count = h->timing_used;
     h->timing_used = 0;
     return BRA_OK;
+}
+
+bra_status_t bra_debug_inject_alloc_failure(int32_t which, int32_t count) {
+    if (count < 0) return fail(BRA_ERR_SHAPE, "bra_debug_inject_alloc_failure: count must be >= 0");
+    std::lock_guard<std::mutex> lock(g_mutex);
+    if (which == BRA_ALLOC_HOST)
+        g_fail_host = count;
+    else if (which == BRA_ALLOC_DEVICE)
+        g_fail_device = count;
+    else
+        return fail(BRA_ERR_SHAPE, "bra_debug_inject_alloc_failure: unknown allocation kind");
+    return BRA_OK;
+}
+
+int32_t bra_debug_live_handles(void) {
+    std::lock_guard<std::mutex> lock(g_mutex);
+    return static_cast<int32_t>(g_live.size());
 }
 
 }  // extern "C"
