@@ -174,6 +174,22 @@ bra_status_t bra_forward_proj(bra_handle_t h, const void* x, const void* w_qkv,
                               const void* w_o, const float* b_o, void* out,
                               int32_t* routing_idx, void* stream);
 
+/* bra_forward without a handle and without allocating, for callers that
+ * cannot allocate device memory: code under HIP graph capture, serving loops,
+ * harnesses that forbid hipMalloc.  Same computation, kernels, arguments and
+ * checks as bra_forward on a handle created with *cfg; the workspace (the
+ * sizes bra_create lists) comes from a device array of 16 MiB that the
+ * library holds on each device it runs on until the process ends.  A
+ * configuration whose workspace exceeds 16 MiB gives BRA_ERR_UNSUPPORTED,
+ * as do projections (bra_forward_proj only).  Every call on a device uses
+ * that device's one array and leaves it in use until its kernels finish:
+ * calls that overlap on one device (another stream, another thread) race,
+ * so serialise them.  Calls no hipMalloc, hipFree or memset; enqueued on
+ * `stream` (the current device's) without synchronising. */
+bra_status_t bra_forward_noalloc(const bra_config_t* cfg, const void* q, const void* k,
+                                const void* v, const float* lepe_w, const float* lepe_b,
+                                void* out, int32_t* routing_idx, void* stream);
+
 /* Release the workspace and the handle.  NULL is a no-op (BRA_OK); a handle
  * that is not live gives BRA_ERR_BAD_HANDLE. */
 bra_status_t bra_destroy(bra_handle_t h);

@@ -123,3 +123,20 @@ def test_alloc_failure_hook_arguments(lib):
     assert bra.bra_debug_inject_alloc_failure(bra.BRA_ALLOC_HOST, -1) == bra.BRA_ERR_SHAPE
     assert bra.bra_debug_inject_alloc_failure(7, 1) == bra.BRA_ERR_SHAPE
     assert bra.bra_debug_inject_alloc_failure(bra.BRA_ALLOC_DEVICE, 0) == bra.BRA_OK
+
+
+def test_noalloc_rejects_before_touching_the_gpu(lib):
+    """bra_forward_noalloc checks its config and pointers, and the workspace
+    size against its fixed scratch array, before any HIP call."""
+    assert bra.bra_forward_noalloc_status(None, 16, 16, 16, None, None, 32) == bra.BRA_ERR_NULL
+    assert bra.bra_forward_noalloc_status(_cfg(batch=0), 16, 16, 16, None, None, 32) == \
+        bra.BRA_ERR_SHAPE
+    assert bra.bra_forward_noalloc_status(_cfg(projections=1), 16, 16, 16, None, None, 32) == \
+        bra.BRA_ERR_UNSUPPORTED
+    assert bra.bra_forward_noalloc_status(_cfg(), 16, 16, 16, None, None, 16) == \
+        bra.BRA_ERR_ALIAS
+    # 512 images of 56 x 56 with per-head routing: 16 MB of region means alone
+    big = _cfg(batch=512, height=56, width=56, channels=64, num_heads=2, n_win=7, topk=1)
+    assert bra.bra_forward_noalloc_status(big, 16, 1 << 40, 2 << 40, None, None, 3 << 40) == \
+        bra.BRA_ERR_UNSUPPORTED
+    assert "scratch" in bra.bra_last_error()

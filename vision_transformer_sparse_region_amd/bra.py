@@ -82,11 +82,13 @@ def load_library(path: str = LIB_PATH):
     lib.bra_last_error.restype = ctypes.c_char_p
     lib.bra_timing_enable.argtypes = [vp, i32]
     lib.bra_timing_read.argtypes = [vp, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(i32)]
+    lib.bra_forward_noalloc.argtypes = [ctypes.POINTER(BraConfig), vp, vp, vp, vp, vp, vp, vp,
+                                        vp]
     lib.bra_debug_inject_alloc_failure.argtypes = [i32, i32]
     lib.bra_debug_live_handles.argtypes = []
     lib.bra_debug_live_handles.restype = i32
     for name in ("bra_create", "bra_forward", "bra_forward_routed", "bra_forward_proj",
-                 "bra_destroy", "bra_debug_inject_alloc_failure",
+                 "bra_forward_noalloc", "bra_destroy", "bra_debug_inject_alloc_failure",
                  "bra_timing_enable", "bra_timing_read"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
@@ -192,6 +194,23 @@ def bra_forward_proj_status(h, x, w_qkv, b_qkv, lepe_w, lepe_b, w_o, b_o, out,
     return load_library().bra_forward_proj(h, _ptr(x), _ptr(w_qkv), _ptr(b_qkv), _ptr(lepe_w),
                                            _ptr(lepe_b), _ptr(w_o), _ptr(b_o), _ptr(out),
                                            _ptr(routing_idx), stream)
+
+
+def bra_forward_noalloc(cfg: BraConfig, q, k, v, lepe_w, lepe_b, out, routing_idx=None,
+                        stream=None):
+    """Enqueue the forward without a handle, on the library's device scratch array."""
+    st = load_library().bra_forward_noalloc(ctypes.byref(cfg), _ptr(q), _ptr(k), _ptr(v),
+                                            _ptr(lepe_w), _ptr(lepe_b), _ptr(out),
+                                            _ptr(routing_idx), _stream(stream))
+    _check(st, "bra_forward_noalloc")
+
+
+def bra_forward_noalloc_status(cfg, q, k, v, lepe_w, lepe_b, out, routing_idx=None,
+                               stream=0) -> int:
+    """Raw status of bra_forward_noalloc (for tests of the argument checks)."""
+    return load_library().bra_forward_noalloc(ctypes.byref(cfg) if cfg is not None else None,
+                                              _ptr(q), _ptr(k), _ptr(v), _ptr(lepe_w),
+                                              _ptr(lepe_b), _ptr(out), _ptr(routing_idx), stream)
 
 
 def bra_destroy(h) -> None:

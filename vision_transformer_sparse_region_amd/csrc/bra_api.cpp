@@ -158,9 +158,13 @@ size_t align256(size_t x) { return (x + 255) & ~size_t{255}; }
 size_t workspace_layout(const bra_config_t& c, const bra::Params& p, bool bf16, char* base,
                         bra_workspace* ws) {
     const size_t R = static_cast<size_t>(p.R);
-    // fp64 Q and K means, then the K means in fp32
-    const size_t mean_bytes = align256(static_cast<size_t>(c.batch) * c.channels * R *
-                                       (2 * sizeof(double) + sizeof(float)));
+    // fp64 Q and K means, then the K means in fp32 (none where the image
+    // kernel computes them on chip, unless the qkv projection writes them)
+    const bool on_chip = bra::image_applies(p, bf16) && !c.projections;
+    const size_t mean_bytes =
+        on_chip ? 0
+                : align256(static_cast<size_t>(c.batch) * c.channels * R *
+                           (2 * sizeof(double) + sizeof(float)));
     const size_t route_bytes =
         align256(static_cast<size_t>(c.batch) * p.rheads * R * p.k * sizeof(int32_t));
     const size_t table_bytes = align256(static_cast<size_t>(p.table_items) * sizeof(uint2));
@@ -482,6 +486,47 @@ bra_status_t bra_forward_routed(bra_handle_t h, const void* q, const void* k, co
                            ws.lepe_table, ws.zero_bias, nullptr, nullptr, out, s);
     if (e != hipSuccess) return fail_hip(e, "bra_forward_routed: attention launch");
     return BRA_OK;
+}
+
+bra_status_t bra_forward_noalloc(const bra_config_t* cfg, const void* q, const void* k,
+                                const void* v, const float* lepe_w, const float* lepe_b,
+                                void* out, int32_t* routing_idx, void* stream) {
+    const char* what = "bra_forward_noalloc";
+    bra::Params p;
+    bool bf16 = false;
+    bra_status_t st = validate_config(cfg, what, p, bf16);
+    if (st != BRA_OK) return st;
+    if (cfg->projections)
+        return fail(BRA_ERR_UNSUPPORTED,
+                    "bra_forward_noalloc: projections run through bra_forward_proj only");
+    st = check_pointers(what, map_bytes(*cfg), q, k, v, lepe_w, lepe_b, out, routing_idx);
+    if (st != BRA_OK) return st;
+    const size_t need = workspace_layout(*cfg, p, bf16, nullptr, nullptr);
+    if (need > bra::scratch_bytes())
+        return fail(BRA_ERR_UNSUPPORTED,
+                    "bra_forward_noalloc: this configuration needs " + std::to_string(need) +
+                        " bytes of scratch, more than the " +
+                        std::to_string(bra::scratch_bytes()) + " the library holds");
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail_hip(e, "bra_forward_noalloc: hipGetDevice");
+    void* base = nullptr;
+    e = bra::scratch_pointer(dev, &base);
+    if (e != hipSuccess) return fail_hip(e, "bra_forward_noalloc: hipGetSymbolAddress");
+    if (bra::image_applies(p, bf16)) {
+        e = bra::prepare_image(p);
+        if (e != hipSuccess) return fail_hip(e, "bra_forward_noalloc: image kernel LDS limit");
+    }
+    bra_workspace ws;
+    workspace_layout(*cfg, p, bf16, static_cast<char*>(base), &ws);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    // the stand-in bias must read zero, whatever the array held before
+    if (lepe_w && !lepe_b) {
+        e = bra::launch_zero_fill(ws.zero_bias, cfg->channels, s);
+        if (e != hipSuccess) return fail_hip(e, "bra_forward_noalloc: zero fill launch");
+    }
+    return enqueue_forward(p, bf16, ws, nullptr, what, nullptr, nullptr, nullptr, q, k, v,
+                           lepe_w, lepe_b, nullptr, nullptr, out, routing_idx, s);
 }
 
 bra_status_t bra_timing_enable(bra_handle_t h, int32_t n) {

@@ -164,4 +164,11 @@ hipError_t launch_kv_pool(const Params& p, bool bf16, const void* k, const void*
 hipError_t launch_lepe_table(const Params& p, const float* lepe_w, uint2* lepe_table,
                              hipStream_t stream);
 
+// The allocation-free forward's device scratch array (bra_noalloc.hip):
+// its size, its device address on the current device `device`, and a
+// graph-safe clear of n floats.
+size_t scratch_bytes();
+hipError_t scratch_pointer(int device, void** ptr);
+hipError_t launch_zero_fill(float* p, int n, hipStream_t stream);
+
 }  // namespace bra
