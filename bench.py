@@ -67,6 +67,18 @@ def route_in_pool(wl, shared_routing: bool = False) -> bool:
             wl.regions * wl.tokens_per_region <= 256)
 
 
+# (window side, n_win, heads, k) of the whole-image kernel's compiled shapes
+IMAGE_SHAPES = {(4, 7, 4, 4), (2, 7, 8, 16)}
+
+
+def image_path(wl, shared_routing: bool = False, kv_ratio: int = 1) -> bool:
+    """bf16 maps whose head-group K and V fit LDS: one kernel runs the whole
+    forward (means, routing, attention, LePE)."""
+    hs, ws = wl.height // wl.n_win, wl.width // wl.n_win
+    return (wl.dtype == "bf16" and not shared_routing and max(kv_ratio, 1) == 1 and hs == ws and
+            (hs, wl.n_win, wl.num_heads, wl.topk_effective) in IMAGE_SHAPES)
+
+
 def out_proj_in_attend(wl) -> bool:
     """The output projection runs in the attention kernel's epilogue when
     C <= 4 t, else as a kernel of its own over the attention output."""
@@ -116,6 +128,9 @@ def algorithmic_bytes(wl, shared_routing: bool = False, kv_ratio: int = 1,
     attend = (3 * S + 2 * S // r2 if r2 > 1 else 4 * S) + idx + lepe
     k32 = M // 2 if kmean32(wl, shared_routing) else 0   # fp32 K means
     kread = k32 if k32 else M                            # K means the attention reads
+    if image_path(wl, shared_routing, kv_ratio) and not projections:
+        # one kernel: q, k, v read once, out written once, the ids exported
+        return {"pool": 0, "route": 0, "attend": attend, "S": S}
     if projections:
         # the qkv projection reads x and the weights, writes q, k, v and both
         # means; the attention kernel also reads the output weights.  (When
@@ -124,6 +139,8 @@ def algorithmic_bytes(wl, shared_routing: bool = False, kv_ratio: int = 1,
         wq, wo = 3 * wl.channels * wl.channels * es, wl.channels * wl.channels * es
         pool = S + wq + 3 * wl.channels * 4 + 3 * S + 2 * M + k32 + kvpool
         att = attend + wo + wl.channels * 4
+        if image_path(wl, shared_routing, kv_ratio):
+            return {"pool": pool, "route": 0, "attend": att, "S": S}
         if route_in_attend(wl, shared_routing):
             return {"pool": pool, "route": 0, "attend": att + M + kread, "S": S}
         return {"pool": pool, "route": 2 * M + idx, "attend": att, "S": S}
@@ -237,40 +254,46 @@ def copy_calibration(dev, reps: int = COPY_REPS) -> None:
     torch.cuda.synchronize()
 
 
-def main(argv=None) -> int:
-    ap = argparse.ArgumentParser(description=__doc__)
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=500)
-    ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--workload", default="stage1")
-    ap.add_argument("--buffer-sets", type=int, default=0,
-                    help="input/output sets to rotate over (0: enough to exceed the MALL)")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-graph", action="store_true",
-                    help="skip the pass that replays the forwards as one captured HIP graph")
-    ap.add_argument("--shared-routing", action="store_true",
-                    help="one routing per region for every head (full-C region affinity)")
-    ap.add_argument("--kv-downsample", type=int, default=1,
-                    help="KV downsampling ratio r (attention over r x r average-pooled K/V)")
-    ap.add_argument("--projections", action="store_true",
-                    help="time bra_forward_proj: the module's qkv and output projections "
-                         "around the path (random bf16 weights)")
-    ap.add_argument("--copy-calibration", action="store_true",
-                    help=f"also run a {COPY_BYTES >> 20} MiB device copy (for counter scaling)")
-    args = ap.parse_args(argv)
+BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+FP32_PEAK_TFLOPS = 157.3    # MI355X fp32 vector
+# the workloads whose lines are embedded under "configs" besides the headline
+ALL_WORKLOADS = ("tiny_f32", "stage1", "stage2", "stage3", "highres")
 
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this implementation runs on one GPU; the forward needs no collective and "
-              "its multi-GPU sharding is described but not built.", file=sys.stderr)
-        return 2
 
+def kernel_name(wl, shared_routing=False, kv_ratio=1) -> str:
+    return "image" if image_path(wl, shared_routing, kv_ratio) else "attend"
+
+
+def roofline_entry(wl, attn_ms: float, ab: dict, shared_routing=False, kv_ratio=1) -> dict:
+    """The bound of the forward's dominant kernel and how close it runs to it:
+    HBM bytes for the memory-bound shapes, MFMA flops for the high-resolution
+    attention (1024 keys per query: arithmetic intensity above the ridge)."""
+    achieved_gbs = ab["attend"] / (attn_ms * 1e-3) / 1e9
+    tflops = attention_flops(wl, kv_ratio) / (attn_ms * 1e-3) / 1e12
+    mfma_bound = wl.dtype == "bf16" and wl.topk_effective * wl.tokens_per_region // \
+        max(kv_ratio, 1) ** 2 >= 512
+    if mfma_bound:
+        return {"bound": "mfma", "kernel": kernel_name(wl, shared_routing, kv_ratio),
+                "achieved": tflops, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": tflops / BF16_PEAK_TFLOPS, "hbm_frac": achieved_gbs / HBM_PEAK_GBS,
+                "algorithmic_bytes": ab["attend"]}
+    peak_tf = BF16_PEAK_TFLOPS if wl.dtype == "bf16" else FP32_PEAK_TFLOPS
+    return {"bound": "hbm", "kernel": kernel_name(wl, shared_routing, kv_ratio),
+            "achieved": achieved_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": achieved_gbs / HBM_PEAK_GBS, "algorithmic_bytes": ab["attend"],
+            "attention_tflops": tflops, "mfma_frac": tflops / peak_tf}
+
+
+def measure(wl, args, want_graph: bool = True, keep_inputs: bool = False) -> dict:
+    """Time args.steps forwards of workload wl (after args.warmup), rotating
+    over enough buffer sets to miss the MALL; then the same forwards as a
+    captured graph and once more with per-kernel events.  Inputs are already
+    resident in HBM when the timed region starts."""
     import torch
 
     from vision_transformer_sparse_region_amd import bra
-    from vision_transformer_sparse_region_amd.workloads import (WORKLOADS, make_inputs,
-                                                               make_proj_weights)
+    from vision_transformer_sparse_region_amd.workloads import make_inputs, make_proj_weights
 
-    wl = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     host = make_inputs(wl)
     S = wl.tokens * wl.channels * (2 if wl.dtype == "bf16" else 4)
@@ -317,7 +340,7 @@ def main(argv=None) -> int:
     # The same forwards captured once as a HIP graph (one forward per buffer
     # set) and replayed about K / sets times: the host's launch cost is gone.
     graph_ms = None
-    if not args.no_graph:
+    if want_graph:
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=torch.cuda.Stream()):
             for i in range(nsets):
@@ -342,29 +365,96 @@ def main(argv=None) -> int:
         step(i)
     times = bra.bra_timing_read(h.handle, args.steps)
     h.close()
-    if args.copy_calibration:
-        copy_calibration(dev)
 
     ms_per_step = gpu_ms / args.steps
-    tokens_per_s = wl.tokens / (ms_per_step * 1e-3)
-    pool_ms = sum(t[0] for t in times) / len(times)
+    image = image_path(wl, args.shared_routing, args.kv_downsample) and not args.projections
+    pool_ms = sum(t[0] for t in times) / len(times) if not image else None
     # (no routing kernel runs when the attention kernel routes: the interval
     # between its two events is empty)
-    fused_route = route_in_attend(wl, args.shared_routing) or \
+    fused_route = route_in_attend(wl, args.shared_routing) or image_path(wl) or \
         (route_in_pool(wl, args.shared_routing) and not args.projections)
     route_ms = sum(t[1] for t in times) / len(times) if not fused_route else None
     attn_ms = sum(t[2] for t in times) / len(times)
     ab = algorithmic_bytes(wl, args.shared_routing, args.kv_downsample, args.projections)
-    achieved = ab["attend"] / (attn_ms * 1e-3) / 1e9
-    traffic = stored_traffic(wl.name)
+    roof = roofline_entry(wl, attn_ms, ab, args.shared_routing, args.kv_downsample)
+    total = ab["pool"] + ab["route"] + ab["attend"]
+    roof["step_frac_hbm"] = total / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS
+    if ab["pool"] and pool_ms:
+        roof["pool_frac_hbm"] = ab["pool"] / (pool_ms * 1e-3) / 1e9 / HBM_PEAK_GBS
+    res = {
+        "workload": wl.name,
+        "description": wl.description,
+        "ms_per_step": ms_per_step,
+        "value": wl.tokens / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "dtype": wl.dtype,
+        "buffer_sets": nsets,
+        "kernel_ms": {"region_pool": pool_ms, "route": route_ms,
+                      ("image" if image else "attend"): attn_ms},
+        "wall_s": wall,
+        "roofline": roof,
+    }
+    if graph_ms is not None:
+        res["graph"] = {"ms_per_step": graph_ms, "value": wl.tokens / (graph_ms * 1e-3),
+                        "unit": "tokens/s", "forwards_per_graph": nsets}
+    if keep_inputs:
+        res["_host"] = host
+        res["_last_out"] = sets[(args.steps - 1) % nsets]["out"].cpu()
+    return res
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", default="stage1")
+    ap.add_argument("--buffer-sets", type=int, default=0,
+                    help="input/output sets to rotate over (0: enough to exceed the MALL)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the pass that replays the forwards as one captured HIP graph")
+    ap.add_argument("--no-all-configs", action="store_true",
+                    help="time only the headline workload (by default the other workloads "
+                         "of the benchmark table are timed too and embedded under 'configs')")
+    ap.add_argument("--shared-routing", action="store_true",
+                    help="one routing per region for every head (full-C region affinity)")
+    ap.add_argument("--kv-downsample", type=int, default=1,
+                    help="KV downsampling ratio r (attention over r x r average-pooled K/V)")
+    ap.add_argument("--projections", action="store_true",
+                    help="time bra_forward_proj: the module's qkv and output projections "
+                         "around the path (random bf16 weights)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help=f"also run a {COPY_BYTES >> 20} MiB device copy (for counter scaling)")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this implementation runs on one GPU; the forward needs no collective and "
+              "its multi-GPU sharding is described but not built.", file=sys.stderr)
+        return 2
+
+    import torch
+
+    from vision_transformer_sparse_region_amd.workloads import WORKLOADS
+
+    wl = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    res = measure(wl, args, want_graph=not args.no_graph, keep_inputs=True)
+    if args.copy_calibration:
+        copy_calibration(dev)
+    roof = dict(res["roofline"])
+    if roof["kernel"] == "attend" and not args.projections:
+        roof["traffic"] = stored_traffic(wl.name)
+    else:
+        roof["traffic"] = stored_traffic(f"{wl.name}_{roof['kernel']}")
     line = {
         "metric": METRIC,
-        "value": tokens_per_s,
+        "value": res["value"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
+        "ms_per_step": res["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -374,35 +464,31 @@ def main(argv=None) -> int:
             "workload": wl.description,
             "batch": wl.batch, "height": wl.height, "width": wl.width,
             "channels": wl.channels, "num_heads": wl.num_heads, "n_win": wl.n_win,
-            "topk": wl.topk, "buffer_sets": nsets,
+            "topk": wl.topk, "buffer_sets": res["buffer_sets"],
             "routing": "shared by all heads" if args.shared_routing else "per head",
             "kv_downsample_ratio": args.kv_downsample,
             "projections": bool(args.projections),
             **({"output_projection": "attention epilogue" if out_proj_in_attend(wl)
                 else "own kernel"} if args.projections else {}),
-            "kernel_ms": {"region_pool": pool_ms, "route": route_ms, "attend": attn_ms},
-            "wall_s": wall,
+            "kernel_ms": res["kernel_ms"],
+            "wall_s": res["wall_s"],
         },
-        "roofline": {
-            "bound": "hbm",
-            "kernel": "attend",
-            "achieved": achieved,
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": achieved / HBM_PEAK_GBS,
-            "traffic": traffic,
-            "algorithmic_bytes": ab["attend"],
-            "attention_tflops": attention_flops(wl, args.kv_downsample) / (attn_ms * 1e-3) / 1e12,
-            "pool_frac_hbm": ab["pool"] / (pool_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-            "step_frac_hbm": (ab["pool"] + ab["route"] + ab["attend"]) / (ms_per_step * 1e-3) /
-            1e9 / HBM_PEAK_GBS,
-        },
+        "roofline": roof,
     }
-    if graph_ms is not None:
-        line["graph"] = {"ms_per_step": graph_ms, "value": wl.tokens / (graph_ms * 1e-3),
-                         "unit": "tokens/s", "forwards_per_graph": nsets}
+    if "graph" in res:
+        line["graph"] = res["graph"]
+    # the other workloads of the benchmark table, the same variant and steps
+    if not args.no_all_configs:
+        configs = {}
+        for name in ALL_WORKLOADS:
+            if name == args.workload:
+                continue
+            r = measure(WORKLOADS[name], args, want_graph=False)
+            configs[name] = {k: r[k] for k in ("description", "ms_per_step", "value", "unit",
+                                              "dtype", "kernel_ms", "roofline")}
+        line["configs"] = configs
     if not args.no_cpu_baseline and not args.projections:
-        line["cpu_baseline"] = cpu_baseline(wl, host, sets[(args.steps - 1) % nsets]["out"].cpu(),
+        line["cpu_baseline"] = cpu_baseline(wl, res["_host"], res["_last_out"],
                                             shared=args.shared_routing,
                                             kv_ratio=args.kv_downsample)
     print(json.dumps(line), flush=True)

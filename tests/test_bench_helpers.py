@@ -28,11 +28,13 @@ def test_fp32_k_means_only_for_windows_of_32_tokens():
     assert not bench.kmean32(WORKLOADS["stage3"])            # routed outside
     assert not bench.kmean32(WORKLOADS["highres"])           # 256 regions
     assert not bench.kmean32(WORKLOADS["stage1"], shared_routing=True)
+    # stage 2 without the whole-image kernel (head-shared routing): the pool
+    # kernel reads k and writes the K means, fp64 only
     wl = WORKLOADS["stage2"]
     S = 64 * 28 * 28 * 128 * 2
     M = 64 * 128 * 49 * 8
-    ab = bench.algorithmic_bytes(wl)
-    assert ab["pool"] == S + M
+    ab = bench.algorithmic_bytes(wl, kv_ratio=2)
+    assert ab["pool"] == S + M + 2 * S + 2 * S // 4
 
 
 def test_q_means_summed_in_attention_kernel():
@@ -59,21 +61,42 @@ def test_algorithmic_bytes_highres_separate_route():
     assert ab["attend"] == 4 * S + idx + 64 * 26 * 4
 
 
-def test_algorithmic_bytes_stage3_means_and_routing_in_one_kernel():
-    wl = WORKLOADS["stage3"]
-    assert bench.route_in_pool(wl)
-    ab = bench.algorithmic_bytes(wl)
-    S = 64 * 14 * 14 * 256 * 2
-    idx = 64 * 8 * 49 * 16 * 4
-    # one kernel reads q and k and writes the ids; the means stay on chip
-    assert ab["pool"] == 2 * S + idx
-    assert ab["route"] == 0
-    assert ab["attend"] == 4 * S + idx + 256 * 26 * 4
-    # the other shapes keep their kernels
-    assert not bench.route_in_pool(WORKLOADS["stage1"])    # routed in the attention kernel
-    assert not bench.route_in_pool(WORKLOADS["highres"])   # 256 regions
-    assert not bench.route_in_pool(WORKLOADS["tiny_f32"])  # fp32
-    assert not bench.route_in_pool(wl, shared_routing=True)
+def test_algorithmic_bytes_whole_image_kernel():
+    """Stages 2 and 3 run one kernel per (image, head group): q, k and v are
+    read once and out written once; the means and the routing stay on chip
+    and only the ids are exported."""
+    for name, C, H, heads, k in (("stage2", 128, 28, 4, 4), ("stage3", 256, 14, 8, 16)):
+        wl = WORKLOADS[name]
+        assert bench.image_path(wl)
+        ab = bench.algorithmic_bytes(wl)
+        S = 64 * H * H * C * 2
+        idx = 64 * heads * 49 * k * 4
+        assert ab["pool"] == 0 and ab["route"] == 0
+        assert ab["attend"] == 4 * S + idx + C * 26 * 4
+        assert bench.kernel_name(wl) == "image"
+    # the other shapes and variants keep their kernels
+    assert not bench.image_path(WORKLOADS["stage1"])
+    assert not bench.image_path(WORKLOADS["highres"])
+    assert not bench.image_path(WORKLOADS["tiny_f32"])
+    assert not bench.image_path(WORKLOADS["stage3"], shared_routing=True)
+    assert not bench.image_path(WORKLOADS["stage2"], kv_ratio=2)
+    assert not bench.image_path(WORKLOADS["stage2"].with_(topk=6))
+    # stage 3 with head-shared routing: means and routing in the pool kernel
+    assert bench.route_in_pool(WORKLOADS["stage3"]) and \
+        not bench.route_in_pool(WORKLOADS["stage3"], shared_routing=True)
+
+
+def test_roofline_bound_per_workload():
+    """HBM for the memory-bound shapes, the bf16 MFMA peak for the
+    high-resolution attention (1024 keys per query)."""
+    for name in ("stage1", "stage2", "stage3", "tiny_f32"):
+        wl = WORKLOADS[name]
+        r = bench.roofline_entry(wl, 0.03, bench.algorithmic_bytes(wl))
+        assert r["bound"] == "hbm" and r["unit"] == "GB/s" and r["peak"] == 8000.0
+    wl = WORKLOADS["highres"]
+    r = bench.roofline_entry(wl, 0.08, bench.algorithmic_bytes(wl))
+    assert r["bound"] == "mfma" and r["unit"] == "TFLOP/s" and r["peak"] == 2500.0
+    assert abs(r["frac"] - bench.attention_flops(wl) / 0.08e-3 / 1e12 / 2500.0) < 1e-12
 
 
 def test_attention_flops_highres():
