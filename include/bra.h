@@ -30,12 +30,20 @@
  *   5. out = attention + LePE, LePE = depthwise 5x5 convolution of V with
  *      zero padding 2 over the whole map, plus a per-channel bias
  *      [P5 §五 self.lepe and ⑧; P2 §2.2].
- *   Routing is computed in fp64 (region sums are exact for bf16 input), so
- *   routing_idx equals a float64 evaluation of steps 2-3.  (Where a faster
- *   fp32 pass is taken first, an error bound decides whether its order is
- *   the fp64 one; otherwise the fp64 values decide.)  Attention runs on
- *   bf16 MFMA with fp32 accumulation and an fp32 online softmax (bf16 I/O)
- *   or in fp32 VALU arithmetic (fp32 I/O); LePE accumulates in fp32.
+ *   Routing is computed in fp64, so routing_idx equals a float64 evaluation
+ *   of steps 2-3 with the region sums taken in slot order.  fp32 I/O sums in
+ *   that order.  bf16 I/O sums in other orders (trees over lanes), which
+ *   give the same sums because a sum of bf16 values is exact in fp64 while
+ *   the nonzero values of one (region, channel) span at most
+ *   2^(45 - ceil(log2 t)) in magnitude (2^39 for 64-token regions); inputs
+ *   beyond that span may route differently where two affinities differ by
+ *   less than the rounding of those sums.  (Where a faster fp32 pass is
+ *   taken first, an error bound decides whether its order is the fp64 one;
+ *   otherwise the fp64 values decide.)  Attention runs on bf16 MFMA with
+ *   fp32 accumulation and an fp32 online softmax (bf16 I/O) or in fp32 VALU
+ *   arithmetic (fp32 I/O).  LePE accumulates in fp32; for bf16 windows that
+ *   tile by 4 x 4 (the benchmark shapes) it runs on MFMA, which first rounds
+ *   lepe_w once to bf16 (the bias stays fp32).
  *
  * Layouts (device memory, C-contiguous, owned by the caller):
  *   q, k, v, out   [B, H, W, C] (NHWC), C = heads * head_dim, the channel of
@@ -71,8 +79,9 @@ typedef enum {
                                 shared_routing or projections not 0/1, or
                                 kv_downsample_ratio not dividing the window sides */
     BRA_ERR_UNSUPPORTED = 3, /* head_dim != 32, unknown dtype, n_win > 16, H*W >= 2^23,
-                                a region too large for the kernels' on-chip tiles, or
-                                projections with fp32 (or on a handle without them) */
+                                a region whose on-chip tiles (with its LePE halo) need
+                                more than a CU's 160 KB of LDS, or projections with
+                                fp32 (or on a handle without them) */
     BRA_ERR_HIP = 4,         /* a HIP runtime call failed (see bra_last_error) */
     BRA_ERR_NOMEM = 5,       /* device memory for the workspace could not be allocated */
     BRA_ERR_BAD_HANDLE = 6,  /* not a live handle (never created, or destroyed) */
@@ -140,9 +149,11 @@ bra_status_t bra_forward(bra_handle_t h, const void* q, const void* k, const voi
  * the regions routing_idx names, without computing the region means or the
  * routing (for reusing one routing across several calls, the reuse the pages
  * suggest for consecutive slices [P2 §4.2]).
- *   routing_idx   device [B,heads,R,k] int32, required; row (b,h,r) lists the
- *                 k regions whose tokens the queries of region r attend to
- *                 (any order; a region listed twice counts twice).  Ids are
+ *   routing_idx   device [B,rheads,R,k] int32, required (rheads = 1 on a
+ *                 handle with shared_routing, else heads); row (b,h,r) lists
+ *                 the k regions whose tokens the queries of region r attend
+ *                 to, for head h (every head, with shared_routing) -- any
+ *                 order; a region listed twice counts twice.  Ids are
  *                 clamped into [0, R) before use.
  *   the other arguments and the checks are those of bra_forward.
  * Enqueued on `stream` without synchronising or allocating. */
@@ -155,8 +166,9 @@ bra_status_t bra_forward_routed(bra_handle_t h, const void* q, const void* k, co
  * with projections = 1:
  *   q|k|v = x w_qkv^T + b_qkv, each rounded once to bf16 (channel blocks
  *           [0,C), [C,2C), [2C,3C) of the 3C outputs)
- *   y     = the bra_forward result of (q, k, v, lepe_w, lepe_b), kept in fp32
- *   out   = y w_o^T + b_o, rounded once to bf16
+ *   y     = the bra_forward result of (q, k, v, lepe_w, lepe_b), rounded
+ *           once to bf16 (as bra_forward's out is)
+ *   out   = y w_o^T + b_o, accumulated in fp32, rounded once to bf16
  *   x             device [B,H,W,C] bf16, 16-byte aligned
  *   w_qkv         device [3C, C] bf16 (a PyTorch Linear weight), 16-byte aligned
  *   b_qkv         device [3C] fp32, or NULL for none
@@ -165,10 +177,12 @@ bra_status_t bra_forward_routed(bra_handle_t h, const void* q, const void* k, co
  *   lepe_w, lepe_b, routing_idx, stream: as bra_forward; out: [B,H,W,C] bf16,
  *   must not overlap x.
  * The qkv projection runs on MFMA with the region means of the projected q
- * and k computed in the same pass; the output projection runs in the
- * attention kernel's epilogue, so y never goes to memory.  Enqueued without
- * synchronising or allocating.  BRA_ERR_UNSUPPORTED for a handle created
- * without projections. */
+ * and k computed in the same pass, writing q, k, v to the handle's
+ * workspace.  For C <= 4t the output projection runs in the attention
+ * kernel's epilogue on the y tile in LDS, so y never goes to memory; for
+ * larger C, y goes to the workspace and a kernel of its own applies the
+ * projection.  Enqueued without synchronising or allocating.
+ * BRA_ERR_UNSUPPORTED for a handle created without projections. */
 bra_status_t bra_forward_proj(bra_handle_t h, const void* x, const void* w_qkv,
                               const float* b_qkv, const float* lepe_w, const float* lepe_b,
                               const void* w_o, const float* b_o, void* out,

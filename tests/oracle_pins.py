@@ -217,6 +217,40 @@ def pin_means_match_numpy(orc):
                                rtol=1e-13, atol=1e-15)
 
 
+def pin_region_sums_exact_within_span(orc):
+    """Region sums of bf16 values [P4 §1.2; P5 §五 ③].  The nonzero values of one
+    (region, channel) are multiples of the smallest one's last significand
+    bit; while they span at most 2^(45 - ceil(log2 t)) in magnitude every
+    partial sum is an integer below 2^53 of those units, so every order of
+    the additions gives the exact sum (math.fsum) -- the fact that lets the
+    kernels sum as trees.  Here t = 64 and the span 2^39: the oracle's mean
+    is fsum / t to the last bit, and so is a pairwise tree.  Past the span
+    the orders differ, and the oracle keeps the slot order: 1 + 1 + 2^60 -
+    2^60 is 0 summed left to right, 2 summed as a tree."""
+    cfg = OracleConfig(1, 8, 8, 32, 1, 1, 1)  # one region of 64 tokens
+    rng = _rng(29)
+    e = rng.integers(-20, 20, size=(1, 8, 8, 32))  # exponents span 39 binades
+    sig = rng.integers(128, 256, size=e.shape) * rng.choice([-1, 1], size=e.shape)
+    x = sig * np.exp2(e - 7.0)  # 8-bit significands: exact bf16 values
+    means = orc.region_means(cfg, x)[0, 0, 0]
+    for c in range(32):
+        col = x[0, :, :, c].reshape(-1)  # slot order = row-major in the window
+        exact = math.fsum(col.tolist())
+        tree = col.copy()
+        while tree.size > 1:
+            tree = tree[0::2] + tree[1::2]
+        assert tree[0] == exact, c
+        assert means[c] == exact / 64, (c, means[c], exact / 64)
+    y = np.zeros((1, 8, 8, 32))
+    y[0, 0, :4, 0] = [1.0, 1.0, 2.0 ** 60, -(2.0 ** 60)]
+    col = y[0, :, :, 0].reshape(-1)
+    tree = col.copy()
+    while tree.size > 1:
+        tree = tree[0::2] + tree[1::2]
+    assert tree[0] == 2.0 and math.fsum(col.tolist()) == 2.0
+    assert orc.region_means(cfg, y)[0, 0, 0, 0] == 0.0
+
+
 def pin_routing_bruteforce_argsort(orc):
     """Routing equals a stable argsort of an independently computed affinity."""
     for (B, H, W, heads, hd, n, topk, seed) in [
@@ -603,6 +637,7 @@ ALL_PINS = [
     pin_constant_v,
     pin_zero_k_uniform_over_lowest_regions,
     pin_means_match_numpy,
+    pin_region_sums_exact_within_span,
     pin_routing_bruteforce_argsort,
     pin_ties_go_to_lower_region,
     pin_positive_scaling_keeps_routing,

@@ -54,10 +54,14 @@ def _cfg(**kw):
     (dict(projections=1, kv_downsample_ratio=2), bra.BRA_ERR_UNSUPPORTED),  # no KV downsampling
     (dict(projections=1, channels=544, num_heads=17), bra.BRA_ERR_UNSUPPORTED),  # C <= 512
     (dict(kv_downsample_ratio=3), bra.BRA_ERR_SHAPE),  # 3 does not divide the 4x4 windows
-    (dict(height=256, width=256, n_win=16, channels=32, num_heads=1),
-     bra.BRA_ERR_UNSUPPORTED),                     # 16 x 16 windows at C = 32: past the LDS tiles
-    (dict(height=110, width=110, n_win=10, channels=64, num_heads=2),
-     bra.BRA_ERR_UNSUPPORTED),                     # 11 x 11 windows at C = 64
+    (dict(height=104, width=104, n_win=4, channels=32, num_heads=1),
+     bra.BRA_ERR_UNSUPPORTED),                     # 26 x 26 windows at C = 32: past 160 KB of LDS
+    (dict(height=76, width=76, n_win=4, channels=64, num_heads=2),
+     bra.BRA_ERR_UNSUPPORTED),                     # 19 x 19 windows at C = 64
+    (dict(height=72, width=72, n_win=8, channels=256, num_heads=8),
+     bra.BRA_ERR_UNSUPPORTED),                     # 9 x 9 windows at C = 256
+    (dict(height=60, width=60, n_win=4, channels=128, num_heads=4, dtype=bra.BRA_F32),
+     bra.BRA_ERR_UNSUPPORTED),                     # fp32: 15 x 15 windows at C = 128
     (dict(height=4096, width=4096, n_win=256, channels=32, num_heads=1),
      bra.BRA_ERR_UNSUPPORTED),                     # H*W = 2^24 tokens: beyond 24-bit indexing
     (dict(height=34, width=34, n_win=17, channels=32, num_heads=1),
@@ -66,6 +70,26 @@ def _cfg(**kw):
 def test_create_rejects(lib, kw, status):
     assert bra.bra_create_status(_cfg(**kw)) == status
     assert bra.bra_last_error() != ""
+
+
+@pytest.mark.parametrize("kw", [
+    # "从静态到动态" §4.1: dim 128, n_win 7, topk 4, kv_downsample_ratio 4, on a
+    # 56 x 56 map with 4 heads of 32
+    dict(channels=128, num_heads=4, height=56, width=56, topk=4, kv_downsample_ratio=4),
+    # the segmentation module of "【医学图像分割模块】BiFormer" §六: dim 256, 8 heads,
+    # n_win 7, topk 4 (on a 56 x 56 map; the page gives none)
+    dict(channels=256, num_heads=8, height=56, width=56, topk=4),
+    dict(height=64, width=64, n_win=4, channels=64, num_heads=2),    # 16 x 16 windows
+    dict(height=100, width=100, n_win=4, channels=32, num_heads=1),  # 25 x 25 windows
+    dict(height=72, width=72, n_win=4, channels=64, num_heads=2),    # 18 x 18 windows
+    dict(height=48, width=48, n_win=8, channels=256, num_heads=8, dtype=bra.BRA_F32),
+], ids=["page_dim128_kvds4", "page_dim256_heads8", "win16_c64", "win25_c32", "win18_c64",
+        "f32_window6_c256"])
+def test_create_accepts_tiles_up_to_160_kb(lib, kw):
+    """Tiles above 64 KB and up to the CU's 160 KB of LDS pass the checks
+    (without a GPU, creation then stops at the first HIP call)."""
+    st = bra.bra_create_status(_cfg(**kw))
+    assert st not in (bra.BRA_ERR_UNSUPPORTED, bra.BRA_ERR_SHAPE), bra.bra_last_error()
 
 
 def test_create_null_arguments(lib):

@@ -24,6 +24,9 @@ CASES = [
     (Workload("kvds_ragged_bias", 2, 24, 16, 64, 2, 4, 3, "bf16", 406, lepe_bias=True), 2),
     (Workload("kvds_f32", 2, 28, 28, 64, 2, 7, 4, "f32", 407, lepe_bias=True), 2),
     (Workload("kvds_f32_r4", 2, 28, 28, 64, 2, 7, 4, "f32", 408), 4),
+    # "从静态到动态" §4.1: dim 128, n_win 7, topk 4, kv_downsample_ratio 4 (4 heads
+    # of 32, a 56 x 56 map): tiles above 64 KB of LDS
+    (Workload("page_dim128", 2, 56, 56, 128, 4, 7, 4, "bf16", 409, lepe_bias=True), 4),
 ]
 
 

@@ -57,12 +57,22 @@ SMALL = [
     Workload("pool_route_ragged", 2, 12, 18, 192, 6, 6, 5, "bf16", 129, lepe_bias=True),
     Workload("pool_route_r64_topk1", 1, 16, 16, 160, 5, 8, 1, "bf16", 130),
     Workload("pool_route_r4", 3, 8, 8, 192, 6, 2, 3, "bf16", 131),
-    # the largest windows the on-chip tiles take (bra_create refuses the next
-    # size up): 15 x 15 at C = 32 with 256 regions, 10 x 10 at C = 64, 6 x 6
-    # at C = 128
-    Workload("max_window_c32_r256", 1, 240, 240, 32, 1, 16, 4, "bf16", 133),
-    Workload("max_window_c64", 1, 100, 100, 64, 2, 10, 3, "bf16", 134, lepe_bias=True),
-    Workload("max_window_c128", 2, 36, 36, 128, 4, 6, 5, "bf16", 135),
+    # large windows: 15 x 15 at C = 32 with 256 regions, 10 x 10 at C = 64,
+    # 6 x 6 at C = 128 (tiles under 64 KB of LDS) ...
+    Workload("window15_c32_r256", 1, 240, 240, 32, 1, 16, 4, "bf16", 133),
+    Workload("window10_c64", 1, 100, 100, 64, 2, 10, 3, "bf16", 134, lepe_bias=True),
+    Workload("window6_c128", 2, 36, 36, 128, 4, 6, 5, "bf16", 135),
+    # ... and the largest the 160 KB of a CU's LDS takes (bra_create refuses
+    # the next size up): 25 x 25 at C = 32, 18 x 18 at C = 64, 12 x 12 at
+    # C = 128, 8 x 8 at C = 256, and fp32's 15 x 15 at C = 64; 16 x 16 at C = 64
+    Workload("max_window_c32", 1, 100, 100, 32, 1, 4, 4, "bf16", 136),
+    Workload("max_window_c64", 1, 72, 72, 64, 2, 4, 3, "bf16", 137, lepe_bias=True),
+    Workload("max_window_c128", 1, 48, 48, 128, 4, 4, 5, "bf16", 138),
+    Workload("max_window_f32_c64", 1, 60, 60, 64, 2, 4, 3, "f32", 139, lepe_bias=True),
+    Workload("window16_c64", 2, 64, 64, 64, 2, 4, 4, "bf16", 140, lepe_bias=True),
+    # the segmentation module of "【医学图像分割模块】BiFormer" §六: dim 256, 8
+    # heads, n_win 7, topk 4, on a 56 x 56 map (8 x 8 windows at C = 256)
+    Workload("page_dim256_heads8", 2, 56, 56, 256, 8, 7, 4, "bf16", 141, lepe_bias=True),
     # the whole-image kernel (the head group's K and V resident in LDS):
     # stage-3 geometry with a bias and a batch of 3
     Workload("image_stage3_bias_b3", 3, 14, 14, 256, 8, 7, 16, "bf16", 150, lepe_bias=True),

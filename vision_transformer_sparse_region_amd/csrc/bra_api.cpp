@@ -256,6 +256,11 @@ bra_status_t bra_create(const bra_config_t* cfg, bra_handle_t* out) {
         return fail_hip(e, "bra_create: hipGetDevice");
     }
     h->device = dev;
+    e = bra::prepare_attend(p, bf16);
+    if (e != hipSuccess) {
+        delete h;
+        return fail_hip(e, "bra_create: attention kernel LDS limit");
+    }
     if (bra::image_applies(p, bf16)) {
         e = bra::prepare_image(p);
         if (e != hipSuccess) {
@@ -513,6 +518,8 @@ bra_status_t bra_forward_noalloc(const bra_config_t* cfg, const void* q, const v
     void* base = nullptr;
     e = bra::scratch_pointer(dev, &base);
     if (e != hipSuccess) return fail_hip(e, "bra_forward_noalloc: hipGetSymbolAddress");
+    e = bra::prepare_attend(p, bf16);
+    if (e != hipSuccess) return fail_hip(e, "bra_forward_noalloc: attention kernel LDS limit");
     if (bra::image_applies(p, bf16)) {
         e = bra::prepare_image(p);
         if (e != hipSuccess) return fail_hip(e, "bra_forward_noalloc: image kernel LDS limit");

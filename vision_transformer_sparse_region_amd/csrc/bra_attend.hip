@@ -6,7 +6,8 @@
 //      64 regions, at most 4 heads), the K means of the image --, the LePE
 //      weights or Toeplitz operands, the V window with its 2-token halo, the
 //      first job's Q operands                                  [P5 §五 ⑤]
-//   1b in-kernel routing: the Q means from the Q operands (exact fp64 sums),
+//   1b in-kernel routing: the Q means from the Q operands (fp64 sums, exact
+//      within the span condition of row16_sum_exact),
 //      the affinity with every region -- screened with fp32 K means and an
 //      error bound, the fp64 affinities where the bound cannot decide --,
 //      arg-max or bitonic top-k, wave h for head h
@@ -576,7 +577,8 @@ __device__ __forceinline__ void lepe_mfma_compute(const Params& p, const uint16_
 // job is some wave's first job, the first Q operands of the waves hold each
 // query of the region once: wave w (< njobs) sums, in fp64, the queries of
 // its job (job w) for dims 8g..8g+7 of the job's head on lane row g, and
-// stores the 32 sums at sQp[w][..].  Every partial sum of bf16 values is an
+// stores the 32 sums at sQp[w][..].  Within the span condition of
+// row16_sum_exact (bra_device.h) every partial sum of bf16 values is an
 // exact fp64 number, so neither this split nor the order of the additions
 // can change the total: it equals the pool kernel's and the plain loop's.
 __device__ __forceinline__ void qmean_partial(const Params& p, const WaveJobs& J, int w,
@@ -1249,6 +1251,34 @@ bool plan(Params& p, int B, int H, int W, int C, int heads, int n_win, int k, fl
     // LDS of the pool kernel's staged path (fp32, or C/8 not dividing 64)
     p.pool_lds_bytes = p.pool_chunk * C * static_cast<int>(es);
     return off <= kMaxLdsBytes && C <= kMaxChannels && C % 32 == 0 && p.R <= kMaxRegions;
+}
+
+hipError_t prepare_attend(const Params& p, bool bf16) {
+    if (p.lds_bytes <= kDefaultLdsBytes) return hipSuccess;
+    auto raise = [](const void* f) {
+        return hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLdsBytes);
+    };
+#define BRA_ATTEND_PREP(T, HS, WS, NW, HEADS, KTOP)                                             \
+    if (p.kv_ratio == 1 && matches(Inst<T, HS, WS, NW, HEADS, KTOP>::key, p, bf16, true)) {     \
+        hipError_t e = raise(reinterpret_cast<const void*>(                                     \
+            &attend_kernel<T, HS, WS, NW, HEADS, KTOP, false>));                                \
+        if (e != hipSuccess || !route_fused(NW * NW, HEADS)) return e;                          \
+        return raise(reinterpret_cast<const void*>(                                             \
+            &attend_kernel<T, HS, WS, NW, HEADS, KTOP, route_fused(NW * NW, HEADS)>));          \
+    }
+    BRA_FOR_EACH_SHAPE(BRA_ATTEND_PREP)
+#undef BRA_ATTEND_PREP
+    hipError_t e;
+    if (bf16) {
+        e = raise(reinterpret_cast<const void*>(&attend_kernel<uint16_t, 0, 0, 0, 0, 0, false>));
+        if (e == hipSuccess)
+            e = raise(reinterpret_cast<const void*>(&attend_kernel<uint16_t, 0, 0, 0, 0, 0, true>));
+    } else {
+        e = raise(reinterpret_cast<const void*>(&attend_kernel<float, 0, 0, 0, 0, 0, false>));
+        if (e == hipSuccess)
+            e = raise(reinterpret_cast<const void*>(&attend_kernel<float, 0, 0, 0, 0, 0, true>));
+    }
+    return e;
 }
 
 hipError_t launch_attend(const Params& p, bool bf16, const void* q, const void* v,

@@ -316,9 +316,14 @@ __device__ __forceinline__ void argmax_swap(double& best, int& bs) {
     bs = ia;
 }
 // Sum of x over the 16 lanes of each DPP row (partners lane ^ 1, lane ^ 2,
-// the other quad, the other half).  For exact sums only -- fp64 sums of bf16
-// values -- where the pairing cannot change the result; every lane of the
-// row ends with the same value.
+// the other quad, the other half); every lane of the row ends with the same
+// value.  For exact sums only, where the pairing cannot change the result:
+// fp64 sums of the t bf16 values of one (region, channel).  Those are
+// multiples of the smallest nonzero value's last significand bit, so while
+// the nonzero values span at most 2^(45 - ceil(log2 t)) in magnitude every
+// partial sum is an integer number of those units below 2^53, exact in
+// fp64, and every order of the additions gives the slot-order sum.  Wider
+// spans may round differently (include/bra.h states the condition).
 template <int CTRL>
 __device__ __forceinline__ double dpp_f64(double x) {
     const int2 u = __builtin_bit_cast(int2, x);

@@ -10,7 +10,11 @@ namespace bra {
 constexpr int kHeadDim = 32;     // the only head_dim the kernels implement
 constexpr int kThreads = 256;    // threads per workgroup (4 wave64s)
 constexpr int kWaves = kThreads / 64;
-constexpr int kMaxLdsBytes = 64 * 1024;
+// LDS one workgroup may take: a gfx950 CU's whole 160 KB.  A kernel whose
+// tiles need more than the default 64 KB has its dynamic-LDS limit raised
+// first (prepare_attend).
+constexpr int kMaxLdsBytes = 160 * 1024;
+constexpr int kDefaultLdsBytes = 64 * 1024;
 constexpr int kPoolChunkBytes = 16 * 1024;
 constexpr int kVtStride = 36;    // bf16 elements per staged V row (32 dims + pad)
 constexpr int kMaxQTiles = 2;    // 16-query tiles one wave carries at once
@@ -120,6 +124,12 @@ constexpr JobShape job_shape(int t, int heads) {
 constexpr bool qmean_in_attend(bool bf16, bool fused, int t, int heads) {
     return bf16 && fused && job_shape(t, heads).njobs <= kWaves;
 }
+
+// Raises the dynamic-LDS limit of the attention kernel instance that
+// launch_attend picks for p to kMaxLdsBytes when its tiles need more than
+// kDefaultLdsBytes (a no-op otherwise).  Every handle raises it to the same
+// value, so no handle lowers it under another.
+hipError_t prepare_attend(const Params& p, bool bf16);
 
 //   kg, vg: the K and V the attention gathers from -- k and v, or their
 //   downsampled copies ([B, kH, kW, C]) when kv_ratio > 1; v still feeds LePE.

@@ -47,10 +47,10 @@ __device__ __forceinline__ void token_group_sum(double (&acc)[8], int nvec) {
 // the Q means itself (p.qmean_attend).
 //  bf16, C/8 dividing 64: one wave per (region, tensor).  Lane (pv, tg) holds
 //        fp64 sums of channels 8pv..8pv+7 over every (64/(C/8))-th token of the
-//        window; the lanes of one pv are then combined with shuffles.  A bf16
-//        value has an 8-bit significand, so every partial sum of a window is an
-//        exact fp64 number: the order of the additions cannot change the
-//        result, and the mean is the correctly rounded exact mean.
+//        window; the lanes of one pv are then combined with shuffles.  Within
+//        the span condition of row16_sum_exact (bra_device.h) every partial
+//        sum is an exact fp64 number: the order of the additions cannot
+//        change the result, and the mean is the slot-order mean.
 //  otherwise (fp32, or other channel counts): one thread per channel sums
 //        the tokens in slot order -- the order of a plain loop -- staged
 //        through LDS in chunks.

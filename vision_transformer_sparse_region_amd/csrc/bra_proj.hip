@@ -26,8 +26,9 @@
 // qkv: a slice is the tokens of `group` whole regions of one image when a
 // region is smaller than a slice, else one region taken a slice at a time.
 // For q and k each (region, channel) sums its tokens' rounded values in fp64
-// -- every partial sum of bf16 values is exact, so the region means equal
-// those of the pool kernel over the stored maps, bit for bit.
+// -- within the span condition of row16_sum_exact (bra_device.h) every
+// partial sum of bf16 values is exact, so the region means equal those of
+// the pool kernel over the stored maps, bit for bit.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 

@@ -262,8 +262,9 @@ route_large_kernel(const double* __restrict__ means, int32_t* __restrict__ idx_o
 //   1. K of head h for all R regions (R * t tokens, 64 bytes each) and Q of
 //      the chunk's regions reach LDS by LDS DMA (global_load_lds_dwordx4: a
 //      wave instruction fills 64 consecutive 16-byte slots, lane L slot L).
-//   2. Threads take (region, dim) items: the exact fp64 sum of the t bf16
-//      values divided by t -- bit for bit the pool kernel's mean -- into
+//   2. Threads take (region, dim) items: the fp64 sum of the t bf16 values
+//      (exact within the span condition of row16_sum_exact in bra_device.h)
+//      divided by t -- bit for bit the pool kernel's mean -- into
 //      K-bar [32][R] (lane s reads region s) and Q-bar [rows][32], which
 //      overlay the staged K and Q once every sum is taken.
 //   3. Each wave routes kRouteChains rows as route_small_kernel does, from
@@ -348,7 +349,8 @@ __global__ __launch_bounds__(kThreads) void pool_route_kernel(
     }
     __builtin_amdgcn_s_waitcnt(0);  // this wave's DMA has landed
     __syncthreads();
-    // 2. the means: exact fp64 sums of bf16 values (any order), then / t,
+    // 2. the means: fp64 sums of bf16 values (any order: exact within the
+    //    span condition of row16_sum_exact), then / t,
     //    held in registers until every staged value is read
     double km[kKMeanItems], qm[kQMeanItems];
 #pragma unroll
