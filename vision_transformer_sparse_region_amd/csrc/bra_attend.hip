@@ -138,15 +138,25 @@ __device__ __forceinline__ bool pair_chunk(const WaveJobs& J, int u, int ch) {
 
 // V chunk (in registers, one 16-byte piece per lane and half) through the
 // wave's LDS buffer, read back as the two V^T operands of O^T += V^T P^T.
+// A staged row (one key) is 32 dims = 8 units of 8 bytes (dims 4u .. 4u+3);
+// unit u of row r sits at slot u ^ vt_swizzle(r).  Rows two apart (and, with
+// 64 banks, four and eight apart) would otherwise meet on the same banks --
+// in the writes, where a 16-lane group writes units of the same parity to
+// four rows, and in the transposing reads, where it reads units 4db .. 4db+3
+// of four rows: bit 1 of the row flips a unit's parity and its half (5),
+// bit 2 its parity (1), bit 3 its half (4).
+__device__ __forceinline__ int vt_swizzle(int r) {
+    return (((r >> 1) & 1) * 5) ^ ((r >> 2) & 1) ^ (((r >> 3) & 1) * 4);
+}
 __device__ __forceinline__ void v_transpose(const StepRegs& cur, uint16_t* sVt,
                                             bf16x8_t (&va)[2]) {
     const int lane = threadIdx.x & 63, li = lane & 15, g = lane >> 4;
 #pragma unroll
     for (int pp = 0; pp < 2; ++pp) {
-        const int pc = lane + 64 * pp;
-        uint2* dst = reinterpret_cast<uint2*>(sVt + (pc >> 2) * kVtStride + 8 * (pc & 3));
-        dst[0] = uint2{cur.vv[pp].x, cur.vv[pp].y};
-        dst[1] = uint2{cur.vv[pp].z, cur.vv[pp].w};
+        const int pc = lane + 64 * pp, row = pc >> 2, q = pc & 3, sw = vt_swizzle(row);
+        uint2* dst = reinterpret_cast<uint2*>(sVt + row * kVtRow);
+        dst[(2 * q) ^ sw] = uint2{cur.vv[pp].x, cur.vv[pp].y};
+        dst[(2 * q + 1) ^ sw] = uint2{cur.vv[pp].z, cur.vv[pp].w};
     }
     // A wave's LDS operations complete in order; the fences keep the
     // compiler from moving the transposed reads above the writes, or the
@@ -160,13 +170,15 @@ __device__ __forceinline__ void v_transpose(const StepRegs& cur, uint16_t* sVt,
     // key 8g + r (then 8g + 4 + r), so lane i gets dim 16 db + i of keys
     // 8g .. 8g + 3 (then 8g + 4 .. 8g + 7): the operand, without repacking.
     const int tr_r = li >> 2, tr_a = li & 3;
+    const int r_lo = 8 * g + tr_r, r_hi = r_lo + 4;
+    const int sw_lo = vt_swizzle(r_lo), sw_hi = vt_swizzle(r_hi);
 #pragma unroll
     for (int db = 0; db < 2; ++db) {
-        const uint16_t* base = sVt + (8 * g + tr_r) * kVtStride + 16 * db + 4 * tr_a;
+        const int unit = 4 * db + tr_a;
         const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) s16x4_t*)(base));
+            (__attribute__((address_space(3))) s16x4_t*)(sVt + r_lo * kVtRow + 4 * (unit ^ sw_lo)));
         const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) s16x4_t*)(base + 4 * kVtStride));
+            (__attribute__((address_space(3))) s16x4_t*)(sVt + r_hi * kVtRow + 4 * (unit ^ sw_hi)));
         va[db] = __builtin_bit_cast(
             bf16x8_t, u32x4_t{__builtin_bit_cast(u32x2_t, lo)[0], __builtin_bit_cast(u32x2_t, lo)[1],
                               __builtin_bit_cast(u32x2_t, hi)[0], __builtin_bit_cast(u32x2_t, hi)[1]});
@@ -192,7 +204,7 @@ __device__ __forceinline__ void attend_mfma(const Params& p, const WaveJobs& J, 
                             StepRegs (&ring)[2], bf16x8_t (&qb)[kMaxQTiles], bool sum_mfma) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int li = lane & 15, g = lane >> 4;
-    uint16_t* sVt = sVt_all + w * 32 * kVtStride;
+    uint16_t* sVt = sVt_all + w * 32 * kVtRow;
     const int npair = (J.nchunks + 1) / 2;
     const int njl = J.nchunks > 0 ? J.nsteps / J.nchunks : 0;  // this wave's jobs
 
@@ -1211,7 +1223,7 @@ bool plan(Params& p, int B, int H, int W, int C, int heads, int n_win, int k, fl
     const long t = p.t;
     // per-wave V^T staging (bf16 attention); before the attention, the
     // partial Q sums of each wave (32 doubles)
-    p.off_vt = take(std::max(bf16 ? static_cast<long>(kWaves) * 32 * kVtStride * 2 : 0L,
+    p.off_vt = take(std::max(bf16 ? static_cast<long>(kWaves) * 32 * kVtRow * 2 : 0L,
                              static_cast<long>(kWaves) * kHeadDim * 8));
     // The fixed bf16 shapes whose windows tile by 4x4 run LePE on MFMA with a
     // channel-planar halo; the others on VALU with an NHWC halo.

@@ -16,7 +16,7 @@ constexpr int kWaves = kThreads / 64;
 constexpr int kMaxLdsBytes = 160 * 1024;
 constexpr int kDefaultLdsBytes = 64 * 1024;
 constexpr int kPoolChunkBytes = 16 * 1024;
-constexpr int kVtStride = 36;    // bf16 elements per staged V row (32 dims + pad)
+constexpr int kVtRow = 32;       // bf16 elements per staged V row (32 dims; swizzled, no pad)
 constexpr int kMaxQTiles = 2;    // 16-query tiles one wave carries at once
 constexpr int kLepeCols = 8;     // output columns one LePE work item covers
 constexpr int kHaloRegs = 8;     // 16-byte halo pieces a thread keeps in flight
