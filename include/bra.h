@@ -244,6 +244,14 @@ enum { BRA_ALLOC_HOST = 1, BRA_ALLOC_DEVICE = 2 };
 bra_status_t bra_debug_inject_alloc_failure(int32_t which, int32_t count);
 int32_t bra_debug_live_handles(void);
 
+/* Testing hook: the q, k, v of the last bra_forward_proj on h (the bf16
+ * outputs of its qkv projection, kept in the handle's workspace until the
+ * next call on h), copied into q, k, v (device [B,H,W,C] bf16 each, owned by
+ * the caller) on `stream`, enqueued after that call when on its stream.
+ * BRA_ERR_BAD_HANDLE, BRA_ERR_UNSUPPORTED for a handle without projections,
+ * BRA_ERR_NULL for a missing pointer, BRA_ERR_HIP if a copy fails. */
+bra_status_t bra_debug_projected_qkv(bra_handle_t h, void* q, void* k, void* v, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -7,7 +7,8 @@ Bar (stated once, used by every GPU parity test):
     (a near-tie); every such slot is reported, and the output is then
     compared against the oracle's attention with the GPU's routing;
   * out: max|gpu - oracle| / max|oracle| <= 1e-4 for fp32 I/O and 2e-2 for
-    bf16 I/O (fp32 accumulation).
+    bf16 I/O (fp32 accumulation), over the whole output and over each head's
+    channels on their own (a head of small magnitude cannot hide).
 """
 from __future__ import annotations
 
@@ -83,9 +84,28 @@ def check_routing(gpu_idx: np.ndarray, res: dict):
     return ties
 
 
-def max_rel_err(gpu_out: torch.Tensor, ref: np.ndarray) -> float:
+def max_rel_err(gpu_out: torch.Tensor, ref: np.ndarray, heads: int | None = None) -> float:
+    """max|gpu - oracle| / max|oracle|; with `heads`, the largest of that and
+    of the same ratio over each head's channels (per_head_rel_err)."""
     g = gpu_out.double().numpy()
-    return float(np.abs(g - ref).max() / np.abs(ref).max())
+    err = float(np.abs(g - ref).max() / np.abs(ref).max())
+    if heads is not None:
+        err = max([err] + per_head_rel_err(gpu_out, ref, heads))
+    return err
+
+
+def per_head_rel_err(gpu_out: torch.Tensor, ref: np.ndarray, heads: int) -> list[float]:
+    """max|gpu - oracle| / max|oracle| over each head's channels separately, so
+    that a head of small magnitude cannot hide behind the others."""
+    g = gpu_out.double().numpy()
+    hd = g.shape[-1] // heads
+    out = []
+    for h in range(heads):
+        sl = slice(h * hd, (h + 1) * hd)
+        den = np.abs(ref[..., sl]).max()
+        num = np.abs(g[..., sl] - ref[..., sl]).max()
+        out.append(float(num / den) if den > 0 else float(num))
+    return out
 
 
 def check_parity(wl: Workload, inp: dict | None = None, lepe: bool = True,
@@ -105,7 +125,12 @@ def check_parity(wl: Workload, inp: dict | None = None, lepe: bool = True,
                                          f["lepe_w"] if lepe else None,
                                          f["lepe_b"] if lepe else None, gidx)
     err = max_rel_err(gout, ref)
+    heads = per_head_rel_err(gout, ref, wl.num_heads)
+    worst = int(np.argmax(heads))
     bound = tol if tol is not None else TOL[wl.dtype]
-    say(f"[gpu] {wl.name}: max rel err {err:.3e} (bound {bound:g}), near-ties {len(ties)}")
+    say(f"[gpu] {wl.name}: max rel err {err:.3e} (bound {bound:g}), worst head {worst}: "
+        f"{heads[worst]:.3e}, near-ties {len(ties)}")
     assert err <= bound, f"{wl.name}: max relative error {err:.3e} > {bound:g}"
+    assert heads[worst] <= bound, \
+        f"{wl.name}: head {worst} relative error {heads[worst]:.3e} > {bound:g}"
     return err, ties

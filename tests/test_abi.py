@@ -54,8 +54,8 @@ def _cfg(**kw):
     (dict(projections=1, kv_downsample_ratio=2), bra.BRA_ERR_UNSUPPORTED),  # no KV downsampling
     (dict(projections=1, channels=544, num_heads=17), bra.BRA_ERR_UNSUPPORTED),  # C <= 512
     (dict(kv_downsample_ratio=3), bra.BRA_ERR_SHAPE),  # 3 does not divide the 4x4 windows
-    (dict(height=104, width=104, n_win=4, channels=32, num_heads=1),
-     bra.BRA_ERR_UNSUPPORTED),                     # 26 x 26 windows at C = 32: past 160 KB of LDS
+    (dict(height=108, width=108, n_win=4, channels=32, num_heads=1),
+     bra.BRA_ERR_UNSUPPORTED),                     # 27 x 27 windows at C = 32: past 160 KB of LDS
     (dict(height=76, width=76, n_win=4, channels=64, num_heads=2),
      bra.BRA_ERR_UNSUPPORTED),                     # 19 x 19 windows at C = 64
     (dict(height=72, width=72, n_win=8, channels=256, num_heads=8),
@@ -80,10 +80,10 @@ def test_create_rejects(lib, kw, status):
     # n_win 7, topk 4 (on a 56 x 56 map; the page gives none)
     dict(channels=256, num_heads=8, height=56, width=56, topk=4),
     dict(height=64, width=64, n_win=4, channels=64, num_heads=2),    # 16 x 16 windows
-    dict(height=100, width=100, n_win=4, channels=32, num_heads=1),  # 25 x 25 windows
+    dict(height=104, width=104, n_win=4, channels=32, num_heads=1),  # 26 x 26 windows
     dict(height=72, width=72, n_win=4, channels=64, num_heads=2),    # 18 x 18 windows
     dict(height=48, width=48, n_win=8, channels=256, num_heads=8, dtype=bra.BRA_F32),
-], ids=["page_dim128_kvds4", "page_dim256_heads8", "win16_c64", "win25_c32", "win18_c64",
+], ids=["page_dim128_kvds4", "page_dim256_heads8", "win16_c64", "win26_c32", "win18_c64",
         "f32_window6_c256"])
 def test_create_accepts_tiles_up_to_160_kb(lib, kw):
     """Tiles above 64 KB and up to the CU's 160 KB of LDS pass the checks
@@ -108,6 +108,7 @@ def test_dead_handles(lib):
     assert bra.bra_forward_proj_status(fake, 16, 16, None, None, None, 16, None, 32) == \
         bra.BRA_ERR_BAD_HANDLE
     assert lib.bra_topk_effective(fake) == -1
+    assert bra.bra_debug_projected_qkv_status(fake, 16, 16, 16) == bra.BRA_ERR_BAD_HANDLE
     assert lib.bra_timing_enable(fake, 4) == bra.BRA_ERR_BAD_HANDLE
     buf = (ctypes.c_float * 2)()
     n = ctypes.c_int32()

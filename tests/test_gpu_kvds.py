@@ -58,7 +58,7 @@ def test_kv_downsampling_matches_oracle(wl, ratio):
     aff = oracle.bra_forward(cfg, f["q"], f["k"], f["v"], want_aff=True)["aff"]
     ties = check_routing(gidx, {"idx": res["idx"], "aff": aff})
     assert not ties, "near-ties would need the downsampled attention on the GPU's routing"
-    err = max_rel_err(out, res["out"])
+    err = max_rel_err(out, res["out"], wl.num_heads)
     say(f"[gpu] kvds {wl.name} r={ratio}: max rel err {err:.3e} (bound {TOL[wl.dtype]:g})")
     assert err <= TOL[wl.dtype]
     # the routed entry point on the forward's own routing gives the same output
@@ -91,7 +91,7 @@ def test_kv_downsampling_with_shared_routing():
     full = np.ascontiguousarray(np.repeat(gidx, wl.num_heads, axis=1))
     ref = oracle.attend_kvds(cfg, ratio, f["q"], f["k"], f["v"], full) + \
         oracle.lepe(cfg, f["v"], f["lepe_w"], f["lepe_b"])
-    err = max_rel_err(out.cpu(), ref)
+    err = max_rel_err(out.cpu(), ref, wl.num_heads)
     say(f"[gpu] kvds + shared routing: max rel err {err:.3e}, near-ties {len(ties)}")
     assert err <= TOL[wl.dtype]
 
@@ -118,6 +118,6 @@ def test_routed_entry_with_kv_downsampling():
     cfg = oracle_cfg(wl)
     ref = oracle.attend_kvds(cfg, ratio, f["q"], f["k"], f["v"], idx) + \
         oracle.lepe(cfg, f["v"], f["lepe_w"], f["lepe_b"])
-    err = max_rel_err(out.cpu(), ref)
+    err = max_rel_err(out.cpu(), ref, wl.num_heads)
     say(f"[gpu] kvds routed entry: max rel err {err:.3e}")
     assert err <= TOL[wl.dtype]

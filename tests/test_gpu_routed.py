@@ -60,7 +60,7 @@ def test_given_routing_matches_oracle(wl):
     say(f"[gpu] routed {wl.name}: B={wl.batch} {wl.height}x{wl.width} C={wl.channels} "
         f"heads={wl.num_heads} n_win={wl.n_win} k={wl.topk_effective} {wl.dtype}")
     out = run_routed(wl, inp, idx)
-    err = max_rel_err(out, oracle_routed(wl, inp, idx))
+    err = max_rel_err(out, oracle_routed(wl, inp, idx), wl.num_heads)
     say(f"[gpu] routed {wl.name}: max rel err {err:.3e} (bound {TOL[wl.dtype]:g})")
     assert err <= TOL[wl.dtype]
 
@@ -71,7 +71,8 @@ def test_out_of_range_ids_are_clamped():
     idx = random_routing(wl, 207, lo=-8, hi=wl.regions + 8)
     say("[gpu] routed out-of-range ids")
     out = run_routed(wl, inp, idx)
-    err = max_rel_err(out, oracle_routed(wl, inp, np.clip(idx, 0, wl.regions - 1)))
+    err = max_rel_err(out, oracle_routed(wl, inp, np.clip(idx, 0, wl.regions - 1)),
+                      wl.num_heads)
     say(f"[gpu] routed out-of-range ids: max rel err {err:.3e}")
     assert err <= TOL[wl.dtype]
 

@@ -53,7 +53,7 @@ def check_shared(wl: Workload, inp: dict | None = None):
         full = np.ascontiguousarray(np.repeat(gidx, wl.num_heads, axis=1))
         ref = oracle.attend_with_routing(cfg, f["q"], f["k"], f["v"], f["lepe_w"], f["lepe_b"],
                                          full)
-    err = max_rel_err(out, ref)
+    err = max_rel_err(out, ref, wl.num_heads)
     say(f"[gpu] shared {wl.name}: max rel err {err:.3e} (bound {TOL[wl.dtype]:g}), "
         f"near-ties {len(ties)}")
     assert err <= TOL[wl.dtype]

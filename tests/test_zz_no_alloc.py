@@ -42,7 +42,7 @@ def test_noalloc_equals_forward_two_calls(wl):
     say(f"[gpu] noalloc {wl.name} B={wl.batch}")
     ref, ref_idx, out, idx = _both(wl)
     assert torch.equal(idx, ref_idx)
-    err = max_rel_err(out.cpu(), ref.cpu().double().numpy())
+    err = max_rel_err(out.cpu(), ref.cpu().double().numpy(), wl.num_heads)
     assert err <= TOL[wl.dtype]
     assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
 

@@ -87,8 +87,10 @@ def load_library(path: str = LIB_PATH):
     lib.bra_debug_inject_alloc_failure.argtypes = [i32, i32]
     lib.bra_debug_live_handles.argtypes = []
     lib.bra_debug_live_handles.restype = i32
+    lib.bra_debug_projected_qkv.argtypes = [vp, vp, vp, vp, vp]
     for name in ("bra_create", "bra_forward", "bra_forward_routed", "bra_forward_proj",
                  "bra_forward_noalloc", "bra_destroy", "bra_debug_inject_alloc_failure",
+                 "bra_debug_projected_qkv",
                  "bra_timing_enable", "bra_timing_read"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
@@ -238,6 +240,11 @@ def bra_debug_live_handles() -> int:
     return int(load_library().bra_debug_live_handles())
 
 
+def bra_debug_projected_qkv_status(h, q, k, v, stream=0) -> int:
+    """Raw status of bra_debug_projected_qkv (a testing hook)."""
+    return load_library().bra_debug_projected_qkv(h, _ptr(q), _ptr(k), _ptr(v), stream)
+
+
 KERNELS = ("region_pool", "route", "attend")
 
 
@@ -358,6 +365,18 @@ class BRA:
         bra_forward_proj(self.handle, x, w_qkv, b_qkv, lepe_w, lepe_b, w_o, b_o, out, idx,
                          stream)
         return out, idx
+
+    def projected_qkv(self, stream=None):
+        """The bf16 q, k, v the last forward_proj on this handle projected
+        (a testing hook: copies out of the handle's workspace)."""
+        import torch
+        c = self.cfg
+        shape = (c.batch, c.height, c.width, c.channels)
+        dev = torch.device("cuda", torch.cuda.current_device())
+        q, k, v = (torch.empty(shape, dtype=torch.bfloat16, device=dev) for _ in range(3))
+        _check(bra_debug_projected_qkv_status(self.handle, q, k, v, _stream(stream)),
+               "bra_debug_projected_qkv")
+        return q, k, v
 
     def close(self):
         if self.handle:

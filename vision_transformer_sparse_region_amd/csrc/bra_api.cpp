@@ -591,4 +591,21 @@ int32_t bra_debug_live_handles(void) {
     return static_cast<int32_t>(g_live.size());
 }
 
+bra_status_t bra_debug_projected_qkv(bra_handle_t h, void* q, void* k, void* v, void* stream) {
+    if (!is_live(h)) return fail(BRA_ERR_BAD_HANDLE, "bra_debug_projected_qkv: not a live handle");
+    if (!h->ws.qs)
+        return fail(BRA_ERR_UNSUPPORTED,
+                    "bra_debug_projected_qkv: the handle was created without projections");
+    if (!q || !k || !v) return fail(BRA_ERR_NULL, "bra_debug_projected_qkv: q, k, v are required");
+    const size_t bytes = map_bytes(h->cfg);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const void* src[3] = {h->ws.qs, h->ws.ks, h->ws.vs};
+    void* dst[3] = {q, k, v};
+    for (int i = 0; i < 3; ++i) {
+        hipError_t e = hipMemcpyAsync(dst[i], src[i], bytes, hipMemcpyDeviceToDevice, s);
+        if (e != hipSuccess) return fail_hip(e, "bra_debug_projected_qkv: hipMemcpyAsync");
+    }
+    return BRA_OK;
+}
+
 }  // extern "C"
