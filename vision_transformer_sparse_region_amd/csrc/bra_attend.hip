@@ -543,7 +543,7 @@ __device__ __forceinline__ void lepe_mfma_compute(const Params& p, const uint16_
         const int cg = w + kWaves * g;
         if (cg < S::NG) {
             const int c = 16 * cg + blk;
-            const uint16_t* plane = sVp + c * S::PS;
+            const uint16_t* plane = sVp + lepe_plane_offset(c, S::PS);
 #pragma unroll
             for (int ty = 0; ty < S::TY; ++ty)
 #pragma unroll
@@ -966,7 +966,9 @@ attend_kernel(const T* __restrict__ q, const T* __restrict__ v, const T* __restr
         const int cell = i / nvec, pv = i - cell * nvec;
         if constexpr (kLepeMfma) {
             using S = LepeMfmaShape<HS, WS, HEADS>;
-            uint16_t* dst = reinterpret_cast<uint16_t*>(sVh) + pv * 8 * S::PS + cell;
+            // channels 8 pv + e (e < 8) share the 4-element step of 8 pv
+            uint16_t* dst =
+                reinterpret_cast<uint16_t*>(sVh) + lepe_plane_offset(8 * pv, S::PS) + cell;
             const uint32_t wd[4] = {val.x, val.y, val.z, val.w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -998,8 +1000,9 @@ attend_kernel(const T* __restrict__ q, const T* __restrict__ v, const T* __restr
                             wd[j][2] = hreg[u * 4 + j].z & mk;
                             wd[j][3] = hreg[u * 4 + j].w & mk;
                         }
-                        uint16_t* base = reinterpret_cast<uint16_t*>(sVh) + pv * 8 * S::PS +
-                                         hy * S::HWP + 4 * gx;
+                        uint16_t* base = reinterpret_cast<uint16_t*>(sVh) +
+                                         lepe_plane_offset(8 * pv, S::PS) + hy * S::HWP +
+                                         4 * gx;
 #pragma unroll
                         for (int e = 0; e < 8; ++e) {
                             const int sh = 16 * (e & 1);
@@ -1229,7 +1232,7 @@ bool plan(Params& p, int B, int H, int W, int C, int heads, int n_win, int k, fl
     // channel-planar halo; the others on VALU with an NHWC halo.
     p.lepe_mfma = bf16 && is_fixed_shape(p, bf16) && lepe_mfma_fits(p.hs, p.ws, heads);
     const long vh_bytes =
-        p.lepe_mfma ? static_cast<long>(C) * ((p.hs + 4) * (p.ws + 4) + 4) * 2
+        p.lepe_mfma ? static_cast<long>(lepe_plane_offset(C, lepe_plane_stride(p.hs, p.ws))) * 2
                     : static_cast<long>(p.hs + 4) * (p.ws + 4) * C * es;
     const long l_bytes = t * p.lstride * 4;
     p.lepe_alias = p.lepe_mfma || p.lepe_items <= kThreads;

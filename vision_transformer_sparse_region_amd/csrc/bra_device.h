@@ -264,12 +264,27 @@ __host__ __device__ constexpr bool lepe_mfma_fits(int hs, int ws, int heads) {
            (hs / 4) * (ws / 4) * ((heads * kHeadDim / 16 + kWaves - 1) / kWaves) <= 8;
 }
 
+// The channel-planar halo of the MFMA LePE: channel c's (hs + 4) x (ws + 4)
+// plane starts at element lepe_plane_offset(c, ps).  The stride and the
+// 4-element step per 8 channels spread over the LDS banks both the halo
+// writes (the 8 lanes of one cell write channels 8 apart: 2-byte stores for
+// 8 x 8 windows, 8-byte stores of 4 cells for 4 x 4) and the 4x4x4 operand
+// reads (16 channels x 4 rows per instruction).  The strides come from a
+// bank model of those two patterns (32 banks serving 16 lanes, or 64
+// serving 32): 8 x 8 windows conflict-free (the unpadded 148 took 4- and
+// 2-way conflicts), 4 x 4 writes conflict-free and reads 2-way (68: 8-way
+// and 2-way).
+__host__ __device__ constexpr int lepe_plane_stride(int hs, int ws) {
+    return hs == 8 && ws == 8 ? 176 : hs == 4 && ws == 4 ? 76 : (hs + 4) * (ws + 4) + 4;
+}
+__host__ __device__ constexpr int lepe_plane_offset(int c, int ps) { return c * ps + 4 * (c >> 3); }
+
 template <int HS, int WS, int HEADS>
 struct LepeMfmaShape {
     static constexpr int C = HEADS * kHeadDim;
     static constexpr int TY = HS / 4, TX = WS / 4;
     static constexpr int HWP = WS + 4;                    // halo row pitch (elements)
-    static constexpr int PS = (HS + 4) * (WS + 4) + 4;    // channel plane stride (elements)
+    static constexpr int PS = lepe_plane_stride(HS, WS);  // channel plane stride (elements)
     static constexpr int NG = C / 16;                     // groups of 16 channels
     static constexpr int GPW = (NG + kWaves - 1) / kWaves;  // groups per wave
     static constexpr bool ok = lepe_mfma_fits(HS, WS, HEADS);
