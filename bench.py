@@ -79,6 +79,39 @@ def image_path(wl, shared_routing: bool = False, kv_ratio: int = 1) -> bool:
             (hs, wl.n_win, wl.num_heads, wl.topk_effective) in IMAGE_SHAPES)
 
 
+def small_lds_bytes(wl) -> int:
+    """LDS of the one-launch fp32 kernel (its layout: the head's K map, the
+    fp64 K means, the routed V rows, the probabilities, the V window with its
+    halo, the Q rows, the LePE weights, the ids and the token tables; the DMA
+    arrays whole rounds of 256 16-byte slots)."""
+    t, nk = wl.tokens_per_region, wl.topk_effective * wl.tokens_per_region
+    hs, ws = wl.height // wl.n_win, wl.width // wl.n_win
+    rnd = lambda slots: -(-slots // 256) * 4096
+    a16 = lambda x: (x + 15) & ~15
+    off = rnd(wl.height * wl.width * 8)
+    off = a16(off + wl.regions * 32 * 8)
+    off += rnd(nk * 8)
+    off = a16(off + t * (nk + 4) * 4)
+    off += rnd((hs + 4) * (ws + 4) * 8)
+    off += rnd(t * 8)
+    off = a16(off + (32 * 25 + 32) * 4)
+    off = a16(off + 2 * 16 * 4)
+    return a16(off + 2 * 64 * 4)
+
+
+def small_path(wl, shared_routing: bool = False, kv_ratio: int = 1) -> bool:
+    """fp32 problems of at most 256 (image, head, region) triples: one kernel,
+    one workgroup per triple, runs the whole forward."""
+    t = wl.tokens_per_region
+    return (wl.dtype == "f32" and not shared_routing and max(kv_ratio, 1) == 1 and
+            wl.batch * wl.num_heads * wl.regions <= 256 and wl.regions <= 64 and t <= 64 and
+            wl.topk_effective <= 16 and small_lds_bytes(wl) <= 160 * 1024)
+
+
+def one_kernel(wl, shared_routing: bool = False, kv_ratio: int = 1) -> bool:
+    return image_path(wl, shared_routing, kv_ratio) or small_path(wl, shared_routing, kv_ratio)
+
+
 def out_proj_in_attend(wl) -> bool:
     """The output projection runs in the attention kernel's epilogue when
     C <= 4 t, else as a kernel of its own over the attention output."""
@@ -128,7 +161,7 @@ def algorithmic_bytes(wl, shared_routing: bool = False, kv_ratio: int = 1,
     attend = (3 * S + 2 * S // r2 if r2 > 1 else 4 * S) + idx + lepe
     k32 = M // 2 if kmean32(wl, shared_routing) else 0   # fp32 K means
     kread = k32 if k32 else M                            # K means the attention reads
-    if image_path(wl, shared_routing, kv_ratio) and not projections:
+    if one_kernel(wl, shared_routing, kv_ratio) and not projections:
         # one kernel: q, k, v read once, out written once, the ids exported
         return {"pool": 0, "route": 0, "attend": attend, "S": S}
     if projections:
@@ -261,7 +294,9 @@ ALL_WORKLOADS = ("tiny_f32", "stage1", "stage2", "stage3", "highres")
 
 
 def kernel_name(wl, shared_routing=False, kv_ratio=1) -> str:
-    return "image" if image_path(wl, shared_routing, kv_ratio) else "attend"
+    if image_path(wl, shared_routing, kv_ratio):
+        return "image"
+    return "small" if small_path(wl, shared_routing, kv_ratio) else "attend"
 
 
 def roofline_entry(wl, attn_ms: float, ab: dict, shared_routing=False, kv_ratio=1) -> dict:
@@ -367,11 +402,11 @@ def measure(wl, args, want_graph: bool = True, keep_inputs: bool = False) -> dic
     h.close()
 
     ms_per_step = gpu_ms / args.steps
-    image = image_path(wl, args.shared_routing, args.kv_downsample) and not args.projections
-    pool_ms = sum(t[0] for t in times) / len(times) if not image else None
+    single = one_kernel(wl, args.shared_routing, args.kv_downsample) and not args.projections
+    pool_ms = sum(t[0] for t in times) / len(times) if not single else None
     # (no routing kernel runs when the attention kernel routes: the interval
     # between its two events is empty)
-    fused_route = route_in_attend(wl, args.shared_routing) or image_path(wl) or \
+    fused_route = route_in_attend(wl, args.shared_routing) or one_kernel(wl) or \
         (route_in_pool(wl, args.shared_routing) and not args.projections)
     route_ms = sum(t[1] for t in times) / len(times) if not fused_route else None
     attn_ms = sum(t[2] for t in times) / len(times)
@@ -390,7 +425,8 @@ def measure(wl, args, want_graph: bool = True, keep_inputs: bool = False) -> dic
         "dtype": wl.dtype,
         "buffer_sets": nsets,
         "kernel_ms": {"region_pool": pool_ms, "route": route_ms,
-                      ("image" if image else "attend"): attn_ms},
+                      (kernel_name(wl, args.shared_routing, args.kv_downsample)
+                       if single else "attend"): attn_ms},
         "wall_s": wall,
         "roofline": roof,
     }

@@ -86,6 +86,24 @@ def test_algorithmic_bytes_whole_image_kernel():
         not bench.route_in_pool(WORKLOADS["stage3"], shared_routing=True)
 
 
+def test_algorithmic_bytes_small_fp32_kernel():
+    """The tiny fp32 problem (49 regions x 2 heads = 98 workgroups) runs the
+    one-launch kernel: q, k, v read once, out written once, the ids exported.
+    Larger fp32 problems, KV downsampling and shared routing keep the
+    pool/routing/attention kernels."""
+    wl = WORKLOADS["tiny_f32"]
+    assert bench.small_path(wl) and bench.kernel_name(wl) == "small"
+    ab = bench.algorithmic_bytes(wl)
+    S = 28 * 28 * 64 * 4
+    assert ab["pool"] == 0 and ab["route"] == 0
+    assert ab["attend"] == 4 * S + 2 * 49 * 4 * 4 + 64 * 26 * 4
+    assert bench.small_lds_bytes(wl) <= 160 * 1024
+    assert not bench.small_path(WORKLOADS["stage1"])
+    assert not bench.small_path(wl.with_(batch=4, channels=128, num_heads=4))  # 784 triples
+    assert not bench.small_path(wl, kv_ratio=2)
+    assert not bench.small_path(wl, shared_routing=True)
+
+
 def test_roofline_bound_per_workload():
     """HBM for the memory-bound shapes, the bf16 MFMA peak for the
     high-resolution attention (1024 keys per query)."""

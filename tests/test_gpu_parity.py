@@ -78,6 +78,14 @@ SMALL = [
     Workload("image_stage3_bias_b3", 3, 14, 14, 256, 8, 7, 16, "bf16", 150, lepe_bias=True),
     Workload("f32_stage2_shape", 4, 28, 28, 128, 4, 7, 4, "f32", 109),
     Workload("f32_ragged_bias", 2, 12, 20, 64, 2, 4, 3, "f32", 110, lepe_bias=True),
+    # the one-launch fp32 kernel (at most 256 (image, head, region) triples):
+    # every region routed (16 scores a lane), 64-token regions (4 lanes a
+    # query, 8 dims a lane), a single region, 4-token regions (32 lanes a
+    # query, the cap) with three heads
+    Workload("small_f32_all_regions", 1, 16, 16, 64, 2, 4, -1, "f32", 161, lepe_bias=True),
+    Workload("small_f32_t64", 1, 24, 24, 32, 1, 3, 1, "f32", 162, lepe_bias=True),
+    Workload("small_f32_one_region", 2, 8, 8, 64, 2, 1, 1, "f32", 163),
+    Workload("small_f32_t4_three_heads", 1, 8, 8, 96, 3, 4, 5, "f32", 164, lepe_bias=True),
 ]
 
 
@@ -88,6 +96,10 @@ def test_small_case(wl):
 
 def test_without_lepe():
     check_parity(Workload("no_lepe", 4, 56, 56, 64, 2, 7, 1, "bf16", 111), lepe=False)
+
+
+def test_without_lepe_small_f32():
+    check_parity(Workload("small_f32_no_lepe", 1, 28, 28, 64, 2, 7, 4, "f32", 165), lepe=False)
 
 
 def test_without_lepe_image_kernel():
@@ -117,9 +129,11 @@ def test_routing_export_optional_and_deterministic():
                                 Workload("all_tied_image_k4", 2, 28, 28, 128, 4, 7, 4, "bf16",
                                          152),
                                 Workload("all_tied_image_k16", 2, 14, 14, 256, 8, 7, 16, "bf16",
-                                         153)],
+                                         153),
+                                Workload("all_tied_small_f32", 1, 28, 28, 64, 2, 7, 4, "f32",
+                                         166)],
                          ids=["attention_kernel_routes", "pool_kernel_routes",
-                              "image_kernel_k4", "image_kernel_k16"])
+                              "image_kernel_k4", "image_kernel_k16", "small_f32_kernel"])
 def test_exact_ties_pick_lower_regions(wl):
     """Every K window identical: all affinities of a row tie exactly, so the
     routing is regions 0..k-1 in order."""

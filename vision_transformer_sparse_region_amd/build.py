@@ -17,8 +17,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG, "libbra.so")
 SOURCES = [os.path.join(CSRC, n) for n in
-           ("bra_pool.hip", "bra_route.hip", "bra_attend.hip", "bra_image.hip", "bra_proj.hip",
-             "bra_noalloc.hip", "bra_api.cpp")]
+           ("bra_pool.hip", "bra_route.hip", "bra_attend.hip", "bra_image.hip", "bra_small.hip",
+             "bra_proj.hip", "bra_noalloc.hip", "bra_api.cpp")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -15,6 +15,7 @@
 #include <vector>
 
 #include "bra_image.h"
+#include "bra_small.h"
 #include "bra_launch.h"
 
 // Device workspace of the forward: the region means (fp64 Q means
@@ -257,6 +258,7 @@ bra_status_t bra_create(const bra_config_t* cfg, bra_handle_t* out) {
     }
     h->device = dev;
     e = bra::prepare_attend(p, bf16);
+    if (e == hipSuccess && bra::small_applies(p, bf16)) e = bra::prepare_small(p);
     if (e != hipSuccess) {
         delete h;
         return fail_hip(e, "bra_create: attention kernel LDS limit");
@@ -361,11 +363,14 @@ static bra_status_t enqueue_forward(const bra::Params& P, bool bf16, const bra_w
         return fail_hip(e, (wh + ": hipEventRecord").c_str());
     // the routing goes to the caller's buffer when one is given
     int32_t* routing = routing_idx ? routing_idx : ws.routing;
+    // small fp32 problems: the whole forward in one kernel, one workgroup per
+    // (image, head, region)
+    const bool small = !x && !ws.kd && bra::small_applies(P, bf16);
     // maps whose head-group K and V fit LDS: the whole forward in one kernel
-    const bool image = bra::image_applies(P, bf16);
+    const bool image = !small && bra::image_applies(P, bf16);
     // small region grids with many heads: means and routing in one kernel
-    const bool pool_route =
-        !x && !image && bra::route_in_pool(bf16, P.shared != 0, P.R, P.heads, P.t);
+    const bool pool_route = !x && !image && !small &&
+                            bra::route_in_pool(bf16, P.shared != 0, P.R, P.heads, P.t);
     if (x) {
         e = bra::launch_proj_qkv(P, x, w_qkv, b_qkv, ws.qs, ws.ks, ws.vs, ws.means, lepe_w,
                                  ws.lepe_table, s);
@@ -376,7 +381,7 @@ static bra_status_t enqueue_forward(const bra::Params& P, bool bf16, const bra_w
     } else if (pool_route) {
         e = bra::launch_pool_route(P, q, k, lepe_w, ws.lepe_table, routing, s);
         if (e != hipSuccess) return fail_hip(e, (wh + ": region-pool and routing launch").c_str());
-    } else if (!image) {
+    } else if (!image && !small) {
         e = bra::launch_pool_qk(P, bf16, q, k, lepe_w, ws.means, ws.lepe_table, s);
         if (e != hipSuccess) return fail_hip(e, (wh + ": region-pool launch").c_str());
     }
@@ -387,7 +392,7 @@ static bra_status_t enqueue_forward(const bra::Params& P, bool bf16, const bra_w
     if (ev && (e = hipEventRecord(ev[1], s)) != hipSuccess)
         return fail_hip(e, (wh + ": hipEventRecord").c_str());
     // small region grids are routed inside the attention kernel
-    if (!image && !bra::route_in_attend(P) && !pool_route) {
+    if (!image && !small && !bra::route_in_attend(P) && !pool_route) {
         e = bra::launch_route(P, bf16, ws.means, routing, s);
         if (e != hipSuccess) return fail_hip(e, (wh + ": routing launch").c_str());
     }
@@ -396,7 +401,12 @@ static bra_status_t enqueue_forward(const bra::Params& P, bool bf16, const bra_w
     // the output projection: in the attention kernel's epilogue, or over y
     // in a kernel of its own (ws.ys is set for the shapes that take that)
     const bool proj_after = w_o && ws.ys;
-    if (image) {
+    if (small) {
+        e = bra::launch_small(P, static_cast<const float*>(q), static_cast<const float*>(k),
+                              static_cast<const float*>(v), lepe_w, lepe_b, routing,
+                              static_cast<float*>(out), s);
+        if (e != hipSuccess) return fail_hip(e, (wh + ": small-problem kernel launch").c_str());
+    } else if (image) {
         e = bra::launch_image(P, q, k, v, lepe_w, lepe_b, routing, false,
                               proj_after ? ws.ys : out, s);
         if (e != hipSuccess) return fail_hip(e, (wh + ": image kernel launch").c_str());
@@ -519,6 +529,7 @@ bra_status_t bra_forward_noalloc(const bra_config_t* cfg, const void* q, const v
     e = bra::scratch_pointer(dev, &base);
     if (e != hipSuccess) return fail_hip(e, "bra_forward_noalloc: hipGetSymbolAddress");
     e = bra::prepare_attend(p, bf16);
+    if (e == hipSuccess && bra::small_applies(p, bf16)) e = bra::prepare_small(p);
     if (e != hipSuccess) return fail_hip(e, "bra_forward_noalloc: attention kernel LDS limit");
     if (bra::image_applies(p, bf16)) {
         e = bra::prepare_image(p);
