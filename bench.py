@@ -28,9 +28,13 @@ METRIC = "BRA fwd tokens/s (bf16) + % HBM roofline / % MFMA peak vs CPU oracle"
 HBM_PEAK_GBS = 8000.0
 MALL_BYTES = 256 << 20
 CSRC = os.path.join(ROOT, "vision_transformer_sparse_region_amd", "csrc")
-# Sources that determine the attention kernel's code (its counters go stale
+# Sources that determine each dominant kernel's code (its counters go stale
 # when any of them changes).
-ATTEND_SOURCES = ("bra_attend.hip", "bra_device.h", "bra_shapes.h", "bra_launch.h")
+KERNEL_SOURCES = {
+    "attend": ("bra_attend.hip", "bra_device.h", "bra_shapes.h", "bra_launch.h"),
+    "image": ("bra_image.hip", "bra_image.h", "bra_device.h", "bra_launch.h"),
+    "small": ("bra_small.hip", "bra_small.h", "bra_device.h", "bra_launch.h"),
+}
 PROFILES = os.path.join(ROOT, "profiles")
 COPY_BYTES = 512 << 20  # size of the calibration copy (read and written once each)
 COPY_REPS = 5
@@ -44,9 +48,9 @@ def _code_only(text: str) -> str:
     return "\n".join(line for line in lines if line)
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(kernel: str = "attend") -> str:
     h = hashlib.sha256()
-    for name in ATTEND_SOURCES:
+    for name in KERNEL_SOURCES[kernel]:
         with open(os.path.join(CSRC, name), encoding="utf-8") as f:
             h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
@@ -198,8 +202,8 @@ def attention_flops(wl, kv_ratio: int = 1) -> float:
         (wl.tokens_per_region // max(kv_ratio, 1) ** 2) * wl.head_dim
 
 
-def traffic_summary_path(workload: str) -> str:
-    return os.path.join(PROFILES, f"attend_{workload}_traffic.md")
+def traffic_summary_path(workload: str, kernel: str = "attend") -> str:
+    return os.path.join(PROFILES, f"{kernel}_{workload}_traffic.md")
 
 
 def read_traffic_record(path: str):
@@ -210,14 +214,15 @@ def read_traffic_record(path: str):
     return json.loads(text[start:text.index("```", start)])
 
 
-def stored_traffic(workload: str):
-    """HBM bytes per launch of the attention kernel from the committed counter
-    summary, or None when absent or taken on a different kernel source."""
-    path = traffic_summary_path(workload)
+def stored_traffic(workload: str, kernel: str = "attend"):
+    """HBM bytes per launch of the workload's dominant kernel from the
+    committed counter summary, or None when absent or taken on a different
+    kernel source."""
+    path = traffic_summary_path(workload, kernel)
     if not os.path.exists(path):
         return None
     rec = read_traffic_record(path)
-    if rec.get("kernel_source_sha256_16") != kernel_source_hash():
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash(kernel):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -479,10 +484,9 @@ def main(argv=None) -> int:
     if args.copy_calibration:
         copy_calibration(dev)
     roof = dict(res["roofline"])
-    if roof["kernel"] == "attend" and not args.projections:
-        roof["traffic"] = stored_traffic(wl.name)
-    else:
-        roof["traffic"] = stored_traffic(f"{wl.name}_{roof['kernel']}")
+    # (counter summaries exist for the plain forward of each workload)
+    plain = not (args.projections or args.shared_routing or args.kv_downsample > 1)
+    roof["traffic"] = stored_traffic(wl.name, roof["kernel"]) if plain else None
     line = {
         "metric": METRIC,
         "value": res["value"],
@@ -522,6 +526,9 @@ def main(argv=None) -> int:
             r = measure(WORKLOADS[name], args, want_graph=False)
             configs[name] = {k: r[k] for k in ("description", "ms_per_step", "value", "unit",
                                               "dtype", "kernel_ms", "roofline")}
+            configs[name]["roofline"] = dict(r["roofline"])
+            configs[name]["roofline"]["traffic"] = \
+                stored_traffic(name, r["roofline"]["kernel"]) if plain else None
         line["configs"] = configs
     if not args.no_cpu_baseline and not args.projections:
         line["cpu_baseline"] = cpu_baseline(wl, res["_host"], res["_last_out"],

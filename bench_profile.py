@@ -1,17 +1,26 @@
 """Summaries of rocprofv3 output for the bench workloads, written to profiles/.
 
-    python bench_profile.py stats   <trace_dir> <workload> "<command>"
-    python bench_profile.py traffic <fetch_dir> <write_dir> <workload> "<fetch cmd>" "<write cmd>"
+    python bench_profile.py stats    <trace_dir> <workload> "<command>"
+    python bench_profile.py traffic  <fetch_dir> <write_dir> <req_dir> <workload>
+                                     "<fetch cmd>" "<write cmd>" "<req cmd>"
+    python bench_profile.py counters <sq1_dir> <sq2_dir> <workload> "<cmd 1>" "<cmd 2>"
 
 `stats` reads <trace_dir>/run_kernel_stats.csv (rocprofv3 --kernel-trace
 --stats -f csv -o run) and writes profiles/kernels_<workload>_stats.md.
 
-`traffic` reads the counter_collection CSVs of two `rocprofv3 --pmc` runs of
-`bench.py --copy-calibration` (FETCH_SIZE, then WRITE_SIZE).  Each counter is
-scaled by what it reads for the calibration copy, whose bytes are known
-(bench.COPY_BYTES read and written), and the per-dispatch averages of the
-attention kernel go to profiles/attend_<workload>_traffic.md together with
-the hash of the kernel sources they were taken on.
+`traffic` reads the counter_collection CSVs of three `rocprofv3 --pmc` runs of
+`bench.py --copy-calibration`: FETCH_SIZE, WRITE_SIZE, and the TCC read
+request counts by size (TCC_EA0_RDREQ{,_32B,_64B,_128B}_sum).  FETCH_SIZE and
+WRITE_SIZE are scaled by what they read for the calibration copy, whose bytes
+are known (bench.COPY_BYTES read and written); the request sizes give the
+read bytes a second way, as a check of that scale on the kernel's own request
+mix.  The per-dispatch figures of the workload's dominant kernel go to
+profiles/<kernel>_<workload>_traffic.md with the hash of its sources.
+
+`counters` reads two SQ counter runs and writes, per kernel, the instruction
+mix per wave, the VALU and MFMA busy fractions, the share of wave time spent
+waiting, and the LDS bank-conflict cycles, to
+profiles/<kernel>_<workload>_counters.md.
 """
 from __future__ import annotations
 
@@ -29,7 +38,9 @@ import bench  # noqa: E402
 KERNELS = {"pool_qk_kernel": "region_pool", "pool_route_kernel": "region_pool_and_route",
            "proj_qkv_kernel": "qkv_projection",
            "proj_out_kernel": "output_projection", "route_small_kernel": "route",
-           "route_large_kernel": "route", "attend_kernel": "attend"}
+           "route_large_kernel": "route", "attend_kernel": "attend", "image_kernel": "image",
+           "small_kernel": "small", "kv_pool_kernel": "kv_pool",
+           "lepe_table_kernel": "lepe_table"}
 COPY_KERNELS = ("__amd_rocclr_copyBuffer",)
 
 
@@ -82,52 +93,141 @@ def counter_means(run_dir: str, counter: str):
     return {k: sum(v) / len(v) for k, v in vals.items()}, {k: len(v) for k, v in vals.items()}
 
 
-def write_traffic(fetch_dir: str, write_dir: str, workload: str, fetch_cmd: str,
-                  write_cmd: str) -> str:
+def write_traffic(fetch_dir: str, write_dir: str, req_dir: str, workload: str, fetch_cmd: str,
+                  write_cmd: str, req_cmd: str) -> str:
+    from vision_transformer_sparse_region_amd.workloads import WORKLOADS
+    wl = WORKLOADS[workload]
+    kernel = bench.kernel_name(wl)
     fetch, nf = counter_means(fetch_dir, "FETCH_SIZE")
     write, nw = counter_means(write_dir, "WRITE_SIZE")
     if "copy" not in fetch or "copy" not in write:
         raise SystemExit("the calibration copy kernel is missing from the counter runs")
     f_fetch = bench.COPY_BYTES / (fetch["copy"] * 1024)
     f_write = bench.COPY_BYTES / (write["copy"] * 1024)
-    from vision_transformer_sparse_region_amd.workloads import WORKLOADS
-    wl = WORKLOADS[workload]
+    # read requests by size: bytes = 32 n32 + 64 n64 + 128 n128
+    req = {c: counter_means(req_dir, f"TCC_EA0_RDREQ{c}_sum")[0]
+           for c in ("", "_32B", "_64B", "_128B")}
+
+    def req_bytes(k):
+        return 32 * req["_32B"].get(k, 0) + 64 * req["_64B"].get(k, 0) + \
+            128 * req["_128B"].get(k, 0)
+    f_req = bench.COPY_BYTES / req_bytes("copy") if req_bytes("copy") else None
     alg = bench.algorithmic_bytes(wl)
     per = {}
-    for k in ("region_pool", "route", "attend"):
-        if k in fetch and k in write:
-            rd, wr = fetch[k] * 1024 * f_fetch, write[k] * 1024 * f_write
-            per[k] = {"fetch_kib_raw": fetch[k], "write_kib_raw": write[k],
-                      "read_bytes": rd, "write_bytes": wr, "hbm_bytes": rd + wr,
-                      "dispatches": min(nf.get(k, 0), nw.get(k, 0))}
+    for k in fetch:
+        if k == "copy" or k not in write:
+            continue
+        rd, wr = fetch[k] * 1024 * f_fetch, write[k] * 1024 * f_write
+        per[k] = {"fetch_kib_raw": fetch[k], "write_kib_raw": write[k],
+                  "read_bytes": rd, "write_bytes": wr, "hbm_bytes": rd + wr,
+                  "rdreq": req[""].get(k), "rdreq_32b": req["_32B"].get(k),
+                  "rdreq_64b": req["_64B"].get(k), "rdreq_128b": req["_128B"].get(k),
+                  "read_bytes_by_request_size": req_bytes(k) * f_req if f_req else None,
+                  "dispatches": min(nf.get(k, 0), nw.get(k, 0))}
     rec = {
         "workload": workload,
-        "kernel": "attend",
-        "kernel_source_sha256_16": bench.kernel_source_hash(),
-        "hbm_bytes_per_launch": per["attend"]["hbm_bytes"],
+        "kernel": kernel,
+        "kernel_source_sha256_16": bench.kernel_source_hash(kernel),
+        "hbm_bytes_per_launch": per[kernel]["hbm_bytes"],
         "algorithmic_bytes_per_launch": alg["attend"],
         "copy_bytes": bench.COPY_BYTES,
         "copy_fetch_kib_raw": fetch["copy"], "copy_write_kib_raw": write["copy"],
-        "fetch_scale": f_fetch, "write_scale": f_write,
+        "copy_rdreq": {c or "all": req[c].get("copy") for c in req},
+        "fetch_scale": f_fetch, "write_scale": f_write, "request_scale": f_req,
         "kernels": per,
     }
-    lines = [f"# HBM traffic per launch, workload `{workload}`", "",
-             "FETCH_SIZE and WRITE_SIZE (KiB per dispatch) from two rocprofv3 counter runs, each",
+    lines = [f"# HBM traffic per launch, workload `{workload}`, kernel `{kernel}`", "",
+             "FETCH_SIZE and WRITE_SIZE (KiB per dispatch) from rocprofv3 counter runs, each",
              f"scaled by the same counter's reading for a {bench.COPY_BYTES >> 20} MiB device copy "
-             "(bytes known: read once, written once).", "",
-             "Commands (from the repository root):", "", "```", fetch_cmd, write_cmd, "```", "",
-             "| kernel | FETCH KiB raw | WRITE KiB raw | read MB | write MB | total MB |",
-             "|---|---|---|---|---|---|"]
+             "(bytes known: read once, written once).  The read bytes again from the TCC read",
+             "requests by size (32, 64, 128 bytes), scaled the same way, check that scale on each",
+             "kernel's own request mix.", "",
+             "Commands (from the repository root):", "", "```", fetch_cmd, write_cmd, req_cmd,
+             "```", "",
+             "| kernel | FETCH KiB raw | WRITE KiB raw | read MB | write MB | total MB | "
+             "read MB by request size |",
+             "|---|---|---|---|---|---|---|"]
     for k, v in per.items():
+        rq = v["read_bytes_by_request_size"]
         lines.append(f"| {k} | {v['fetch_kib_raw']:.0f} | {v['write_kib_raw']:.0f} | "
                      f"{v['read_bytes'] / 1e6:.2f} | {v['write_bytes'] / 1e6:.2f} | "
-                     f"{v['hbm_bytes'] / 1e6:.2f} |")
+                     f"{v['hbm_bytes'] / 1e6:.2f} | "
+                     f"{rq / 1e6 if rq is not None else float('nan'):.2f} |")
     lines += ["", f"Copy calibration: FETCH {fetch['copy']:.0f} KiB, WRITE {write['copy']:.0f} KiB "
               f"for {bench.COPY_BYTES >> 10} KiB each way; scale {f_fetch:.4f} (fetch), "
-              f"{f_write:.4f} (write).", "",
-              f"Algorithmic bytes of the attention kernel per launch: {alg['attend'] / 1e6:.2f} MB.",
+              f"{f_write:.4f} (write), {f_req if f_req else float('nan'):.4f} (read requests).",
+              "", f"Algorithmic bytes of `{kernel}` per launch: {alg['attend'] / 1e6:.2f} MB.",
               "", "```json", json.dumps(rec, indent=1), "```", ""]
-    out = bench.traffic_summary_path(workload)
+    out = bench.traffic_summary_path(workload, kernel)
+    os.makedirs(bench.PROFILES, exist_ok=True)
+    with open(out, "w") as f:
+        f.write("\n".join(lines))
+    return out
+
+
+SQ_COUNTERS = ("SQ_WAVES", "SQ_BUSY_CYCLES", "SQ_WAVE_CYCLES", "SQ_INSTS_VALU", "SQ_INSTS_MFMA",
+               "SQ_ACTIVE_INST_VALU", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_WAIT_INST_ANY",
+               "SQ_INSTS_LDS", "SQ_LDS_BANK_CONFLICT", "SQ_ACTIVE_INST_LDS", "SQ_INSTS_VMEM_RD",
+               "SQ_WAIT_ANY", "SQ_ACTIVE_INST_ANY", "SQ_INSTS_SALU", "SQ_INSTS_VALU_TRANS_F32",
+               "GRBM_GUI_ACTIVE")
+CUS, SIMDS, XCDS = 256, 1024, 8
+
+
+def write_counters(sq1_dir: str, sq2_dir: str, workload: str, cmd1: str, cmd2: str) -> str:
+    from vision_transformer_sparse_region_amd.workloads import WORKLOADS
+    wl = WORKLOADS[workload]
+    kernel = bench.kernel_name(wl)
+    vals = defaultdict(dict)
+    for d in (sq1_dir, sq2_dir):
+        for c in SQ_COUNTERS:
+            means, _ = counter_means(d, c)
+            for k, v in means.items():
+                if k != "copy":
+                    vals[k].setdefault(c, v)
+    rows = []
+    for k, c in vals.items():
+        waves = c.get("SQ_WAVES") or 1.0
+        # GRBM_GUI_ACTIVE is summed over the XCDs: per XCD, the kernel's cycles
+        cyc = (c.get("GRBM_GUI_ACTIVE") or 0.0) / XCDS
+        rows.append({
+            "kernel": k, "waves": waves,
+            "valu_per_wave": c.get("SQ_INSTS_VALU", 0) / waves,
+            "mfma_per_wave": c.get("SQ_INSTS_MFMA", 0) / waves,
+            "lds_per_wave": c.get("SQ_INSTS_LDS", 0) / waves,
+            "vmem_rd_per_wave": c.get("SQ_INSTS_VMEM_RD", 0) / waves,
+            "trans_per_wave": c.get("SQ_INSTS_VALU_TRANS_F32", 0) / waves,
+            "valu_busy_pct": 100 * c.get("SQ_ACTIVE_INST_VALU", 0) / (CUS * cyc) if cyc else None,
+            "mfma_busy_pct": 100 * c.get("SQ_VALU_MFMA_BUSY_CYCLES", 0) / (SIMDS * cyc)
+            if cyc else None,
+            "wait_inst_share": c.get("SQ_WAIT_INST_ANY", 0) / c["SQ_WAVE_CYCLES"]
+            if c.get("SQ_WAVE_CYCLES") else None,
+            "lds_conflict_per_active": c.get("SQ_LDS_BANK_CONFLICT", 0) / c["SQ_ACTIVE_INST_LDS"]
+            if c.get("SQ_ACTIVE_INST_LDS") else None,
+            "gui_active_cycles_per_xcd": cyc,
+            "raw": c,
+        })
+    fmt = lambda x, f="{:.1f}": "-" if x is None else f.format(x)
+    lines = [f"# SQ counters per dispatch, workload `{workload}` (dominant kernel `{kernel}`)", "",
+             "Two rocprofv3 counter runs (8 SQ counters and GRBM_GUI_ACTIVE each), averaged per",
+             "dispatch.  VALU busy = SQ_ACTIVE_INST_VALU / (CUs x GRBM cycles per XCD) and MFMA",
+             "busy = SQ_VALU_MFMA_BUSY_CYCLES / (SIMDs x GRBM cycles per XCD), rocprofv3's VALUBusy",
+             "and MfmaUtil; wait share = SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES (waves stalled on a",
+             "dependency); LDS conflict = SQ_LDS_BANK_CONFLICT / SQ_ACTIVE_INST_LDS.", "",
+             "Commands (from the repository root):", "", "```", cmd1, cmd2, "```", "",
+             "| kernel | waves | VALU/wave | MFMA/wave | LDS/wave | VMEM rd/wave | exp/wave | "
+             "VALU busy % | MFMA busy % | wait share | LDS conflict/active |",
+             "|---|---|---|---|---|---|---|---|---|---|---|"]
+    for r in rows:
+        lines.append(f"| {r['kernel']} | {r['waves']:.0f} | {r['valu_per_wave']:.0f} | "
+                     f"{r['mfma_per_wave']:.0f} | {r['lds_per_wave']:.0f} | "
+                     f"{r['vmem_rd_per_wave']:.0f} | {r['trans_per_wave']:.0f} | "
+                     f"{fmt(r['valu_busy_pct'])} | {fmt(r['mfma_busy_pct'])} | "
+                     f"{fmt(r['wait_inst_share'], '{:.2f}')} | "
+                     f"{fmt(r['lds_conflict_per_active'], '{:.2f}')} |")
+    lines += ["", "```json", json.dumps({"workload": workload, "kernel": kernel,
+                                         "kernel_source_sha256_16": bench.kernel_source_hash(kernel),
+                                         "kernels": rows}, indent=1), "```", ""]
+    out = os.path.join(bench.PROFILES, f"{kernel}_{workload}_counters.md")
     os.makedirs(bench.PROFILES, exist_ok=True)
     with open(out, "w") as f:
         f.write("\n".join(lines))
@@ -137,8 +237,10 @@ def write_traffic(fetch_dir: str, write_dir: str, workload: str, fetch_cmd: str,
 def main(argv):
     if len(argv) >= 4 and argv[0] == "stats":
         print(write_stats(argv[1], argv[2], argv[3]))
-    elif len(argv) >= 6 and argv[0] == "traffic":
-        print(write_traffic(argv[1], argv[2], argv[3], argv[4], argv[5]))
+    elif len(argv) >= 8 and argv[0] == "traffic":
+        print(write_traffic(*argv[1:8]))
+    elif len(argv) >= 6 and argv[0] == "counters":
+        print(write_counters(*argv[1:6]))
     else:
         print(__doc__, file=sys.stderr)
         return 2

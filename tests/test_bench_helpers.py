@@ -1,5 +1,6 @@
 """Host-side pieces of bench.py: the byte counts the roofline divides by, the
 committed traffic summary it reads, and the refusal of more than one GPU."""
+import glob
 import os
 
 import bench
@@ -123,17 +124,17 @@ def test_attention_flops_highres():
     assert bench.attention_flops(wl) == 4.0 * 8 * 128 * 128 * 2 * 16 * 64 * 32
 
 
-def test_traffic_summary_parses_and_matches_sources():
-    path = bench.traffic_summary_path("stage1")
-    if not os.path.exists(path):
-        return
-    rec = bench.read_traffic_record(path)
-    assert rec["workload"] == "stage1" and rec["kernel"] == "attend"
-    assert rec["hbm_bytes_per_launch"] > 0
-    # the stored figure is used only while the kernel sources are unchanged
-    expect = rec["hbm_bytes_per_launch"] if rec["kernel_source_sha256_16"] == \
-        bench.kernel_source_hash() else None
-    assert bench.stored_traffic("stage1") == expect
+def test_traffic_summaries_parse_and_match_sources():
+    """Every committed traffic summary names its workload and kernel, and its
+    figure is used only while that kernel's sources are unchanged."""
+    for path in glob.glob(os.path.join(bench.PROFILES, "*_traffic.md")):
+        rec = bench.read_traffic_record(path)
+        kernel, wl = rec["kernel"], rec["workload"]
+        assert os.path.basename(path) == f"{kernel}_{wl}_traffic.md"
+        assert rec["hbm_bytes_per_launch"] > 0
+        expect = rec["hbm_bytes_per_launch"] if rec["kernel_source_sha256_16"] == \
+            bench.kernel_source_hash(kernel) else None
+        assert bench.stored_traffic(wl, kernel) == expect
 
 
 def test_source_hash_ignores_comments_only():

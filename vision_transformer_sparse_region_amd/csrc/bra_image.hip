@@ -66,7 +66,6 @@ struct ImgShape {
     static constexpr int PASSES = HG * PPH;
     static constexpr int NT = (R + 15) / 16;      // 16-region tiles of the affinity
     static constexpr int ROWS = HG * R;
-    static constexpr int KMI = (HG * R * kHeadDim + kImgThreads - 1) / kImgThreads;
     static constexpr int RI = (HG * R * KTOP + kImgThreads - 1) / kImgThreads;
     static constexpr int NCH = 2 * NPAIR;         // 32-key chunks (pairs of)
     static constexpr int GXN = PW / 4;            // 4-cell column groups of a plane row
@@ -220,26 +219,43 @@ __device__ __forceinline__ void put_route(const ImgLds<S>& L, int hl, int r, int
     L.sOffV[e] = L.sRegV[id];
 }
 
-// Region means of the staged map `src` ([H][RS]): item (head hl, region s,
-// dim d), the t values of the region's slots added in slot order, as the
-// oracle does.  Returns the max |mean| of the thread's items.
+// Region means of the staged K and Q maps ([H][RS] each), both in one pass:
+// item (tensor, head hl, region s, dims 8o .. 8o + 7) reads the region's
+// slots as 16-byte pieces and adds each dim's values in slot order, as the
+// oracle does.  Returns the max |K mean| of the thread's items.
 template <typename S>
-__device__ __forceinline__ float region_means(const uint16_t* src, double* dst) {
+__device__ __forceinline__ float region_means_kq(const uint16_t* sK, const uint16_t* sQ,
+                                                 double* sKbar, double* sQbar) {
+    constexpr int NHR = S::HG * S::R, NI = 2 * NHR * 4;
     float mx = 0.f;
 #pragma unroll
-    for (int u = 0; u < S::KMI; ++u) {
+    for (int u = 0; u < (NI + kImgThreads - 1) / kImgThreads; ++u) {
         const int item = threadIdx.x + u * kImgThreads;
-        if (item < S::HG * S::R * kHeadDim) {
-            const int d = item & (kHeadDim - 1), hs = item >> 5;
+        if (item < NI) {
+            const int o = item & 3, rest = item >> 2;
+            const int tensor = rest >= NHR ? 1 : 0, hs = rest - tensor * NHR;
             const int hl = hs / S::R, s = hs - hl * S::R;
-            const uint16_t* p = src + hl * kHeadDim + d;
-            double acc = 0.0;
+            const uint16_t* src = (tensor ? sQ : sK) + hl * kHeadDim + 8 * o;
+            double acc[8] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-            for (int uu = 0; uu < S::T; ++uu)
-                acc += static_cast<double>(bf16_to_f32(p[region_kofs<S>(s, uu)]));
-            const double m = mean_of(acc, S::T);
-            dst[(hl * S::R + s) * S::QS + d] = m;
-            mx = fmaxf(mx, static_cast<float>(fabs(m)));
+            for (int uu = 0; uu < S::T; ++uu) {
+                const uint4 x = *reinterpret_cast<const uint4*>(src + region_kofs<S>(s, uu));
+                acc[0] += bf16lo(x.x);
+                acc[1] += bf16hi(x.x);
+                acc[2] += bf16lo(x.y);
+                acc[3] += bf16hi(x.y);
+                acc[4] += bf16lo(x.z);
+                acc[5] += bf16hi(x.z);
+                acc[6] += bf16lo(x.w);
+                acc[7] += bf16hi(x.w);
+            }
+            double* dst = (tensor ? sQbar : sKbar) + (hl * S::R + s) * S::QS + 8 * o;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const double m = mean_of(acc[e], S::T);
+                dst[e] = m;
+                if (!tensor) mx = fmaxf(mx, static_cast<float>(fabs(m)));
+            }
         }
     }
     return mx;
@@ -514,8 +530,7 @@ __device__ __forceinline__ void image_body(
 
     // 2. the region means (or the caller's routing)
     if constexpr (!ROUTED) {
-        const float kmx = region_means<S>(L.sK, L.sKbar);
-        region_means<S>(L.sQs, L.sQbar);
+        const float kmx = region_means_kq<S>(L.sK, L.sQs, L.sKbar, L.sQbar);
         // the float bits of a nonnegative value order like the value
         // (rounded to nearest, plus one ulp; the bound it feeds carries a
         // factor 4); one max over all items of the wave, for every head
