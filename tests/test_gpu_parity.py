@@ -79,13 +79,15 @@ SMALL = [
     Workload("f32_stage2_shape", 4, 28, 28, 128, 4, 7, 4, "f32", 109),
     Workload("f32_ragged_bias", 2, 12, 20, 64, 2, 4, 3, "f32", 110, lepe_bias=True),
     # the one-launch fp32 kernel (at most 256 (image, head, region) triples):
-    # every region routed (16 scores a lane), 64-token regions (4 lanes a
-    # query, 8 dims a lane), a single region, 4-token regions (32 lanes a
+    # every region routed (8 scores a lane), 64-token regions (8 lanes a
+    # query, 4 dims a lane), a single region, 4-token regions (32 lanes a
     # query, the cap) with three heads
     Workload("small_f32_all_regions", 1, 16, 16, 64, 2, 4, -1, "f32", 161, lepe_bias=True),
     Workload("small_f32_t64", 1, 24, 24, 32, 1, 3, 1, "f32", 162, lepe_bias=True),
     Workload("small_f32_one_region", 2, 8, 8, 64, 2, 1, 1, "f32", 163),
     Workload("small_f32_t4_three_heads", 1, 8, 8, 96, 3, 4, 5, "f32", 164, lepe_bias=True),
+    # 5 x 5 windows: 16 lanes per query
+    Workload("small_f32_t25", 1, 20, 20, 64, 2, 4, 3, "f32", 167, lepe_bias=True),
 ]
 
 

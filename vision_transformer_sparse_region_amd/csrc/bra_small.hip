@@ -17,7 +17,7 @@
 //   4. gathers the routed regions' V rows by LDS DMA -- their K rows are
 //      already staged -- and, while they land, forms the scores and the
 //      softmax (fp32, one query per group of L lanes, L a compile-time
-//      4, 8, 16 or 32)                                   [P3 §2.2; P5 §五 ⑤-⑥]
+//      8, 16 or 32)                                   [P3 §2.2; P5 §五 ⑤-⑥]
 //   5. out = P V + dwconv5x5(V) + bias, in fp32, stored as the map's rows
 //                                             [P5 §五 ⑦-⑧, lepe; P2 §2.2]
 // Staged rows are 8 pieces of 16 bytes (32 fp32 dims); piece c of row i sits
@@ -71,6 +71,40 @@ __device__ __forceinline__ void dims(const float* base, int i, int d0, float (&x
     } else {
         x[0] = elem(base, i, d0);
     }
+}
+
+// Max and sum over the L consecutive lanes of one query (L = 8, 16 or 32):
+// DPP within rows of 16 (lane ^ 1, ^ 2, the half-row and row mirrors), the
+// row swap for lanes 16 apart.  Each step pairs lanes symmetrically, so every
+// lane of the group ends with the same value; no step goes through the LDS
+// crossbar.
+template <int L>
+__device__ __forceinline__ float group_max(float x) {
+    static_assert(L == 8 || L == 16 || L == 32, "8, 16 or 32 lanes a query");
+    x = fmaxf(x, dpp_f32<0xB1>(x));
+    x = fmaxf(x, dpp_f32<0x4E>(x));
+    x = fmaxf(x, dpp_f32<0x141>(x));
+    if constexpr (L >= 16) x = fmaxf(x, dpp_f32<0x140>(x));
+    if constexpr (L == 32) {
+        const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x),
+                                                        false, false);
+        x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    }
+    return x;
+}
+template <int L>
+__device__ __forceinline__ float group_sum(float x) {
+    static_assert(L == 8 || L == 16 || L == 32, "8, 16 or 32 lanes a query");
+    x += dpp_f32<0xB1>(x);
+    x += dpp_f32<0x4E>(x);
+    x += dpp_f32<0x141>(x);
+    if constexpr (L >= 16) x += dpp_f32<0x140>(x);
+    if constexpr (L == 32) {
+        const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x),
+                                                        false, false);
+        x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    }
+    return x;
 }
 
 // floor(a / b) for 0 <= a < 2^12, 1 <= b <= 64: a + 1/2 stays at least
@@ -270,8 +304,7 @@ __device__ __forceinline__ void small_body(const float* __restrict__ q,
             prow[kk] = sc;
             mx = fmaxf(mx, sc);
         }
-#pragma unroll
-        for (int o = 1; o < L; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+        mx = group_max<L>(mx);
         float sum = 0.f;
 #pragma unroll 4
         for (int kk = li; kk < nk; kk += L) {
@@ -279,8 +312,7 @@ __device__ __forceinline__ void small_body(const float* __restrict__ q,
             prow[kk] = e;
             sum += e;
         }
-#pragma unroll
-        for (int o = 1; o < L; o <<= 1) sum += __shfl_xor(sum, o);
+        sum = group_sum<L>(sum);
         inv = 1.f / sum;
     }
     __builtin_amdgcn_s_waitcnt(0);  // this wave's V DMA has landed
@@ -292,7 +324,7 @@ __device__ __forceinline__ void small_body(const float* __restrict__ q,
         float o[DPL];
 #pragma unroll
         for (int e = 0; e < DPL; ++e) o[e] = 0.f;
-#pragma unroll 8
+#pragma unroll 16
         for (int kk = 0; kk < nk; ++kk) {
             const float pk = prow[kk];
             float x[DPL];
@@ -368,8 +400,7 @@ int small_lds_bytes(const Params& p) { return small_geo(p).lds; }
 
 hipError_t prepare_small(const Params& p) {
     if (small_geo(p).lds <= kDefaultLdsBytes) return hipSuccess;
-    for (const void* f : {small::kernel_of<4>(), small::kernel_of<8>(), small::kernel_of<16>(),
-                          small::kernel_of<32>()}) {
+    for (const void* f : {small::kernel_of<8>(), small::kernel_of<16>(), small::kernel_of<32>()}) {
         const hipError_t e =
             hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLdsBytes);
         if (e != hipSuccess) return e;
@@ -390,7 +421,6 @@ hipError_t launch_small(const Params& p, const float* q, const float* k, const f
                            lepe_w, lepe_b, routing, out, pp);                                  \
         break;
     switch (G.L) {
-        BRA_SMALL_L(4)
         BRA_SMALL_L(8)
         BRA_SMALL_L(16)
         BRA_SMALL_L(32)
