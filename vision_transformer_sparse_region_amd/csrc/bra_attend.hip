@@ -501,12 +501,15 @@ __device__ __forceinline__ void lepe_phase(const Params& p, const T* sVh, float*
 // products give all 25 taps.  Lane l is block l/4; it holds A row l%4 (four
 // consecutive halo columns of one channel: the halo is staged channel-planar)
 // and B / D column l%4.  The Toeplitz B operands depend only on the channel
-// and the lane's column: the pool kernel writes them once per forward to a
-// small table (lepe_toeplitz_entry).  Weights enter the product as bf16 (the
-// accumulation is fp32).
+// and the lane's column n.  The pool kernel writes each channel's 25 weights
+// once per forward as a 64-byte row of bf16 (lepe_table_entry); the four
+// lanes of a channel load a quarter of the row each and share the quarters by
+// DPP, and each lane builds its ten operands: for tap row i, the eight bf16
+// [0]*n, w[i][0..4], 0.. make the B operands of ks = 0 and 1.  Weights enter
+// the product as bf16 (the accumulation is fp32).
 
 // The Toeplitz B operands and the bias of this lane's channel in each of the
-// wave's channel groups, loaded from the table the pool kernel built.
+// wave's channel groups, built from the weight table the pool kernel wrote.
 template <int HS, int WS, int HEADS>
 struct LepeOperands {
     uint4 tb[LepeMfmaShape<HS, WS, HEADS>::GPW][5];  // 10 x 8 bytes per group
@@ -521,12 +524,54 @@ __device__ __forceinline__ void lepe_mfma_load(const uint2* __restrict__ table,
                                                LepeOperands<HS, WS, HEADS>& o) {
     using S = LepeMfmaShape<HS, WS, HEADS>;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int n = lane & 3;
+    // the shift of a lane's operands: 16 bits when n is odd, one word when n >= 2
+    const bool half = (n & 1) != 0, word = n >= 2;
 #pragma unroll
     for (int g = 0; g < S::GPW; ++g) {
         const int cg = min(w + kWaves * g, S::NG - 1);
-        const uint4* src = reinterpret_cast<const uint4*>(table + (cg * 64 + lane) * 10);
+        // taps 8n .. 8n + 7 of channel 16 cg + lane / 4
+        const uint4 x4 =
+            *reinterpret_cast<const uint4*>(table + (16 * cg + (lane >> 2)) * 8 + 2 * n);
+        const uint32_t x[4] = {x4.x, x4.y, x4.z, x4.w};
+        // word m of the row (taps 2m, 2m + 1), from lane m / 4 of the quad
+        auto row_word = [&](int m) -> uint32_t {
+            const int q = m >> 2, e = m & 3;
+            const int v = static_cast<int>(x[e]);
+            const int r = q == 0 ? __builtin_amdgcn_mov_dpp(v, 0x00, 0xf, 0xf, false)
+                        : q == 1 ? __builtin_amdgcn_mov_dpp(v, 0x55, 0xf, 0xf, false)
+                        : q == 2 ? __builtin_amdgcn_mov_dpp(v, 0xAA, 0xf, 0xf, false)
+                                 : __builtin_amdgcn_mov_dpp(v, 0xFF, 0xf, 0xf, false);
+            return static_cast<uint32_t>(r);
+        };
 #pragma unroll
-        for (int e = 0; e < 5; ++e) o.tb[g][e] = src[e];
+        for (int i = 0; i < 5; ++i) {
+            // z = w[i][0..4], 0, 0, 0 as four words (taps 5i .. 5i + 4 start on
+            // a half word when i is odd)
+            uint32_t z[4];
+            if ((5 * i) % 2 == 0) {
+                const int m = 5 * i / 2;
+                z[0] = row_word(m);
+                z[1] = row_word(m + 1);
+                z[2] = row_word(m + 2) & 0xffffu;
+            } else {
+                const int m = (5 * i - 1) / 2;
+                const uint32_t a = row_word(m), b = row_word(m + 1), c = row_word(m + 2);
+                z[0] = __builtin_amdgcn_alignbit(b, a, 16);
+                z[1] = __builtin_amdgcn_alignbit(c, b, 16);
+                z[2] = c >> 16;
+            }
+            z[3] = 0u;
+            // shifted left by 16 n bits: [0]*n, w[i][0..4], 0 ..
+            uint32_t e[4];
+            e[0] = half ? z[0] << 16 : z[0];
+#pragma unroll
+            for (int k = 1; k < 4; ++k)
+                e[k] = half ? __builtin_amdgcn_alignbit(z[k], z[k - 1], 16) : z[k];
+            const uint32_t o0 = word ? 0u : e[0], o1 = word ? e[0] : e[1];
+            const uint32_t o2 = word ? e[1] : e[2], o3 = word ? e[2] : e[3];
+            o.tb[g][i] = uint4{o0, o1, o2, o3};
+        }
         o.bias[g] = bias[16 * cg + (lane >> 2)];
     }
 }
@@ -1149,7 +1194,7 @@ bool plan(Params& p, int B, int H, int W, int C, int heads, int n_win, int k, fl
         p.off_w = -1;
     }
     p.lds_bytes = static_cast<int>(off);
-    p.table_items = p.lepe_mfma ? C * 40 : 0;
+    p.table_items = p.lepe_mfma ? C * 8 : 0;
     p.qmean_attend = qmean_in_attend(bf16, route_in_attend(p), p.t, heads) ? 1 : 0;
     p.kmean32 = route_in_attend(p) && kmean32_pays(p.t) ? 1 : 0;
     {

@@ -221,27 +221,20 @@ __device__ __forceinline__ Params fold_geometry(const Params& in) {
     return p;
 }
 
-// One entry of the Toeplitz operand table of the MFMA LePE (see
-// lepe_mfma_compute): entry it = ((cg * 64 + lane) * 5 + i) * 2 + ks holds the
-// B operand of lane `lane` for channel group cg, tap row i and column step ks:
-// four bf16 w[c][i][4ks + kk - n] (zero outside 0..4), c = 16cg + lane/4,
-// n = lane % 4.
-__device__ __forceinline__ uint2 lepe_toeplitz_entry(const float* __restrict__ lepe_w, int it) {
-    const int ks = it & 1, i = (it >> 1) % 5, lane_cg = it / 10;
-    const int lane = lane_cg & 63, cg = lane_cg >> 6;
-    const int c = 16 * cg + (lane >> 2), n = lane & 3;
+// One entry of the weight table of the MFMA LePE (see lepe_mfma_load): row c
+// of the table is channel c's 25 weights w[c][i][j] in tap order (5i + j) as
+// bf16, then 7 zeros -- 64 bytes, eight 8-byte entries.  Entry it = 8c + q
+// holds taps 4q .. 4q + 3 of channel c.
+__device__ __forceinline__ uint2 lepe_table_entry(const float* __restrict__ lepe_w, int it) {
+    const int c = it >> 3, q = it & 7;
     // the four loads go out together (clamped tap, always in the row), the
-    // taps outside the kernel are zeroed afterwards
+    // taps past the 25th are zeroed afterwards
     float wv[4];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-        wv[kk] = lepe_w[c * 25 + i * 5 + min(max(4 * ks + kk - n, 0), 4)];
+    for (int kk = 0; kk < 4; ++kk) wv[kk] = lepe_w[c * 25 + min(4 * q + kk, 24)];
     uint32_t h[4];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-        const int j = 4 * ks + kk - n;
-        h[kk] = (j >= 0 && j <= 4) ? f32_to_bf16(wv[kk]) : 0u;
-    }
+    for (int kk = 0; kk < 4; ++kk) h[kk] = 4 * q + kk < 25 ? f32_to_bf16(wv[kk]) : 0u;
     return uint2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
 }
 

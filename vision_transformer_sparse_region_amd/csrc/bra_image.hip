@@ -465,7 +465,7 @@ __device__ __forceinline__ void image_body(
             if (tid + u * kImgThreads < S::NVT && x == xc) vvalid |= 1u << (4 * u + jj);
         }
     }
-    // the four taps of each Toeplitz entry (see lepe_toeplitz_entry), clamped
+    // the four taps of each Toeplitz entry (w[c][i][4ks + kk - n]), clamped
     // into the row; the taps outside the kernel are zeroed when it is built
     float wv[S::TE][4];
     float bias = 0.f;

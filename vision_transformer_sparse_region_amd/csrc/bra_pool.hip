@@ -67,7 +67,7 @@ __global__ __launch_bounds__(kThreads) void pool_qk_kernel(const T* __restrict__
     if (static_cast<int>(blockIdx.x) >= p.pool_blocks) {
         // Trailing workgroups: the Toeplitz LePE operands of the MFMA LePE.
         const int it = (blockIdx.x - p.pool_blocks) * kThreads + tid;
-        if (it < p.table_items) lepe_table[it] = lepe_toeplitz_entry(lepe_w, it);
+        if (it < p.table_items) lepe_table[it] = lepe_table_entry(lepe_w, it);
         return;
     }
     const int nvec = p.C / VEC;
@@ -173,7 +173,7 @@ __global__ __launch_bounds__(kThreads) void lepe_table_kernel(const float* __res
                                                               uint2* __restrict__ lepe_table,
                                                               int items) {
     const int it = blockIdx.x * kThreads + threadIdx.x;
-    if (it < items) lepe_table[it] = lepe_toeplitz_entry(lepe_w, it);
+    if (it < items) lepe_table[it] = lepe_table_entry(lepe_w, it);
 }
 }  // namespace
 

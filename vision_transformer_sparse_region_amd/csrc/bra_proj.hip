@@ -185,7 +185,7 @@ __global__ __launch_bounds__(kThreads) void proj_qkv_kernel(
     if (static_cast<int>(blockIdx.x) >= tasks) {
         // trailing workgroups: the Toeplitz operands of the MFMA LePE
         const int it = (blockIdx.x - tasks) * kThreads + tid;
-        if (it < p.table_items) lepe_table[it] = lepe_toeplitz_entry(lepe_w, it);
+        if (it < p.table_items) lepe_table[it] = lepe_table_entry(lepe_w, it);
         return;
     }
     uint16_t* sX = reinterpret_cast<uint16_t*>(smem);  // stage_pieces(C) rounds of slots

@@ -311,7 +311,7 @@ __global__ __launch_bounds__(kThreads) void pool_route_kernel(
     if (static_cast<int>(blockIdx.x) >= tasks) {
         // trailing workgroups: the Toeplitz operands of the MFMA LePE
         const int it = (blockIdx.x - tasks) * kThreads + tid;
-        if (it < p.table_items) lepe_table[it] = lepe_toeplitz_entry(lepe_w, it);
+        if (it < p.table_items) lepe_table[it] = lepe_table_entry(lepe_w, it);
         return;
     }
     const int krounds = pr_k_rounds(R, t), qrounds = pr_q_rounds(t);
