@@ -517,7 +517,8 @@ struct LepeOperands {
 };
 
 // `bias` is never NULL (a zero vector stands in for a missing bias); groups
-// past the last one re-read the last group (they are never used).
+// past the last one re-read the last group (they are never used).  Every lane
+// of the wave runs this (the quads exchange their quarters by DPP).
 template <int HS, int WS, int HEADS>
 __device__ __forceinline__ void lepe_mfma_load(const uint2* __restrict__ table,
                                                const float* __restrict__ bias,
