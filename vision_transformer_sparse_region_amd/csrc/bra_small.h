@@ -7,15 +7,14 @@
 
 namespace bra {
 
-constexpr int kSmallThreads = 512;  // 8 waves: the phases after the DMA are latency-bound
+constexpr int kSmallThreads = 512;    // 8 waves: the phases after the DMA are latency-bound
 constexpr int kSmallMaxBlocks = 256;  // (image, head, region) triples: one workgroup per CU
 constexpr int kMaxSmallK = 16;        // routed regions per row
 
 // LDS layout (byte offsets, 16-byte aligned) and the lane split of a small
 // problem.  A query takes L lanes (L = kSmallThreads / the power of two >= t,
-// 8 to 32):
-// lane li scores keys li, li + L, .. and outputs dims li * 32 / L ..  Staged
-// arrays are whole rounds of kSmallThreads 16-byte DMA slots.
+// 8 to 32): lane li scores keys li, li + L, .. and outputs dims li * 32 / L ..
+// Staged arrays are whole rounds of kSmallThreads 16-byte DMA slots.
 struct SmallGeo {
     int L, pstride;
     int rk, rq, rh, rv;  // DMA rounds: K map, Q rows, V halo, routed V rows
