@@ -63,11 +63,13 @@ __device__ __forceinline__ int xcd_logical_block(int bid, int nblocks) {
     return (bid & 7) * (full >> 3) + (bid >> 3);
 }
 
-// max(a, b) for non-NaN operands as one v_med3_f32 (the median of a, b and
-// +inf); fmaxf would first quiet each operand that the compiler cannot prove
-// canonical, an extra instruction per operand.
+// max(a, b) for non-NaN operands.  IEEE 754-2019 maximum (NaN-propagating)
+// lowers to gfx950's v_maximum3_f32 with its operands as they are; fmaxf and
+// a median with +inf both become maxNum, for which the compiler first quiets
+// every operand it cannot prove canonical (an MFMA result, a lane exchange):
+// an extra instruction per operand.
 __device__ __forceinline__ float max_f(float a, float b) {
-    return __builtin_amdgcn_fmed3f(a, b, INFINITY);
+    return __builtin_elementwise_maximum(a, b);
 }
 // Max and sum over the four lanes l, l^16, l^32, l^48 -- in the MFMA
 // attention these hold the four key groups of one query.  v_permlane16_swap
