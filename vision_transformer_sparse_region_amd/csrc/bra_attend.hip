@@ -96,39 +96,99 @@ constexpr int kBufferDword3 = 0x00020000;
 // the element offset of the routed region's first token.  Keys past the
 // routed set (a ragged last chunk) re-read the last key: their scores are
 // masked to -inf, so they weigh nothing, and every load stays unconditional.
-__device__ __forceinline__ void gather_chunk(const Params& p, const WaveJobs& J, int w, int jl,
-                                             int c, const uint16_t* __restrict__ kimg,
-                                             const uint16_t* __restrict__ vimg, const int* sOff,
-                                             StepRegs& g8) {
-    const int lane = threadIdx.x & 63, li = lane & 15, g = lane >> 4;
-    const int job = w + kWaves * jl;
-    const int h = job / J.G;
-    const int hoff = h * kHeadDim;
-    const int* off = sOff + h * p.k;
+// The K half fills g8.ka (MFMA operands as loaded), the V half g8.vv.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t image_rsrc(const Params& p,
+                                                            const uint16_t* img) {
     // buffer loads: a 32-bit byte offset per lane against the image's base
     // in a buffer descriptor (no 64-bit address arithmetic per load)
     const uint32_t map_bytes = static_cast<uint32_t>(p.kH) * p.kW * p.C * 2u;
-    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(kimg), 0, static_cast<int>(map_bytes), kBufferDword3);
-    const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(vimg), 0, static_cast<int>(map_bytes), kBufferDword3);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(img), 0,
+                                             static_cast<int>(map_bytes), kBufferDword3);
+}
+__device__ __forceinline__ void gather_k_chunk(const Params& p, const WaveJobs& J, int w, int jl,
+                                               int c, const uint16_t* __restrict__ kimg,
+                                               const int* sOff, StepRegs& g8) {
+    const int lane = threadIdx.x & 63, li = lane & 15, g = lane >> 4;
+    const int h = (w + kWaves * jl) / J.G;
+    const int* off = sOff + h * p.k;
+    const __amdgpu_buffer_rsrc_t krs = image_rsrc(p, kimg);
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
         const int key = min(32 * c + 8 * (li >> 2) + 4 * blk + (li & 3), p.nkeys - 1);
         const int j = key / p.kt, slot = key - j * p.kt;
-        const int e = off[j] + slot_offset_kv(p, slot) + hoff + 8 * g;
+        const int e = off[j] + slot_offset_kv(p, slot) + h * kHeadDim + 8 * g;
         g8.ka[blk] = __builtin_bit_cast(bf16x8_t,
                                         __builtin_amdgcn_raw_buffer_load_b128(krs, 2 * e, 0, 0));
     }
+}
+__device__ __forceinline__ void gather_v_chunk(const Params& p, const WaveJobs& J, int w, int jl,
+                                               int c, const uint16_t* __restrict__ vimg,
+                                               const int* sOff, StepRegs& g8) {
+    const int lane = threadIdx.x & 63;
+    const int h = (w + kWaves * jl) / J.G;
+    const int* off = sOff + h * p.k;
+    const __amdgpu_buffer_rsrc_t vrs = image_rsrc(p, vimg);
 #pragma unroll
     for (int pp = 0; pp < 2; ++pp) {
         const int pc = lane + 64 * pp;
         const int key = min(32 * c + (pc >> 2), p.nkeys - 1);
         const int j = key / p.kt, slot = key - j * p.kt;
-        const int e = off[j] + slot_offset_kv(p, slot) + hoff + 8 * (pc & 3);
+        const int e = off[j] + slot_offset_kv(p, slot) + h * kHeadDim + 8 * (pc & 3);
         g8.vv[pp] = __builtin_bit_cast(uint4,
                                        __builtin_amdgcn_raw_buffer_load_b128(vrs, 2 * e, 0, 0));
     }
+}
+__device__ __forceinline__ void gather_chunk(const Params& p, const WaveJobs& J, int w, int jl,
+                                             int c, const uint16_t* __restrict__ kimg,
+                                             const uint16_t* __restrict__ vimg, const int* sOff,
+                                             StepRegs& g8) {
+    gather_k_chunk(p, J, w, jl, c, kimg, sOff, g8);
+    gather_v_chunk(p, J, w, jl, c, vimg, sOff, g8);
+}
+
+// Gathers of the shared-V windows (64 tokens, so a pair of 32-key chunks is
+// exactly one routed region): within a pair every lane reads the same
+// offsets from the region's first token, so they are computed once, and the
+// region's base is wave-uniform (the buffer loads' scalar offset).
+struct PairLanes {
+    int k[2][2];  // K operand piece of chunk ch, block blk
+    int v[2];     // the two V pieces of this wave's chunk
+};
+__device__ __forceinline__ PairLanes pair_lanes(const Params& p, int h, int mine) {
+    const int lane = threadIdx.x & 63, li = lane & 15, g = lane >> 4;
+    PairLanes L;
+#pragma unroll
+    for (int ch = 0; ch < 2; ++ch)
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk)
+            L.k[ch][blk] = 2 * (slot_offset_kv(p, 32 * ch + 8 * (li >> 2) + 4 * blk + (li & 3)) +
+                                h * kHeadDim + 8 * g);
+#pragma unroll
+    for (int pp = 0; pp < 2; ++pp) {
+        const int pc = lane + 64 * pp;
+        L.v[pp] = 2 * (slot_offset_kv(p, 32 * mine + (pc >> 2)) + h * kHeadDim + 8 * (pc & 3));
+    }
+    return L;
+}
+// Byte offset of routed region j of head h (wave-uniform).
+__device__ __forceinline__ int pair_base(const Params& p, const int* sOff, int h, int j) {
+    return __builtin_amdgcn_readfirstlane(2 * sOff[h * p.k + j]);
+}
+__device__ __forceinline__ void gather_k_pair(const PairLanes& L, __amdgpu_buffer_rsrc_t krs,
+                                              int base, StepRegs (&ring)[2]) {
+#pragma unroll
+    for (int ch = 0; ch < 2; ++ch)
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk)
+            ring[ch].ka[blk] = __builtin_bit_cast(
+                bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(krs, L.k[ch][blk], base, 0));
+}
+__device__ __forceinline__ void gather_v_mine(const PairLanes& L, __amdgpu_buffer_rsrc_t vrs,
+                                              int base, StepRegs& g8) {
+#pragma unroll
+    for (int pp = 0; pp < 2; ++pp)
+        g8.vv[pp] = __builtin_bit_cast(
+            uint4, __builtin_amdgcn_raw_buffer_load_b128(vrs, L.v[pp], base, 0));
 }
 
 // Chunk `ch` (0 or 1) of pair u of local job jl, if it exists.
@@ -136,8 +196,9 @@ __device__ __forceinline__ bool pair_chunk(const WaveJobs& J, int u, int ch) {
     return 2 * u + ch < J.nchunks;
 }
 
-// V chunk (in registers, one 16-byte piece per lane and half) through the
-// wave's LDS buffer, read back as the two V^T operands of O^T += V^T P^T.
+// V chunk (in registers, one 16-byte piece per lane and half) through an LDS
+// buffer -- the wave's own, or, for the shared-V windows, one its head's two
+// waves share -- read back as the two V^T operands of O^T += V^T P^T.
 // A staged row (one key) is 32 dims = 8 units of 8 bytes (dims 4u .. 4u+3);
 // unit u of row r sits at slot u ^ vt_swizzle(r).  Rows two apart (and, with
 // 64 banks, four and eight apart) would otherwise meet on the same banks --
@@ -148,9 +209,9 @@ __device__ __forceinline__ bool pair_chunk(const WaveJobs& J, int u, int ch) {
 __device__ __forceinline__ int vt_swizzle(int r) {
     return (((r >> 1) & 1) * 5) ^ ((r >> 2) & 1) ^ (((r >> 3) & 1) * 4);
 }
-__device__ __forceinline__ void v_transpose(const StepRegs& cur, uint16_t* sVt,
-                                            bf16x8_t (&va)[2]) {
-    const int lane = threadIdx.x & 63, li = lane & 15, g = lane >> 4;
+// The staging writes (one chunk, 32 keys) and the transposing reads.
+__device__ __forceinline__ void v_stage(const StepRegs& cur, uint16_t* sVt) {
+    const int lane = threadIdx.x & 63;
 #pragma unroll
     for (int pp = 0; pp < 2; ++pp) {
         const int pc = lane + 64 * pp, row = pc >> 2, q = pc & 3, sw = vt_swizzle(row);
@@ -158,12 +219,9 @@ __device__ __forceinline__ void v_transpose(const StepRegs& cur, uint16_t* sVt,
         dst[(2 * q) ^ sw] = uint2{cur.vv[pp].x, cur.vv[pp].y};
         dst[(2 * q + 1) ^ sw] = uint2{cur.vv[pp].z, cur.vv[pp].w};
     }
-    // A wave's LDS operations complete in order; the fences keep the
-    // compiler from moving the transposed reads above the writes, or the
-    // next chunk's writes above these reads.
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+__device__ __forceinline__ void v_read_t(const uint16_t* sVt, bf16x8_t (&va)[2]) {
+    const int lane = threadIdx.x & 63, li = lane & 15, g = lane >> 4;
     // ds_read_b64_tr_b16: in each 16-lane group, lane i receives element
     // i % 4 of the 8-byte pieces that lanes i / 4, 4 + i / 4, 8 + i / 4 and
     // 12 + i / 4 read.  Lane 4r + a of group g reads dims 16 db + 4a .. + 3 of
@@ -186,6 +244,17 @@ __device__ __forceinline__ void v_transpose(const StepRegs& cur, uint16_t* sVt,
         // loop spills)
         __builtin_amdgcn_sched_barrier(0);
     }
+}
+// One chunk through the wave's own buffer.  A wave's LDS operations complete
+// in order; the fences keep the compiler from moving the transposed reads
+// above the writes, or the next chunk's writes above these reads.
+__device__ __forceinline__ void v_transpose(const StepRegs& cur, uint16_t* sVt,
+                                            bf16x8_t (&va)[2]) {
+    v_stage(cur, sVt);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    v_read_t(sVt, va);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -198,6 +267,11 @@ __device__ __forceinline__ void v_transpose(const StepRegs& cur, uint16_t* sVt,
 // softmax with no rescaling; longer key lists carry an online softmax across
 // pairs.  The next pair's gathers are issued as soon as this pair's K and V
 // registers are consumed.
+template <int N>
+struct NextTag {
+    static constexpr int value = N;
+};
+template <bool SHARE_V>
 __device__ __forceinline__ void attend_mfma(const Params& p, const WaveJobs& J, const uint16_t* __restrict__ qimg,
                             const uint16_t* __restrict__ kimg, const uint16_t* __restrict__ vimg,
                             int r, uint16_t* sVt_all, float* sL, const int* sOff,
@@ -206,6 +280,9 @@ __device__ __forceinline__ void attend_mfma(const Params& p, const WaveJobs& J, 
     const int li = lane & 15, g = lane >> 4;
     uint16_t* sVt = sVt_all + w * 32 * kVtRow;
     const int npair = (J.nchunks + 1) / 2;
+    // (SHARE_V: one job per wave, whole pairs, one routed region per pair)
+    const PairLanes pl = SHARE_V ? pair_lanes(p, w / J.G, w & 1) : PairLanes{};
+    const __amdgpu_buffer_rsrc_t krs = image_rsrc(p, kimg), vrs = image_rsrc(p, vimg);
     const int njl = J.nchunks > 0 ? J.nsteps / J.nchunks : 0;  // this wave's jobs
 
     // Softmax denominator.  sum_mfma (long key lists, where the VALU softmax
@@ -218,7 +295,13 @@ __device__ __forceinline__ void attend_mfma(const Params& p, const WaveJobs& J, 
                                                               0x3f803f80u, 0x3f803f80u});
     float m[kMaxQTiles];
     f32x4_t o0[kMaxQTiles], o1[kMaxQTiles], l[kMaxQTiles];
-    for (int ss = 0; ss < njl * npair; ++ss) {
+    // One pair step.  NEXT: 2, the next step's gathers are issued if there
+    // is one (general path); 1, always (shared-V steps before the last); 0,
+    // never (the shared-V last step).  The shared-V loop then issues its
+    // loads in the same order on every path into the loop's head, which the
+    // compiler's counts of loads in flight need to wait for only the oldest.
+    auto step = [&](int ss, auto next_tag) {
+        constexpr int NEXT = decltype(next_tag)::value;
         const int jl = ss / npair, u = ss - jl * npair;
         const int job = w + kWaves * jl;
         const int h = job / J.G, grp = job - h * J.G;
@@ -230,8 +313,23 @@ __device__ __forceinline__ void attend_mfma(const Params& p, const WaveJobs& J, 
         if (u == 0 && jl > 0) load_q_operands(p, J, job, qimg, r, qb);
 
         bf16x8_t va[2][2];
-        v_transpose(ring[0], sVt, va[0]);
-        if (two) v_transpose(ring[1], sVt, va[1]);
+        if constexpr (SHARE_V) {
+            // this wave's chunk of the pair (ring[0].vv) into its head's
+            // buffer of this pair's parity; then the next pair's V chunk goes
+            // out, and both chunks are read back once both waves have written
+            // (the buffer of this parity is written again two pairs on, after
+            // the next pair's barrier, which every wave passes only once its
+            // reads of this one have returned)
+            uint16_t* hb = sVt_all + ((ss & 1) * 2 + h) * 2 * 32 * kVtRow;
+            v_stage(ring[0], hb + (w & 1) * 32 * kVtRow);
+            if constexpr (NEXT == 1) gather_v_mine(pl, vrs, pair_base(p, sOff, h, u + 1), ring[0]);
+            __syncthreads();
+            v_read_t(hb, va[0]);
+            v_read_t(hb + 32 * kVtRow, va[1]);
+        } else {
+            v_transpose(ring[0], sVt, va[0]);
+            if (two) v_transpose(ring[1], sVt, va[1]);
+        }
 
 #pragma unroll
         for (int jq = 0; jq < kMaxQTiles; ++jq) {
@@ -252,10 +350,14 @@ __device__ __forceinline__ void attend_mfma(const Params& p, const WaveJobs& J, 
             // the next pair's gathers go out now
             if (jq == nq - 1) {
                 const int nss = ss + 1, njl2 = nss / npair, nu = nss - njl2 * npair;
-                if (njl2 < njl) {
-                    gather_chunk(p, J, w, njl2, 2 * nu, kimg, vimg, sOff, ring[0]);
-                    if (pair_chunk(J, nu, 1))
-                        gather_chunk(p, J, w, njl2, 2 * nu + 1, kimg, vimg, sOff, ring[1]);
+                if (NEXT == 1 || (NEXT == 2 && njl2 < njl)) {
+                    if constexpr (SHARE_V) {
+                        gather_k_pair(pl, krs, pair_base(p, sOff, h, nu), ring);
+                    } else {
+                        gather_chunk(p, J, w, njl2, 2 * nu, kimg, vimg, sOff, ring[0]);
+                        if (pair_chunk(J, nu, 1))
+                            gather_chunk(p, J, w, njl2, 2 * nu + 1, kimg, vimg, sOff, ring[1]);
+                    }
                 }
             }
             // raw scores; the running max is kept in raw units and the
@@ -338,6 +440,13 @@ __device__ __forceinline__ void attend_mfma(const Params& p, const WaveJobs& J, 
                 }
             }
         }
+        };
+    if constexpr (SHARE_V) {
+        // one job per wave, so the steps are the job's pairs
+        for (int ss = 0; ss + 1 < npair; ++ss) step(ss, NextTag<1>{});
+        if (npair > 0) step(npair - 1, NextTag<0>{});
+    } else {
+        for (int ss = 0; ss < njl * npair; ++ss) step(ss, NextTag<2>{});
     }
 }
 
@@ -698,6 +807,11 @@ attend_kernel(const T* __restrict__ q, const T* __restrict__ v, const T* __restr
 
     constexpr int VEC = Elem<T>::kVec;
     constexpr bool kLepeMfma = VEC == 8 && LepeMfmaShape<HS, WS, HEADS>::ok;
+    // 64-token windows of two heads: the two waves of a head share the
+    // routed V chunks through LDS (every wave holds one job, so all take the
+    // same number of pair steps and workgroup barriers)
+    constexpr bool kShareV = VEC == 8 && HS > 0 && WS > 0 && NW > 0 && KTOP > 0 &&
+                             share_v(HS, WS, HEADS);
     const int tid = threadIdx.x, w = tid >> 6;
     const int blk = xcd_logical_block(blockIdx.x, gridDim.x);
     const int b = blk / p.R, r = blk - b * p.R;
@@ -1006,11 +1120,21 @@ attend_kernel(const T* __restrict__ q, const T* __restrict__ v, const T* __restr
     StepRegs ring[2];
     if constexpr (VEC == 8) {
         if (J.nsteps > 0) {
+            const uint16_t* kgi = reinterpret_cast<const uint16_t*>(kg) + kimg;
+            const uint16_t* vgi = reinterpret_cast<const uint16_t*>(vg) + kimg;
+            if constexpr (kShareV) {
+                // V only of this wave's chunk (w & 1), then both K chunks:
+                // the order the pair loop issues them in (V of a pair one pair
+                // ahead of its K), so that its waits count the same loads
+                const PairLanes pl = pair_lanes(p, w / J.G, w & 1);
+                const int base = pair_base(p, sOff, w / J.G, 0);
+                gather_v_mine(pl, image_rsrc(p, vgi), base, ring[0]);
+                gather_k_pair(pl, image_rsrc(p, kgi), base, ring);
+            } else {
 #pragma unroll
-            for (int ch = 0; ch < 2; ++ch)
-                if (ch < J.nchunks)
-                    gather_chunk(p, J, w, 0, ch, reinterpret_cast<const uint16_t*>(kg) + kimg,
-                                 reinterpret_cast<const uint16_t*>(vg) + kimg, sOff, ring[ch]);
+                for (int ch = 0; ch < 2; ++ch)
+                    if (ch < J.nchunks) gather_chunk(p, J, w, 0, ch, kgi, vgi, sOff, ring[ch]);
+            }
         }
     }
     if constexpr (kPrioPrologue) __builtin_amdgcn_s_setprio(0);
@@ -1034,7 +1158,7 @@ attend_kernel(const T* __restrict__ q, const T* __restrict__ v, const T* __restr
         // the denominator on the MFMA for key lists longer than one pair of chunks
         constexpr bool kFixedKeys = HS > 0 && WS > 0 && KTOP > 0;
         const bool sum_mfma = kFixedKeys ? KTOP * HS * WS > 64 : p.nkeys > 64;
-        attend_mfma(p, J, reinterpret_cast<const uint16_t*>(q) + img,
+        attend_mfma<kShareV>(p, J, reinterpret_cast<const uint16_t*>(q) + img,
                     reinterpret_cast<const uint16_t*>(kg) + kimg,
                     reinterpret_cast<const uint16_t*>(vg) + kimg, r,
                     reinterpret_cast<uint16_t*>(smem + p.off_vt), sL, sOff, ring, qb, sum_mfma);
@@ -1169,7 +1293,11 @@ bool plan(Params& p, int B, int H, int W, int C, int heads, int n_win, int k, fl
     const long t = p.t;
     // per-wave V^T staging (bf16 attention); before the attention, the
     // partial Q sums of each wave (32 doubles)
-    p.off_vt = take(std::max(bf16 ? static_cast<long>(kWaves) * 32 * kVtRow * 2 : 0L,
+    const long vt_bytes = !bf16 ? 0L
+                          : (is_fixed_shape(p, bf16) && share_v(p.hs, p.ws, heads))
+                              ? static_cast<long>(kVtSharedBytes)
+                              : static_cast<long>(kWaves) * 32 * kVtRow * 2;
+    p.off_vt = take(std::max(vt_bytes,
                              static_cast<long>(kWaves) * kHeadDim * 8));
     // The fixed bf16 shapes whose windows tile by 4x4 run LePE on MFMA with a
     // channel-planar halo; the others on VALU with an NHWC halo.

@@ -117,6 +117,15 @@ constexpr JobShape job_shape(int t, int heads) {
     const int G = (QT + tpg - 1) / tpg;  // every group non-empty
     return JobShape{QT, tpg, G, heads * G};
 }
+// 64-token windows with two heads (four query tiles per head, two per wave):
+// the two waves of a head split each routed pair of 32-key V chunks, one
+// chunk each, and share them through an LDS buffer per head, double-buffered
+// over pairs: 2 parities x 2 heads x 2 chunks x 32 keys x 32 dims of bf16.
+constexpr bool share_v(int hs, int ws, int heads) {
+    return hs * ws == 64 && heads == 2 && job_shape(64, 2).njobs == kWaves &&
+           job_shape(64, 2).G == 2;
+}
+constexpr int kVtSharedBytes = 2 * 2 * 2 * 32 * kVtRow * 2;
 // bf16 maps routed inside the attention kernel whose jobs are each some
 // wave's first job hold every query of the region in the waves' first Q
 // operands, so the kernel sums the Q means from them (exactly, in fp64) and
