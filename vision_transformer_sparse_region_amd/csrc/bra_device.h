@@ -116,12 +116,14 @@ __device__ __forceinline__ void load_kmean(const Params& p, const double* __rest
     }
 }
 
-// The fp32 copy of the K means (each rounded to nearest), in the same order,
-// after the fp64 Q and K means; written when p.kmean32 is set.  The routing
-// inside the attention kernel screens with it (half the bytes of the fp64
-// means) and reads the fp64 means only where the screen cannot decide.
+// The fp32 copy of the K means (each rounded to nearest), after the fp64 Q
+// and K means, in dim quads: [B][heads][8][R][4], so that lane s reads dims
+// 4j .. 4j + 3 of region s as one 16-byte load; written when p.kmean32 is
+// set.  The routing inside the attention kernel screens with it (half the
+// bytes of the fp64 means) and reads the fp64 means only where the screen
+// cannot decide.
 __device__ __forceinline__ size_t kmean32_offset(const Params& p, int bh, int d, int s) {
-    return ((static_cast<size_t>(bh) * (kHeadDim / 2) + (d >> 1)) * p.R + s) * 2 + (d & 1);
+    return ((static_cast<size_t>(bh) * (kHeadDim / 4) + (d >> 2)) * p.R + s) * 4 + (d & 3);
 }
 __device__ __forceinline__ const float* kmean32_base(const Params& p, const double* means) {
     return reinterpret_cast<const float*>(means +
@@ -145,14 +147,18 @@ __device__ __forceinline__ void store_kmean_pair(const Params& p, double* __rest
             float2{static_cast<float>(m0), static_cast<float>(m1)};
 }
 // The fp32 K mean of region s, head bh: dims 2j, 2j + 1 as the two halves
-// of kb[j], j < 16 (16 coalesced 8-byte loads; kb[16..31] untouched, so the
+// of kb[j], j < 16 (8 coalesced 16-byte loads; kb[16..31] untouched, so the
 // same registers can hold the fp64 mean instead).
 __device__ __forceinline__ void load_kmean32(const Params& p, const double* __restrict__ means,
                                              int bh, int s, double (&kb)[kHeadDim]) {
     const float* base = kmean32_base(p, means);
 #pragma unroll
-    for (int j = 0; j < kHeadDim / 2; ++j)
-        kb[j] = *reinterpret_cast<const double*>(base + kmean32_offset(p, bh, 2 * j, s));
+    for (int j = 0; j < kHeadDim / 4; ++j) {
+        const u32x4_t v =
+            *reinterpret_cast<const u32x4_t*>(base + kmean32_offset(p, bh, 4 * j, s));
+        kb[2 * j] = __builtin_bit_cast(double, u32x2_t{v[0], v[1]});
+        kb[2 * j + 1] = __builtin_bit_cast(double, u32x2_t{v[2], v[3]});
+    }
 }
 
 // mean = sum / t, as a multiplication when t is a power of two (exact then).

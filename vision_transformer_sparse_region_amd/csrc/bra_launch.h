@@ -63,8 +63,8 @@ bool plan(Params& p, int B, int H, int W, int C, int heads, int n_win, int k, fl
 
 // Kernel launches on `stream`; return the launch status.
 //   means: fp64 region means, Q as [B][heads][R][32], then K as [B][heads][16][R][2]
-//   (kmean_index: dims in pairs), then K again in fp32, same order (kmean32_offset;
-//   written when p.kmean32).
+//   (kmean_index: dims in pairs), then K again in fp32 as [B][heads][8][R][4]
+//   (kmean32_offset: dims in quads; written when p.kmean32).
 //   lepe_table: p.table_items 8-byte entries (written by the pool kernel when
 //   lepe_w is given and the shape runs LePE on MFMA).
 //   routing: [B][rheads][R][k] int32 region ids.
