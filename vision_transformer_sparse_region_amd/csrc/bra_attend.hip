@@ -920,35 +920,41 @@ attend_kernel(const T* __restrict__ q, const T* __restrict__ v, const T* __restr
     static_assert(kHR * kHTask <= 32, "one validity bit per halo register");
     uint4 hreg[kHR * kHTask];
     unsigned hvalid = 0;
-    if constexpr (kHalo4) {
-        constexpr int NV = HEADS * kHeadDim / 8, GX = (WS + 4) / 4;
+    // The halo loads.  Where this kernel routes, they go out after the Q
+    // means: issued before, they held each wave in the load queue that the
+    // Q operands and K means, which the routing needs first, also wait on.
+    auto issue_halo = [&]() {
+        if constexpr (kHalo4) {
+            constexpr int NV = HEADS * kHeadDim / 8, GX = (WS + 4) / 4;
 #pragma unroll
-        for (int u = 0; u < kHR; ++u) {
-            const int task = tid + u * kThreads;
-            const int tc = min(task, kHTasks - 1);
-            const int pv = tc % NV, cg = tc / NV, hy = cg / GX, gx = cg - hy * GX;
-            const int y = y0 + hy - 2, yc = min(max(y, 0), p.H - 1);
+            for (int u = 0; u < kHR; ++u) {
+                const int task = tid + u * kThreads;
+                const int tc = min(task, kHTasks - 1);
+                const int pv = tc % NV, cg = tc / NV, hy = cg / GX, gx = cg - hy * GX;
+                const int y = y0 + hy - 2, yc = min(max(y, 0), p.H - 1);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int x = x0 + 4 * gx + j - 2, xc = min(max(x, 0), p.W - 1);
-                hreg[u * 4 + j] =
-                    *reinterpret_cast<const uint4*>(v + img + (yc * p.W + xc) * p.C + pv * 8);
-                if (task < kHTasks && y == yc && x == xc) hvalid |= 1u << (u * 4 + j);
+                for (int j = 0; j < 4; ++j) {
+                    const int x = x0 + 4 * gx + j - 2, xc = min(max(x, 0), p.W - 1);
+                    hreg[u * 4 + j] =
+                        *reinterpret_cast<const uint4*>(v + img + (yc * p.W + xc) * p.C + pv * 8);
+                    if (task < kHTasks && y == yc && x == xc) hvalid |= 1u << (u * 4 + j);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int u = 0; u < kHR; ++u) {
+                const int i = tid + u * kThreads;
+                const int ic = min(i, p.halo_pieces - 1);
+                const int cell = ic / nvec, pv = ic - cell * nvec;
+                const int hy = cell / hw, hx = cell - hy * hw;
+                const int y = y0 + hy - 2, x = x0 + hx - 2;
+                const int yc = min(max(y, 0), p.H - 1), xc = min(max(x, 0), p.W - 1);
+                hreg[u] = *reinterpret_cast<const uint4*>(v + img + (yc * p.W + xc) * p.C + pv * VEC);
+                if (i < p.halo_pieces && y == yc && x == xc) hvalid |= 1u << u;
             }
         }
-    } else {
-#pragma unroll
-        for (int u = 0; u < kHR; ++u) {
-            const int i = tid + u * kThreads;
-            const int ic = min(i, p.halo_pieces - 1);
-            const int cell = ic / nvec, pv = ic - cell * nvec;
-            const int hy = cell / hw, hx = cell - hy * hw;
-            const int y = y0 + hy - 2, x = x0 + hx - 2;
-            const int yc = min(max(y, 0), p.H - 1), xc = min(max(x, 0), p.W - 1);
-            hreg[u] = *reinterpret_cast<const uint4*>(v + img + (yc * p.W + xc) * p.C + pv * VEC);
-            if (i < p.halo_pieces && y == yc && x == xc) hvalid |= 1u << u;
-        }
-    }
+    };
+    if constexpr (!FUSED) issue_halo();
     if constexpr (!FUSED && VEC == 8)
         load_q_operands(p, J, min(w, J.njobs - 1), reinterpret_cast<const uint16_t*>(q) + img, r,
                         qb);
@@ -983,6 +989,7 @@ attend_kernel(const T* __restrict__ q, const T* __restrict__ v, const T* __restr
                 }
             }
         }
+        issue_halo();
         if (wu < p.heads) {
             const size_t row = (static_cast<size_t>(b) * p.heads + wu) * p.R + r;
             route_row_wave(p, qmean_lane, screen, kreg, means, b * p.heads + wu,
