@@ -21,7 +21,8 @@
 //      apart are routed again exactly, a wave per row, on the sequential
 //      fp64 affinities                       [P1 §2.1 TopkRouting; P5 §五 ④]
 //   3b V goes to LDS channel-planar with a 2-cell zero border in x (the
-//      LePE halo of the whole map is that border)
+//      LePE halo of the whole map is that border), written by the waves
+//      that do not route while the others route
 //   4  each job -- one 4 x 4 token tile of one head: one region of 4 x 4
 //      tokens, or four regions of 2 x 2 -- runs the 5 x 5 depthwise LePE of
 //      the tile on the 4x4x4 MFMA from the planar V, the token attention
@@ -70,14 +71,13 @@ struct ImgShape {
     static constexpr int NCH = 2 * NPAIR;         // 32-key chunks (pairs of)
     static constexpr int GXN = PW / 4;            // 4-cell column groups of a plane row
     static constexpr int NVT = PCT * H * GXN;     // V staging tasks
-    static constexpr int VT = (NVT + kImgThreads - 1) / kImgThreads;
     static constexpr int NTE = CG * 40;           // Toeplitz entries
-    static constexpr int TE = (NTE + kImgThreads - 1) / kImgThreads;
     static_assert(HS == 2 || HS == 4, "4 x 4 tiles of whole regions");
     static_assert(R <= 64 && KTOP <= 16 && KTOP >= 1, "quad routing: R <= 64, k <= 16");
     static_assert(NT <= 4, "16 keys per lane");
     static_assert(HEADS % HG == 0, "whole head groups");
     static_assert(RS % 8 == 0, "16-byte rows");
+    static_assert(PASSES < kImgWaves, "waves left to stage V while the others route");
 };
 
 // 26-bit fixed point keys: region id in the low 6 bits (63 - id, so that the
@@ -403,6 +403,109 @@ __device__ __forceinline__ void route_exact(const ImgLds<S>& L, int b, int hg,
     }
 }
 
+// V staging task `task` = (piece pv, map row y, column group gx): the four
+// map cells 4gx - 2 .. 4gx + 1 of row y (clamped into the map; bit jj of
+// the returned mask says cell jj is inside it).
+template <typename S>
+__device__ __forceinline__ unsigned load_vtask(const uint16_t* __restrict__ v, size_t img, int task,
+                                               uint4 (&vr)[4]) {
+    const int t = min(task, S::NVT - 1);
+    const int pv = t % S::PCT, rest = t / S::PCT;
+    const int gx = rest % S::GXN, y = rest / S::GXN;
+    unsigned valid = 0;
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+        const int x = 4 * gx + jj - 2, xc = min(max(x, 0), S::W - 1);
+        vr[jj] = *reinterpret_cast<const uint4*>(v + img + static_cast<size_t>(y * S::W + xc) * S::C +
+                                                 8 * pv);
+        if (x == xc) valid |= 1u << jj;
+    }
+    return task < S::NVT ? valid : 0u;
+}
+
+// ... writes it to plane columns 4gx .. 4gx + 3 of the 8 channel planes of
+// piece pv (the cells outside the map as zeros).
+template <typename S>
+__device__ __forceinline__ void store_vtask(const ImgLds<S>& L, int task, const uint4 (&vr)[4],
+                                            unsigned valid) {
+    if (task >= S::NVT) return;
+    const int pv = task % S::PCT, rest = task / S::PCT;
+    const int gx = rest % S::GXN, y = rest / S::GXN;
+    uint32_t wd[4][4];
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+        const unsigned mk = 0u - ((valid >> jj) & 1u);
+        wd[jj][0] = vr[jj].x & mk;
+        wd[jj][1] = vr[jj].y & mk;
+        wd[jj][2] = vr[jj].z & mk;
+        wd[jj][3] = vr[jj].w & mk;
+    }
+    uint16_t* base = L.sVp + (8 * pv) * S::PS + y * S::PW + 4 * gx;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const int sh = 16 * (e & 1);
+        const uint32_t c0 = (wd[0][e >> 1] >> sh) & 0xffffu;
+        const uint32_t c1 = (wd[1][e >> 1] >> sh) & 0xffffu;
+        const uint32_t c2 = (wd[2][e >> 1] >> sh) & 0xffffu;
+        const uint32_t c3 = (wd[3][e >> 1] >> sh) & 0xffffu;
+        *reinterpret_cast<uint2*>(base + e * S::PS) = uint2{c0 | (c1 << 16), c2 | (c3 << 16)};
+    }
+}
+
+// The V planes, the LePE operand table and the bias, by NST threads (st =
+// 0 .. NST - 1 of them).  Task st of the V staging came in with the
+// prologue's loads (vr0, valid0); the later tasks and the LePE taps are
+// loaded here, their loads in flight while the first task is written.
+template <typename S, int NST>
+__device__ __forceinline__ void stage_planes(const ImgLds<S>& L, const uint16_t* __restrict__ v,
+                                             size_t img, const float* __restrict__ lepe_w,
+                                             const float* __restrict__ lepe_b, int hg,
+                                             int has_lepe, int st, const uint4 (&vr0)[4],
+                                             unsigned valid0) {
+    constexpr int VR = (S::NVT + NST - 1) / NST;  // V tasks per thread
+    constexpr int TR = (S::NTE + NST - 1) / NST;  // Toeplitz entries per thread
+    uint4 vr[VR > 1 ? VR - 1 : 1][4];
+    unsigned valid[VR > 1 ? VR - 1 : 1];
+#pragma unroll
+    for (int u = 1; u < VR; ++u) valid[u - 1] = load_vtask<S>(v, img, st + u * NST, vr[u - 1]);
+    // the four taps of each Toeplitz entry (w[c][i][4ks + kk - n]), clamped
+    // into the row; the taps outside the kernel are zeroed below
+    float wv[TR][4];
+    float bias = 0.f;
+    if (has_lepe) {
+#pragma unroll
+        for (int u = 0; u < TR; ++u) {
+            const int it = min(st + u * NST, S::NTE - 1);
+            const int ks = it & 1, i = (it >> 1) % 5, lane_cg = it / 10;
+            const int c = 16 * (lane_cg >> 6) + ((lane_cg & 63) >> 2), n = lane_cg & 3;
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+                wv[u][kk] = lepe_w[(hg * S::CG + c) * 25 + i * 5 + min(max(4 * ks + kk - n, 0), 4)];
+        }
+        if (lepe_b) bias = lepe_b[hg * S::CG + min(st, S::CG - 1)];
+    }
+    store_vtask<S>(L, st, vr0, valid0);
+#pragma unroll
+    for (int u = 1; u < VR; ++u) store_vtask<S>(L, st + u * NST, vr[u - 1], valid[u - 1]);
+    if (has_lepe) {
+#pragma unroll
+        for (int u = 0; u < TR; ++u) {
+            const int it = st + u * NST;
+            if (it < S::NTE) {
+                const int ks = it & 1, lane_cg = it / 10, n = lane_cg & 3;
+                uint32_t hh[4];
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) {
+                    const int jj = 4 * ks + kk - n;
+                    hh[kk] = (jj >= 0 && jj <= 4) ? f32_to_bf16(wv[u][kk]) : 0u;
+                }
+                L.sTab[it] = uint2{hh[0] | (hh[1] << 16), hh[2] | (hh[3] << 16)};
+            }
+        }
+        if (st < S::CG) L.sBias[st] = bias;
+    }
+}
+
 template <int HS, int NW, int HG, int HEADS, int KTOP, bool ROUTED>
 __device__ __forceinline__ void image_body(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
@@ -448,39 +551,14 @@ __device__ __forceinline__ void image_body(
                                                                     S::C +
                                                       hl * kHeadDim + 8 * g));
     }
-    // V staging tasks: (piece pv, row y, column group gx) -> plane columns
-    // 4gx .. 4gx + 3, map columns 4gx - 2 .. 4gx + 1 (zero outside the map)
-    uint4 vreg[S::VT][4];
+    // the first V staging task of each thread that stages the V planes:
+    // every thread when the routing is the caller's, else the threads of
+    // the waves that do not route (they stage while the others route)
+    constexpr int NST = ROUTED ? kImgThreads : kImgThreads - 64 * S::PASSES;
+    const int st = ROUTED ? tid : tid - 64 * S::PASSES;
+    uint4 vreg[4];
     unsigned vvalid = 0;
-#pragma unroll
-    for (int u = 0; u < S::VT; ++u) {
-        const int task = min(tid + u * kImgThreads, S::NVT - 1);
-        const int pv = task % S::PCT, rest = task / S::PCT;
-        const int gx = rest % S::GXN, y = rest / S::GXN;
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-            const int x = 4 * gx + jj - 2, xc = min(max(x, 0), S::W - 1);
-            vreg[u][jj] = *reinterpret_cast<const uint4*>(
-                v + img + static_cast<size_t>(y * S::W + xc) * S::C + 8 * pv);
-            if (tid + u * kImgThreads < S::NVT && x == xc) vvalid |= 1u << (4 * u + jj);
-        }
-    }
-    // the four taps of each Toeplitz entry (w[c][i][4ks + kk - n]), clamped
-    // into the row; the taps outside the kernel are zeroed when it is built
-    float wv[S::TE][4];
-    float bias = 0.f;
-    if (has_lepe) {
-#pragma unroll
-        for (int u = 0; u < S::TE; ++u) {
-            const int it = min(tid + u * kImgThreads, S::NTE - 1);
-            const int ks = it & 1, i = (it >> 1) % 5, lane_cg = it / 10;
-            const int c = 16 * (lane_cg >> 6) + ((lane_cg & 63) >> 2), n = lane_cg & 3;
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk)
-                wv[u][kk] = lepe_w[(hg * S::CG + c) * 25 + i * 5 + min(max(4 * ks + kk - n, 0), 4)];
-        }
-        if (lepe_b) bias = lepe_b[hg * S::CG + min(tid, S::CG - 1)];
-    }
+    if (ROUTED || w >= S::PASSES) vvalid = load_vtask<S>(v, img, st, vreg);
     int rid[ROUTED ? S::RI : 1];
     if constexpr (ROUTED) {
 #pragma unroll
@@ -553,62 +631,24 @@ __device__ __forceinline__ void image_body(
     }
     lds_barrier();
 
-    // 3. routing
+    // 3. routing; the waves that do not route stage the V planes (over the
+    //    staged Q, read only by the means), the LePE operand table and the
+    //    bias meanwhile
     if constexpr (!ROUTED) {
-        route_rows<S>(L, b, hg, routing);
+        if (w < S::PASSES)
+            route_rows<S>(L, b, hg, routing);
+        else
+            stage_planes<S, NST>(L, v, img, lepe_w, lepe_b, hg, has_lepe, st, vreg,
+                                 vvalid);
         lds_barrier();
         if (*L.sNFail > 0) {  // workgroup-uniform
             route_exact<S>(L, b, hg, routing);
+            lds_barrier();
         }
+    } else {
+        stage_planes<S, NST>(L, v, img, lepe_w, lepe_b, hg, has_lepe, st, vreg, vvalid);
+        lds_barrier();
     }
-
-    // 3b. V to the planes (over the staged Q, read only by the means); the
-    //     LePE operand table and the bias
-#pragma unroll
-    for (int u = 0; u < S::VT; ++u) {
-        const int task = tid + u * kImgThreads;
-        if (task < S::NVT) {
-            const int pv = task % S::PCT, rest = task / S::PCT;
-            const int gx = rest % S::GXN, y = rest / S::GXN;
-            uint32_t wd[4][4];
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                const unsigned mk = 0u - ((vvalid >> (4 * u + jj)) & 1u);
-                wd[jj][0] = vreg[u][jj].x & mk;
-                wd[jj][1] = vreg[u][jj].y & mk;
-                wd[jj][2] = vreg[u][jj].z & mk;
-                wd[jj][3] = vreg[u][jj].w & mk;
-            }
-            uint16_t* base = L.sVp + (8 * pv) * S::PS + y * S::PW + 4 * gx;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int sh = 16 * (e & 1);
-                const uint32_t c0 = (wd[0][e >> 1] >> sh) & 0xffffu;
-                const uint32_t c1 = (wd[1][e >> 1] >> sh) & 0xffffu;
-                const uint32_t c2 = (wd[2][e >> 1] >> sh) & 0xffffu;
-                const uint32_t c3 = (wd[3][e >> 1] >> sh) & 0xffffu;
-                *reinterpret_cast<uint2*>(base + e * S::PS) = uint2{c0 | (c1 << 16), c2 | (c3 << 16)};
-            }
-        }
-    }
-    if (has_lepe) {
-#pragma unroll
-        for (int u = 0; u < S::TE; ++u) {
-            const int it = tid + u * kImgThreads;
-            if (it < S::NTE) {
-                const int ks = it & 1, lane_cg = it / 10, n = lane_cg & 3;
-                uint32_t hh[4];
-#pragma unroll
-                for (int kk = 0; kk < 4; ++kk) {
-                    const int jj = 4 * ks + kk - n;
-                    hh[kk] = (jj >= 0 && jj <= 4) ? f32_to_bf16(wv[u][kk]) : 0u;
-                }
-                L.sTab[it] = uint2{hh[0] | (hh[1] << 16), hh[2] | (hh[3] << 16)};
-            }
-        }
-        if (tid < S::CG) L.sBias[tid] = bias;
-    }
-    lds_barrier();
 
     // 4. jobs: LePE, attention, store.  Per-lane gather constants: the K
     //    operand rows (key 32c + 8(li/4) + 4blk + li%4: routed rank and the
