@@ -728,6 +728,15 @@ __device__ __forceinline__ void image_body(
 
         // attention over the routed keys of each region of the tile
         const int my_m = S::RPT == 1 ? 0 : ((li >> 3) << 1) | ((li & 3) >> 1);
+        // the Q operand for each region of the tile: this lane's query where
+        // the query lies in that region, else zero (bit masks, no branches)
+        bf16x8_t qm[S::RPT];
+#pragma unroll
+        for (int m = 0; m < S::RPT; ++m) {
+            const uint32_t mk = (S::RPT == 1 || my_m == m) ? 0xffffffffu : 0u;
+            const u32x4_t qw = __builtin_bit_cast(u32x4_t, qj);
+            qm[m] = __builtin_bit_cast(bf16x8_t, u32x4_t{qw[0] & mk, qw[1] & mk, qw[2] & mk, qw[3] & mk});
+        }
         int rb[S::RPT];  // row base of (hl, region m) in the routing tables
 #pragma unroll
         for (int m = 0; m < S::RPT; ++m) {
@@ -742,33 +751,34 @@ __device__ __forceinline__ void image_body(
         f32x4_t o0 = {0.f, 0.f, 0.f, 0.f}, o1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int u = 0; u < S::NPAIR; ++u) {
+            // S^T of each 32-key chunk, one accumulator per key block: the
+            // regions' products are summed with their own queries' Q (the
+            // other query slots zeroed), so a query's sum holds its own
+            // region's scores plus exact zeros (K is finite)
             float x[2][8];
 #pragma unroll
-            for (int ch = 0; ch < 2; ++ch)
+            for (int ch = 0; ch < 2; ++ch) {
+                const int c = 2 * u + ch;
+                if (32 * c >= S::NKEYS) {
 #pragma unroll
-                for (int e = 0; e < 8; ++e) x[ch][e] = -INFINITY;
+                    for (int e = 0; e < 8; ++e) x[ch][e] = -INFINITY;
+                    continue;
+                }
+                f32x4_t sc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-            for (int m = 0; m < S::RPT; ++m) {
-#pragma unroll
-                for (int ch = 0; ch < 2; ++ch) {
-                    const int c = 2 * u + ch;
-                    if (32 * c >= S::NKEYS) break;
-                    f32x4_t sc[2];
+                for (int m = 0; m < S::RPT; ++m) {
 #pragma unroll
                     for (int blk = 0; blk < 2; ++blk) {
                         const int off = L.sOffK[rb[m] + jrk[c][blk]] + slk[c][blk];
                         const bf16x8_t ka =
                             __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(kh + off));
-                        sc[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            ka, qj, f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                        sc[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qm[m], sc[blk], 0, 0, 0);
                     }
-                    if (S::RPT == 1 || my_m == m) {
+                }
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            x[ch][e] = sc[0][e];
-                            x[ch][4 + e] = sc[1][e];
-                        }
-                    }
+                for (int e = 0; e < 4; ++e) {
+                    x[ch][e] = sc[0][e];
+                    x[ch][4 + e] = sc[1][e];
                 }
             }
             // keys past the routed set (a ragged last chunk) weigh nothing
