@@ -220,38 +220,52 @@ __device__ __forceinline__ void put_route(const ImgLds<S>& L, int hl, int r, int
 }
 
 // Region means of the staged K and Q maps ([H][RS] each), both in one pass:
-// item (tensor, head hl, region s, dims 8o .. 8o + 7) reads the region's
-// slots as 16-byte pieces and adds each dim's values in slot order, as the
-// oracle does.  Returns the max |K mean| of the thread's items.
+// item (tensor, head hl, region s, dims DPI o .. DPI o + DPI - 1) reads the
+// region's slots as 16- or 8-byte pieces and adds each dim's values in slot
+// order, as the oracle does.  DPI is 4 where the items of 4 dims still fit
+// one a thread (16-token regions: half the chain of 8-dim items), else 8.
+// Returns the max |K mean| of the thread's items.
 template <typename S>
 __device__ __forceinline__ float region_means_kq(const uint16_t* sK, const uint16_t* sQ,
                                                  double* sKbar, double* sQbar) {
-    constexpr int NHR = S::HG * S::R, NI = 2 * NHR * 4;
+    constexpr int NHR = S::HG * S::R;
+    constexpr int DPI = 2 * NHR * (kHeadDim / 4) <= kImgThreads ? 4 : 8;
+    constexpr int IPR = kHeadDim / DPI, NI = 2 * NHR * IPR;
     float mx = 0.f;
 #pragma unroll
     for (int u = 0; u < (NI + kImgThreads - 1) / kImgThreads; ++u) {
         const int item = threadIdx.x + u * kImgThreads;
         if (item < NI) {
-            const int o = item & 3, rest = item >> 2;
+            const int o = item % IPR, rest = item / IPR;
             const int tensor = rest >= NHR ? 1 : 0, hs = rest - tensor * NHR;
             const int hl = hs / S::R, s = hs - hl * S::R;
-            const uint16_t* src = (tensor ? sQ : sK) + hl * kHeadDim + 8 * o;
-            double acc[8] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
+            const uint16_t* src = (tensor ? sQ : sK) + hl * kHeadDim + DPI * o;
+            double acc[DPI];
+#pragma unroll
+            for (int e = 0; e < DPI; ++e) acc[e] = 0.0;
 #pragma unroll
             for (int uu = 0; uu < S::T; ++uu) {
-                const uint4 x = *reinterpret_cast<const uint4*>(src + region_kofs<S>(s, uu));
-                acc[0] += bf16lo(x.x);
-                acc[1] += bf16hi(x.x);
-                acc[2] += bf16lo(x.y);
-                acc[3] += bf16hi(x.y);
-                acc[4] += bf16lo(x.z);
-                acc[5] += bf16hi(x.z);
-                acc[6] += bf16lo(x.w);
-                acc[7] += bf16hi(x.w);
-            }
-            double* dst = (tensor ? sQbar : sKbar) + (hl * S::R + s) * S::QS + 8 * o;
+                uint32_t x[DPI / 2];
+                if constexpr (DPI == 8) {
+                    const uint4 v4 = *reinterpret_cast<const uint4*>(src + region_kofs<S>(s, uu));
+                    x[0] = v4.x;
+                    x[1] = v4.y;
+                    x[2] = v4.z;
+                    x[3] = v4.w;
+                } else {
+                    const uint2 v2 = *reinterpret_cast<const uint2*>(src + region_kofs<S>(s, uu));
+                    x[0] = v2.x;
+                    x[1] = v2.y;
+                }
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
+                for (int e = 0; e < DPI / 2; ++e) {
+                    acc[2 * e] += bf16lo(x[e]);
+                    acc[2 * e + 1] += bf16hi(x[e]);
+                }
+            }
+            double* dst = (tensor ? sQbar : sKbar) + (hl * S::R + s) * S::QS + DPI * o;
+#pragma unroll
+            for (int e = 0; e < DPI; ++e) {
                 const double m = mean_of(acc[e], S::T);
                 dst[e] = m;
                 if (!tensor) mx = fmaxf(mx, static_cast<float>(fabs(m)));
