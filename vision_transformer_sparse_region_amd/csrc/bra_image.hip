@@ -4,9 +4,9 @@
 // (page keys in bra_device.h).
 //
 // A workgroup of 16 waves owns image b and heads hg*HG .. hg*HG + HG - 1:
-//   1  every load at once, into registers: the group's K slice of the whole
-//      map, the Q operands of the wave's jobs, the V slice and the LePE
-//      weights; K and Q go to LDS token-major as they arrive   [P5 §五 ⑤]
+//   1  the group's K slice of the whole map and the Q operands of the
+//      wave's jobs, all at once into registers, then to LDS token-major as
+//      they arrive; the V slice loads once they are in     [P5 §五 ⑤]
 //   2  the K and Q region means: slot-order fp64 sums of the staged K and Q
 //      (the oracle's operations)            [P4 §1.2; P2 §2.1; P5 §五 ③]
 //   3  routing, four lanes per query row: the fp64 MFMA forms the affinities
@@ -572,7 +572,7 @@ __device__ __forceinline__ void image_body(
     const int st = ROUTED ? tid : tid - 64 * S::PASSES;
     uint4 vreg[4];
     unsigned vvalid = 0;
-    if (ROUTED || w >= S::PASSES) vvalid = load_vtask<S>(v, img, st, vreg);
+    if constexpr (ROUTED) vvalid = load_vtask<S>(v, img, st, vreg);
     int rid[ROUTED ? S::RI : 1];
     if constexpr (ROUTED) {
 #pragma unroll
@@ -619,6 +619,13 @@ __device__ __forceinline__ void image_body(
         }
     }
     lds_barrier();
+
+    // Where this kernel routes, the V loads go out now, once K and Q are in:
+    // issued with them, they shared the HBM bandwidth that the means and the
+    // routing wait on; from here they arrive during the means
+    if constexpr (!ROUTED) {
+        if (w >= S::PASSES) vvalid = load_vtask<S>(v, img, st, vreg);
+    }
 
     // 2. the region means (or the caller's routing)
     if constexpr (!ROUTED) {
