@@ -754,7 +754,8 @@ __device__ __forceinline__ void qmean_partial(const Params& p, const WaveJobs& J
     const int grp = w - (w / J.G) * J.G;
     const int qt0 = grp * J.tpg, nq = min(J.tpg, J.QT - qt0);
     double* dst = sQp + w * kHeadDim + 8 * g;
-    // one dim at a time (the K means are in flight in most of the registers)
+    // the lane's sums of its 8 dims over its tiles
+    double sd[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         double acc = 0.0;
@@ -766,10 +767,27 @@ __device__ __forceinline__ void qmean_partial(const Params& p, const WaveJobs& J
             acc += in ? static_cast<double>(__uint_as_float(static_cast<uint32_t>(u[e]) << 16))
                       : 0.0;
         }
-        acc = row16_sum_exact(acc);
-        if (li == 0) dst[e] = acc;
-        __builtin_amdgcn_sched_barrier(0);
+        sd[e] = acc;
     }
+    // A reduce-scatter over the row's 16 lanes: each step adds the DPP
+    // partner's half of the dims this lane keeps (partners 15 - li, then
+    // 7 - li within each half, li ^ 2, li ^ 1), 8 additions in all instead
+    // of 4 per dim; lane li ends with dim 4 [li >= 8] + 2 [li & 4] + [li & 2].
+    const bool ha = li >= 8, hb = (li & 4) != 0, hc = (li & 2) != 0;
+    double a[4], bb[2];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const double send = ha ? sd[j] : sd[4 + j];
+        a[j] = (ha ? sd[4 + j] : sd[j]) + dpp_f64<0x140>(send);
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const double send = hb ? a[j] : a[2 + j];
+        bb[j] = (hb ? a[2 + j] : a[j]) + dpp_f64<0x141>(send);
+    }
+    double c = (hc ? bb[1] : bb[0]) + dpp_f64<0x4E>(hc ? bb[0] : bb[1]);
+    c += dpp_f64<0xB1>(c);
+    if ((li & 1) == 0) dst[4 * ha + 2 * hb + hc] = c;
 }
 
 
