@@ -38,6 +38,10 @@ KERNEL_SOURCES = {
 PROFILES = os.path.join(ROOT, "profiles")
 COPY_BYTES = 512 << 20  # size of the calibration copy (read and written once each)
 COPY_REPS = 5
+# the embedded workloads of the benchmark table: at least this many timed and
+# untimed steps
+CONFIG_MIN_STEPS = 200
+CONFIG_MIN_WARMUP = 50
 
 
 def _code_only(text: str) -> str:
@@ -517,15 +521,23 @@ def main(argv=None) -> int:
     }
     if "graph" in res:
         line["graph"] = res["graph"]
-    # the other workloads of the benchmark table, the same variant and steps
+    # the other workloads of the benchmark table, the same variant, timed over
+    # at least CONFIG_MIN_STEPS steps after at least CONFIG_MIN_WARMUP untimed
+    # ones: a few warm-up forwards of the shorter workloads leave the core
+    # clock below its loaded rate (the high-res attention ran ~10% slower)
     if not args.no_all_configs:
         configs = {}
+        cargs = argparse.Namespace(**vars(args))
+        cargs.steps = max(args.steps, CONFIG_MIN_STEPS)
+        cargs.warmup = max(args.warmup, CONFIG_MIN_WARMUP)
         for name in ALL_WORKLOADS:
             if name == args.workload:
                 continue
-            r = measure(WORKLOADS[name], args, want_graph=False)
+            r = measure(WORKLOADS[name], cargs, want_graph=False)
             configs[name] = {k: r[k] for k in ("description", "ms_per_step", "value", "unit",
                                               "dtype", "kernel_ms", "roofline")}
+            configs[name]["steps"] = cargs.steps
+            configs[name]["warmup"] = cargs.warmup
             configs[name]["roofline"] = dict(r["roofline"])
             configs[name]["roofline"]["traffic"] = \
                 stored_traffic(name, r["roofline"]["kernel"]) if plain else None

@@ -762,7 +762,8 @@ __device__ __forceinline__ void qmean_partial(const Params& p, const WaveJobs& J
 #pragma unroll
         for (int jq = 0; jq < kMaxQTiles; ++jq) {
             // tiles past the job's and slots past the window hold duplicates
-            const bool in = jq < nq && (qt0 + jq) * 16 + li < p.t;
+            // (no slot is past the window when it is a whole number of tiles)
+            const bool in = jq < nq && (p.t % 16 == 0 || (qt0 + jq) * 16 + li < p.t);
             const u16x8_t u = __builtin_bit_cast(u16x8_t, qb[jq]);
             acc += in ? static_cast<double>(__uint_as_float(static_cast<uint32_t>(u[e]) << 16))
                       : 0.0;
