@@ -4,6 +4,7 @@
     python bench_profile.py traffic  <fetch_dir> <write_dir> <req_dir> <workload>
                                      "<fetch cmd>" "<write cmd>" "<req cmd>"
     python bench_profile.py counters <sq1_dir> <sq2_dir> <workload> "<cmd 1>" "<cmd 2>"
+    python bench_profile.py l2       <l2_dir> <workload> "<command>"
 
 `stats` reads <trace_dir>/run_kernel_stats.csv (rocprofv3 --kernel-trace
 --stats -f csv -o run) and writes profiles/kernels_<workload>_stats.md.
@@ -16,6 +17,13 @@ are known (bench.COPY_BYTES read and written); the request sizes give the
 read bytes a second way, as a check of that scale on the kernel's own request
 mix.  The per-dispatch figures of the workload's dominant kernel go to
 profiles/<kernel>_<workload>_traffic.md with the hash of its sources.
+
+`l2` reads one counter run of the L1-to-L2 and L2 request counters
+(TCP_TCC_READ_REQ, TCP_TCC_WRITE_REQ, TCC_REQ, TCC_HIT, TCC_MISS, each summed
+over the chip) of `bench.py --copy-calibration` and writes, per kernel, the
+requests per launch and the L1-to-L2 read bytes they stand for (scaled by the
+calibration copy's bytes per read request) against the kernel's algorithmic
+read bytes, to profiles/<kernel>_<workload>_l2.md.
 
 `counters` reads two SQ counter runs and writes, per kernel, the instruction
 mix per wave, the VALU and MFMA busy fractions, the share of wave time spent
@@ -234,6 +242,73 @@ def write_counters(sq1_dir: str, sq2_dir: str, workload: str, cmd1: str, cmd2: s
     return out
 
 
+L2_COUNTERS = ("TCP_TCC_READ_REQ_sum", "TCP_TCC_WRITE_REQ_sum", "TCC_REQ_sum", "TCC_HIT_sum",
+               "TCC_MISS_sum")
+
+
+def write_l2(l2_dir: str, workload: str, command: str) -> str:
+    from vision_transformer_sparse_region_amd.workloads import WORKLOADS
+    wl = WORKLOADS[workload]
+    kernel = bench.kernel_name(wl)
+    vals = {c: counter_means(l2_dir, c)[0] for c in L2_COUNTERS}
+    rd = vals["TCP_TCC_READ_REQ_sum"]
+    if "copy" not in rd:
+        raise SystemExit("the calibration copy kernel is missing from the counter run")
+    # the copy reads COPY_BYTES once: bytes per L1-to-L2 read request
+    bpr = bench.COPY_BYTES / rd["copy"]
+    alg = bench.algorithmic_bytes(wl)["attend"]
+    # algorithmic reads: the kernel's bytes less its output (S) and routing ids (I)
+    out_bytes = wl.tokens * wl.channels * (2 if wl.dtype == "bf16" else 4)
+    ids = wl.batch * wl.num_heads * wl.regions * wl.topk_effective * 4
+    alg_read = alg - out_bytes - ids
+    per = {}
+    for k in rd:
+        if k == "copy":
+            continue
+        per[k] = {c: vals[c].get(k) for c in L2_COUNTERS}
+        # a request moves 64 or 128 bytes (the copy's are all 128): the two
+        # bounds of the bytes behind a kernel's requests
+        per[k]["l1_to_l2_read_bytes"] = rd[k] * bpr
+        per[k]["l1_to_l2_read_bytes_at_64"] = rd[k] * 64
+    rec = {"workload": workload, "kernel": kernel,
+           "kernel_source_sha256_16": bench.kernel_source_hash(kernel),
+           "copy_bytes": bench.COPY_BYTES, "copy_read_requests": rd["copy"],
+           "bytes_per_read_request": bpr, "algorithmic_read_bytes": alg_read,
+           "l2_read_amplification": per[kernel]["l1_to_l2_read_bytes"] / alg_read,
+           "l2_read_amplification_at_64": per[kernel]["l1_to_l2_read_bytes_at_64"] / alg_read,
+           "kernels": per}
+    lines = [f"# L2 requests per launch, workload `{workload}`, kernel `{kernel}`", "",
+             "L1-to-L2 read and write requests (TCP_TCC_*_REQ) and L2 requests, hits and misses",
+             "(TCC_*), summed over the chip, per dispatch.  A read request moves 64 or 128 bytes;",
+             f"the calibration copy's are all {bpr:.0f} bytes (it reads {bench.COPY_BYTES >> 20} MiB once).  The read bytes",
+             "are given at 128 bytes a request (an upper bound) and at 64 (a lower bound); the",
+             "amplification is those bytes over the kernel's algorithmic reads (its compulsory",
+             "bytes less the output and the routing ids): the bytes its CUs pull from L2 for",
+             "each byte the method must read.", "",
+             "Command (from the repository root):", "", "```", command, "```", "",
+             "| kernel | L1-to-L2 read req | write req | L2 req | L2 hit | L2 miss | "
+             "L1-to-L2 read MB (128 / 64 B a request) |",
+             "|---|---|---|---|---|---|---|"]
+    for k, v in per.items():
+        lines.append(f"| {k} | {v['TCP_TCC_READ_REQ_sum'] or 0:.0f} | "
+                     f"{v['TCP_TCC_WRITE_REQ_sum'] or 0:.0f} | {v['TCC_REQ_sum'] or 0:.0f} | "
+                     f"{v['TCC_HIT_sum'] or 0:.0f} | {v['TCC_MISS_sum'] or 0:.0f} | "
+                     f"{v['l1_to_l2_read_bytes'] / 1e6:.2f} / "
+                     f"{v['l1_to_l2_read_bytes_at_64'] / 1e6:.2f} |")
+    lines += ["", f"Copy calibration: {rd['copy']:.0f} read requests for "
+              f"{bench.COPY_BYTES >> 20} MiB, {bpr:.1f} bytes a request.", "",
+              f"`{kernel}`: {per[kernel]['l1_to_l2_read_bytes_at_64'] / 1e6:.2f} to "
+              f"{per[kernel]['l1_to_l2_read_bytes'] / 1e6:.2f} MB from L2 against "
+              f"{alg_read / 1e6:.2f} MB of algorithmic reads, "
+              f"{rec['l2_read_amplification_at_64']:.2f}x to {rec['l2_read_amplification']:.2f}x.",
+              "", "```json", json.dumps(rec, indent=1), "```", ""]
+    out = os.path.join(bench.PROFILES, f"{kernel}_{workload}_l2.md")
+    os.makedirs(bench.PROFILES, exist_ok=True)
+    with open(out, "w") as f:
+        f.write("\n".join(lines))
+    return out
+
+
 def main(argv):
     if len(argv) >= 4 and argv[0] == "stats":
         print(write_stats(argv[1], argv[2], argv[3]))
@@ -241,6 +316,8 @@ def main(argv):
         print(write_traffic(*argv[1:8]))
     elif len(argv) >= 6 and argv[0] == "counters":
         print(write_counters(*argv[1:6]))
+    elif len(argv) >= 4 and argv[0] == "l2":
+        print(write_l2(*argv[1:4]))
     else:
         print(__doc__, file=sys.stderr)
         return 2
